@@ -1,0 +1,22 @@
+"""fp64 CPU oracle for the IPA forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` and by nothing on the product
+path. Independent of the HIP library: no shared kernels, headers, helpers or
+constants.
+
+Pinning status of each function (see the tests under ``tests/``):
+  ipa_forward     pinned: textbook-attention reduction (library SDPA), MEET
+                  lifting identity through library SDPA, SE(3) invariance,
+                  L = 1 and two-residue closed forms, uniform-attention pair
+                  closed form, permutation equivariance, mask semantics.
+  ipa_bruteforce  pinned against the same closed forms on tiny inputs.
+  ipa_lifted      pinned to ipa_forward (exact algebra, 1e-12 relative).
+"""
+
+from .ipa_oracle import ipa_forward, ipa_logits, to_global
+from .bruteforce import ipa_bruteforce
+from .lifted import ipa_lifted, block_centres
+
+__all__ = ["ipa_forward", "ipa_logits", "to_global", "ipa_bruteforce",
+           "ipa_lifted", "block_centres"]

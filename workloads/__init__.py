@@ -1,0 +1,195 @@
+"""Seeded synthetic inputs for invariant point attention (IPA) workloads.
+
+This module only draws and shapes random inputs. It holds none of the
+attention arithmetic, so both the fp64 oracle and the GPU path can take
+their inputs from it without sharing any of the method.
+
+Input recipe (one ``numpy.random.default_rng(seed)`` per call, draws in a
+fixed order: quaternions, chain steps, q, k, v, q_pts, k_pts, v_pts, z1, z2,
+gamma logits, pair-bias weights, lengths, padding garbage):
+
+* rotations: a Gaussian quaternion normalised to unit length, turned into a
+  rotation matrix that maps local column vectors to the global frame
+  (Haar-uniform on SO(3));
+* translations: a chain that starts at the origin and takes steps of fixed
+  length (3.8 A for protein-like chains, 5.9 A for RNA-like ones) in
+  uniformly random directions, then is centred on its mean;
+* per-head scalars and local points ~ N(0, 1);
+* pair factors z1, z2 ~ N(0, 1) / sqrt(c_z) (standard deviation 1/sqrt(c_z));
+* gamma = softplus(N(0, 1)) per head, pair-bias weights W_b ~ N(0, 1);
+* ragged batches: true lengths uniform in [lo, hi], a prefix validity mask,
+  and padded rows filled with finite garbage (N(0, 10^2) features,
+  non-orthogonal N(0, 1) "rotations", translations uniform in +-1e3).
+
+For the bf16-storage workloads every per-residue feature tensor (q, k, v,
+points, z1, z2) is rounded to bfloat16 (round to nearest even) here, before
+either side sees it; frames, W_b and gamma stay float32.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, asdict
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class IPAWorkload:
+    name: str
+    B: int
+    L: int
+    H: int
+    C: int = 16
+    Pqk: int = 4
+    Pv: int = 8
+    R: int = 2
+    Cz: int = 128
+    dtype: str = "bf16"          # storage of q, k, v, points, z1, z2
+    step: float = 3.8            # chain step length in Angstrom
+    ragged: tuple | None = None  # (lo, hi) true lengths, prefix mask
+    seed: int = 0
+
+    def dims(self) -> dict:
+        return dict(B=self.B, L=self.L, H=self.H, C=self.C, Pqk=self.Pqk,
+                    Pv=self.Pv, R=self.R, Cz=self.Cz)
+
+    def with_(self, **kw) -> "IPAWorkload":
+        d = asdict(self)
+        d.update(kw)
+        return IPAWorkload(**d)
+
+
+# The five workload families the method is measured on.
+WORKLOADS = {
+    "tiny_fp32": IPAWorkload("tiny_fp32", B=1, L=64, H=12, Cz=16, dtype="fp32"),
+    "single_chain": IPAWorkload("single_chain", B=1, L=512, H=12, Cz=128),
+    "long_chain_2048": IPAWorkload("long_chain_2048", B=1, L=2048, H=12, Cz=128),
+    "long_chain_4096": IPAWorkload("long_chain_4096", B=1, L=4096, H=12, Cz=128),
+    "ragged_batch": IPAWorkload("ragged_batch", B=32, L=128, H=8, Cz=64,
+                                step=5.9, ragged=(40, 128)),
+    "very_long_8192": IPAWorkload("very_long_8192", B=1, L=8192, H=8, Cz=128),
+    "very_long_16384": IPAWorkload("very_long_16384", B=1, L=16384, H=8, Cz=128),
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32).reshape(a.shape)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of float32 values that are already bf16-representable."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _quat_to_rot(u: np.ndarray) -> np.ndarray:
+    u = u / np.linalg.norm(u, axis=-1, keepdims=True)
+    w, x, y, z = u[..., 0], u[..., 1], u[..., 2], u[..., 3]
+    R = np.empty(u.shape[:-1] + (3, 3), dtype=np.float64)
+    R[..., 0, 0] = 1 - 2 * (y * y + z * z)
+    R[..., 0, 1] = 2 * (x * y - w * z)
+    R[..., 0, 2] = 2 * (x * z + w * y)
+    R[..., 1, 0] = 2 * (x * y + w * z)
+    R[..., 1, 1] = 1 - 2 * (x * x + z * z)
+    R[..., 1, 2] = 2 * (y * z - w * x)
+    R[..., 2, 0] = 2 * (x * z - w * y)
+    R[..., 2, 1] = 2 * (y * z + w * x)
+    R[..., 2, 2] = 1 - 2 * (x * x + y * y)
+    return R
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def default_weights(Pqk: int) -> tuple[float, float]:
+    """Default logit weights w_L = sqrt(1/3), w_C = sqrt(2 / (9 Pqk))."""
+    return math.sqrt(1.0 / 3.0), math.sqrt(2.0 / (9.0 * Pqk))
+
+
+def make_inputs(w: IPAWorkload, seed: int | None = None) -> dict:
+    """Draw one seeded input set for workload ``w``.
+
+    Returns a dict of numpy arrays: float32 features (bf16-representable for
+    bf16 workloads), float32 frames, uint8 mask, plus scalars and metadata.
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    B, L, H, C, Pqk, Pv, R, Cz = w.B, w.L, w.H, w.C, w.Pqk, w.Pv, w.R, w.Cz
+
+    quat = rng.standard_normal((B, L, 4))
+    steps = rng.standard_normal((B, L, 3))
+    q = rng.standard_normal((B, L, H, C))
+    k = rng.standard_normal((B, L, H, C))
+    v = rng.standard_normal((B, L, H, C))
+    q_pts = rng.standard_normal((B, L, H, Pqk, 3))
+    k_pts = rng.standard_normal((B, L, H, Pqk, 3))
+    v_pts = rng.standard_normal((B, L, H, Pv, 3))
+    z1 = rng.standard_normal((B, L, R, Cz)) / math.sqrt(Cz)
+    z2 = rng.standard_normal((B, L, R, Cz)) / math.sqrt(Cz)
+    gamma = _softplus(rng.standard_normal(H))
+    w_b = rng.standard_normal((Cz, H))
+
+    if w.ragged is not None:
+        lo, hi = w.ragged
+        lengths = rng.integers(lo, hi + 1, size=B)
+    else:
+        lengths = np.full(B, L, dtype=np.int64)
+
+    rot = _quat_to_rot(quat)
+    trans = np.zeros((B, L, 3))
+    mask = np.zeros((B, L), dtype=np.uint8)
+    for b in range(B):
+        n = int(lengths[b])
+        mask[b, :n] = 1
+        g = steps[b, :n]
+        g = g / np.linalg.norm(g, axis=-1, keepdims=True)
+        x = np.zeros((n, 3))
+        if n > 1:
+            x[1:] = np.cumsum(w.step * g[1:], axis=0)
+        trans[b, :n] = x - x.mean(axis=0)
+
+    if w.ragged is not None:
+        # finite garbage in every padded row
+        pad = mask == 0
+        npad = int(pad.sum())
+        if npad:
+            def garb(shape):
+                return 10.0 * rng.standard_normal((npad,) + shape)
+            q[pad] = garb((H, C)); k[pad] = garb((H, C)); v[pad] = garb((H, C))
+            q_pts[pad] = garb((H, Pqk, 3)); k_pts[pad] = garb((H, Pqk, 3))
+            v_pts[pad] = garb((H, Pv, 3))
+            z1[pad] = garb((R, Cz)); z2[pad] = garb((R, Cz))
+            rot[pad] = rng.standard_normal((npad, 3, 3))
+            trans[pad] = rng.uniform(-1e3, 1e3, size=(npad, 3))
+
+    feats = dict(q=q, k=k, v=v, q_pts=q_pts, k_pts=k_pts, v_pts=v_pts, z1=z1, z2=z2)
+    for name, a in feats.items():
+        a32 = a.astype(np.float32)
+        feats[name] = round_to_bf16(a32) if w.dtype == "bf16" else a32
+
+    w_L, w_C = default_weights(Pqk)
+    out = dict(feats)
+    out.update(
+        rot=rot.astype(np.float32), trans=trans.astype(np.float32),
+        gamma=gamma.astype(np.float32), w_b=w_b.astype(np.float32),
+        mask=mask, lengths=lengths.astype(np.int64),
+        w_L=w_L, w_C=w_C, dtype=w.dtype, dims=w.dims(), workload=w.name,
+        has_mask=w.ragged is not None,
+    )
+    return out
+
+
+def stress_pair(inp: dict) -> dict:
+    """Pair-stress variant: z1, z2 rescaled to unit variance so that the pair
+    bias and pair output are O(1) and a pair-path error is visible."""
+    out = dict(inp)
+    Cz = inp["dims"]["Cz"]
+    for name in ("z1", "z2"):
+        a = inp[name].astype(np.float32) * np.float32(math.sqrt(Cz))
+        out[name] = round_to_bf16(a) if inp["dtype"] == "bf16" else a
+    return out
