@@ -1,0 +1,205 @@
+"""ctypes binding of the C ABI in include/ipa.h.
+
+Argument marshalling only: every step of the IPA forward runs in the HIP
+library. PyTorch provides device memory and the current stream. If the
+library is missing this module raises; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from pathlib import Path
+
+import torch
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = Path(os.environ.get("IPA_MI355_LIB", _PKG / "libipa_mi355.so"))
+
+IPA_F32 = 0
+IPA_BF16 = 1
+
+STATUS = {
+    0: "IPA_OK", -1: "IPA_ERR_NULL", -2: "IPA_ERR_DIMS", -3: "IPA_ERR_DTYPE",
+    -4: "IPA_ERR_WORKSPACE", -5: "IPA_ERR_ALIGN", -6: "IPA_ERR_UNSUPPORTED",
+    -7: "IPA_ERR_HIP", -8: "IPA_ERR_ARG",
+}
+
+
+class IpaDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "H", "C", "Pqk", "Pv", "R", "Cz")]
+
+
+class IPAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
+    """Load (once) and return the HIP library; raise if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(
+            f"IPA HIP library not found at {p}; build it with "
+            "`python -m geometric_invariant_attention_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    lib.ipa_workspace_bytes.argtypes = [ctypes.POINTER(IpaDims), i32]
+    lib.ipa_workspace_bytes.restype = sz
+    for fn in (lib.ipa_forward, lib.ipa_lift, lib.ipa_attend):
+        fn.argtypes = [ctypes.POINTER(IpaDims), i32] + [vp] * 13 + [f32, f32] + [vp] * 5 + [sz, vp]
+        fn.restype = i32
+    lib.ipa_status_string.argtypes = [i32]
+    lib.ipa_status_string.restype = ctypes.c_char_p
+    lib.ipa_version.argtypes = []
+    lib.ipa_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ipa_status_string(status).decode()
+
+
+def make_dims(B, L, H, C, Pqk, Pv, R, Cz) -> IpaDims:
+    return IpaDims(B, L, H, C, Pqk, Pv, R, Cz)
+
+
+def workspace_bytes(dims: dict | IpaDims, dtype: int) -> int:
+    d = dims if isinstance(dims, IpaDims) else IpaDims(**dims)
+    return int(load_library().ipa_workspace_bytes(ctypes.byref(d), int(dtype)))
+
+
+def default_weights(Pqk: int) -> tuple[float, float]:
+    return math.sqrt(1.0 / 3.0), math.sqrt(2.0 / (9.0 * Pqk))
+
+
+def _dev_ptr(t: torch.Tensor | None) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _prep(t: torch.Tensor, dtype: torch.dtype, device, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous() or t.data_ptr() % 16 != 0:
+        t = t.contiguous() if not t.is_contiguous() else t.clone()
+    return t
+
+
+class IPAForward:
+    """Reusable forward plan: validated shapes, preallocated workspace and
+    outputs on one device. ``__call__`` enqueues one forward on the current
+    stream and returns the output dict (the same tensors on every call)."""
+
+    def __init__(self, B, L, H, C, Pqk, Pv, R, Cz, dtype=torch.bfloat16, device=None):
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("dtype must be torch.bfloat16 or torch.float32")
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.dims = IpaDims(B, L, H, C, Pqk, Pv, R, Cz)
+        self.shape = dict(B=B, L=L, H=H, C=C, Pqk=Pqk, Pv=Pv, R=R, Cz=Cz)
+        self.dtype = dtype
+        self.code = IPA_BF16 if dtype == torch.bfloat16 else IPA_F32
+        self.lib = load_library()
+        self.ws_bytes = int(self.lib.ipa_workspace_bytes(ctypes.byref(self.dims), self.code))
+        if self.ws_bytes == 0:
+            raise IPAError(-6, f"unsupported dims {self.shape} for {dtype}")
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.out = {
+            "s": torch.empty(B, L, H, C, **f32),
+            "pts": torch.empty(B, L, H, Pv, 3, **f32),
+            "pts_norm": torch.empty(B, L, H, Pv, **f32),
+            "pair": torch.empty(B, L, H, Cz, **f32),
+        }
+
+    def bind(self, q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma,
+             mask=None, w_L=None, w_C=None, stream=None) -> tuple:
+        """Validate the tensors once and return the raw argument tuple of the
+        C entry points (tensors that needed a contiguous copy are kept alive
+        in ``self.bound``)."""
+        s = self.shape
+        B, L, H, C, Pqk, Pv, R, Cz = (s[n] for n in ("B", "L", "H", "C", "Pqk", "Pv", "R", "Cz"))
+        dev, dt = self.device, self.dtype
+        expect = {
+            "q": (B, L, H, C), "k": (B, L, H, C), "v": (B, L, H, C),
+            "q_pts": (B, L, H, Pqk, 3), "k_pts": (B, L, H, Pqk, 3), "v_pts": (B, L, H, Pv, 3),
+            "z1": (B, L, R, Cz), "z2": (B, L, R, Cz),
+            "rot": (B, L, 3, 3), "trans": (B, L, 3), "w_b": (Cz, H), "gamma": (H,),
+        }
+        args = dict(q=q, k=k, v=v, q_pts=q_pts, k_pts=k_pts, v_pts=v_pts, z1=z1, z2=z2,
+                    rot=rot, trans=trans, w_b=w_b, gamma=gamma)
+        for name, shp in expect.items():
+            t = args[name]
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+            want = dt if name in ("q", "k", "v", "q_pts", "k_pts", "v_pts", "z1", "z2") else torch.float32
+            args[name] = _prep(t, want, dev, name)
+        m = None
+        if mask is not None:
+            if tuple(mask.shape) != (B, L):
+                raise ValueError(f"mask has shape {tuple(mask.shape)}, expected {(B, L)}")
+            if mask.device != dev:
+                raise ValueError(f"mask is on {mask.device}, expected {dev}")
+            m = mask.to(torch.uint8) if mask.dtype != torch.uint8 else mask
+            m = m.contiguous()
+        dwL, dwC = default_weights(Pqk)
+        w_L = dwL if w_L is None else float(w_L)
+        w_C = dwC if w_C is None else float(w_C)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        o = self.out
+        self.bound = (args, m)
+        return (ctypes.byref(self.dims), self.code,
+                *(_dev_ptr(args[n]) for n in ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot",
+                                              "trans", "z1", "z2", "w_b", "gamma")),
+                _dev_ptr(m), ctypes.c_float(w_L), ctypes.c_float(w_C),
+                o["s"].data_ptr(), o["pts"].data_ptr(), o["pts_norm"].data_ptr(), o["pair"].data_ptr(),
+                self.workspace.data_ptr(), ctypes.c_size_t(self.ws_bytes),
+                ctypes.c_void_p(stream.cuda_stream))
+
+    def _call(self, fn, raw: tuple) -> None:
+        rc = fn(*raw)
+        if rc != 0:
+            raise IPAError(rc, status_string(rc))
+
+    def forward_raw(self, raw: tuple) -> dict:
+        self._call(self.lib.ipa_forward, raw)
+        return self.out
+
+    def lift_raw(self, raw: tuple) -> None:
+        self._call(self.lib.ipa_lift, raw)
+
+    def attend_raw(self, raw: tuple) -> dict:
+        self._call(self.lib.ipa_attend, raw)
+        return self.out
+
+    def __call__(self, *args, **kw) -> dict:
+        return self.forward_raw(self.bind(*args, **kw))
+
+
+def ipa_forward(q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma,
+                mask=None, w_L=None, w_C=None) -> dict:
+    """One IPA forward on the device of ``q``; returns freshly allocated
+    float32 outputs {"s", "pts", "pts_norm", "pair"}."""
+    B, L, H, C = q.shape
+    Pqk, Pv = q_pts.shape[3], v_pts.shape[3]
+    R, Cz = z1.shape[2], z1.shape[3]
+    plan = IPAForward(B, L, H, C, Pqk, Pv, R, Cz, dtype=q.dtype, device=q.device)
+    out = plan(q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma,
+               mask=mask, w_L=w_L, w_C=w_C)
+    return out

@@ -1,0 +1,157 @@
+// Host side of the C ABI declared in include/ipa.h: argument validation,
+// workspace layout and the two launches (lift, fused attention) on the
+// caller's stream. Nothing is launched unless every check passes.
+
+#include "../../include/ipa.h"
+#include "ipa_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace ipa {
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool make_layout(const int32_t d[8], int esize, Layout* o) {
+  const int64_t B = d[0], L = d[1], H = d[2], C = d[3], Pqk = d[4], Pv = d[5], R = d[6], Cz = d[7];
+  if (B < 1 || L < 1 || H < 1 || C < 1 || Pqk < 1 || Pv < 1 || R < 1 || Cz < 1) return false;
+  if (C > kCSlot || Pv > kPvSlot || kCSlot + 9 * Pqk > kHeadW) return false;
+  if (Cz % 8 != 0 || Cz > 128 || R * Cz > kMaxD - kHeadW) return false;
+  const int64_t Lp = (L + kTileM - 1) / kTileM * kTileM;
+  if (B * H * Lp >= (int64_t(1) << 31) || B * L * R * Cz >= (int64_t(1) << 31)) return false;
+  const int64_t PW = (R * Cz + 63) / 64 * 64;
+  Layout& ly = *o;
+  ly.B = (int)B; ly.L = (int)L; ly.H = (int)H; ly.C = (int)C; ly.Pqk = (int)Pqk;
+  ly.Pv = (int)Pv; ly.R = (int)R; ly.Cz = (int)Cz;
+  ly.Lp = (int)Lp; ly.nJ = (int)(Lp / kTileN); ly.PW = (int)PW; ly.D = (int)(kHeadW + PW);
+  ly.esize = esize;
+  if (esize == 4 && ly.D > kMaxDF32) return false;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  const size_t es = (size_t)esize;
+  ly.off_qh = take((size_t)B * H * Lp * kHeadW * es);
+  ly.off_kh = take((size_t)B * H * Lp * kHeadW * es);
+  ly.off_kz = take((size_t)B * ly.nJ * PW * kTileN * es);
+  ly.off_vth = take((size_t)B * H * ly.nJ * kHeadW * kTileN * es);
+  ly.off_vtz = take((size_t)B * ly.nJ * PW * kTileN * es);
+  ly.off_kcol = take((size_t)B * H * Lp * 16);
+  ly.off_qrow = take((size_t)B * H * Lp * 16);
+  ly.off_cen = take((size_t)B * ly.nJ * 16);
+  ly.off_wbt = take((size_t)H * Cz * 4);
+  ly.total = off;
+  return true;
+}
+
+}  // namespace ipa
+
+namespace {
+
+bool valid_dims_struct(const ipa_dims* d, int32_t out[8]) {
+  if (!d) return false;
+  out[0] = d->B; out[1] = d->L; out[2] = d->H; out[3] = d->C;
+  out[4] = d->Pqk; out[5] = d->Pv; out[6] = d->R; out[7] = d->Cz;
+  return true;
+}
+
+bool basic_dims_ok(const int32_t v[8]) {
+  for (int e = 0; e < 8; ++e)
+    if (v[e] < 1) return false;
+  return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+namespace {
+
+enum Stage { kLift = 1, kAttend = 2, kBoth = 3 };
+
+int32_t run(int stages, const ipa_dims* dims, int32_t dtype,
+            const void* q, const void* k, const void* v,
+            const void* q_pts, const void* k_pts, const void* v_pts,
+            const float* rot, const float* trans,
+            const void* z1, const void* z2,
+            const float* w_b, const float* gamma,
+            const uint8_t* mask,
+            float w_L, float w_C,
+            float* out_s, float* out_pts, float* out_pts_norm,
+            float* out_pair,
+            void* workspace, size_t workspace_bytes,
+            void* stream) {
+  int32_t dv[8];
+  if (!valid_dims_struct(dims, dv)) return IPA_ERR_NULL;
+  if (!basic_dims_ok(dv)) return IPA_ERR_DIMS;
+  if (dtype != IPA_F32 && dtype != IPA_BF16) return IPA_ERR_DTYPE;
+  const void* req[] = {q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma,
+                       out_s, out_pts, out_pts_norm, out_pair, workspace};
+  for (const void* p : req)
+    if (!p) return IPA_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return IPA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return IPA_ERR_ALIGN;
+  if (!std::isfinite(w_L) || !std::isfinite(w_C) || w_L < 0.f || w_C < 0.f) return IPA_ERR_ARG;
+
+  ipa::FwdArgs a;
+  const bool bf16 = dtype == IPA_BF16;
+  if (!ipa::make_layout(dv, bf16 ? 2 : 4, &a.lay)) return IPA_ERR_UNSUPPORTED;
+  if (workspace_bytes < a.lay.total) return IPA_ERR_WORKSPACE;
+
+  a.q = q; a.k = k; a.v = v; a.q_pts = q_pts; a.k_pts = k_pts; a.v_pts = v_pts;
+  a.rot = rot; a.trans = trans; a.z1 = z1; a.z2 = z2; a.w_b = w_b; a.gamma = gamma;
+  a.mask = mask; a.w_L = w_L; a.w_C = w_C;
+  a.out_s = out_s; a.out_pts = out_pts; a.out_pts_norm = out_pts_norm; a.out_pair = out_pair;
+  a.ws = static_cast<unsigned char*>(workspace);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((stages & kLift) && ipa::launch_lift(a, bf16, s) != hipSuccess) return IPA_ERR_HIP;
+  if ((stages & kAttend) && ipa::launch_attn(a, bf16, s) != hipSuccess) return IPA_ERR_HIP;
+  return IPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ipa_workspace_bytes(const ipa_dims* dims, int32_t dtype) {
+  int32_t v[8];
+  if (!valid_dims_struct(dims, v) || !basic_dims_ok(v)) return 0;
+  if (dtype != IPA_F32 && dtype != IPA_BF16) return 0;
+  ipa::Layout ly;
+  if (!ipa::make_layout(v, dtype == IPA_BF16 ? 2 : 4, &ly)) return 0;
+  return ly.total;
+}
+
+#define IPA_ARGS_DECL                                                               \
+  const ipa_dims *dims, int32_t dtype, const void *q, const void *k, const void *v, \
+      const void *q_pts, const void *k_pts, const void *v_pts, const float *rot,     \
+      const float *trans, const void *z1, const void *z2, const float *w_b,          \
+      const float *gamma, const uint8_t *mask, float w_L, float w_C, float *out_s,   \
+      float *out_pts, float *out_pts_norm, float *out_pair, void *workspace,         \
+      size_t workspace_bytes, void *stream
+#define IPA_ARGS_PASS                                                                \
+  dims, dtype, q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma, mask,   \
+      w_L, w_C, out_s, out_pts, out_pts_norm, out_pair, workspace, workspace_bytes, stream
+
+int32_t ipa_forward(IPA_ARGS_DECL) { return run(kBoth, IPA_ARGS_PASS); }
+int32_t ipa_lift(IPA_ARGS_DECL) { return run(kLift, IPA_ARGS_PASS); }
+int32_t ipa_attend(IPA_ARGS_DECL) { return run(kAttend, IPA_ARGS_PASS); }
+
+const char* ipa_status_string(int32_t status) {
+  switch (status) {
+    case IPA_OK: return "ok";
+    case IPA_ERR_NULL: return "a required pointer is NULL";
+    case IPA_ERR_DIMS: return "a dimension is < 1 or too large";
+    case IPA_ERR_DTYPE: return "dtype must be IPA_F32 or IPA_BF16";
+    case IPA_ERR_WORKSPACE: return "workspace is smaller than ipa_workspace_bytes()";
+    case IPA_ERR_ALIGN: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
+    case IPA_ERR_UNSUPPORTED: return "dims outside the supported envelope";
+    case IPA_ERR_HIP: return "a HIP kernel launch failed";
+    case IPA_ERR_ARG: return "w_L and w_C must be finite and >= 0";
+    default: return "unknown status";
+  }
+}
+
+int32_t ipa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal declarations shared by the host entry points and the HIP kernels
+// of the fused IPA forward. Not part of the public ABI (include/ipa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ipa {
+
+// Key tile of the attention kernel and the residue block whose mean
+// translation centres the global points (the same 64 residues).
+constexpr int kTileN = 64;
+// Query rows per attention workgroup (4 waves x 32 rows).
+constexpr int kTileM = 128;
+// Width of the per-head part of a lifted row (scalar + point columns).
+constexpr int kHeadW = 64;
+// Largest supported lifted row width (head part + pair part).
+constexpr int kMaxD = 320;
+// Largest lifted row width of the float32 path.
+constexpr int kMaxDF32 = 192;
+// Scalar channels and value points are laid out in slots of these sizes.
+constexpr int kCSlot = 16;
+constexpr int kPvSlot = 8;
+// fp32 path: first column of the unscaled centred query points in a query
+// head row (key points start at kCSlot).
+constexpr int kFpQPts = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Byte layout of the caller-supplied workspace. Everything the attention
+// kernel reads is produced here by the lift kernel; sizes are linear in
+// B * L.
+struct Layout {
+  int B, L, H, C, Pqk, Pv, R, Cz;
+  int Lp;     // L rounded up to kTileM
+  int nJ;     // Lp / kTileN key tiles (= centring blocks)
+  int D;      // lifted row width: kHeadW + PW
+  int PW;     // pair part width: R * Cz rounded up to 64
+  int esize;  // bytes per lifted element (2 bf16, 4 fp32)
+  size_t off_qh;    // [B][H][Lp][kHeadW]        query head part
+  size_t off_kh;    // [B][H][Lp][kHeadW]        key head part
+  size_t off_kz;    // [B][nJ][PW/64][64][64]    key pair part (z2) in 64x64 panels, shared by heads
+  size_t off_vth;   // [B][H][nJ][kHeadW][64]    value head part, feature-major
+  size_t off_vtz;   // [B][nJ][PW][64]           value pair part (z2), feature-major
+  size_t off_kcol;  // [B][H][Lp] float4         per-key column terms
+  size_t off_qrow;  // [B][H][Lp] float4         per-query row terms
+  size_t off_cen;   // [B][nJ] float4            block centre xyz, valid count
+  size_t off_wbt;   // [H][Cz] float             w_L log2(e) W_b^T
+  size_t total;
+};
+
+// Returns false if the dims are outside the supported envelope.
+bool make_layout(const int32_t d[8], int esize, Layout* out);
+
+struct FwdArgs {
+  Layout lay;
+  const void* q; const void* k; const void* v;
+  const void* q_pts; const void* k_pts; const void* v_pts;
+  const float* rot; const float* trans;
+  const void* z1; const void* z2;
+  const float* w_b; const float* gamma;
+  const uint8_t* mask;
+  float w_L, w_C;
+  float* out_s; float* out_pts; float* out_pts_norm; float* out_pair;
+  unsigned char* ws;
+};
+
+// Kernel launchers (return the hipError_t of the launch).
+hipError_t launch_lift(const FwdArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_attn(const FwdArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace ipa

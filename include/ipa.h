@@ -1,0 +1,167 @@
+/*
+ * ipa.h -- C ABI of the fused invariant point attention (IPA) forward pass
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one call = one forward over a batch) follows
+ *   - "Flash Invariant Point Attention" (arXiv 2505.11580), TL;DR and
+ *     abstract: IPA over scalar, point and pair channels with a factorised
+ *     pair representation z_ij = sum_r z1_ir * z2_jr, lifted into one
+ *     softmax attention so that no L x L tensor is stored (linear memory);
+ *   - MEET ("Scalable peptide design with memory-efficient equivariant
+ *     transformers"), section 2.2, eq. 6-8: a squared point distance in the
+ *     logit is carried by augmented query and key columns;
+ *   - "Geometric direction-and-distance attention" (BioTorch), Required
+ *     behavior: frame convention (rotation maps local column vectors to the
+ *     global frame, translation is the origin), an edge is allowed when both
+ *     frames are valid, all-masked rows return exact zeros, and inputs are
+ *     never modified.
+ *
+ * Per head h, residues i (query) and j (key), with global points
+ * x_g = R x + t:
+ *   S_ijh  = w_L * ( q_ih.k_jh / sqrt(C) + sum_c Z_ijc W_b[c,h]
+ *                    - gamma_h * w_C / 2 * sum_p |T_i q_ihp - T_j k_jhp|^2 )
+ *   a_ijh  = softmax over allowed j
+ *   out_s[b,i,h,:]        = sum_j a v_jh
+ *   out_pts[b,i,h,p,:]    = R_i^T ( sum_j a (R_j v_jhp + t_j) - t_i )
+ *   out_pts_norm[b,i,h,p] = |out_pts[b,i,h,p,:]|        (no epsilon)
+ *   out_pair[b,i,h,:]     = sum_j a Z_ij,  Z_ij = sum_r z1_ir * z2_jr
+ * Rows whose own mask entry is 0 get +0.0 in every output.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous in
+ *     the shapes given below. They are owned by the caller; the library keeps
+ *     no reference after the call returns and never writes its inputs.
+ *   - Returns IPA_OK (0) or a negative status; see ipa_status_string().
+ *     Every argument is validated before anything is launched: on a negative
+ *     status nothing was written.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream). The library allocates no device memory: scratch space
+ *     is the caller's `workspace`, sized by ipa_workspace_bytes().
+ *   - Reentrant; no global mutable state. Calls that share a workspace must
+ *     be ordered on one stream.
+ */
+#ifndef IPA_MI355_H
+#define IPA_MI355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem dimensions.
+ *   B   batch size                    L   (padded) residues per batch element
+ *   H   heads                         C   scalar channels per head
+ *   Pqk query/key points per head     Pv  value points per head
+ *   R   rank of the factorised pair   Cz  pair channels
+ * Supported envelope: every dim >= 1, C <= 16, Pqk <= 5, Pv <= 8,
+ * Cz % 8 == 0, Cz <= 128, R * Cz <= 256 (bf16) or <= 128 (fp32),
+ * B * H * L < 2^31. Other shapes return IPA_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t B, L, H, C, Pqk, Pv, R, Cz;
+} ipa_dims;
+
+/* Storage type of q, k, v, q_pts, k_pts, v_pts, z1, z2.
+ * IPA_F32: float32 storage, float32 arithmetic throughout.
+ * IPA_BF16: bfloat16 storage, bf16 matrix-core products with float32
+ * accumulation (point coordinates carried as bf16 hi/lo pairs). Frames,
+ * w_b, gamma and every output are float32 for both. */
+typedef enum { IPA_F32 = 0, IPA_BF16 = 1 } ipa_dtype;
+
+enum {
+  IPA_OK = 0,
+  IPA_ERR_NULL = -1,        /* a required pointer is NULL                   */
+  IPA_ERR_DIMS = -2,        /* a dimension is < 1 or too large              */
+  IPA_ERR_DTYPE = -3,       /* dtype is not an ipa_dtype value              */
+  IPA_ERR_WORKSPACE = -4,   /* workspace_bytes < ipa_workspace_bytes(...)   */
+  IPA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned             */
+  IPA_ERR_UNSUPPORTED = -6, /* dims outside the supported envelope          */
+  IPA_ERR_HIP = -7,         /* a HIP launch failed                          */
+  IPA_ERR_ARG = -8          /* a scalar argument is not finite / negative   */
+};
+
+/* Bytes of device workspace that ipa_forward needs for these dims and dtype.
+ * Linear in B*L (no L x L term). Returns 0 if the dims are invalid or
+ * unsupported. */
+size_t ipa_workspace_bytes(const ipa_dims* dims, int32_t dtype);
+
+/* Fused IPA forward.
+ *   q, k, v   [B,L,H,C]        dtype storage
+ *   q_pts     [B,L,H,Pqk,3]    local query points, dtype storage
+ *   k_pts     [B,L,H,Pqk,3]    local key points, dtype storage
+ *   v_pts     [B,L,H,Pv,3]     local value points, dtype storage
+ *   rot       [B,L,3,3] float32, rot[b,l] maps local column vectors to global
+ *   trans     [B,L,3]   float32, global origin of each frame
+ *   z1, z2    [B,L,R,Cz]       pair factors, dtype storage
+ *   w_b       [Cz,H]    float32, pair-bias projection
+ *   gamma     [H]       float32, point weight per head (already positive)
+ *   mask      [B,L]     uint8, 1 = valid residue; NULL = all valid. An edge
+ *                       (i,j) is used when both mask entries are 1.
+ *   w_L, w_C  logit weights (finite, >= 0); the usual values are sqrt(1/3)
+ *             and sqrt(2 / (9 Pqk)).
+ *   out_s        [B,L,H,C]      float32
+ *   out_pts      [B,L,H,Pv,3]   float32
+ *   out_pts_norm [B,L,H,Pv]     float32
+ *   out_pair     [B,L,H,Cz]     float32
+ *   workspace    device scratch of at least ipa_workspace_bytes(dims, dtype)
+ *                bytes, 256-byte aligned; its contents on entry are ignored.
+ *   stream       hipStream_t to enqueue on.
+ * Every output element is overwritten. Padded rows may hold any finite
+ * values in every input; they never influence valid rows. */
+int32_t ipa_forward(const ipa_dims* dims, int32_t dtype,
+                    const void* q, const void* k, const void* v,
+                    const void* q_pts, const void* k_pts, const void* v_pts,
+                    const float* rot, const float* trans,
+                    const void* z1, const void* z2,
+                    const float* w_b, const float* gamma,
+                    const uint8_t* mask,
+                    float w_L, float w_C,
+                    float* out_s, float* out_pts, float* out_pts_norm,
+                    float* out_pair,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* The two stages of ipa_forward, for callers that time or schedule them
+ * separately. ipa_lift applies the frames and writes the lifted query/key/
+ * value operands into `workspace`; ipa_attend runs the fused attention and
+ * the output epilogue from that workspace. ipa_attend must follow an
+ * ipa_lift with identical arguments on the same stream (or after it has
+ * completed); ipa_lift + ipa_attend is exactly ipa_forward. Arguments,
+ * validation and status codes are those of ipa_forward. */
+int32_t ipa_lift(const ipa_dims* dims, int32_t dtype,
+                 const void* q, const void* k, const void* v,
+                 const void* q_pts, const void* k_pts, const void* v_pts,
+                 const float* rot, const float* trans,
+                 const void* z1, const void* z2,
+                 const float* w_b, const float* gamma,
+                 const uint8_t* mask,
+                 float w_L, float w_C,
+                 float* out_s, float* out_pts, float* out_pts_norm,
+                 float* out_pair,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream);
+int32_t ipa_attend(const ipa_dims* dims, int32_t dtype,
+                   const void* q, const void* k, const void* v,
+                   const void* q_pts, const void* k_pts, const void* v_pts,
+                   const float* rot, const float* trans,
+                   const void* z1, const void* z2,
+                   const float* w_b, const float* gamma,
+                   const uint8_t* mask,
+                   float w_L, float w_C,
+                   float* out_s, float* out_pts, float* out_pts_norm,
+                   float* out_pair,
+                   void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ipa_status_string(int32_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t ipa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IPA_MI355_H */

@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its workspace linearly in L, and rejects bad
+arguments before anything is launched."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from geometric_invariant_attention_amd import _binding as bd
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "ipa.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not bd.LIB_PATH.exists():
+        pytest.skip("HIP library not built (run __graft_entry__.build())")
+    return bd.load_library()
+
+
+def _declared():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ipa_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert names == ["ipa_attend", "ipa_forward", "ipa_lift", "ipa_status_string", "ipa_version",
+                     "ipa_workspace_bytes"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ipa_version() >= 100
+    for code in list(bd.STATUS) + [-99]:
+        s = bd.status_string(code)
+        assert isinstance(s, str) and s
+
+
+def _dims(**kw):
+    base = dict(B=1, L=512, H=12, C=16, Pqk=4, Pv=8, R=2, Cz=128)
+    base.update(kw)
+    return bd.IpaDims(**base)
+
+
+def test_workspace_linear_in_L(lib):
+    sizes = {L: bd.workspace_bytes(_dims(L=L), bd.IPA_BF16) for L in (1024, 2048, 4096, 8192, 16384)}
+    assert all(v > 0 for v in sizes.values())
+    # exactly linear for multiples of the tile sizes (no L*L term)
+    per = (sizes[16384] - sizes[8192]) / 8192
+    for L, v in sizes.items():
+        assert abs(v - sizes[1024] - per * (L - 1024)) < 4096, (L, v)
+    # modest: about 6 KB per residue at H=12, c_z=128 in bf16
+    assert per < 8192
+
+
+@pytest.mark.parametrize("kw,dtype", [
+    (dict(L=0), bd.IPA_BF16), (dict(H=-1), bd.IPA_BF16), (dict(C=17), bd.IPA_BF16),
+    (dict(Pqk=6), bd.IPA_BF16), (dict(Pv=9), bd.IPA_BF16), (dict(Cz=12), bd.IPA_BF16),
+    (dict(Cz=256, R=1), bd.IPA_BF16), (dict(R=3), bd.IPA_BF16), (dict(R=2), bd.IPA_F32),
+    (dict(), 7),
+])
+def test_workspace_zero_when_unsupported(lib, kw, dtype):
+    assert bd.workspace_bytes(_dims(**kw), dtype) == 0
+
+
+def _call(lib, dims, dtype=bd.IPA_BF16, ptr=0x100000, ws_bytes=1 << 40, w_L=0.5, w_C=0.3,
+          null_idx=None, misalign_idx=None, ws_ptr=None):
+    """Call ipa_forward with fake device pointers. Every case used here fails
+    validation, so nothing is ever launched."""
+    ptrs = [ptr + 4096 * i for i in range(13)]
+    outs = [ptr + 4096 * (13 + i) for i in range(4)]
+    allp = ptrs + outs
+    if null_idx is not None:
+        allp[null_idx] = 0
+    if misalign_idx is not None:
+        allp[misalign_idx] += 4
+    ws = ptr + (1 << 30) if ws_ptr is None else ws_ptr
+    d = ctypes.byref(dims) if dims is not None else None
+    return lib.ipa_forward(d, dtype, *allp[:12], 0, ctypes.c_float(w_L), ctypes.c_float(w_C),
+                           *allp[13:17], ws, ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("entry", ["ipa_forward", "ipa_lift", "ipa_attend"])
+def test_stages_reject_before_launch(lib, entry):
+    fn = getattr(lib, entry)
+    d = _dims()
+    assert fn(None, 1, *([0x100000] * 12), 0, ctypes.c_float(0.5), ctypes.c_float(0.3),
+              *([0x200000] * 4), 0x40000000, ctypes.c_size_t(1 << 40), None) == -1
+    assert fn(ctypes.byref(d), 1, *([0x100000] * 12), 0, ctypes.c_float(0.5), ctypes.c_float(0.3),
+              *([0x200000] * 4), 0x40000000, ctypes.c_size_t(16), None) == -4
+
+
+def test_forward_rejects_before_launch(lib):
+    assert _call(lib, None) == -1                                  # IPA_ERR_NULL
+    assert _call(lib, _dims(L=0)) == -2                            # IPA_ERR_DIMS
+    assert _call(lib, _dims(), dtype=5) == -3                      # IPA_ERR_DTYPE
+    for idx in (0, 5, 9, 11, 13, 16):
+        assert _call(lib, _dims(), null_idx=idx) == -1             # NULL tensor
+        assert _call(lib, _dims(), misalign_idx=idx) == -5         # IPA_ERR_ALIGN
+    assert _call(lib, _dims(), ws_ptr=0x100000 + (1 << 30) + 16) == -5
+    assert _call(lib, _dims(), w_L=float("nan")) == -8             # IPA_ERR_ARG
+    assert _call(lib, _dims(), w_C=-1.0) == -8
+    assert _call(lib, _dims(C=20)) == -6                           # IPA_ERR_UNSUPPORTED
+    assert _call(lib, _dims(R=2, Cz=128), dtype=bd.IPA_F32) == -6
+    need = bd.workspace_bytes(_dims(), bd.IPA_BF16)
+    assert _call(lib, _dims(), ws_bytes=need - 1) == -4            # IPA_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        bd.load_library(tmp_path / "missing.so")

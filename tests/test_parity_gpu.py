@@ -1,0 +1,184 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: max-abs 1e-4 for the fp32 path and 3e-2 for the bf16 path per
+output over valid rows; masked rows must be bit-exact +0.0. Inputs are the
+seeded synthetic workloads; for L >= 2048 the oracle checks a fixed sample
+of query rows (each query row is independent), including every tile edge.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ipa_forward as oracle_forward
+from workloads import WORKLOADS, make_inputs, stress_pair
+
+from ipa_gpu_util import (assert_masked_positive_zero, compare, run_gpu, to_device)
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_BF16 = 3e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check(w, device, tol, seed=None, rows=None, stress=False):
+    inp = make_inputs(w, seed=seed)
+    if stress:
+        inp = stress_pair(inp)
+    _say(f"case {w.name} B={w.B} L={w.L} H={w.H} Cz={w.Cz} {w.dtype} seed={seed} stress={stress}")
+    gpu = run_gpu(to_device(inp, device))
+    ref = oracle_forward(inp, rows=rows)
+    valid = inp["mask"].astype(bool)
+    errs = compare(gpu, ref, tol, valid_rows=valid, rows=rows)
+    if w.ragged is not None:
+        assert_masked_positive_zero(gpu, inp["mask"])
+    _say(f"  errors {errs}")
+    return inp, gpu, ref, errs
+
+
+def _edge_rows(L, n_random=96, seed=0):
+    edges = set()
+    for t in range(0, L, 64):
+        edges.update({t, t + 1, t + 31, t + 32, t + 63})
+    edges = {r for r in edges if r < L} | {L - 1}
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(L, size=min(L, n_random), replace=False)
+    return np.array(sorted(edges | set(extra.tolist())))
+
+
+def test_tiny_fp32(device):
+    _check(WORKLOADS["tiny_fp32"], device, TOL_F32)
+
+
+@pytest.mark.parametrize("L", [1, 37, 200])
+def test_fp32_ragged_tail(device, L):
+    _check(WORKLOADS["tiny_fp32"].with_(L=L, H=3), device, TOL_F32, seed=L)
+
+
+def test_fp32_odd_dims(device):
+    w = WORKLOADS["tiny_fp32"].with_(L=150, H=2, C=12, Pqk=3, Pv=5, R=1, Cz=24)
+    _check(w, device, TOL_F32, seed=3)
+
+
+def test_single_chain_bf16(device):
+    _check(WORKLOADS["single_chain"], device, TOL_BF16)
+
+
+def test_single_chain_bf16_pair_stress(device):
+    """Unit-variance pair factors make pair-path errors visible: the pair bias
+    reaches several logits and the pair output is O(1)."""
+    w = WORKLOADS["single_chain"].with_(L=256, H=4)
+    inp, gpu, ref, errs = _check(w, device, 1.0, stress=True)
+    for k in errs:
+        rms = float(np.sqrt(np.mean(ref[k] ** 2)))
+        assert errs[k] <= 3e-2 * max(rms, 1.0), (k, errs[k], rms)
+
+
+def test_tiny_fp32_pair_stress(device):
+    """fp32 path with unit-variance pair factors: every channel at 1e-4 of
+    max(1, RMS), so the pair bias / pair output logic shared by both paths is
+    checked without bf16 rounding."""
+    w = WORKLOADS["tiny_fp32"].with_(L=150, H=4)
+    inp, gpu, ref, errs = _check(w, device, 1.0, stress=True)
+    for k in errs:
+        rms = float(np.sqrt(np.mean(ref[k] ** 2)))
+        assert errs[k] <= TOL_F32 * max(rms, 1.0), (k, errs[k], rms)
+
+
+@pytest.mark.parametrize("L", [70, 200, 333])
+def test_bf16_ragged_tail(device, L):
+    _check(WORKLOADS["single_chain"].with_(L=L, H=3), device, TOL_BF16, seed=L)
+
+
+def test_bf16_odd_dims(device):
+    w = WORKLOADS["single_chain"].with_(L=190, H=2, C=12, Pqk=5, Pv=5, R=3, Cz=40)
+    _check(w, device, TOL_BF16, seed=4)
+
+
+def test_ragged_batch(device):
+    w = WORKLOADS["ragged_batch"]
+    inp = make_inputs(w)
+    dev = to_device(inp, device)
+    before = {k: v.clone() for k, v in dev.items() if isinstance(v, torch.Tensor)}
+    gpu = run_gpu(dev)
+    for k, v in before.items():
+        assert torch.equal(v, dev[k]), f"input {k} was modified"
+    ref = oracle_forward(inp)
+    errs = compare(gpu, ref, TOL_BF16, valid_rows=inp["mask"].astype(bool))
+    assert_masked_positive_zero(gpu, inp["mask"])
+    _say(f"ragged batch errors {errs}")
+
+
+def test_long_chain_2048_sampled(device):
+    w = WORKLOADS["long_chain_2048"]
+    _check(w, device, TOL_BF16, rows=_edge_rows(w.L))
+
+
+@pytest.mark.parametrize("name", ["long_chain_4096", "very_long_8192", "very_long_16384"])
+def test_long_sampled(device, name):
+    w = WORKLOADS[name]
+    _check(w, device, TOL_BF16, rows=_edge_rows(w.L, n_random=24)[::4])
+
+
+def test_determinism_and_noncontiguous(device):
+    w = WORKLOADS["single_chain"].with_(L=300, H=4)
+    inp = make_inputs(w, seed=21)
+    dev = to_device(inp, device)
+    a = run_gpu(dev)
+    b = run_gpu(dev)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    # the same values through non-contiguous views
+    nc = dict(dev)
+    for k in ("q", "k", "v", "z1", "z2", "q_pts", "v_pts"):
+        t = dev[k]
+        big = torch.zeros((2,) + tuple(t.shape), dtype=t.dtype, device=t.device)
+        big[1] = t
+        view = big.transpose(0, 1)[:, 1]
+        assert not view.is_contiguous() or view.data_ptr() != t.data_ptr()
+        nc[k] = view
+    c = run_gpu(nc)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), c[k].view(np.uint32)), k
+
+
+def test_se3_invariance_gpu(device):
+    w = WORKLOADS["tiny_fp32"].with_(L=128, H=4)
+    inp = make_inputs(w, seed=5)
+    base = run_gpu(to_device(inp, device))
+    rng = np.random.default_rng(3)
+    u = rng.standard_normal(4)
+    u /= np.linalg.norm(u)
+    a0, x, y, z = u
+    Rg = np.array([[1 - 2 * (y * y + z * z), 2 * (x * y - a0 * z), 2 * (x * z + a0 * y)],
+                   [2 * (x * y + a0 * z), 1 - 2 * (x * x + z * z), 2 * (y * z - a0 * x)],
+                   [2 * (x * z - a0 * y), 2 * (y * z + a0 * x), 1 - 2 * (x * x + y * y)]])
+    moved = dict(inp)
+    moved["rot"] = np.einsum("xy,blyz->blxz", Rg, inp["rot"].astype(np.float64)).astype(np.float32)
+    moved["trans"] = (np.einsum("xy,bly->blx", Rg, inp["trans"].astype(np.float64))
+                      + rng.normal(0, 100.0, 3)).astype(np.float32)
+    out = run_gpu(to_device(moved, device))
+    for k in base:
+        np.testing.assert_allclose(out[k], base[k], rtol=0, atol=TOL_F32, err_msg=k)
+
+
+def test_binding_errors(device):
+    from geometric_invariant_attention_amd import IPAForward
+    w = WORKLOADS["tiny_fp32"].with_(L=16, H=2)
+    dev = to_device(make_inputs(w), device)
+    plan = IPAForward(1, 16, 2, 16, 4, 8, 2, 16, dtype=torch.float32, device=device)
+    args = {k: dev[k] for k in ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans",
+                                "z1", "z2", "w_b", "gamma")}
+    with pytest.raises(TypeError):
+        plan(**dict(args, q=args["q"].to(torch.bfloat16)))
+    with pytest.raises(ValueError):
+        plan(**dict(args, v=args["v"][:, :8]))
+    with pytest.raises(ValueError):
+        plan(**dict(args, z1=args["z1"].cpu()))
