@@ -25,6 +25,13 @@ HIPCC_FLAGS = [
     "-I", str(ROOT / "include"),
 ]
 
+# Per-source extra flags. The attention kernel keeps its matrix-core
+# accumulators in architectural VGPRs (operands of the online-softmax
+# rescale), leaving the AGPRs for the query operand.
+EXTRA_FLAGS = {
+    "ipa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -41,7 +48,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> Path:
 
     def compile_one(src: str) -> Path:
         obj = BUILD_DIR / (src + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+        cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", str(CSRC / src), "-o", str(obj)]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         res = subprocess.run(cmd, capture_output=True, text=True)

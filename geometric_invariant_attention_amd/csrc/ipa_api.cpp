@@ -18,6 +18,7 @@ bool make_layout(const int32_t d[8], int esize, Layout* o) {
   if (C > kCSlot || Pv > kPvSlot || kCSlot + 9 * Pqk > kHeadW) return false;
   if (Cz % 8 != 0 || Cz > 128 || R * Cz > kMaxD - kHeadW) return false;
   const int64_t Lp = (L + kTileM - 1) / kTileM * kTileM;
+  if (Lp / kTileN > kMaxTiles) return false;
   if (B * H * Lp >= (int64_t(1) << 31) || B * L * R * Cz >= (int64_t(1) << 31)) return false;
   const int64_t PW = (R * Cz + 63) / 64 * 64;
   Layout& ly = *o;

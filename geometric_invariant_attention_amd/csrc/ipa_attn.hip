@@ -4,9 +4,12 @@
 // Point Attention", abstract: linear memory through a flash-style kernel).
 //
 // Work split. One workgroup = 4 waves = 128 query rows of one (batch, head);
-// each wave owns 32 query rows for the whole key loop. Key tiles of 64 keys
-// are staged in LDS: the key tile row-major [key][feature] and the value tile
-// feature-major [feature][key].
+// each wave owns 32 query rows for the whole key loop (one wave per SIMD,
+// all 512 registers per lane available). Keys are visited in tiles of 32:
+// the key tile row-major [key][feature] and the value tile feature-major
+// [feature][key] are double-buffered in LDS, staged through registers (the
+// next tile's global loads are in flight while the current tile computes),
+// with one workgroup barrier per tile.
 //
 // Products are taken transposed, S^T = K Q^T and O^T = V^T P^T, on 32x32
 // matrix-core tiles: lane l then holds query l % 32 for both products, the
@@ -28,26 +31,26 @@
 
 #include "ipa_internal.h"
 
+#include <type_traits>
+
 namespace ipa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLazy = 8.0f;
+// Keys per tile of the key loop (the centring blocks stay 64 residues).
+constexpr int kKT = 32;
 // Operand fragments read ahead of the matrix-core products that use them.
 constexpr int kLook = 4;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
 }
 // Round to nearest even fp16, saturating at the largest finite value.
 __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
@@ -58,7 +61,6 @@ __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
 // Element-type policy: bf16 storage with 32x32x16 bf16 products, or fp32
 // storage with 32x32x2 fp32 products.
 template <typename T> struct Mma;
-
 template <> struct Mma<uint16_t> {
   static constexpr int kStep = 16;   // reduction length of one product
   static constexpr int kPad = 8;     // LDS row padding (elements)
@@ -75,6 +77,9 @@ template <> struct Mma<float> {
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mma(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
 // pair part of S^T on the bf16 path: fp16 operands (bits carried in bf16x8)
 __device__ __forceinline__ f32x16 mma_pair(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -83,9 +88,22 @@ __device__ __forceinline__ f32x16 mma_pair(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ f32x16 mma_pair(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x16 mma(float a, float b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
+
+// N registers of 16 bytes addressed by compile-time index only (no array, so
+// they always stay in registers).
+template <int N> struct Regs : Regs<N - 1> { u32x4 v; };
+template <> struct Regs<0> {};
+template <int M, int N>
+__device__ __forceinline__ u32x4& reg(Regs<N>& r) { return static_cast<Regs<M + 1>&>(r).v; }
 
 template <typename T> __device__ __forceinline__ float ld_in(const void* p, size_t i);
 template <> __device__ __forceinline__ float ld_in<uint16_t>(const void* p, size_t i) {
@@ -95,66 +113,29 @@ template <> __device__ __forceinline__ float ld_in<float>(const void* p, size_t 
   return static_cast<const float*>(p)[i];
 }
 
-// LDS tiles are made of panels: 64 rows x 64 features (key tile, row =
-// key) or 64 rows x 64 keys (value tile, row = feature). Each panel row is
-// padded by one 16-byte chunk, which spreads the 32 rows that one
-// matrix-core operand read touches over distinct LDS banks.
+// LDS layout. The key tile is kNP panels of [32 keys][64 features], the
+// value tile [D features][32 keys]; every row is padded by one 16-byte chunk,
+// which spreads the 32 rows that one matrix-core operand read touches over
+// distinct LDS banks. Two buffers of each.
 template <typename T, int D>
 struct Smem {
   static constexpr int kPW = D - kHeadW;
   static constexpr int kEpc = Mma<T>::kEpc;
-  static constexpr int kRow = 64 + Mma<T>::kPad;                 // elements per padded panel row
-  static constexpr int kPanel = 64 * kRow * (int)sizeof(T);       // bytes per panel
-  static constexpr int kNP = D / 64;                              // panels per tile
-  static constexpr int kK = 0;                                    // key tile panels
-  static constexpr int kV = kK + kNP * kPanel;                    // value tile panels
-  static constexpr int kMain = kV + kNP * kPanel;
+  static constexpr int kNP = D / 64;                               // 64-feature panels
+  static constexpr int kKRow = 64 + Mma<T>::kPad;                  // elements per key-panel row
+  static constexpr int kKPanel = kKT * kKRow;                      // elements per key panel
+  static constexpr int kKBuf = kNP * kKPanel;                      // elements per key buffer
+  static constexpr int kVRow = kKT + Mma<T>::kPad;                 // elements per value row
+  static constexpr int kVBuf = D * kVRow;                          // elements per value buffer
   static constexpr int kCzMax = kPW < 128 ? kPW : 128;
   static constexpr int kPairBytes = 4 * 32 * (kCzMax > 0 ? kCzMax : 1) * 4;
-  static constexpr int kBytes = kMain > kPairBytes ? kMain : kPairBytes;
+  // the key buffers also hold the pair-output buffer of the epilogue
+  static constexpr int kKBytes = 2 * kKBuf * (int)sizeof(T) > kPairBytes
+                                     ? 2 * kKBuf * (int)sizeof(T) : kPairBytes;
+  static constexpr int kVBytes = 2 * kVBuf * (int)sizeof(T);
+  // 16-byte chunks each thread stages per tile (key part or value part)
+  static constexpr int kCPT = kNP * (64 / kEpc) * kKT / 256;
 };
-
-// Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit data
-// format); loads outside the range return zero instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Direct-to-LDS panel loads. A panel's source is 64 contiguous rows of 64
-// elements; in LDS each row takes kRC = 64/EPC + 1 chunks. One wave-wide
-// load writes 64 consecutive LDS chunks (lane l -> chunk l), so a load that
-// covers kRPL whole padded rows has the same per-lane source offset for
-// every load: lane l copies chunk l % kRC (the padding chunk copies any
-// chunk of its row) of row l / kRC, and lanes past kRPL rows stay idle.
-template <typename T>
-struct PanelLoad {
-  static constexpr int kEpc = Mma<T>::kEpc;
-  static constexpr int kDC = 64 / kEpc;                 // data chunks per row
-  static constexpr int kRC = kDC + 1;                   // LDS chunks per row
-  static constexpr int kRPL = 64 / kRC;                 // rows per load
-  static constexpr int kLoads = (64 + kRPL - 1) / kRPL; // loads per panel
-  static constexpr uint32_t kSrcBytes = 64u * kDC * 16u;
-  int lane_off;   // source byte offset of this lane within its rows, -1 = idle lane
-  int lane_row;   // row of this lane within a load
-  __device__ void init(int lane) {
-    lane_row = lane / kRC;
-    const int c = lane - lane_row * kRC;
-    const int cc = c < kDC ? c : kDC - 1;
-    lane_off = lane_row < kRPL ? (lane_row * kDC + cc) * 16 : -1;
-  }
-  // Enqueue loads k = k0, k0 + kStride, ... of one panel.
-  __device__ void load(const unsigned char* src, unsigned char* lds, int k0, int kStride) const {
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, kSrcBytes);
-    for (int k = k0; k < kLoads; k += kStride) {
-      if (lane_off >= 0 && k * kRPL + lane_row < 64)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(lds + k * kRPL * kRC * 16), 16,
-            lane_off, k * kRPL * kDC * 16, 0, 0);
-    }
-  }
-};
-
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -162,24 +143,31 @@ void ipa_attn_kernel(FwdArgs a) {
   using M = Mma<T>;
   using Frag = typename M::Frag;
   using SM = Smem<T, D>;
-  constexpr int NKS = D / M::kStep;     // products per 32-key block of S^T
-  constexpr int NFB = D / 32;           // 32-feature blocks of O^T
-  constexpr int NKH = kHeadW / M::kStep; // products over the head part of a row
-  constexpr int EPC = M::kEpc;
+  constexpr int NKS = D / M::kStep;        // products per S^T tile
+  constexpr int NKH = kHeadW / M::kStep;   // of which cover the head part
+  constexpr int NFB = D / 32;              // 32-feature blocks of O^T
   constexpr int NP = SM::kNP;
-  constexpr int NST = kTileN / M::kStep;  // products per 32-feature block of O^T
+  constexpr int EPC = M::kEpc;
+  constexpr int NST = kKT / M::kStep;      // products per O^T block per tile
+  constexpr int CPT = SM::kCPT;
+  static_assert(CPT * 256 == NP * (64 / EPC) * kKT, "tile chunks must split over 256 threads");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SM::kBytes];
-  __shared__ __attribute__((aligned(1024))) float4 kcS[kTileN];
-  __shared__ float colbuf[4][kTileN];
+  __shared__ __attribute__((aligned(16))) unsigned char smemK[SM::kKBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smemV[SM::kVBytes];
+  __shared__ float4 kcS[2][kKT];
+  __shared__ float colbuf[4][kKT];
+  // per 64-key block: centre xyz and valid-key count, staged once so the key
+  // loop issues no vector-memory reads besides its tile loads
+  __shared__ float4 cenS[kMaxTiles];
 
-  const T* Ks = reinterpret_cast<const T*>(smem + SM::kK);
-  const T* Vs = reinterpret_cast<const T*>(smem + SM::kV);
+  T* const Kb = reinterpret_cast<T*>(smemK);
+  T* const Vb = reinterpret_cast<T*>(smemV);
 
   const Layout& ly = a.lay;
-  const int L = ly.L, H = ly.H, Lp = ly.Lp, nJ = ly.nJ, PW = ly.PW;
+  const int L = ly.L, H = ly.H, Lp = ly.Lp, nJ = ly.nJ;
   const int C = ly.C, Pqk = ly.Pqk, Pv = ly.Pv, Cz = ly.Cz, RCz = ly.R * ly.Cz;
   const int nQB = Lp / kTileM;
+  const int nT = Lp / kKT;
 
   // XCD-aware order: consecutive workgroup ids are dealt to the 8 XCDs in
   // turn, so remap them so that the query blocks of one (batch, head), which
@@ -195,16 +183,15 @@ void ipa_attn_kernel(FwdArgs a) {
   const int i = qw + n;                 // this lane's query row
 
   const size_t bh = (size_t)b * H + h;
-  constexpr size_t kPanelSrc = 64 * 64 * sizeof(T);   // bytes of one source panel
-  const unsigned char* Kh = a.ws + ly.off_kh + bh * Lp * kHeadW * sizeof(T);
-  const unsigned char* Kz = a.ws + ly.off_kz + (size_t)b * nJ * (NP - 1) * kPanelSrc;
-  const unsigned char* Vth = a.ws + ly.off_vth + bh * nJ * kPanelSrc;
-  const unsigned char* Vtz = a.ws + ly.off_vtz + (size_t)b * nJ * (NP - 1) * kPanelSrc;
-  const unsigned char* kcol = a.ws + ly.off_kcol + bh * Lp * 16;
-  const float4* cen = reinterpret_cast<const float4*>(a.ws + ly.off_cen) + (size_t)b * nJ;
-
-  PanelLoad<T> pl;
-  pl.init(lane);
+  const T* Kh = reinterpret_cast<const T*>(a.ws + ly.off_kh) + bh * Lp * kHeadW;
+  const T* Kz = reinterpret_cast<const T*>(a.ws + ly.off_kz) + (size_t)b * nJ * (NP - 1) * 4096;
+  const T* Vth = reinterpret_cast<const T*>(a.ws + ly.off_vth) + bh * nJ * 4096;
+  const T* Vtz = reinterpret_cast<const T*>(a.ws + ly.off_vtz) + (size_t)b * nJ * (NP - 1) * 4096;
+  const float4* kcol = reinterpret_cast<const float4*>(a.ws + ly.off_kcol) + bh * Lp;
+  {
+    const float4* cen = reinterpret_cast<const float4*>(a.ws + ly.off_cen) + (size_t)b * nJ;
+    for (int e = tid; e < nJ; e += 256) cenS[e] = cen[e];
+  }
 
   const float kap = a.w_L * a.gamma[h] * a.w_C * 0.5f * kLog2e;
   const bool row_valid = (i < L) && (a.mask == nullptr || a.mask[(size_t)b * L + i] != 0);
@@ -248,15 +235,15 @@ void ipa_attn_kernel(FwdArgs a) {
         if (f < kHeadW) {
           v = reinterpret_cast<const float*>(Qh)[f];
         } else {
-          const int u = f - kHeadW;
-          if (u < RCz && i < L)
-            v = static_cast<const float*>(a.z1)[((size_t)b * L + i) * RCz + u] * wbt[u % Cz];
+          const int uu = f - kHeadW;
+          if (uu < RCz && i < L)
+            v = static_cast<const float*>(a.z1)[((size_t)b * L + i) * RCz + uu] * wbt[uu % Cz];
         }
         qf[s] = v;
       }
     }
   }
-  const float4 qr = reinterpret_cast<const float4*>(a.ws + ly.off_qrow)[bh * Lp + (i < Lp ? i : 0)];
+  const float4 qr = reinterpret_cast<const float4*>(a.ws + ly.off_qrow)[bh * Lp + i];
   // fp32 path: the centred query points themselves (the point term is taken
   // from explicit differences, see below)
   float apt[sizeof(T) == 4 ? 15 : 1];
@@ -265,36 +252,67 @@ void ipa_attn_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 15; ++e) apt[e] = e < 3 * Pqk ? Qh[kFpQPts + e] : 0.f;
   }
-  const float4 cI = cen[qw / kTileN];
+  __syncthreads();  // cenS
+  const float4 cI = cenS[qw / kTileN];
 
-  // ---- tile loaders: global -> LDS directly, no registers involved ----
-  auto load_k = [&](int J) {
-    pl.load(Kh + (size_t)J * kPanelSrc, smem + SM::kK, w, 4);
-#pragma unroll
-    for (int P = 1; P < NP; ++P)
-      pl.load(Kz + ((size_t)J * (NP - 1) + P - 1) * kPanelSrc, smem + SM::kK + P * SM::kPanel, w, 4);
-    if (w == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          make_rsrc(kcol + (size_t)J * kTileN * 16, kTileN * 16),
-          (__attribute__((address_space(3))) void*)kcS, 16, lane * 16, 0, 0, 0);
+  // ---- tile staging: global -> registers -> LDS ----
+  // Key tile t (keys 32t .. 32t+31): chunk m of this thread lies in panel
+  // ch / (32 * KCPR), key (ch / KCPR) % 32, column chunk ch % KCPR, with
+  // ch = tid + 256 m. Value tile: chunk m is feature ch / VCPR, key chunk
+  // ch % VCPR of the tile's half of its 64-key value block.
+  constexpr int KCPR = 64 / EPC;               // chunks per key-panel row
+  constexpr int VCPR = kKT / EPC;              // chunks per value row
+  Regs<CPT> st;
+  float4 kcst = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto load_k = [&](int t) {
+    const int J = t >> 1, half = t & 1;
+    static_for<0, CPT>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      const int ch = tid + 256 * m;
+      const int P = ch / (kKT * KCPR), r = (ch / KCPR) % kKT, c = ch % KCPR;
+      const int key = 32 * half + r;                      // key within the 64-block
+      const T* src = P == 0 ? Kh + ((size_t)J * 64 + key) * kHeadW + c * EPC
+                            : Kz + (((size_t)J * (NP - 1) + P - 1) * 64 + key) * 64 + c * EPC;
+      reg<m>(st) = *reinterpret_cast<const u32x4*>(src);
+    });
+    if (tid < kKT) kcst = kcol[(size_t)t * kKT + tid];
   };
-  auto load_v = [&](int J) {
-    pl.load(Vth + (size_t)J * kPanelSrc, smem + SM::kV, w, 4);
-#pragma unroll
-    for (int P = 1; P < NP; ++P)
-      pl.load(Vtz + ((size_t)J * (NP - 1) + P - 1) * kPanelSrc, smem + SM::kV + P * SM::kPanel, w, 4);
+  auto store_k = [&](int bf) {
+    static_for<0, CPT>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      const int ch = tid + 256 * m;
+      const int P = ch / (kKT * KCPR), r = (ch / KCPR) % kKT, c = ch % KCPR;
+      *reinterpret_cast<u32x4*>(Kb + bf * SM::kKBuf + P * SM::kKPanel + r * SM::kKRow + c * EPC) = reg<m>(st);
+    });
+    if (tid < kKT) kcS[bf][tid] = kcst;
+  };
+  auto load_v = [&](int t) {
+    const int J = t >> 1, half = t & 1;
+    static_for<0, CPT>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      const int ch = tid + 256 * m;
+      const int f = ch / VCPR, c = ch % VCPR;
+      const T* src = f < kHeadW ? Vth + ((size_t)J * 64 + f) * 64 + 32 * half + c * EPC
+                                : Vtz + ((size_t)J * (NP - 1) * 64 + (f - kHeadW)) * 64 + 32 * half + c * EPC;
+      reg<m>(st) = *reinterpret_cast<const u32x4*>(src);
+    });
+  };
+  auto store_v = [&](int bf) {
+    static_for<0, CPT>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      const int ch = tid + 256 * m;
+      const int f = ch / VCPR, c = ch % VCPR;
+      *reinterpret_cast<u32x4*>(Vb + bf * SM::kVBuf + f * SM::kVRow + c * EPC) = reg<m>(st);
+    });
   };
 
   // key tiles are visited starting at this block's own diagonal tile; tiles
-  // with no valid key are skipped (their keys could only add zeros)
-  const int J0 = (qb * kTileM / kTileN) % nJ;
-  auto tile_of = [&](int t) {
-    int J = J0 + t;
-    return __builtin_amdgcn_readfirstlane(J >= nJ ? J - nJ : J);
-  };
-  auto next_nonempty = [&](int t) {
-    while (t < nJ && cen[tile_of(t)].w == 0.f) ++t;
-    return t;
+  // whose 64-key block has no valid key are skipped (they could only add zeros)
+  const int T0 = (qb * kTileM / kKT) % nT;
+  auto tile_of = [&](int uu) { int t = T0 + uu; return t >= nT ? t - nT : t; };
+  auto next_nonempty = [&](int uu) {
+    while (uu < nT && cenS[tile_of(uu) >> 1].w == 0.f) ++uu;
+    return uu;
   };
 
   f32x16 oacc[NFB];
@@ -303,51 +321,56 @@ void ipa_attn_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_own = 0.f;
   float ocx = 0.f, ocy = 0.f, ocz = 0.f;
 
-  int t = next_nonempty(0);
-  if (t < nJ) load_k(tile_of(t));
-  wait_vm();
+  int u = next_nonempty(0);
+  int buf = 0;
+  if (u < nT) {
+    load_k(tile_of(u));
+    store_k(0);
+    load_v(tile_of(u));
+    store_v(0);
+  }
   __syncthreads();
 
-  while (t < nJ) {
-    const int J = tile_of(t);
-    const int tn = next_nonempty(t + 1);
-    load_v(J);
+  while (u < nT) {
+    const int t = tile_of(u);
+    const int un = next_nonempty(u + 1);
+    const bool more = un < nT;
+    const int tn = more ? tile_of(un) : 0;
+    if (more) load_k(tn);
 
     // ---------------- phase A: scores and probabilities ----------------
-    const float4 cJ = cen[J];
+    const float4 cJ = cenS[t >> 1];
     const float dx = cI.x - cJ.x, dy = cI.y - cJ.y, dz = cI.z - cJ.z;
-    {
-      const float4 kc = kcS[lane];
+    if (lane < kKT) {
+      const float4 kc = kcS[buf][lane];
       colbuf[w][lane] = kc.w + 2.f * kap * (dx * kc.x + dy * kc.y + dz * kc.z);
     }
     const float rterm = sizeof(T) == 4 ? 0.f
                         : -kap * (2.f * (dx * qr.x + dy * qr.y + dz * qr.z) +
                                   (float)Pqk * (dx * dx + dy * dy + dz * dz));
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    f32x16 sacc = f32x16{};
     {
       // operand reads run kLook products ahead of the matrix core
-      const T* krow = Ks + n * SM::kRow;
-      auto kfrag = [&](int idx) -> Frag {
-        const int s = idx >> 1, kb = idx & 1;
+      const T* krow = Kb + buf * SM::kKBuf + n * SM::kKRow;
+      auto kfrag = [&](int s) -> Frag {
         const int f = M::kStep * s;
-        const T* r = krow + (f / 64) * (SM::kPanel / (int)sizeof(T)) + 32 * kb * SM::kRow + (f % 64);
+        const T* r = krow + (f / 64) * SM::kKPanel + (f % 64);
         if constexpr (sizeof(T) == 2)
           return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + 8 * g));
         else
           return r[g];
       };
-      constexpr int NA = 2 * NKS;
-      Frag buf[kLook];
+      Frag look[kLook];
 #pragma unroll
-      for (int x = 0; x < kLook; ++x) buf[x] = kfrag(x);
+      for (int x = 0; x < kLook; ++x) look[x] = kfrag(x);
 #pragma unroll
-      for (int idx = 0; idx < NA; ++idx) {
-        const Frag cur = buf[idx % kLook];
-        if (idx + kLook < NA) buf[idx % kLook] = kfrag(idx + kLook);
-        if ((idx >> 1) < NKH)
-          sacc[idx & 1] = mma(cur, qf[idx >> 1], sacc[idx & 1]);
+      for (int s = 0; s < NKS; ++s) {
+        const Frag cur = look[s % kLook];
+        if (s + kLook < NKS) look[s % kLook] = kfrag(s + kLook);
+        if (s < NKH)
+          sacc = mma(cur, qf[s], sacc);
         else
-          sacc[idx & 1] = mma_pair(cur, qf[idx >> 1], sacc[idx & 1]);
+          sacc = mma_pair(cur, qf[s], sacc);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -358,35 +381,30 @@ void ipa_attn_kernel(FwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 15; ++e) ad[e] = apt[e] + (e % 3 == 0 ? dx : e % 3 == 1 ? dy : dz);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int v = 0; v < 16; ++v) {
+        const int j = 8 * (v >> 2) + 4 * g + (v & 3);
+        const float* bp = reinterpret_cast<const float*>(Kb) + buf * SM::kKBuf + j * SM::kKRow + kCSlot;
+        float d = 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
-          const float* bp = reinterpret_cast<const float*>(Ks) + j * SM::kRow + kCSlot;
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 15; ++e) {
-            if (e < 3 * Pqk) {
-              const float t = ad[e] - bp[e];
-              d = fmaf(t, t, d);
-            }
+        for (int e = 0; e < 15; ++e) {
+          if (e < 3 * Pqk) {
+            const float tt = ad[e] - bp[e];
+            d = fmaf(tt, tt, d);
           }
-          sacc[kb][v] = fmaf(-kap, d, sacc[kb][v]);
         }
+        sacc[v] = fmaf(-kap, d, sacc[v]);
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int k = 0; k < 4; ++k) {
+      const float4 cv = *reinterpret_cast<const float4*>(&colbuf[w][8 * k + 4 * g]);
+      sacc[4 * k + 0] += cv.x;
+      sacc[4 * k + 1] += cv.y;
+      sacc[4 * k + 2] += cv.z;
+      sacc[4 * k + 3] += cv.w;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 cv = *reinterpret_cast<const float4*>(&colbuf[w][32 * kb + 8 * k + 4 * g]);
-        sacc[kb][4 * k + 0] += cv.x;
-        sacc[kb][4 * k + 1] += cv.y;
-        sacc[kb][4 * k + 2] += cv.z;
-        sacc[kb][4 * k + 3] += cv.w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kb][4 * k + e]);
-      }
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[4 * k + e]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float Mt = mx + rterm;
@@ -397,69 +415,77 @@ void ipa_attn_kernel(FwdArgs a) {
       m_run = mn;
       l_own *= al; ocx *= al; ocy *= al; ocz *= al;
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb) oacc[fb] *= al;
+      for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+        for (int v = 0; v < 16; v += 4) {
+          // a few registers at a time keeps the accumulator copies short-lived
+          oacc[fb][v] *= al; oacc[fb][v + 1] *= al; oacc[fb][v + 2] *= al; oacc[fb][v + 3] *= al;
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
     const float shift = (m_run == -INFINITY) ? 0.f : m_run - rterm;
 
     // probabilities -> B operand of O^T = V^T P^T
-    Frag pf[sizeof(T) == 2 ? 4 : 32];
+    Frag pf[NST];
     float lt = 0.f;
     if constexpr (sizeof(T) == 2) {
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kb = st >> 1, v0 = 8 * (st & 1);
+      for (int s2 = 0; s2 < NST; ++s2) {
         bf16x2 pk[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          f32x2 pv = {__builtin_amdgcn_exp2f(sacc[kb][v0 + 2 * e] - shift),
-                      __builtin_amdgcn_exp2f(sacc[kb][v0 + 2 * e + 1] - shift)};
+          f32x2 pv = {__builtin_amdgcn_exp2f(sacc[8 * s2 + 2 * e] - shift),
+                      __builtin_amdgcn_exp2f(sacc[8 * s2 + 2 * e + 1] - shift)};
           pk[e] = __builtin_convertvector(pv, bf16x2);
           lt = __builtin_amdgcn_fdot2_f32_bf16(pk[e], ones, lt, false);
         }
-        pf[st] = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1],
+        pf[s2] = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1],
                         pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
       }
     } else {
 #pragma unroll
-      for (int st = 0; st < 32; ++st) {
-        const float p = __builtin_amdgcn_exp2f(sacc[st >> 4][st & 15] - shift);
-        pf[st] = p;
+      for (int s2 = 0; s2 < NST; ++s2) {
+        const float p = __builtin_amdgcn_exp2f(sacc[s2] - shift);
+        pf[s2] = p;
         lt += p;
       }
     }
     l_own += lt;
     ocx += lt * cJ.x; ocy += lt * cJ.y; ocz += lt * cJ.z;
 
-    wait_vm();        // this wave's part of the value tile has landed
-    __syncthreads();  // ... and everyone's; all waves are done with the key tile
-    if (tn < nJ) load_k(tile_of(tn));
+    if (more) {
+      store_k(buf ^ 1);
+      load_v(tn);
+    }
 
     // ---------------- phase B: O^T += V^T P^T ----------------
     {
+      const T* vrow = Vb + buf * SM::kVBuf + n * SM::kVRow;
       auto vfrag = [&](int idx) -> Frag {
-        const int fb = idx / NST, st = idx % NST;
-        const T* vrow = Vs + (fb / 2) * (SM::kPanel / (int)sizeof(T)) + (32 * (fb % 2) + n) * SM::kRow;
+        const int fb = idx / NST, s2 = idx % NST;
+        const T* r = vrow + 32 * fb * SM::kVRow;
         if constexpr (sizeof(T) == 2)
-          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vrow + 16 * st + 8 * g));
+          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + 16 * s2 + 8 * g));
         else
-          return vrow[2 * st + g];
+          return r[2 * s2 + g];
       };
       constexpr int NB = NFB * NST;
-      Frag buf[kLook];
+      Frag look[kLook];
 #pragma unroll
-      for (int x = 0; x < kLook; ++x) buf[x] = vfrag(x);
+      for (int x = 0; x < kLook; ++x) look[x] = vfrag(x);
 #pragma unroll
       for (int idx = 0; idx < NB; ++idx) {
-        const Frag cur = buf[idx % kLook];
-        if (idx + kLook < NB) buf[idx % kLook] = vfrag(idx + kLook);
+        const Frag cur = look[idx % kLook];
+        if (idx + kLook < NB) look[idx % kLook] = vfrag(idx + kLook);
         oacc[idx / NST] = mma(cur, pf[idx % NST], oacc[idx / NST]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    wait_vm();        // next key tile has landed
-    __syncthreads();  // all waves are done with the value tile
-    t = tn;
+    if (more) store_v(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    u = un;
   }
 
   // ---------------- epilogue ----------------
@@ -472,8 +498,8 @@ void ipa_attn_kernel(FwdArgs a) {
   const bool in_range = i < L;
   const size_t rowh = ((size_t)b * L + i) * H + h;
 
-  // scalar channels: features 8k + 4g + e (k = 0, 1) of the first block
   if (in_range) {
+    // scalar channels: features 8k + 4g + e (k = 0, 1) of the first block
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
@@ -511,7 +537,7 @@ void ipa_attn_kernel(FwdArgs a) {
 
   // pair channels: accumulate sum_r z1_ir * O_pair,r in LDS, then write rows
   __syncthreads();  // every wave is done with the key/value tiles
-  float* pbuf = reinterpret_cast<float*>(smem) + (size_t)w * 32 * Cz;
+  float* pbuf = reinterpret_cast<float*>(smemK) + (size_t)w * 32 * Cz;
   for (int e = lane; e < 32 * Cz; e += 64) pbuf[e] = 0.f;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -522,10 +548,10 @@ void ipa_attn_kernel(FwdArgs a) {
       for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int u = 32 * (fb - 2) + 8 * k + 4 * g + e;
-          if (u < RCz) {
-            const int c = u % Cz;
-            const float z = ld_in<T>(a.z1, ((size_t)b * L + i) * RCz + u);
+          const int uu = 32 * (fb - 2) + 8 * k + 4 * g + e;
+          if (uu < RCz) {
+            const int c = uu % Cz;
+            const float z = ld_in<T>(a.z1, ((size_t)b * L + i) * RCz + uu);
             pbuf[n * Cz + c] += z * oacc[fb][4 * k + e] * inv;
           }
         }

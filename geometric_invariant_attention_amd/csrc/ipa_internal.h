@@ -11,6 +11,8 @@ namespace ipa {
 // Key tile of the attention kernel and the residue block whose mean
 // translation centres the global points (the same 64 residues).
 constexpr int kTileN = 64;
+// Largest number of key tiles (L <= kMaxTiles * kTileN).
+constexpr int kMaxTiles = 1024;
 // Query rows per attention workgroup (4 waves x 32 rows).
 constexpr int kTileM = 128;
 // Width of the per-head part of a lifted row (scalar + point columns).

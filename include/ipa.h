@@ -57,7 +57,7 @@ extern "C" {
  *   R   rank of the factorised pair   Cz  pair channels
  * Supported envelope: every dim >= 1, C <= 16, Pqk <= 5, Pv <= 8,
  * Cz % 8 == 0, Cz <= 128, R * Cz <= 256 (bf16) or <= 128 (fp32),
- * B * H * L < 2^31. Other shapes return IPA_ERR_UNSUPPORTED. */
+ * L <= 65536, B * H * L < 2^31. Other shapes return IPA_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t B, L, H, C, Pqk, Pv, R, Cz;
 } ipa_dims;
