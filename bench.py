@@ -177,6 +177,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of fp64 oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-mem-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB mebibytes (3 times) and exit; "
+                         "a reference for hardware byte counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -192,6 +195,15 @@ def main(argv=None) -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
+        return 0
     w = WORKLOADS[args.workload]
     d = w.dims()
 

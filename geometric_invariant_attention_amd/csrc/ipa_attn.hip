@@ -5,11 +5,13 @@
 //
 // Work split. One workgroup = 4 waves = 128 query rows of one (batch, head);
 // each wave owns 32 query rows for the whole key loop (one wave per SIMD,
-// all 512 registers per lane available). Keys are visited in tiles of 32:
-// the key tile row-major [key][feature] and the value tile feature-major
-// [feature][key] are double-buffered in LDS, staged through registers (the
-// next tile's global loads are in flight while the current tile computes),
-// with one workgroup barrier per tile.
+// all 512 registers per lane available). Keys are visited in tiles of 32.
+// The key tile (row-major [key][feature]) and the value tile (feature-major
+// [feature][key]) of the next tile are copied global -> LDS by direct-to-LDS
+// buffer loads while the current tile computes; the two buffers of each are
+// separate LDS arrays and the loop is unrolled by two, so the compiler can
+// see that reads of the current buffers never wait for loads into the next
+// ones. One workgroup barrier per tile.
 //
 // Products are taken transposed, S^T = K Q^T and O^T = V^T P^T, on 32x32
 // matrix-core tiles: lane l then holds query l % 32 for both products, the
@@ -31,8 +33,6 @@
 
 #include "ipa_internal.h"
 
-#include <type_traits>
-
 namespace ipa {
 namespace {
 
@@ -41,7 +41,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLazy = 8.0f;
 // Keys per tile of the key loop (the centring blocks stay 64 residues).
@@ -89,22 +88,6 @@ __device__ __forceinline__ f32x16 mma_pair(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// N registers of 16 bytes addressed by compile-time index only (no array, so
-// they always stay in registers).
-template <int N> struct Regs : Regs<N - 1> { u32x4 v; };
-template <> struct Regs<0> {};
-template <int M, int N>
-__device__ __forceinline__ u32x4& reg(Regs<N>& r) { return static_cast<Regs<M + 1>&>(r).v; }
-
 template <typename T> __device__ __forceinline__ float ld_in(const void* p, size_t i);
 template <> __device__ __forceinline__ float ld_in<uint16_t>(const void* p, size_t i) {
   return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
@@ -113,29 +96,71 @@ template <> __device__ __forceinline__ float ld_in<float>(const void* p, size_t 
   return static_cast<const float*>(p)[i];
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit data
+// format); loads outside the range return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Wait until every vector-memory load of this wave (the direct-to-LDS tile
+// loads) has completed; a builtin, so the compiler's own bookkeeping knows.
+__device__ __forceinline__ void wait_vmem() {
+  // vmcnt(0), expcnt and lgkmcnt unconstrained (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // LDS layout. The key tile is kNP panels of [32 keys][64 features], the
-// value tile [D features][32 keys]; every row is padded by one 16-byte chunk,
-// which spreads the 32 rows that one matrix-core operand read touches over
-// distinct LDS banks. Two buffers of each.
+// value tile [D features][32 keys]; rows are unpadded runs of 16-byte chunks
+// and chunk c of row r sits in slot c ^ sw(r) (Swz below). Without padding
+// one wave-wide direct-to-LDS load fills whole rows, and the swizzle spreads
+// the 16 rows that 16 consecutive lanes read in one LDS cycle over distinct
+// banks.
 template <typename T, int D>
 struct Smem {
   static constexpr int kPW = D - kHeadW;
-  static constexpr int kEpc = Mma<T>::kEpc;
   static constexpr int kNP = D / 64;                               // 64-feature panels
-  static constexpr int kKRow = 64 + Mma<T>::kPad;                  // elements per key-panel row
-  static constexpr int kKPanel = kKT * kKRow;                      // elements per key panel
-  static constexpr int kKBuf = kNP * kKPanel;                      // elements per key buffer
-  static constexpr int kVRow = kKT + Mma<T>::kPad;                 // elements per value row
-  static constexpr int kVBuf = D * kVRow;                          // elements per value buffer
+  static constexpr int kKPanel = kKT * 64 * (int)sizeof(T);         // bytes per key panel
+  static constexpr int kKBuf = kNP * kKPanel;                       // bytes per key buffer
+  static constexpr int kVPanel = 64 * kKT * (int)sizeof(T);         // bytes per 64 value rows
+  static constexpr int kVBuf = kNP * kVPanel;                       // bytes per value buffer
   static constexpr int kCzMax = kPW < 128 ? kPW : 128;
-  static constexpr int kPairBytes = 4 * 32 * (kCzMax > 0 ? kCzMax : 1) * 4;
-  // the key buffers also hold the pair-output buffer of the epilogue
-  static constexpr int kKBytes = 2 * kKBuf * (int)sizeof(T) > kPairBytes
-                                     ? 2 * kKBuf * (int)sizeof(T) : kPairBytes;
-  static constexpr int kVBytes = 2 * kVBuf * (int)sizeof(T);
-  // 16-byte chunks each thread stages per tile (key part or value part)
-  static constexpr int kCPT = kNP * (64 / kEpc) * kKT / 256;
+  static constexpr int kPRow = kCzMax + 1;                          // floats per pair-buffer row
 };
+
+// XOR swizzle of rows made of RCH 16-byte chunks (RCH a power of two, <= 16).
+// The LDS bank pattern repeats every 256 bytes, i.e. every kRPB = 16 / RCH
+// rows; sw(r) = (r / kRPB) % RCH gives the rows that share bank positions
+// distinct slots.
+template <int RCH>
+struct Swz {
+  static_assert(RCH >= 1 && RCH <= 16 && (RCH & (RCH - 1)) == 0, "chunks per row");
+  static constexpr int kRPB = 16 / RCH;   // rows per 256-byte bank period
+  static constexpr int kRPL = 64 / RCH;   // rows per wave-wide 16-byte-per-lane load
+  __device__ static __forceinline__ int sw(int r) { return (r / kRPB) % RCH; }
+  // byte offset of element e (of `es` bytes) of row r
+  __device__ static __forceinline__ int at(int r, int e, int es) {
+    const int epc = 16 / es;
+    return r * RCH * 16 + (((e / epc) ^ sw(r)) * 16) + (e % epc) * es;
+  }
+  // Per-lane source byte offset for the wave-wide load number k of a block
+  // of rows (source rows srcRow bytes apart). Load k covers rows
+  // k kRPL .. k kRPL + kRPL - 1 and lane l lands in LDS slot l % RCH of row
+  // l / RCH, so it fetches source chunk (l % RCH) ^ sw(row). Since
+  // kRPL = 4 kRPB and RCH <= 16, sw(row) depends on k only through k % 4:
+  // a wave that issues loads k = w, w + 4, ... keeps one offset for all.
+  __device__ static __forceinline__ uint32_t voff(int lane, int k, int srcRow) {
+    const int r = k * kRPL + lane / RCH;
+    return (uint32_t)((lane / RCH) * srcRow + (((lane % RCH) ^ sw(r)) * 16));
+  }
+};
+
+// One wave-wide direct-to-LDS load: 16 bytes per lane from
+// rsrc + soff + voff into LDS bytes lds + 16 lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                                      unsigned char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -149,19 +174,28 @@ void ipa_attn_kernel(FwdArgs a) {
   constexpr int NP = SM::kNP;
   constexpr int EPC = M::kEpc;
   constexpr int NST = kKT / M::kStep;      // products per O^T block per tile
-  constexpr int CPT = SM::kCPT;
-  static_assert(CPT * 256 == NP * (64 / EPC) * kKT, "tile chunks must split over 256 threads");
+  constexpr int ES = (int)sizeof(T);
 
-  __shared__ __attribute__((aligned(16))) unsigned char smemK[SM::kKBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char smemV[SM::kVBytes];
-  __shared__ float4 kcS[2][kKT];
+  // key rows: 64 elements of one panel; value rows: 32 keys
+  using KS = Swz<64 * ES / 16>;
+  using VS = Swz<kKT * ES / 16>;
+  constexpr int KJ = kKT / KS::kRPL / 4;   // key loads per panel per wave
+  constexpr int VJ = 64 / VS::kRPL / 4;    // value loads per 64 rows per wave
+  static_assert(KJ >= 1 && KJ * 4 * KS::kRPL == kKT, "key tile rows per load");
+  static_assert(VJ >= 1 && VJ * 4 * VS::kRPL == 64, "value tile rows per load");
+
+  __shared__ __attribute__((aligned(16))) unsigned char K0[SM::kKBuf];
+  __shared__ __attribute__((aligned(16))) unsigned char K1[SM::kKBuf];
+  __shared__ __attribute__((aligned(16))) unsigned char V0[SM::kVBuf];
+  __shared__ __attribute__((aligned(16))) unsigned char V1[SM::kVBuf];
+  __shared__ __attribute__((aligned(16))) float4 kc0[kKT];
+  __shared__ __attribute__((aligned(16))) float4 kc1[kKT];
   __shared__ float colbuf[4][kKT];
   // per 64-key block: centre xyz and valid-key count, staged once so the key
-  // loop issues no vector-memory reads besides its tile loads
+  // loop reads nothing else from global memory
   __shared__ float4 cenS[kMaxTiles];
-
-  T* const Kb = reinterpret_cast<T*>(smemK);
-  T* const Vb = reinterpret_cast<T*>(smemV);
+  // pair-output accumulation of the epilogue (two waves at a time)
+  __shared__ float pbuf[2][32][SM::kPRow];
 
   const Layout& ly = a.lay;
   const int L = ly.L, H = ly.H, Lp = ly.Lp, nJ = ly.nJ;
@@ -177,17 +211,17 @@ void ipa_attn_kernel(FwdArgs a) {
   const int nid = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
   const int qb = nid % nQB, h = (nid / nQB) % H, b = nid / (nQB * H);
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int qw = qb * kTileM + 32 * w;  // first query row of this wave
   const int i = qw + n;                 // this lane's query row
 
   const size_t bh = (size_t)b * H + h;
-  const T* Kh = reinterpret_cast<const T*>(a.ws + ly.off_kh) + bh * Lp * kHeadW;
-  const T* Kz = reinterpret_cast<const T*>(a.ws + ly.off_kz) + (size_t)b * nJ * (NP - 1) * 4096;
-  const T* Vth = reinterpret_cast<const T*>(a.ws + ly.off_vth) + bh * nJ * 4096;
-  const T* Vtz = reinterpret_cast<const T*>(a.ws + ly.off_vtz) + (size_t)b * nJ * (NP - 1) * 4096;
-  const float4* kcol = reinterpret_cast<const float4*>(a.ws + ly.off_kcol) + bh * Lp;
+  const unsigned char* Kh = a.ws + ly.off_kh + bh * Lp * kHeadW * ES;
+  const unsigned char* Kz = a.ws + ly.off_kz + (size_t)b * nJ * (NP - 1) * 4096 * ES;
+  const unsigned char* Vth = a.ws + ly.off_vth + bh * nJ * 4096 * ES;
+  const unsigned char* Vtz = a.ws + ly.off_vtz + (size_t)b * nJ * (NP - 1) * 4096 * ES;
+  const unsigned char* kcol = a.ws + ly.off_kcol + bh * Lp * 16;
   {
     const float4* cen = reinterpret_cast<const float4*>(a.ws + ly.off_cen) + (size_t)b * nJ;
     for (int e = tid; e < nJ; e += 256) cenS[e] = cen[e];
@@ -255,63 +289,51 @@ void ipa_attn_kernel(FwdArgs a) {
   __syncthreads();  // cenS
   const float4 cI = cenS[qw / kTileN];
 
-  // ---- tile staging: global -> registers -> LDS ----
-  // Key tile t (keys 32t .. 32t+31): chunk m of this thread lies in panel
-  // ch / (32 * KCPR), key (ch / KCPR) % 32, column chunk ch % KCPR, with
-  // ch = tid + 256 m. Value tile: chunk m is feature ch / VCPR, key chunk
-  // ch % VCPR of the tile's half of its 64-key value block.
-  constexpr int KCPR = 64 / EPC;               // chunks per key-panel row
-  constexpr int VCPR = kKT / EPC;              // chunks per value row
-  Regs<CPT> st;
-  float4 kcst = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto load_k = [&](int t) {
+  // ---- direct-to-LDS copy of one tile (keys 32 t .. 32 t + 31) ----
+  // Wave w issues loads w, w + 4, ... of every panel, so its per-lane source
+  // offsets are fixed; all tile-dependent parts are wave-uniform (scalar).
+  const __amdgpu_buffer_rsrc_t rKh = make_rsrc(Kh, (uint32_t)Lp * 64 * ES);
+  const __amdgpu_buffer_rsrc_t rKz = make_rsrc(Kz, (uint32_t)nJ * (NP - 1) * 4096 * ES);
+  const __amdgpu_buffer_rsrc_t rVh = make_rsrc(Vth, (uint32_t)nJ * 4096 * ES);
+  const __amdgpu_buffer_rsrc_t rVz = make_rsrc(Vtz, (uint32_t)nJ * (NP - 1) * 4096 * ES);
+  const __amdgpu_buffer_rsrc_t rKc = make_rsrc(kcol, (uint32_t)Lp * 16);
+  const uint32_t voK = KS::voff(lane, w, 64 * ES);
+  const uint32_t voV = VS::voff(lane, w, 64 * ES);
+  auto copy_tile = [&](int t, unsigned char* Kd, unsigned char* Vd, float4* kcd) {
     const int J = t >> 1, half = t & 1;
-    static_for<0, CPT>([&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      const int ch = tid + 256 * m;
-      const int P = ch / (kKT * KCPR), r = (ch / KCPR) % kKT, c = ch % KCPR;
-      const int key = 32 * half + r;                      // key within the 64-block
-      const T* src = P == 0 ? Kh + ((size_t)J * 64 + key) * kHeadW + c * EPC
-                            : Kz + (((size_t)J * (NP - 1) + P - 1) * 64 + key) * 64 + c * EPC;
-      reg<m>(st) = *reinterpret_cast<const u32x4*>(src);
-    });
-    if (tid < kKT) kcst = kcol[(size_t)t * kKT + tid];
-  };
-  auto store_k = [&](int bf) {
-    static_for<0, CPT>([&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      const int ch = tid + 256 * m;
-      const int P = ch / (kKT * KCPR), r = (ch / KCPR) % kKT, c = ch % KCPR;
-      *reinterpret_cast<u32x4*>(Kb + bf * SM::kKBuf + P * SM::kKPanel + r * SM::kKRow + c * EPC) = reg<m>(st);
-    });
-    if (tid < kKT) kcS[bf][tid] = kcst;
-  };
-  auto load_v = [&](int t) {
-    const int J = t >> 1, half = t & 1;
-    static_for<0, CPT>([&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      const int ch = tid + 256 * m;
-      const int f = ch / VCPR, c = ch % VCPR;
-      const T* src = f < kHeadW ? Vth + ((size_t)J * 64 + f) * 64 + 32 * half + c * EPC
-                                : Vtz + ((size_t)J * (NP - 1) * 64 + (f - kHeadW)) * 64 + 32 * half + c * EPC;
-      reg<m>(st) = *reinterpret_cast<const u32x4*>(src);
-    });
-  };
-  auto store_v = [&](int bf) {
-    static_for<0, CPT>([&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      const int ch = tid + 256 * m;
-      const int f = ch / VCPR, c = ch % VCPR;
-      *reinterpret_cast<u32x4*>(Vb + bf * SM::kVBuf + f * SM::kVRow + c * EPC) = reg<m>(st);
-    });
+#pragma unroll
+    for (int P = 0; P < NP; ++P) {
+      // key rows 32 half .. of 64-key block J, panel P (source rows of 64 elements)
+      const uint32_t kbase = P == 0 ? (uint32_t)(J * 64 + 32 * half) * 64 * ES
+                                    : (uint32_t)((J * (NP - 1) + P - 1) * 64 + 32 * half) * 64 * ES;
+#pragma unroll
+      for (int j = 0; j < KJ; ++j) {
+        const int k = w + 4 * j;
+        dma16(P == 0 ? rKh : rKz, voK, kbase + (uint32_t)(k * KS::kRPL * 64 * ES),
+              Kd + P * SM::kKPanel + k * 1024);
+      }
+      // value rows 64 P .. 64 P + 63 (features), keys 32 half .. of block J
+      const uint32_t vbase = (P == 0 ? (uint32_t)J * 4096 * ES : (uint32_t)(J * (NP - 1) + P - 1) * 4096 * ES) +
+                             (uint32_t)(32 * half * ES);
+#pragma unroll
+      for (int j = 0; j < VJ; ++j) {
+        const int k = w + 4 * j;
+        dma16(P == 0 ? rVh : rVz, voV, vbase + (uint32_t)(k * VS::kRPL * 64 * ES),
+              Vd + P * SM::kVPanel + k * 1024);
+      }
+    }
+    if (w == 0 && lane < kKT)
+      dma16(rKc, (uint32_t)lane * 16, (uint32_t)t * kKT * 16, reinterpret_cast<unsigned char*>(kcd));
   };
 
   // key tiles are visited starting at this block's own diagonal tile; tiles
   // whose 64-key block has no valid key are skipped (they could only add zeros)
   const int T0 = (qb * kTileM / kKT) % nT;
   auto tile_of = [&](int uu) { int t = T0 + uu; return t >= nT ? t - nT : t; };
+  // (the valid-key count is read from LDS; readfirstlane tells the compiler
+  // that it, and hence every tile index and copy address, is wave-uniform)
   auto next_nonempty = [&](int uu) {
-    while (uu < nT && cenS[tile_of(uu) >> 1].w == 0.f) ++uu;
+    while (uu < nT && __builtin_amdgcn_readfirstlane(__float_as_int(cenS[tile_of(uu) >> 1].w)) == 0) ++uu;
     return uu;
   };
 
@@ -321,28 +343,13 @@ void ipa_attn_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_own = 0.f;
   float ocx = 0.f, ocy = 0.f, ocz = 0.f;
 
-  int u = next_nonempty(0);
-  int buf = 0;
-  if (u < nT) {
-    load_k(tile_of(u));
-    store_k(0);
-    load_v(tile_of(u));
-    store_v(0);
-  }
-  __syncthreads();
-
-  while (u < nT) {
-    const int t = tile_of(u);
-    const int un = next_nonempty(u + 1);
-    const bool more = un < nT;
-    const int tn = more ? tile_of(un) : 0;
-    if (more) load_k(tn);
-
+  // ---- one tile of the key loop on the buffers Kc / Vc / kcc ----
+  auto compute_tile = [&](int t, const unsigned char* Kc, const unsigned char* Vc, const float4* kcc) {
     // ---------------- phase A: scores and probabilities ----------------
     const float4 cJ = cenS[t >> 1];
     const float dx = cI.x - cJ.x, dy = cI.y - cJ.y, dz = cI.z - cJ.z;
     if (lane < kKT) {
-      const float4 kc = kcS[buf][lane];
+      const float4 kc = kcc[lane];
       colbuf[w][lane] = kc.w + 2.f * kap * (dx * kc.x + dy * kc.y + dz * kc.z);
     }
     const float rterm = sizeof(T) == 4 ? 0.f
@@ -351,14 +358,13 @@ void ipa_attn_kernel(FwdArgs a) {
     f32x16 sacc = f32x16{};
     {
       // operand reads run kLook products ahead of the matrix core
-      const T* krow = Kb + buf * SM::kKBuf + n * SM::kKRow;
       auto kfrag = [&](int s) -> Frag {
         const int f = M::kStep * s;
-        const T* r = krow + (f / 64) * SM::kKPanel + (f % 64);
+        const unsigned char* r = Kc + (f / 64) * SM::kKPanel;
         if constexpr (sizeof(T) == 2)
-          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + 8 * g));
+          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + KS::at(n, f % 64 + 8 * g, 2)));
         else
-          return r[g];
+          return *reinterpret_cast<const float*>(r + KS::at(n, f % 64 + g, 4));
       };
       Frag look[kLook];
 #pragma unroll
@@ -383,12 +389,11 @@ void ipa_attn_kernel(FwdArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int j = 8 * (v >> 2) + 4 * g + (v & 3);
-        const float* bp = reinterpret_cast<const float*>(Kb) + buf * SM::kKBuf + j * SM::kKRow + kCSlot;
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < 15; ++e) {
           if (e < 3 * Pqk) {
-            const float tt = ad[e] - bp[e];
+            const float tt = ad[e] - *reinterpret_cast<const float*>(Kc + KS::at(j, kCSlot + e, 4));
             d = fmaf(tt, tt, d);
           }
         }
@@ -418,7 +423,7 @@ void ipa_attn_kernel(FwdArgs a) {
       for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
         for (int v = 0; v < 16; v += 4) {
-          // a few registers at a time keeps the accumulator copies short-lived
+          // a few registers at a time keeps the temporaries short-lived
           oacc[fb][v] *= al; oacc[fb][v + 1] *= al; oacc[fb][v + 2] *= al; oacc[fb][v + 3] *= al;
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -454,21 +459,15 @@ void ipa_attn_kernel(FwdArgs a) {
     l_own += lt;
     ocx += lt * cJ.x; ocy += lt * cJ.y; ocz += lt * cJ.z;
 
-    if (more) {
-      store_k(buf ^ 1);
-      load_v(tn);
-    }
-
     // ---------------- phase B: O^T += V^T P^T ----------------
     {
-      const T* vrow = Vb + buf * SM::kVBuf + n * SM::kVRow;
       auto vfrag = [&](int idx) -> Frag {
         const int fb = idx / NST, s2 = idx % NST;
-        const T* r = vrow + 32 * fb * SM::kVRow;
+        const unsigned char* r = Vc + 32 * fb * kKT * ES;
         if constexpr (sizeof(T) == 2)
-          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + 16 * s2 + 8 * g));
+          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + VS::at(n, 16 * s2 + 8 * g, 2)));
         else
-          return r[2 * s2 + g];
+          return *reinterpret_cast<const float*>(r + VS::at(n, 2 * s2 + g, 4));
       };
       constexpr int NB = NFB * NST;
       Frag look[kLook];
@@ -482,10 +481,30 @@ void ipa_attn_kernel(FwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (more) store_v(buf ^ 1);
+  };
+
+  // ---- key loop, unrolled by two over the buffer pairs (0 -> 1 -> 0 ...);
+  //      the second half is a branch of the body, not a second loop exit, so
+  //      the accumulators keep their registers across iterations ----
+  int u = next_nonempty(0);
+  if (u < nT) copy_tile(tile_of(u), K0, V0, kc0);
+  wait_vmem();
+  __syncthreads();
+  while (u < nT) {
+    int un = next_nonempty(u + 1);
+    if (un < nT) copy_tile(tile_of(un), K1, V1, kc1);
+    compute_tile(tile_of(u), K0, V0, kc0);
+    wait_vmem();
     __syncthreads();
-    buf ^= 1;
     u = un;
+    if (u < nT) {
+      un = next_nonempty(u + 1);
+      if (un < nT) copy_tile(tile_of(un), K0, V0, kc0);
+      compute_tile(tile_of(u), K1, V1, kc1);
+      wait_vmem();
+      __syncthreads();
+      u = un;
+    }
   }
 
   // ---------------- epilogue ----------------
@@ -535,33 +554,40 @@ void ipa_attn_kernel(FwdArgs a) {
     }
   }
 
-  // pair channels: accumulate sum_r z1_ir * O_pair,r in LDS, then write rows
-  __syncthreads();  // every wave is done with the key/value tiles
-  float* pbuf = reinterpret_cast<float*>(smemK) + (size_t)w * 32 * Cz;
-  for (int e = lane; e < 32 * Cz; e += 64) pbuf[e] = 0.f;
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  if (ok) {
+  // pair channels: sum_r z1_ir * O_pair,r accumulated in LDS (rows padded by
+  // one float, so the 32 rows of a wave fall in distinct banks), two waves
+  // at a time, then written out row by row
 #pragma unroll
-    for (int fb = 2; fb < NFB; ++fb)
+  for (int pass = 0; pass < 2; ++pass) {
+    if ((w >> 1) == pass) {
+      float* pb = &pbuf[w & 1][0][0];
+      for (int e = lane; e < 32 * SM::kPRow; e += 64) pb[e] = 0.f;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (ok) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+        for (int fb = 2; fb < NFB; ++fb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int uu = 32 * (fb - 2) + 8 * k + 4 * g + e;
-          if (uu < RCz) {
-            const int c = uu % Cz;
-            const float z = ld_in<T>(a.z1, ((size_t)b * L + i) * RCz + uu);
-            pbuf[n * Cz + c] += z * oacc[fb][4 * k + e] * inv;
-          }
-        }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  for (int e = lane; e < 32 * Cz; e += 64) {
-    const int nn = e / Cz, c = e - nn * Cz;
-    const int ii = qw + nn;
-    if (ii < L) a.out_pair[(((size_t)b * L + ii) * H + h) * Cz + c] = pbuf[e];
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int uu = 32 * (fb - 2) + 8 * k + 4 * g + e;
+              if (uu < RCz) {
+                const int c = uu % Cz;
+                const float z = ld_in<T>(a.z1, ((size_t)b * L + i) * RCz + uu);
+                pb[n * SM::kPRow + c] += z * oacc[fb][4 * k + e] * inv;
+              }
+            }
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      for (int e = lane; e < 32 * Cz; e += 64) {
+        const int nn = e / Cz, c = e - nn * Cz;
+        const int ii = qw + nn;
+        if (ii < L) a.out_pair[(((size_t)b * L + ii) * H + h) * Cz + c] = pb[nn * SM::kPRow + c];
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -574,7 +600,6 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
   switch (a.lay.D) {
-    case 64: return launch_d<uint16_t, 64>(a, s);
     case 128: return launch_d<uint16_t, 128>(a, s);
     case 192: return launch_d<uint16_t, 192>(a, s);
     case 256: return launch_d<uint16_t, 256>(a, s);
@@ -587,7 +612,6 @@ hipError_t launch_bf16(const FwdArgs& a, hipStream_t s) {
 // rows wider than kMaxDF32 are rejected by the host checks.
 hipError_t launch_f32(const FwdArgs& a, hipStream_t s) {
   switch (a.lay.D) {
-    case 64: return launch_d<float, 64>(a, s);
     case 128: return launch_d<float, 128>(a, s);
     case 192: return launch_d<float, 192>(a, s);
     default: return hipErrorInvalidValue;
