@@ -25,12 +25,8 @@ HIPCC_FLAGS = [
     "-I", str(ROOT / "include"),
 ]
 
-# Per-source extra flags. The attention kernel keeps its matrix-core
-# accumulators in architectural VGPRs (operands of the online-softmax
-# rescale), leaving the AGPRs for the query operand.
-EXTRA_FLAGS = {
-    "ipa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-}
+# Per-source extra flags (none at present).
+EXTRA_FLAGS: dict[str, list[str]] = {}
 
 
 def _hipcc() -> str:

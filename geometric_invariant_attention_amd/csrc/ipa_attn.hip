@@ -31,6 +31,8 @@
 // the value product, the row sum and the block-centre correction, so the
 // output is a convex combination of the value rows.
 
+#include <type_traits>
+
 #include "ipa_internal.h"
 
 namespace ipa {
@@ -41,12 +43,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLazy = 8.0f;
 // Keys per tile of the key loop (the centring blocks stay 64 residues).
 constexpr int kKT = 32;
 // Operand fragments read ahead of the matrix-core products that use them.
-constexpr int kLook = 4;
+constexpr int kLook = 6;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -88,13 +93,41 @@ __device__ __forceinline__ f32x16 mma_pair(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <typename T> __device__ __forceinline__ float ld_in(const void* p, size_t i);
-template <> __device__ __forceinline__ float ld_in<uint16_t>(const void* p, size_t i) {
-  return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+
+// Step boundary of a hand-scheduled product loop: neither the compiler's IR
+// passes (memory fence) nor its instruction scheduler may move work across.
+__device__ __forceinline__ void step_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
-template <> __device__ __forceinline__ float ld_in<float>(const void* p, size_t i) {
-  return static_cast<const float*>(p)[i];
+
+// An empty, ordered statement that takes an accumulator tile in place: a
+// product whose result passes through it stays in its step. No instruction
+// is emitted and no register is read.
+__device__ __forceinline__ void pin_step(f32x16& acc) { asm volatile("" : "+a"(acc)); }
+__device__ __forceinline__ void pin_step(f32x16&, int) {}
+
+// o *= al for one 32x32 accumulator tile, in place in the accumulation
+// registers, so that the output accumulators never leave them (plain vector
+// code on them would move the whole tile to architectural registers and
+// back on every iteration). The caller first waits out the matrix-core write
+// latency (acc_settle) and, after the last tile, lets the writes settle
+// before the next product reads them.
+__device__ __forceinline__ void scale_acc(f32x16& o, float al) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(o[v]), "=&v"(t)
+        : "v"(al));
+  }
 }
+// 32 wait states: more than any matrix-core result or accumulation-register
+// write needs before the next access to the same registers.
+__device__ __forceinline__ void acc_settle() { asm volatile("s_nop 15\n\ts_nop 15"); }
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit data
 // format); loads outside the range return zero instead of touching memory.
@@ -188,12 +221,14 @@ void ipa_attn_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char K1[SM::kKBuf];
   __shared__ __attribute__((aligned(16))) unsigned char V0[SM::kVBuf];
   __shared__ __attribute__((aligned(16))) unsigned char V1[SM::kVBuf];
-  __shared__ __attribute__((aligned(16))) float4 kc0[kKT];
-  __shared__ __attribute__((aligned(16))) float4 kc1[kKT];
   __shared__ float colbuf[4][kKT];
   // per 64-key block: centre xyz and valid-key count, staged once so the key
   // loop reads nothing else from global memory
   __shared__ float4 cenS[kMaxTiles];
+  // visiting order of the non-empty 32-key tiles (tile indices)
+  __shared__ uint16_t seqS[2 * kMaxTiles];
+  // w_L log2(e) W_b[:, h], the per-channel scale of the query pair columns
+  __shared__ __attribute__((aligned(16))) float wbS[128];
   // pair-output accumulation of the epilogue (two waves at a time)
   __shared__ float pbuf[2][32][SM::kPRow];
 
@@ -225,56 +260,68 @@ void ipa_attn_kernel(FwdArgs a) {
   {
     const float4* cen = reinterpret_cast<const float4*>(a.ws + ly.off_cen) + (size_t)b * nJ;
     for (int e = tid; e < nJ; e += 256) cenS[e] = cen[e];
+    const float* wbt = reinterpret_cast<const float*>(a.ws + ly.off_wbt) + (size_t)h * Cz;
+    for (int e = tid; e < Cz; e += 256) wbS[e] = wbt[e];
   }
+  __syncthreads();  // cenS, wbS
 
   const float kap = a.w_L * a.gamma[h] * a.w_C * 0.5f * kLog2e;
   const bool row_valid = (i < L) && (a.mask == nullptr || a.mask[(size_t)b * L + i] != 0);
 
   // ---- query operand (B operand of S^T = K Q^T), held for the whole loop ----
+  // Loads are unconditional buffer loads (rows past L clamp to row 0, and
+  // are zeroed afterwards) so that they all issue back to back.
   Frag qf[NKS];
-  {
-    const T* Qh = reinterpret_cast<const T*>(a.ws + ly.off_qh) + (bh * Lp + i) * kHeadW;
-    const float* wbt = reinterpret_cast<const float*>(a.ws + ly.off_wbt) + (size_t)h * Cz;
-    if constexpr (sizeof(T) == 2) {
+  const int ic = i < L ? i : 0;
+  if constexpr (sizeof(T) == 2) {
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.ws + ly.off_qh + bh * Lp * kHeadW * ES, (uint32_t)Lp * kHeadW * ES);
+    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(static_cast<const uint16_t*>(a.z1) + (size_t)b * L * RCz,
+                                                (uint32_t)L * RCz * ES);
+    const int vq = (i * kHeadW + 8 * g) * ES;
+    const int vz = (ic * RCz + 8 * g) * ES;
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const int f0 = 16 * s + 8 * g;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (f0 < kHeadW) {
-          raw = *reinterpret_cast<const uint4*>(Qh + f0);
-        } else {
-          const int u0 = f0 - kHeadW;
-          if (u0 < RCz && i < L) {
-            const int c0 = u0 % Cz;
-            const uint16_t* zp = static_cast<const uint16_t*>(a.z1) + ((size_t)b * L + i) * RCz + u0;
-            const uint4 zr = *reinterpret_cast<const uint4*>(zp);
-            const uint32_t zw[4] = {zr.x, zr.y, zr.z, zr.w};
-            uint32_t o[4];
+    for (int s = 0; s < NKH; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, vq + 32 * s, 0, 0));
+    u32x4 zr[NKS - NKH];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float lo = __uint_as_float(zw[e] << 16) * wbt[c0 + 2 * e];
-              const float hi = __uint_as_float(zw[e] & 0xFFFF0000u) * wbt[c0 + 2 * e + 1];
-              o[e] = (uint32_t)f32_to_f16_sat(lo) | ((uint32_t)f32_to_f16_sat(hi) << 16);
-            }
-            raw = make_uint4(o[0], o[1], o[2], o[3]);
-          }
-        }
-        qf[s] = __builtin_bit_cast(bf16x8, raw);
+    for (int s = NKH; s < NKS; ++s) zr[s - NKH] = __builtin_amdgcn_raw_buffer_load_b128(rZ, vz + 32 * (s - NKH), 0, 0);
+    // pair column u0 = 16 (s - NKH) + 8 g scales channel u0 mod Cz (stepped
+    // without division; Cz >= 8)
+    int c0 = 8 * g;
+    if (c0 >= Cz) c0 -= Cz;
+#pragma unroll
+    for (int s = NKH; s < NKS; ++s) {
+      const int u0 = 16 * (s - NKH) + 8 * g;
+      const float4 w0 = *reinterpret_cast<const float4*>(&wbS[c0]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&wbS[c0 + 4]);
+      const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t zw = zr[s - NKH][e];
+        const float lo = __uint_as_float(zw << 16) * ws[2 * e];
+        const float hi = __uint_as_float(zw & 0xFFFF0000u) * ws[2 * e + 1];
+        o[e] = (uint32_t)f32_to_f16_sat(lo) | ((uint32_t)f32_to_f16_sat(hi) << 16);
       }
-    } else {
+      const bool use = u0 < RCz && i < L;
+      qf[s] = __builtin_bit_cast(bf16x8, use ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{0u, 0u, 0u, 0u});
+      c0 += 16;
+      if (c0 >= Cz) c0 -= Cz;
+      if (c0 >= Cz) c0 -= Cz;
+    }
+  } else {
+    const float* Qh = reinterpret_cast<const float*>(a.ws + ly.off_qh) + (bh * Lp + i) * kHeadW;
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const int f = 2 * s + g;
-        float v = 0.f;
-        if (f < kHeadW) {
-          v = reinterpret_cast<const float*>(Qh)[f];
-        } else {
-          const int uu = f - kHeadW;
-          if (uu < RCz && i < L)
-            v = static_cast<const float*>(a.z1)[((size_t)b * L + i) * RCz + uu] * wbt[uu % Cz];
-        }
-        qf[s] = v;
+    for (int s = 0; s < NKS; ++s) {
+      const int f = 2 * s + g;
+      float v = 0.f;
+      if (f < kHeadW) {
+        v = Qh[f];
+      } else {
+        const int uu = f - kHeadW;
+        if (uu < RCz && i < L) v = static_cast<const float*>(a.z1)[((size_t)b * L + i) * RCz + uu] * wbS[uu % Cz];
       }
+      qf[s] = v;
     }
   }
   const float4 qr = reinterpret_cast<const float4*>(a.ws + ly.off_qrow)[bh * Lp + i];
@@ -286,7 +333,6 @@ void ipa_attn_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < 15; ++e) apt[e] = e < 3 * Pqk ? Qh[kFpQPts + e] : 0.f;
   }
-  __syncthreads();  // cenS
   const float4 cI = cenS[qw / kTileN];
 
   // ---- direct-to-LDS copy of one tile (keys 32 t .. 32 t + 31) ----
@@ -299,42 +345,27 @@ void ipa_attn_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rKc = make_rsrc(kcol, (uint32_t)Lp * 16);
   const uint32_t voK = KS::voff(lane, w, 64 * ES);
   const uint32_t voV = VS::voff(lane, w, 64 * ES);
-  auto copy_tile = [&](int t, unsigned char* Kd, unsigned char* Vd, float4* kcd) {
-    const int J = t >> 1, half = t & 1;
-#pragma unroll
-    for (int P = 0; P < NP; ++P) {
-      // key rows 32 half .. of 64-key block J, panel P (source rows of 64 elements)
-      const uint32_t kbase = P == 0 ? (uint32_t)(J * 64 + 32 * half) * 64 * ES
-                                    : (uint32_t)((J * (NP - 1) + P - 1) * 64 + 32 * half) * 64 * ES;
-#pragma unroll
-      for (int j = 0; j < KJ; ++j) {
-        const int k = w + 4 * j;
-        dma16(P == 0 ? rKh : rKz, voK, kbase + (uint32_t)(k * KS::kRPL * 64 * ES),
-              Kd + P * SM::kKPanel + k * 1024);
-      }
-      // value rows 64 P .. 64 P + 63 (features), keys 32 half .. of block J
-      const uint32_t vbase = (P == 0 ? (uint32_t)J * 4096 * ES : (uint32_t)(J * (NP - 1) + P - 1) * 4096 * ES) +
-                             (uint32_t)(32 * half * ES);
-#pragma unroll
-      for (int j = 0; j < VJ; ++j) {
-        const int k = w + 4 * j;
-        dma16(P == 0 ? rVh : rVz, voV, vbase + (uint32_t)(k * VS::kRPL * 64 * ES),
-              Vd + P * SM::kVPanel + k * 1024);
-      }
-    }
-    if (w == 0 && lane < kKT)
-      dma16(rKc, (uint32_t)lane * 16, (uint32_t)t * kKT * 16, reinterpret_cast<unsigned char*>(kcd));
-  };
-
-  // key tiles are visited starting at this block's own diagonal tile; tiles
-  // whose 64-key block has no valid key are skipped (they could only add zeros)
+  // Key tiles are visited starting at this block's own diagonal tile; tiles
+  // whose 64-key block has no valid key are skipped (they could only add
+  // zeros). seqS[0 .. nseq) lists the visited tiles in order: built once,
+  // 64 candidates per ballot, so that the key loop does no searching.
   const int T0 = (qb * kTileM / kKT) % nT;
-  auto tile_of = [&](int uu) { int t = T0 + uu; return t >= nT ? t - nT : t; };
-  // (the valid-key count is read from LDS; readfirstlane tells the compiler
-  // that it, and hence every tile index and copy address, is wave-uniform)
-  auto next_nonempty = [&](int uu) {
-    while (uu < nT && __builtin_amdgcn_readfirstlane(__float_as_int(cenS[tile_of(uu) >> 1].w)) == 0) ++uu;
-    return uu;
+  int nseq = 0;
+  for (int c = 0; c < nT; c += 64) {
+    const int uu = c + lane;
+    int t = T0 + uu;
+    if (t >= nT) t -= nT;
+    const bool f = uu < nT && cenS[(uu < nT ? t : 0) >> 1].w != 0.f;
+    const uint64_t m = __ballot(f);
+    if (f && w == 0) seqS[nseq + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)t;
+    nseq += __popcll(m);
+  }
+  __syncthreads();  // seqS
+  // tile at sequence position s (past the end: the last one, a valid tile
+  // whose copies are never read); readfirstlane marks it wave-uniform, and
+  // with it every copy address
+  auto tile_at = [&](int sq) -> int {
+    return __builtin_amdgcn_readfirstlane((int)seqS[sq < nseq ? sq : nseq - 1]);
   };
 
   f32x16 oacc[NFB];
@@ -343,46 +374,60 @@ void ipa_attn_kernel(FwdArgs a) {
   float m_run = -INFINITY, l_own = 0.f;
   float ocx = 0.f, ocy = 0.f, ocz = 0.f;
 
-  // ---- one tile of the key loop on the buffers Kc / Vc / kcc ----
-  auto compute_tile = [&](int t, const unsigned char* Kc, const unsigned char* Vc, const float4* kcc) {
-    // ---------------- phase A: scores and probabilities ----------------
-    const float4 cJ = cenS[t >> 1];
+  // Column data of tile t (key lane & 31), read straight into registers one
+  // iteration before use; lanes 32..63 duplicate lanes 0..31.
+  auto load_kc = [&](int t) -> float4 {
+    const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rKc, (lane & 31) * 16, t * kKT * 16, 0);
+    return make_float4(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[2]), __uint_as_float(r[3]));
+  };
+  // Column term of tile t (key lane & 31; both halves of the wave write the
+  // same value) into colbuf[w]; returns the row term of this lane's query
+  // against tile t.
+  auto col_prep = [&](const float4 kc, const float4 cJ) -> float {
     const float dx = cI.x - cJ.x, dy = cI.y - cJ.y, dz = cI.z - cJ.z;
-    if (lane < kKT) {
-      const float4 kc = kcc[lane];
-      colbuf[w][lane] = kc.w + 2.f * kap * (dx * kc.x + dy * kc.y + dz * kc.z);
-    }
-    const float rterm = sizeof(T) == 4 ? 0.f
-                        : -kap * (2.f * (dx * qr.x + dy * qr.y + dz * qr.z) +
-                                  (float)Pqk * (dx * dx + dy * dy + dz * dz));
-    f32x16 sacc = f32x16{};
-    {
-      // operand reads run kLook products ahead of the matrix core
-      auto kfrag = [&](int s) -> Frag {
-        const int f = M::kStep * s;
-        const unsigned char* r = Kc + (f / 64) * SM::kKPanel;
-        if constexpr (sizeof(T) == 2)
-          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + KS::at(n, f % 64 + 8 * g, 2)));
-        else
-          return *reinterpret_cast<const float*>(r + KS::at(n, f % 64 + g, 4));
-      };
-      Frag look[kLook];
+    colbuf[w][lane & 31] = kc.w + 2.f * kap * (dx * kc.x + dy * kc.y + dz * kc.z);
+    return sizeof(T) == 4 ? 0.f
+                          : -kap * (2.f * (dx * qr.x + dy * qr.y + dz * qr.z) +
+                                    (float)Pqk * (dx * dx + dy * dy + dz * dz));
+  };
+
+  // Scores of tile t: S^T = K Q^T on the key buffer Kc, accumulated onto
+  // sacc (lane (n, g) register v holds key 8 (v / 4) + 4 g + v % 4 of
+  // query n). Each step issues the operand read kLook products ahead, one
+  // product and side(step), a slice of independent vector work that runs in
+  // the product's shadow; scheduling fences keep exactly this order.
+  auto phase_a = [&](const float4 cJ, const unsigned char* Kc, f32x16 sacc, auto&& side) -> f32x16 {
+    auto kfrag = [&](int s) -> Frag {
+      const int f = M::kStep * s;
+      const unsigned char* r = Kc + (f / 64) * SM::kKPanel;
+      if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + KS::at(n, f % 64 + 8 * g, 2)));
+      else
+        return *reinterpret_cast<const float*>(r + KS::at(n, f % 64 + g, 4));
+    };
+    Frag look[kLook];
 #pragma unroll
-      for (int x = 0; x < kLook; ++x) look[x] = kfrag(x);
+    for (int x = 0; x < kLook; ++x) look[x] = kfrag(x);
+    step_fence();
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const Frag cur = look[s % kLook];
-        if (s + kLook < NKS) look[s % kLook] = kfrag(s + kLook);
-        if (s < NKH)
-          sacc = mma(cur, qf[s], sacc);
-        else
-          sacc = mma_pair(cur, qf[s], sacc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int s = 0; s < NKS; ++s) {
+      const Frag cur = look[s % kLook];
+      if (s + kLook < NKS) look[s % kLook] = kfrag(s + kLook);
+      if (s < NKH)
+        sacc = mma(cur, qf[s], sacc);
+      else
+        sacc = mma_pair(cur, qf[s], sacc);
+      // ties the product to this step (an ordered, empty statement that the
+      // next product depends on); without it the products, which have no
+      // side effects, may all be placed after the last step
+      pin_step(sacc);
+      side(s);
+      step_fence();
     }
     if constexpr (sizeof(T) == 4) {
       // fp32: -k * sum_p |A'_ip + delta - B'_jp|^2 from explicit differences;
       // the expanded form would lose ~1e-5 logits to float32 cancellation
+      const float dx = cI.x - cJ.x, dy = cI.y - cJ.y, dz = cI.z - cJ.z;
       float ad[15];
 #pragma unroll
       for (int e = 0; e < 15; ++e) ad[e] = apt[e] + (e % 3 == 0 ? dx : e % 3 == 1 ? dy : dz);
@@ -400,110 +445,251 @@ void ipa_attn_kernel(FwdArgs a) {
         sacc[v] = fmaf(-kap, d, sacc[v]);
       }
     }
-    float mx = -INFINITY;
+    return sacc;
+  };
+
+  // Column term of the keys this lane holds (colbuf[w] in the score layout).
+  auto col_vals = [&]() -> f32x16 {
+    f32x16 cv;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float4 cv = *reinterpret_cast<const float4*>(&colbuf[w][8 * k + 4 * g]);
-      sacc[4 * k + 0] += cv.x;
-      sacc[4 * k + 1] += cv.y;
-      sacc[4 * k + 2] += cv.z;
-      sacc[4 * k + 3] += cv.w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[4 * k + e]);
+      const float4 c4 = *reinterpret_cast<const float4*>(&colbuf[w][8 * k + 4 * g]);
+      cv[4 * k + 0] = c4.x; cv[4 * k + 1] = c4.y; cv[4 * k + 2] = c4.z; cv[4 * k + 3] = c4.w;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float Mt = mx + rterm;
-    const bool need = Mt > m_run + kLazy;
-    if (__any(need)) {
-      const float mn = need ? Mt : m_run;
-      const float al = (mn == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
-      m_run = mn;
-      l_own *= al; ocx *= al; ocy *= al; ocz *= al;
-#pragma unroll
-      for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-        for (int v = 0; v < 16; v += 4) {
-          // a few registers at a time keeps the temporaries short-lived
-          oacc[fb][v] *= al; oacc[fb][v + 1] *= al; oacc[fb][v + 2] *= al; oacc[fb][v + 3] *= al;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    const float shift = (m_run == -INFINITY) ? 0.f : m_run - rterm;
+    return cv;
+  };
 
-    // probabilities -> B operand of O^T = V^T P^T
-    Frag pf[NST];
-    float lt = 0.f;
-    if constexpr (sizeof(T) == 2) {
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // Row max of a score tile (this lane's 16 keys, then the partner lane's).
+  auto row_max = [&](const f32x16& sc) -> float {
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-      for (int s2 = 0; s2 < NST; ++s2) {
-        bf16x2 pk[4];
+    for (int v = 3; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    return fmaxf(mx, __shfl_xor(mx, 32, 64));
+  };
+
+  // O^T += V^T P^T on the value buffer Vc, with side work as in phase_a.
+  auto phase_b = [&](const unsigned char* Vc, const Frag* pf, auto&& side) {
+    auto vfrag = [&](int idx) -> Frag {
+      const int fb = idx / NST, s2 = idx % NST;
+      const unsigned char* r = Vc + 32 * fb * kKT * ES;
+      if constexpr (sizeof(T) == 2)
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + VS::at(n, 16 * s2 + 8 * g, 2)));
+      else
+        return *reinterpret_cast<const float*>(r + VS::at(n, 2 * s2 + g, 4));
+    };
+    constexpr int NB = NFB * NST;
+    Frag look[kLook];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f32x2 pv = {__builtin_amdgcn_exp2f(sacc[8 * s2 + 2 * e] - shift),
-                      __builtin_amdgcn_exp2f(sacc[8 * s2 + 2 * e + 1] - shift)};
-          pk[e] = __builtin_convertvector(pv, bf16x2);
-          lt = __builtin_amdgcn_fdot2_f32_bf16(pk[e], ones, lt, false);
-        }
-        pf[s2] = bf16x8{pk[0][0], pk[0][1], pk[1][0], pk[1][1],
-                        pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
+    for (int x = 0; x < kLook; ++x) look[x] = vfrag(x);
+    step_fence();
+#pragma unroll
+    for (int idx = 0; idx < NB; ++idx) {
+      const Frag cur = look[idx % kLook];
+      if (idx + kLook < NB) look[idx % kLook] = vfrag(idx + kLook);
+      oacc[idx / NST] = mma(cur, pf[idx % NST], oacc[idx / NST]);
+      side(idx);
+      step_fence();
+    }
+  };
+
+  // ---- software-pipelined key loop ----
+  // Sequence index s visits the non-empty tiles u_0, u_1, ... Iteration s
+  // holds the scores of u_s (sacc, with their row max) and
+  //   1. starts the copies V(u_{s+1}) -> Vbuf[1-p], K(u_{s+2}) -> Kbuf[p]
+  //      (p = s & 1; both buffers were last read in iteration s - 1),
+  //   2. moves the running max if the scores of u_s call for it,
+  //   3. turns the scores of u_s into probabilities while the matrix core
+  //      computes the scores of u_{s+1} from Kbuf[1-p],
+  //   4. accumulates V(u_s)^T P^T from Vbuf[p] while the row max of the new
+  //      scores is taken,
+  //   5. waits for its copies and meets the other waves at a barrier.
+  // The exponentials and the max thus run in the shadow of the products.
+  // Past the last tile the scores of a stale buffer are computed and
+  // dropped (their values are finite or -inf).
+  auto copy_k = [&](int t, unsigned char* Kd) {
+    const int J = t >> 1, half = t & 1;
+#pragma unroll
+    for (int P = 0; P < NP; ++P) {
+      const uint32_t kbase = P == 0 ? (uint32_t)(J * 64 + 32 * half) * 64 * ES
+                                    : (uint32_t)((J * (NP - 1) + P - 1) * 64 + 32 * half) * 64 * ES;
+#pragma unroll
+      for (int j = 0; j < KJ; ++j) {
+        const int k = w + 4 * j;
+        dma16(P == 0 ? rKh : rKz, voK, kbase + (uint32_t)(k * KS::kRPL * 64 * ES),
+              Kd + P * SM::kKPanel + k * 1024);
       }
+    }
+  };
+  // Direct-to-LDS copy op k of a tile pair: ops 0 .. NP VJ - 1 copy value
+  // tile tv into Vd, the next NP KJ ops key tile tk into Kd.
+  constexpr int NDMA = NP * (VJ + KJ);
+  auto dma_op = [&](int k, int tv, unsigned char* Vd, int tk, unsigned char* Kd) {
+    if (k < NP * VJ) {
+      const int P = k / VJ, j = k % VJ, J = tv >> 1, half = tv & 1;
+      const uint32_t vbase = (P == 0 ? (uint32_t)J * 4096 * ES : (uint32_t)(J * (NP - 1) + P - 1) * 4096 * ES) +
+                             (uint32_t)(32 * half * ES);
+      const int kk = w + 4 * j;
+      dma16(P == 0 ? rVh : rVz, voV, vbase + (uint32_t)(kk * VS::kRPL * 64 * ES), Vd + P * SM::kVPanel + kk * 1024);
     } else {
-#pragma unroll
-      for (int s2 = 0; s2 < NST; ++s2) {
-        const float p = __builtin_amdgcn_exp2f(sacc[s2] - shift);
-        pf[s2] = p;
-        lt += p;
-      }
+      const int q = k - NP * VJ;
+      const int P = q / KJ, j = q % KJ, J = tk >> 1, half = tk & 1;
+      const uint32_t kbase = P == 0 ? (uint32_t)(J * 64 + 32 * half) * 64 * ES
+                                    : (uint32_t)((J * (NP - 1) + P - 1) * 64 + 32 * half) * 64 * ES;
+      const int kk = w + 4 * j;
+      dma16(P == 0 ? rKh : rKz, voK, kbase + (uint32_t)(kk * KS::kRPL * 64 * ES), Kd + P * SM::kKPanel + kk * 1024);
     }
-    l_own += lt;
-    ocx += lt * cJ.x; ocy += lt * cJ.y; ocz += lt * cJ.z;
-
-    // ---------------- phase B: O^T += V^T P^T ----------------
-    {
-      auto vfrag = [&](int idx) -> Frag {
-        const int fb = idx / NST, s2 = idx % NST;
-        const unsigned char* r = Vc + 32 * fb * kKT * ES;
-        if constexpr (sizeof(T) == 2)
-          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + VS::at(n, 16 * s2 + 8 * g, 2)));
-        else
-          return *reinterpret_cast<const float*>(r + VS::at(n, 2 * s2 + g, 4));
-      };
-      constexpr int NB = NFB * NST;
-      Frag look[kLook];
+  };
+  auto copy_v = [&](int t, unsigned char* Vd) {
+    const int J = t >> 1, half = t & 1;
 #pragma unroll
-      for (int x = 0; x < kLook; ++x) look[x] = vfrag(x);
+    for (int P = 0; P < NP; ++P) {
+      const uint32_t vbase = (P == 0 ? (uint32_t)J * 4096 * ES : (uint32_t)(J * (NP - 1) + P - 1) * 4096 * ES) +
+                             (uint32_t)(32 * half * ES);
 #pragma unroll
-      for (int idx = 0; idx < NB; ++idx) {
-        const Frag cur = look[idx % kLook];
-        if (idx + kLook < NB) look[idx % kLook] = vfrag(idx + kLook);
-        oacc[idx / NST] = mma(cur, pf[idx % NST], oacc[idx / NST]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < VJ; ++j) {
+        const int k = w + 4 * j;
+        dma16(P == 0 ? rVh : rVz, voV, vbase + (uint32_t)(k * VS::kRPL * 64 * ES),
+              Vd + P * SM::kVPanel + k * 1024);
       }
     }
   };
 
-  // ---- key loop, unrolled by two over the buffer pairs (0 -> 1 -> 0 ...);
-  //      the second half is a branch of the body, not a second loop exit, so
-  //      the accumulators keep their registers across iterations ----
-  int u = next_nonempty(0);
-  if (u < nT) copy_tile(tile_of(u), K0, V0, kc0);
-  wait_vmem();
-  __syncthreads();
-  while (u < nT) {
-    int un = next_nonempty(u + 1);
-    if (un < nT) copy_tile(tile_of(un), K1, V1, kc1);
-    compute_tile(tile_of(u), K0, V0, kc0);
+  if (nseq > 0) {
+    int sq = 0;                                   // sequence position of this iteration
+    int t0 = tile_at(0), t1 = tile_at(1), t2 = tile_at(2);
+    copy_k(t0, K0);
+    copy_v(t0, V0);
+    copy_k(t1, K1);
+    const float4 kc0 = load_kc(t0);
+    float4 kc_n = load_kc(t1);                    // column data of t1
+    float4 cJ0 = cenS[t0 >> 1], cJ1 = cenS[t1 >> 1];
     wait_vmem();
     __syncthreads();
-    u = un;
-    if (u < nT) {
-      un = next_nonempty(u + 1);
-      if (un < nT) copy_tile(tile_of(un), K0, V0, kc0);
-      compute_tile(tile_of(u), K1, V1, kc1);
+    float rterm = col_prep(kc0, cJ0);
+    f32x16 sacc = phase_a(cJ0, K0, col_vals(), [](int) {});
+    float mx = row_max(sacc);
+    __syncthreads();   // K0 is refilled by iteration 0
+
+    // Iteration sq holds the scores of t0 = seq[sq] (sacc, row max mx) and
+    //   1. moves the running max if those scores call for it,
+    //   2. computes the scores of t1 = seq[sq + 1] from Kcur while, in the
+    //      products' shadow, it turns the scores of t0 into probabilities,
+    //      issues the copies V(t1) -> Vfill and K(t2) -> Kfill one per
+    //      step, fetches the column data of t2 and writes the column term
+    //      of t1,
+    //   3. accumulates V(t0)^T P^T from Vcur while it adds the column term
+    //      to the new scores, takes their row max and fetches seq[sq + 3]
+    //      and the centre of t2 for the next iterations,
+    //   4. waits for its copies and meets the other waves at a barrier.
+    // The buffers alternate (p = sq & 1): Kcur holds K(t1), Vcur V(t0);
+    // Kfill and Vfill were last read in iteration sq - 1. Past the end of the
+    // sequence, t1 and t2 repeat its last tile: their scores and copies are
+    // computed and never used.
+    auto iteration = [&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      unsigned char* Kcur = p ? K0 : K1;
+      unsigned char* Kfill = p ? K1 : K0;
+      unsigned char* Vcur = p ? V1 : V0;
+      unsigned char* Vfill = p ? V0 : V1;
+
+      const float Mt = mx + rterm;
+      const bool need = Mt > m_run + kLazy;
+      if (__any(need)) {
+        const float mn = need ? Mt : m_run;
+        const float al = (mn == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+        m_run = mn;
+        l_own *= al; ocx *= al; ocy *= al; ocz *= al;
+        acc_settle();
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb) scale_acc(oacc[fb], al);
+        acc_settle();
+      }
+      const float shift = (m_run == -INFINITY) ? 0.f : m_run - rterm;
+
+      // scores of t1; the probabilities of t0 (bf16, rounded once: the same
+      // values feed V^T P^T and the row sum) are formed two per product step
+      Frag pf[NST];
+      float lt = 0.f;
+      bf16x2 pk[8];
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float4 kc_nn;
+      float rterm_n;
+      f32x16 sacc_n = phase_a(cJ1, Kcur, f32x16{}, [&](int st) {
+        if constexpr (sizeof(T) == 2) {
+          if (st < 8) {
+            const f32x2 pv = {__builtin_amdgcn_exp2f(sacc[2 * st] - shift),
+                              __builtin_amdgcn_exp2f(sacc[2 * st + 1] - shift)};
+            pk[st] = __builtin_convertvector(pv, bf16x2);
+            lt = __builtin_amdgcn_fdot2_f32_bf16(pk[st], ones, lt, false);
+          }
+        }
+        if (st < NDMA) dma_op(st, t1, Vfill, t2, Kfill);
+        if (st == NKS - 3) kc_nn = load_kc(t2);
+        if (st == NKS - 2) rterm_n = col_prep(kc_n, cJ1);
+      });
+#pragma unroll
+      for (int k = NKS; k < NDMA; ++k) dma_op(k, t1, Vfill, t2, Kfill);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int s2 = 0; s2 < NST; ++s2)
+          pf[s2] = bf16x8{pk[4 * s2][0], pk[4 * s2][1], pk[4 * s2 + 1][0], pk[4 * s2 + 1][1],
+                          pk[4 * s2 + 2][0], pk[4 * s2 + 2][1], pk[4 * s2 + 3][0], pk[4 * s2 + 3][1]};
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < NST; ++s2) {
+          const float pp = __builtin_amdgcn_exp2f(sacc[s2] - shift);
+          pf[s2] = pp;
+          lt += pp;
+        }
+      }
+      l_own += lt;
+      ocx += lt * cJ0.x; ocy += lt * cJ0.y; ocz += lt * cJ0.z;
+
+      // values of t0; the column term is added to the new scores and their
+      // row max taken in the shadow of the products (from step 2 on, when the
+      // last score product has completed)
+      const f32x16 cv = col_vals();
+      float mxn = -INFINITY;
+      int t3raw = 0;
+      float4 cJ2;
+      phase_b(Vcur, pf, [&](int st) {
+        if constexpr (sizeof(T) == 2) {
+          if (st >= 2 && st < 10) {
+            const int v = 2 * (st - 2);
+            sacc_n[v] += cv[v];
+            sacc_n[v + 1] += cv[v + 1];
+            mxn = fmaxf(fmaxf(mxn, sacc_n[v]), sacc_n[v + 1]);
+          }
+        }
+        if (st == 10) cJ2 = cenS[t2 >> 1];
+        // a plain LDS read here; it is made wave-uniform after the loop, so
+        // that waiting for it does not stall the operand reads
+        if (st == 11) t3raw = seqS[sq + 3 < nseq ? sq + 3 : nseq - 1];
+      });
+      const int t3 = __builtin_amdgcn_readfirstlane(t3raw);
+      if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          sacc_n[v] += cv[v];
+          mxn = fmaxf(mxn, sacc_n[v]);
+        }
+      }
+      mx = fmaxf(mxn, __shfl_xor(mxn, 32, 64));
+      sacc = sacc_n;
+      rterm = rterm_n;
+      kc_n = kc_nn;
       wait_vmem();
       __syncthreads();
-      u = un;
+      ++sq;
+      t0 = t1; t1 = t2; t2 = t3;
+      cJ0 = cJ1; cJ1 = cJ2;
+    };
+    // unrolled by two (static buffer parity); the second half is a branch of
+    // the body rather than a second loop exit, so the accumulators keep
+    // their registers across iterations
+    while (sq < nseq) {
+      iteration(std::integral_constant<int, 0>{});
+      if (sq < nseq) iteration(std::integral_constant<int, 1>{});
     }
   }
 
@@ -554,9 +740,43 @@ void ipa_attn_kernel(FwdArgs a) {
     }
   }
 
-  // pair channels: sum_r z1_ir * O_pair,r accumulated in LDS (rows padded by
-  // one float, so the 32 rows of a wave fall in distinct banks), two waves
-  // at a time, then written out row by row
+  // ---- pair channels: o_pair[c] = sum_r z1[r Cz + c] O[r Cz + c] / l ----
+  // Lane (n, g) holds O at features 32 fb + 8 k + 4 g + e of query n: 4-wide
+  // groups at feature 8 q + 4 g (q = 4 (fb - 2) + k). Cz is a multiple of 8,
+  // so every rank component of a channel lands in the same lane.
+  // (1) every z1 group this lane needs is loaded at once, through the global
+  //     address space so that the loads are not ordered behind the LDS
+  //     traffic below; (2) the products are formed in registers; (3) they
+  //     are summed over r into a padded per-wave LDS block, two waves at a
+  //     time; (4) the block is written out row by row.
+  constexpr int NG = (NFB - 2) * 4;   // pair feature groups per lane
+  {
+    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(static_cast<const T*>(a.z1) + (size_t)b * L * RCz,
+                                                (uint32_t)L * RCz * ES);
+    const int vz = (ic * RCz + 4 * g) * ES;
+    float z[NG][4];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      // unconditional loads so that they all issue back to back; groups past
+      // R Cz, and rows that output zeros, drop them
+      if constexpr (sizeof(T) == 2) {
+        const u32x2 zr = __builtin_amdgcn_raw_buffer_load_b64(rZ, vz + 16 * q, 0, 0);
+        z[q][0] = __uint_as_float(zr[0] << 16); z[q][1] = __uint_as_float(zr[0] & 0xFFFF0000u);
+        z[q][2] = __uint_as_float(zr[1] << 16); z[q][3] = __uint_as_float(zr[1] & 0xFFFF0000u);
+      } else {
+        const u32x4 zr = __builtin_amdgcn_raw_buffer_load_b128(rZ, vz + 32 * q, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[q][e] = __uint_as_float(zr[e]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const int fb = 2 + q / 4, k = q % 4;
+      const bool use = ok && 8 * q + 4 * g < RCz;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oacc[fb][4 * k + e] *= use ? z[q][e] * inv : 0.f;
+    }
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     if ((w >> 1) == pass) {
@@ -564,27 +784,30 @@ void ipa_attn_kernel(FwdArgs a) {
       for (int e = lane; e < 32 * SM::kPRow; e += 64) pb[e] = 0.f;
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      if (ok) {
+      // channel of group q: (8 q + 4 g) mod Cz, stepped without division
+      int c0 = 4 * g;
 #pragma unroll
-        for (int fb = 2; fb < NFB; ++fb)
+      for (int q = 0; q < NG; ++q) {
+        const int fb = 2 + q / 4, k = q % 4;
+        if (8 * q + 4 * g < RCz) {
+          float* row = pb + n * SM::kPRow + c0;
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int uu = 32 * (fb - 2) + 8 * k + 4 * g + e;
-              if (uu < RCz) {
-                const int c = uu % Cz;
-                const float z = ld_in<T>(a.z1, ((size_t)b * L + i) * RCz + uu);
-                pb[n * SM::kPRow + c] += z * oacc[fb][4 * k + e] * inv;
-              }
-            }
+          for (int e = 0; e < 4; ++e) row[e] += oacc[fb][4 * k + e];
+        }
+        c0 += 8;
+        if (c0 >= Cz) c0 -= Cz;
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      // 32 rows of Cz floats; lane walks entries lane, lane + 64, ...
+      const int dq = 64 / Cz, dr = 64 - dq * Cz;
+      int nn = lane / Cz, c = lane - nn * Cz;
       for (int e = lane; e < 32 * Cz; e += 64) {
-        const int nn = e / Cz, c = e - nn * Cz;
         const int ii = qw + nn;
         if (ii < L) a.out_pair[(((size_t)b * L + ii) * H + h) * Cz + c] = pb[nn * SM::kPRow + c];
+        nn += dq;
+        c += dr;
+        if (c >= Cz) { c -= Cz; ++nn; }
       }
     }
     __syncthreads();
