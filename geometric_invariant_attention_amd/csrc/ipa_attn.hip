@@ -94,12 +94,10 @@ __device__ __forceinline__ f32x16 mma_pair(float a, float b, f32x16 c) {
 }
 
 
-// Step boundary of a hand-scheduled product loop: neither the compiler's IR
-// passes (memory fence) nor its instruction scheduler may move work across.
-__device__ __forceinline__ void step_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
+// Step boundary of a hand-scheduled product loop: memory operations (operand
+// reads, tile copies) stay in their step; the instruction scheduler may still
+// interleave the arithmetic across steps.
+__device__ __forceinline__ void step_fence() { asm volatile("" ::: "memory"); }
 
 // An empty, ordered statement that takes an accumulator tile in place: a
 // product whose result passes through it stays in its step. No instruction
@@ -539,6 +537,15 @@ void ipa_attn_kernel(FwdArgs a) {
       dma16(P == 0 ? rKh : rKz, voK, kbase + (uint32_t)(kk * KS::kRPL * 64 * ES), Kd + P * SM::kKPanel + kk * 1024);
     }
   };
+  // The copy ops of one iteration, spread evenly over its NKS + NB product
+  // steps (op k at step k (NKS + NB) / NDMA): the address unit then drains
+  // them alongside the products instead of holding the wave up in a burst.
+  constexpr int NSTEP = NKS + NFB * NST;
+  auto dma_at = [&](int step, int tv, unsigned char* Vd, int tk, unsigned char* Kd) {
+#pragma unroll
+    for (int k = 0; k < NDMA; ++k)
+      if (k * NSTEP / NDMA == step) dma_op(k, tv, Vd, tk, Kd);
+  };
   auto copy_v = [&](int t, unsigned char* Vd) {
     const int J = t >> 1, half = t & 1;
 #pragma unroll
@@ -557,18 +564,37 @@ void ipa_attn_kernel(FwdArgs a) {
   if (nseq > 0) {
     int sq = 0;                                   // sequence position of this iteration
     int t0 = tile_at(0), t1 = tile_at(1), t2 = tile_at(2);
+    // The running max of each wave is seeded from the scores of seq[w],
+    // which is the wave's own diagonal tile when its block has valid keys:
+    // the nearest keys, whose logits the shared visiting order would
+    // otherwise reach only after up to three tiles, each overtaking the
+    // running max and forcing an output rescale. The keys of seq[2] and
+    // seq[3] are staged in V1 and pbuf, both unused until the key loop.
+    unsigned char* const PB = reinterpret_cast<unsigned char*>(&pbuf[0][0][0]);
+    static_assert(sizeof(pbuf) >= SM::kKBuf && SM::kVBuf >= SM::kKBuf, "seed buffers");
+    const int tw = tile_at(w);
     copy_k(t0, K0);
     copy_v(t0, V0);
     copy_k(t1, K1);
+    copy_k(t2, V1);
+    copy_k(tile_at(3), PB);
     const float4 kc0 = load_kc(t0);
     float4 kc_n = load_kc(t1);                    // column data of t1
+    const float4 kcw = load_kc(tw);
     float4 cJ0 = cenS[t0 >> 1], cJ1 = cenS[t1 >> 1];
+    const float4 cJw = cenS[tw >> 1];
     wait_vmem();
     __syncthreads();
+    {
+      const unsigned char* Kw = w == 0 ? K0 : w == 1 ? K1 : w == 2 ? V1 : PB;
+      const float rw = col_prep(kcw, cJw);
+      const f32x16 sw = phase_a(cJw, Kw, col_vals(), [](int) {});
+      m_run = row_max(sw) + rw;
+    }
     float rterm = col_prep(kc0, cJ0);
     f32x16 sacc = phase_a(cJ0, K0, col_vals(), [](int) {});
     float mx = row_max(sacc);
-    __syncthreads();   // K0 is refilled by iteration 0
+    __syncthreads();   // K0, V1 and pbuf are refilled from iteration 0 on
 
     // Iteration sq holds the scores of t0 = seq[sq] (sacc, row max mx) and
     //   1. moves the running max if those scores call for it,
@@ -597,12 +623,17 @@ void ipa_attn_kernel(FwdArgs a) {
       if (__any(need)) {
         const float mn = need ? Mt : m_run;
         const float al = (mn == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+        // while every lane's running max is still -inf nothing has been
+        // accumulated (all probabilities so far were zero): O needs no scaling
+        const bool any_acc = __any(m_run != -INFINITY);
         m_run = mn;
         l_own *= al; ocx *= al; ocy *= al; ocz *= al;
-        acc_settle();
+        if (any_acc) {
+          acc_settle();
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) scale_acc(oacc[fb], al);
-        acc_settle();
+          for (int fb = 0; fb < NFB; ++fb) scale_acc(oacc[fb], al);
+          acc_settle();
+        }
       }
       const float shift = (m_run == -INFINITY) ? 0.f : m_run - rterm;
 
@@ -623,12 +654,10 @@ void ipa_attn_kernel(FwdArgs a) {
             lt = __builtin_amdgcn_fdot2_f32_bf16(pk[st], ones, lt, false);
           }
         }
-        if (st < NDMA) dma_op(st, t1, Vfill, t2, Kfill);
+        dma_at(st, t1, Vfill, t2, Kfill);
         if (st == NKS - 3) kc_nn = load_kc(t2);
         if (st == NKS - 2) rterm_n = col_prep(kc_n, cJ1);
       });
-#pragma unroll
-      for (int k = NKS; k < NDMA; ++k) dma_op(k, t1, Vfill, t2, Kfill);
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int s2 = 0; s2 < NST; ++s2)
@@ -661,6 +690,7 @@ void ipa_attn_kernel(FwdArgs a) {
             mxn = fmaxf(fmaxf(mxn, sacc_n[v]), sacc_n[v + 1]);
           }
         }
+        dma_at(NKS + st, t1, Vfill, t2, Kfill);
         if (st == 10) cJ2 = cenS[t2 >> 1];
         // a plain LDS read here; it is made wave-uniform after the loop, so
         // that waiting for it does not stall the operand reads
