@@ -38,7 +38,6 @@ bool make_layout(const int32_t d[8], int esize, Layout* o) {
   ly.off_kcol = take((size_t)B * H * Lp * 16);
   ly.off_qrow = take((size_t)B * H * Lp * 16);
   ly.off_cen = take((size_t)B * ly.nJ * 16);
-  ly.off_wbt = take((size_t)H * Cz * 4);
   ly.total = off;
   return true;
 }

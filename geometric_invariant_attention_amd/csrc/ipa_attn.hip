@@ -258,8 +258,8 @@ void ipa_attn_kernel(FwdArgs a) {
   {
     const float4* cen = reinterpret_cast<const float4*>(a.ws + ly.off_cen) + (size_t)b * nJ;
     for (int e = tid; e < nJ; e += 256) cenS[e] = cen[e];
-    const float* wbt = reinterpret_cast<const float*>(a.ws + ly.off_wbt) + (size_t)h * Cz;
-    for (int e = tid; e < Cz; e += 256) wbS[e] = wbt[e];
+    const float ws = a.w_L * kLog2e;
+    for (int e = tid; e < Cz; e += 256) wbS[e] = ws * a.w_b[(size_t)e * H + h];
   }
   __syncthreads();  // cenS, wbS
 
@@ -780,11 +780,11 @@ void ipa_attn_kernel(FwdArgs a) {
   //     are summed over r into a padded per-wave LDS block, two waves at a
   //     time; (4) the block is written out row by row.
   constexpr int NG = (NFB - 2) * 4;   // pair feature groups per lane
+  float z[NG][4];
   {
     const __amdgpu_buffer_rsrc_t rZ = make_rsrc(static_cast<const T*>(a.z1) + (size_t)b * L * RCz,
                                                 (uint32_t)L * RCz * ES);
     const int vz = (ic * RCz + 4 * g) * ES;
-    float z[NG][4];
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       // unconditional loads so that they all issue back to back; groups past
@@ -801,11 +801,59 @@ void ipa_attn_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
-      const int fb = 2 + q / 4, k = q % 4;
       const bool use = ok && 8 * q + 4 * g < RCz;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) oacc[fb][4 * k + e] *= use ? z[q][e] * inv : 0.f;
+      for (int e = 0; e < 4; ++e) z[q][e] = use ? z[q][e] : 0.f;
     }
+  }
+
+  // Cz a multiple of 32: rank component r of channel c = 32 m + 8 k + 4 g + e
+  // is register 4 k + e of tile 2 + m + r Cz / 32, so the sum over r is
+  // formed in registers (one specialisation per Cz / 32) and each lane
+  // stores its channels directly. Other Cz go through LDS below.
+  bool pair_done = false;
+  auto pair_regs = [&](auto sc) {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S * 32 <= SM::kCzMax) {
+      constexpr int RMAX = (NFB - 2) / S;
+      float* orow = a.out_pair + rowh * Cz;
+#pragma unroll
+      for (int m = 0; m < S; ++m)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < RMAX; ++r) {
+            if (r < ly.R) {
+              const int fb = 2 + m + r * S, q = 4 * (m + r * S) + k;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[e] = fmaf(z[q][e], oacc[fb][4 * k + e], acc[e]);
+            }
+          }
+          if (in_range)
+            *reinterpret_cast<float4*>(orow + 32 * m + 8 * k + 4 * g) =
+                make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        }
+      pair_done = true;
+    }
+  };
+  if ((Cz & 31) == 0) {
+    switch (Cz >> 5) {
+      case 1: pair_regs(std::integral_constant<int, 1>{}); break;
+      case 2: pair_regs(std::integral_constant<int, 2>{}); break;
+      case 3: pair_regs(std::integral_constant<int, 3>{}); break;
+      case 4: pair_regs(std::integral_constant<int, 4>{}); break;
+      default: break;
+    }
+  }
+  if (pair_done) return;
+
+  // general Cz: products into registers, then summed over r in LDS
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int fb = 2 + q / 4, k = q % 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) oacc[fb][4 * k + e] *= z[q][e] * inv;
   }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {

@@ -47,7 +47,6 @@ struct Layout {
   size_t off_kcol;  // [B][H][Lp] float4         per-key column terms
   size_t off_qrow;  // [B][H][Lp] float4         per-query row terms
   size_t off_cen;   // [B][nJ] float4            block centre xyz, valid count
-  size_t off_wbt;   // [H][Cz] float             w_L log2(e) W_b^T
   size_t total;
 };
 

@@ -22,7 +22,7 @@
 // term A'.B' is carried by three bf16 products (hi.hi + hi.lo + lo.hi) so
 // that bf16 rounding of coordinates does not reach the logits. The query
 // pair part (w_L log2(e) W_b[:,h] * z1) is formed by the attention kernel
-// itself from z1 and the transposed weights written here.
+// itself from z1 and W_b.
 //
 // The pair parts of the query and key rows are fp16 on the bf16 path: the
 // query side w_L W_b[:,h] * z1 is a rounded product, and fp16's 11-bit
@@ -54,18 +54,23 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest even; inputs are finite by construction.
+// Round to nearest even (the hardware conversion; inputs are finite).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Loads from the inputs go through global-address-space pointers: generic
+// loads could alias the LDS stores between them and would then each wait for
+// the previous one; these issue back to back.
+template <typename X>
+__device__ __forceinline__ X ldg(const void* p, size_t i) {
+  return static_cast<const __attribute__((address_space(1))) X*>(
+      (const __attribute__((address_space(1))) void*)p)[i];
 }
 
 template <typename T> struct Elt;
 template <> struct Elt<float> {
-  static __device__ __forceinline__ float load(const void* p, size_t i) {
-    return static_cast<const float*>(p)[i];
-  }
+  static __device__ __forceinline__ float load(const void* p, size_t i) { return ldg<float>(p, i); }
   // hi/lo split of a value: fp32 storage keeps the value whole.
   static __device__ __forceinline__ void split(float x, float& hi, float& lo) {
     hi = x; lo = 0.f;
@@ -75,9 +80,7 @@ template <> struct Elt<float> {
   static __device__ __forceinline__ S pack_pair(float x) { return x; }
 };
 template <> struct Elt<uint16_t> {
-  static __device__ __forceinline__ float load(const void* p, size_t i) {
-    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  }
+  static __device__ __forceinline__ float load(const void* p, size_t i) { return bf16_to_f32(ldg<uint16_t>(p, i)); }
   static __device__ __forceinline__ void split(float x, float& hi, float& lo) {
     hi = bf16_to_f32(f32_to_bf16(x));
     lo = bf16_to_f32(f32_to_bf16(x - hi));
@@ -132,13 +135,13 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
 
   // --- block centre: mean translation of the valid residues (wave 0) ---
   if (tid < 64) {
-    const int i = J * kTileN + tid;
-    const bool valid = (i < L) && (a.mask == nullptr || a.mask[(size_t)b * L + i] != 0);
-    float tx = 0.f, ty = 0.f, tz = 0.f;
-    if (valid) {
-      const float* t = a.trans + ((size_t)b * L + i) * 3;
-      tx = t[0]; ty = t[1]; tz = t[2];
-    }
+    // loads are unconditional (rows past L read row L - 1) and their values
+    // dropped afterwards, so that they issue together
+    const int i = J * kTileN + tid, ic = i < L ? i : L - 1;
+    const bool valid = (i < L) && (a.mask == nullptr || ldg<uint8_t>(a.mask, (size_t)b * L + ic) != 0);
+    const size_t tb = ((size_t)b * L + ic) * 3;
+    float tx = ldg<float>(a.trans, tb), ty = ldg<float>(a.trans, tb + 1), tz = ldg<float>(a.trans, tb + 2);
+    if (!valid) { tx = 0.f; ty = 0.f; tz = 0.f; }
     float sx = tx, sy = ty, sz = tz, sn = valid ? 1.f : 0.f;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -156,15 +159,6 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     }
     sValid[tid] = valid ? 1 : 0;
   }
-  if (J == 0 && b == 0 && y == 0) {
-    // transposed, pre-scaled pair-bias weights
-    float* wbt = reinterpret_cast<float*>(a.ws + ly.off_wbt);
-    const float s = a.w_L * kLog2e;
-    for (int e = tid; e < H * ly.Cz; e += 256) {
-      const int h = e / ly.Cz, c = e % ly.Cz;
-      wbt[e] = s * a.w_b[(size_t)c * H + h];
-    }
-  }
   __syncthreads();
 
   if (y < H) {
@@ -176,31 +170,113 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     __shared__ float sG[kTileN][3 * kPvSlot + 1];   // centred value points, [x|y|z] x 8
     const float log2e = kLog2e;
     const float alpha = a.w_L * rsqrtf((float)C) * log2e;
-    const float kap = a.w_L * a.gamma[h] * a.w_C * 0.5f * log2e;
+    const float kap = a.w_L * ldg<float>(a.gamma, h) * a.w_C * 0.5f * log2e;
 
-    // wave 0: frames and points of one residue per lane
+    // ---- stage this head's inputs for the block in LDS ----
+    // All threads copy, consecutive lanes on consecutive elements of the
+    // residues' rows: frames, this head's query/key/value points and its
+    // q/k/v scalars. Trip counts are fixed and every load is unconditional
+    // (rows past L read row L - 1, columns past the row read column 0), so
+    // the loads issue together; values outside the data are zeroed when the
+    // rows are used.
+    __shared__ float sFr[kTileN][12];                  // rotation (9), translation (3)
+    __shared__ float sPt[kTileN][2 * 15 + 3 * kPvSlot];  // q points, k points, v points
+    {
+      const int nq = 3 * Pqk, nv = 3 * Pv;
+      const float rq = 1.f / (float)nq, rv = 1.f / (float)nv;
+      const size_t row0 = (size_t)b * L;
+      auto res = [&](int j) -> size_t { const int i = J * kTileN + j; return row0 + (i < L ? i : L - 1); };
+      constexpr int NR = (kTileN * 9 + 255) / 256, NT = (kTileN * 3 + 255) / 256;
+      constexpr int NQ = (kTileN * 15 + 255) / 256, NV = (kTileN * 3 * kPvSlot + 255) / 256;
+      constexpr int NS = 3 * kTileN * kCSlot / 256;
+      float vr[NR], vt[NT], vq[NQ], vk[NQ], vv[NV], vs[NS];
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        const int e = tid + 256 * k, ec = e < kTileN * 9 ? e : 0;
+        vr[k] = ldg<float>(a.rot, res(ec / 9) * 9 + ec % 9);
+      }
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        const int e = tid + 256 * k, ec = e < kTileN * 3 ? e : 0;
+        vt[k] = ldg<float>(a.trans, res(ec / 3) * 3 + ec % 3);
+      }
+      // element e of the block's point rows: residue e / n, component e % n
+      // (quotients from a float reciprocal: e < 1536 and n <= 24 keep
+      // (e + 0.5) / n well clear of an integer)
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        const int e = tid + 256 * k, ec = e < kTileN * nq ? e : 0;
+        const int j = (int)(((float)ec + 0.5f) * rq), c = ec - j * nq;
+        const size_t o = (res(j) * H + h) * nq + c;
+        vq[k] = Elt<T>::load(a.q_pts, o);
+        vk[k] = Elt<T>::load(a.k_pts, o);
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int e = tid + 256 * k, ec = e < kTileN * nv ? e : 0;
+        const int j = (int)(((float)ec + 0.5f) * rv), c = ec - j * nv;
+        vv[k] = Elt<T>::load(a.v_pts, (res(j) * H + h) * nv + c);
+      }
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int e = tid + 256 * k;
+        const int which = e / (kTileN * kCSlot), j = (e / kCSlot) % kTileN, c = e % kCSlot;
+        const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
+        vs[k] = Elt<T>::load(src, (res(j) * H + h) * C + (c < C ? c : 0));
+      }
+      // into LDS
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        const int e = tid + 256 * k;
+        if (e < kTileN * 9) sFr[e / 9][e % 9] = vr[k];
+      }
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        const int e = tid + 256 * k;
+        if (e < kTileN * 3) sFr[e / 3][9 + e % 3] = vt[k];
+      }
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        const int e = tid + 256 * k;
+        if (e < kTileN * nq) {
+          const int j = (int)(((float)e + 0.5f) * rq), c = e - j * nq;
+          sPt[j][c] = vq[k];
+          sPt[j][15 + c] = vk[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int e = tid + 256 * k;
+        if (e < kTileN * nv) {
+          const int j = (int)(((float)e + 0.5f) * rv), c = e - j * nv;
+          sPt[j][30 + c] = vv[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int e = tid + 256 * k;
+        const int which = e / (kTileN * kCSlot), j = (e / kCSlot) % kTileN, c = e % kCSlot;
+        sS[which][j][c] = (sValid[j] && c < C) ? vs[k] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // wave 0: frames and points of one residue per lane, from LDS
     if (tid < 64) {
       const int j = tid, i = J * kTileN + j;
-      float R[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, tc[3] = {0.f, 0.f, 0.f};
       const bool v = sValid[j];
-      if (v) {
-        const float* r = a.rot + ((size_t)b * L + i) * 9;
+      float R[9], tc[3];
 #pragma unroll
-        for (int e = 0; e < 9; ++e) R[e] = r[e];
-        const float* t = a.trans + ((size_t)b * L + i) * 3;
-        tc[0] = t[0] - sCen[0]; tc[1] = t[1] - sCen[1]; tc[2] = t[2] - sCen[2];
-      }
-      const size_t rowh = ((size_t)b * L + i) * H + h;
+      for (int e = 0; e < 9; ++e) R[e] = sFr[j][e];
+#pragma unroll
+      for (int x = 0; x < 3; ++x) tc[x] = sFr[j][9 + x] - sCen[x];
       float ax = 0.f, ay = 0.f, az = 0.f, bx = 0.f, by = 0.f, bz = 0.f, bn = 0.f;
 #pragma unroll
       for (int p = 0; p < 5; ++p) {
         float A[3] = {0.f, 0.f, 0.f}, Bk[3] = {0.f, 0.f, 0.f};
         if (v && p < Pqk) {
-          const size_t pb = (rowh * Pqk + p) * 3;
-          const float q0 = Elt<T>::load(a.q_pts, pb), q1 = Elt<T>::load(a.q_pts, pb + 1),
-                      q2 = Elt<T>::load(a.q_pts, pb + 2);
-          const float k0 = Elt<T>::load(a.k_pts, pb), k1 = Elt<T>::load(a.k_pts, pb + 1),
-                      k2 = Elt<T>::load(a.k_pts, pb + 2);
+          const float q0 = sPt[j][3 * p], q1 = sPt[j][3 * p + 1], q2 = sPt[j][3 * p + 2];
+          const float k0 = sPt[j][15 + 3 * p], k1 = sPt[j][15 + 3 * p + 1], k2 = sPt[j][15 + 3 * p + 2];
 #pragma unroll
           for (int x = 0; x < 3; ++x) {
             A[x] = R[3 * x] * q0 + R[3 * x + 1] * q1 + R[3 * x + 2] * q2 + tc[x];
@@ -218,9 +294,7 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       for (int p = 0; p < kPvSlot; ++p) {
         float G[3] = {0.f, 0.f, 0.f};
         if (v && p < Pv) {
-          const size_t pb = (rowh * Pv + p) * 3;
-          const float v0 = Elt<T>::load(a.v_pts, pb), v1 = Elt<T>::load(a.v_pts, pb + 1),
-                      v2 = Elt<T>::load(a.v_pts, pb + 2);
+          const float v0 = sPt[j][30 + 3 * p], v1 = sPt[j][30 + 3 * p + 1], v2 = sPt[j][30 + 3 * p + 2];
 #pragma unroll
           for (int x = 0; x < 3; ++x) G[x] = R[3 * x] * v0 + R[3 * x + 1] * v1 + R[3 * x + 2] * v2 + tc[x];
         }
@@ -234,23 +308,15 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
              : (sizeof(T) == 2 ? make_float4(bx, by, bz, -kap * bn) : make_float4(0.f, 0.f, 0.f, 0.f));
       reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = make_float4(ax, ay, az, 0.f);
     }
-    // all threads: the block's q, k, v scalars
-    for (int e = tid; e < 3 * kTileN * kCSlot; e += 256) {
-      const int which = e / (kTileN * kCSlot), j = (e / kCSlot) % kTileN, c = e % kCSlot;
-      const int i = J * kTileN + j;
-      float val = 0.f;
-      if (sValid[j] && c < C) {
-        const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
-        val = Elt<T>::load(src, (((size_t)b * L + i) * H + h) * C + c);
-      }
-      sS[which][j][c] = val;
-    }
     __syncthreads();
 
     // --- query / key head rows: 64 rows x 64 features ---
     S* qh = reinterpret_cast<S*>(a.ws + ly.off_qh) + (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW;
     S* kh = reinterpret_cast<S*>(a.ws + ly.off_kh) + (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW;
     const int G3 = 3 * Pqk;
+    // u / G3 for u < 48: (u + 0.5) / G3 stays well clear of an integer, so
+    // the float reciprocal gives the exact quotient without an integer divide
+    const float rG3 = 1.f / (float)G3;
     for (int ch = tid; ch < kTileN * (kHeadW / EPC); ch += 256) {
       const int j = ch / (kHeadW / EPC), f0 = (ch % (kHeadW / EPC)) * EPC;
       S qv[EPC], kv[EPC];
@@ -262,7 +328,7 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
           qo = alpha * sS[0][j][f];
           ko = sS[1][j][f];
         } else if constexpr (sizeof(T) == 2) {
-          const int u = f - kCSlot, grp = u / G3, w = u - grp * G3;
+          const int u = f - kCSlot, grp = (int)(((float)u + 0.5f) * rG3), w = u - grp * G3;
           if (grp < 3) {
             float hi, lo;
             Elt<T>::split(2.f * kap * sA[j][w], hi, lo);
@@ -312,12 +378,22 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     // ================= pair workgroup: one 64-wide panel of z2 =================
     const int P = y - H;
     __shared__ float sZ[kTileN][64 + 1];
-    for (int e = tid; e < kTileN * 64; e += 256) {
-      const int j = e / 64, uu = e % 64, u = P * 64 + uu;
-      const int i = J * kTileN + j;
-      float val = 0.f;
-      if (sValid[j] && u < RCz) val = Elt<T>::load(a.z2, ((size_t)b * L + i) * RCz + u);
-      sZ[j][uu] = val;
+    {
+      constexpr int NE = kTileN * 64 / 256;
+      float val[NE];
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        const int e = tid + 256 * k;
+        const int j = e / 64, u = P * 64 + e % 64;
+        const int i = J * kTileN + j, ic = i < L ? i : L - 1;
+        val[k] = Elt<T>::load(a.z2, ((size_t)b * L + ic) * RCz + (u < RCz ? u : 0));
+      }
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        const int e = tid + 256 * k;
+        const int j = e / 64, uu = e % 64;
+        sZ[j][uu] = (sValid[j] && P * 64 + uu < RCz) ? val[k] : 0.f;
+      }
     }
     __syncthreads();
     S* kz = reinterpret_cast<S*>(a.ws + ly.off_kz) + (((size_t)b * ly.nJ + J) * (PW / 64) + P) * (64 * kTileN);

@@ -102,6 +102,19 @@ def test_bf16_odd_dims(device):
     _check(w, device, TOL_BF16, seed=4)
 
 
+@pytest.mark.parametrize("Cz,R", [(32, 3), (96, 2)])
+def test_bf16_pair_widths(device, Cz, R):
+    """Pair widths whose rank components are summed in registers (Cz a
+    multiple of 32) other than the default 128, with several ranks."""
+    w = WORKLOADS["single_chain"].with_(L=230, H=3, Cz=Cz, R=R)
+    _check(w, device, TOL_BF16, seed=Cz)
+
+
+def test_fp32_pair_width_32(device):
+    w = WORKLOADS["tiny_fp32"].with_(L=140, H=2, Cz=32, R=2)
+    _check(w, device, TOL_F32, seed=32)
+
+
 def test_ragged_batch(device):
     w = WORKLOADS["ragged_batch"]
     inp = make_inputs(w)
