@@ -4,14 +4,14 @@
 // writes the operands that the fused attention kernel consumes, so that the
 // logit of "Flash Invariant Point Attention" (TL;DR: lift every IPA term
 // into one regular attention) is a plain dot product plus cheap per-row /
-// per-column terms:
+// per-column terms. On the bf16 path (point groups of 15 slots; unused
+// slots, 3 Pqk .. 14, are zero):
 //
-//   query head row  [ a q | 2 k A'hi | 2 k A'hi | 2 k A'lo | 0 ]   (64 wide)
-//   key head row    [   k |    B'hi  |    B'lo  |    B'hi  | 0 ]   (64 wide)
-//   key pair row    [ z2_j1 | ... | z2_jR | 0 ]        (shared by all heads,
-//                                                      stored in 64x64 panels)
-//   value head row  [ v | G'hi x,y,z (8 each) | G'lo x,y,z | ]     (64 wide)
-//   value pair row  [ z2_j1 | ... | z2_jR | 0 ]        (shared by all heads)
+//   query head row  [ a q (16) | 2k A'hi (15) | 2k A'hi (15) | 2k A'lo (15) | 0 (3) ]
+//   key head row    [   k (16) |    B'hi (15) |    B'lo (15) |    B'hi (15) | 0 (3) ]
+//   key pair row    [ z2_j1 | ... | z2_jR | 0 ]   (shared by all heads, 64x64 panels)
+//   value head row  [ v (16) | G'hi x, y, z (8 each) | G'lo x, y, z (8 each) ]
+//   value pair row  [ z2_j1 | ... | z2_jR | 0 ]   (shared by all heads)
 //
 // with a = w_L log2(e) / sqrt(C), k = w_L gamma_h w_C / 2 log2(e), and
 // A', B', G' the global query/key/value points R x + t minus the centre of
@@ -40,58 +40,73 @@
 // Residues with mask 0 and rows past L get all-zero rows and a key column
 // term of -inf, so padding garbage never reaches a valid output.
 //
-// Grid: (block J, head h or pair panel, batch b). Head workgroups stage the
-// block's frames and points in LDS and write the head rows with 16-byte
-// stores; pair workgroups each write one 64-wide panel of z2 in both
-// layouts.
+// Work split. Grid (block J, head h or pair panel, batch b), 4 waves, one
+// residue per lane and no LDS: in a head workgroup wave 0 writes the query
+// rows, wave 1 the key rows and the key column terms, waves 2 and 3 the two
+// halves of the value block (lane = key position); every wave forms the
+// block centre itself with cross-lane sums. In a pair workgroup wave 0
+// writes the key pair panel and waves 1 and 2 the two halves of the value
+// pair panel. Rows are assembled in registers and written with 16-byte
+// stores (value blocks: one coalesced row of 64 positions per store); all
+// loads are unconditional buffer loads (rows past L read row L - 1) whose
+// values invalid residues drop.
 
 #include "ipa_internal.h"
 
 namespace ipa {
 namespace {
 
+constexpr int kPtSlot = 15;   // query/key point coordinates per group (3 Pqk <= 15)
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
-
-// Round to nearest even (the hardware conversion; inputs are finite).
+// round to nearest even (hardware conversion; inputs are finite)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
-
-// Loads from the inputs go through global-address-space pointers: generic
-// loads could alias the LDS stores between them and would then each wait for
-// the previous one; these issue back to back.
-template <typename X>
-__device__ __forceinline__ X ldg(const void* p, size_t i) {
-  return static_cast<const __attribute__((address_space(1))) X*>(
-      (const __attribute__((address_space(1))) void*)p)[i];
+// fp16, round to nearest even, saturated to the finite range
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float x) {
+  x = fminf(fmaxf(x, -65504.f), 65504.f);
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Element-type policy of the lifted rows.
 template <typename T> struct Elt;
-template <> struct Elt<float> {
-  static __device__ __forceinline__ float load(const void* p, size_t i) { return ldg<float>(p, i); }
-  // hi/lo split of a value: fp32 storage keeps the value whole.
-  static __device__ __forceinline__ void split(float x, float& hi, float& lo) {
-    hi = x; lo = 0.f;
-  }
-  using S = float;
-  static __device__ __forceinline__ S pack(float x) { return x; }
-  static __device__ __forceinline__ S pack_pair(float x) { return x; }
-};
 template <> struct Elt<uint16_t> {
-  static __device__ __forceinline__ float load(const void* p, size_t i) { return bf16_to_f32(ldg<uint16_t>(p, i)); }
-  static __device__ __forceinline__ void split(float x, float& hi, float& lo) {
-    hi = bf16_to_f32(f32_to_bf16(x));
-    lo = bf16_to_f32(f32_to_bf16(x - hi));
-  }
   using S = uint16_t;
+  static constexpr int kES = 2;
+  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0));
+  }
   static __device__ __forceinline__ S pack(float x) { return f32_to_bf16(x); }
-  // key pair columns (z2) are stored as fp16: exact for bf16 inputs in the
-  // fp16 normal range, saturated beyond it
-  static __device__ __forceinline__ S pack_pair(float x) {
-    x = fminf(fmaxf(x, -65504.f), 65504.f);
-    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  // hi/lo split: hi = bf16(x), lo = bf16(x - hi)
+  static __device__ __forceinline__ void split(float x, S& hi, S& lo) {
+    hi = f32_to_bf16(x);
+    lo = f32_to_bf16(x - bf16_to_f32(hi));
+  }
+  static __device__ __forceinline__ S pack_pair(float x) { return f32_to_f16_sat(x); }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int byte_off, S v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, byte_off, 0, 0);
+  }
+};
+template <> struct Elt<float> {
+  using S = float;
+  static constexpr int kES = 4;
+  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+  }
+  static __device__ __forceinline__ S pack(float x) { return x; }
+  static __device__ __forceinline__ void split(float x, S& hi, S& lo) { hi = x; lo = 0.f; }
+  static __device__ __forceinline__ S pack_pair(float x) { return x; }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int byte_off, S v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
   }
 };
 
@@ -112,305 +127,294 @@ template <> __device__ __forceinline__ int key_of_pos<float>(int pos) {
   return base + 8 * (st >> 2) + 4 * g + (st & 3);
 }
 
-// Store one 16-byte chunk of packed elements.
-template <typename S, int N>
-__device__ __forceinline__ void store16(S* dst, const S (&v)[N]) {
-  static_assert(N * sizeof(S) == 16, "16-byte chunk");
-  uint32_t w[4];
-  __builtin_memcpy(w, v, 16);
-  *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+// Pack N elements into 32-bit words.
+template <int N>
+__device__ __forceinline__ void pack_words(const uint16_t (&v)[N], uint32_t (&wv)[N / 2]) {
+#pragma unroll
+  for (int e = 0; e < N / 2; ++e) wv[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+}
+template <int N>
+__device__ __forceinline__ void pack_words(const float (&v)[N], uint32_t (&wv)[N]) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) wv[e] = __float_as_uint(v[e]);
+}
+
+// Per-wave LDS staging of a 64-row output block, so that global stores go
+// out as whole contiguous 1 KB pieces instead of one row (or one 2-byte
+// column element) per lane. Rows are padded by 16 bytes (conflict-free
+// 16-byte accesses).
+template <int ES>
+struct Stage {
+  static constexpr int kRowB = 64 * ES;        // bytes per row of 64 elements
+  static constexpr int kPitch = kRowB + 16;    // padded LDS row
+  static constexpr int kNC = kRowB / 16;       // 16-byte chunks per row
+  static constexpr int kBytes = 64 * kPitch;
+  // lane `lane` holds row `lane` (64 elements, words packed in w[]) and the
+  // block [64 rows][64 elements] is written contiguously at dst
+  static __device__ __forceinline__ void rows(unsigned char* xb, int lane, const uint32_t (&wv)[kRowB / 4],
+                                              unsigned char* dst) {
+#pragma unroll
+    for (int c = 0; c < kNC; ++c)
+      *reinterpret_cast<uint4*>(xb + lane * kPitch + 16 * c) =
+          make_uint4(wv[4 * c], wv[4 * c + 1], wv[4 * c + 2], wv[4 * c + 3]);
+    __builtin_amdgcn_wave_barrier();
+    const int c = lane % kNC, r0 = lane / kNC;
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) {
+      const int r = r0 + k * (64 / kNC);
+      *reinterpret_cast<uint4*>(dst + r * kRowB + 16 * c) = *reinterpret_cast<const uint4*>(xb + r * kPitch + 16 * c);
+    }
+  }
+};
+
+// 32 feature rows of a feature-major value block: lane p holds element p of
+// each row; the rows (64 elements each) are written contiguously at dst.
+template <typename S>
+__device__ __forceinline__ void store_cols(unsigned char* xb, int lane, const S (&v)[32], unsigned char* dst) {
+  constexpr int ES = (int)sizeof(S);
+  using ST = Stage<ES>;
+#pragma unroll
+  for (int f = 0; f < 32; ++f) *reinterpret_cast<S*>(xb + f * ST::kPitch + lane * ES) = v[f];
+  __builtin_amdgcn_wave_barrier();
+  const int c = lane % ST::kNC, r0 = lane / ST::kNC;
+#pragma unroll
+  for (int k = 0; k < 32 / (64 / ST::kNC); ++k) {
+    const int r = r0 + k * (64 / ST::kNC);
+    *reinterpret_cast<uint4*>(dst + r * ST::kRowB + 16 * c) = *reinterpret_cast<const uint4*>(xb + r * ST::kPitch + 16 * c);
+  }
+}
+
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
-  using S = typename Elt<T>::S;
-  constexpr int EPC = 16 / sizeof(S);        // elements per 16-byte chunk
+  using E = Elt<T>;
+  using S = typename E::S;
+  constexpr int ES = E::kES;
   const Layout& ly = a.lay;
-  const int J = blockIdx.x, y = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int J = blockIdx.x, y = blockIdx.y, b = blockIdx.z;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int L = ly.L, H = ly.H, C = ly.C, Pqk = ly.Pqk, Pv = ly.Pv, RCz = ly.R * ly.Cz;
-  const int Lp = ly.Lp, PW = ly.PW;
-
-  __shared__ float sCen[4];
-  __shared__ int sValid[kTileN];
-
-  // --- block centre: mean translation of the valid residues (wave 0) ---
-  if (tid < 64) {
-    // loads are unconditional (rows past L read row L - 1) and their values
-    // dropped afterwards, so that they issue together
-    const int i = J * kTileN + tid, ic = i < L ? i : L - 1;
-    const bool valid = (i < L) && (a.mask == nullptr || ldg<uint8_t>(a.mask, (size_t)b * L + ic) != 0);
-    const size_t tb = ((size_t)b * L + ic) * 3;
-    float tx = ldg<float>(a.trans, tb), ty = ldg<float>(a.trans, tb + 1), tz = ldg<float>(a.trans, tb + 2);
-    if (!valid) { tx = 0.f; ty = 0.f; tz = 0.f; }
-    float sx = tx, sy = ty, sz = tz, sn = valid ? 1.f : 0.f;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      sx += __shfl_xor(sx, o, 64);
-      sy += __shfl_xor(sy, o, 64);
-      sz += __shfl_xor(sz, o, 64);
-      sn += __shfl_xor(sn, o, 64);
-    }
-    const float inv = sn > 0.f ? 1.f / sn : 0.f;
-    if (tid == 0) {
-      sCen[0] = sx * inv; sCen[1] = sy * inv; sCen[2] = sz * inv; sCen[3] = sn;
-      if (y == 0)
-        reinterpret_cast<float4*>(a.ws + ly.off_cen)[(size_t)b * ly.nJ + J] =
-            make_float4(sx * inv, sy * inv, sz * inv, sn);
-    }
-    sValid[tid] = valid ? 1 : 0;
-  }
-  __syncthreads();
+  const int Lp = ly.Lp, PW = ly.PW, nJ = ly.nJ;
+  const size_t rb = (size_t)b * L;  // first residue row of batch b
+  using ST = Stage<ES>;
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[4][ST::kBytes];
+  unsigned char* xb = xbuf[w];
 
   if (y < H) {
     // ================= head workgroup =================
     const int h = y;
-    __shared__ float sS[3][kTileN][kCSlot + 1];     // q, k, v scalars (zero past C)
-    __shared__ float sA[kTileN][16];                // centred query points (unscaled)
-    __shared__ float sB[kTileN][16];                // centred key points
-    __shared__ float sG[kTileN][3 * kPvSlot + 1];   // centred value points, [x|y|z] x 8
-    const float log2e = kLog2e;
-    const float alpha = a.w_L * rsqrtf((float)C) * log2e;
-    const float kap = a.w_L * ldg<float>(a.gamma, h) * a.w_C * 0.5f * log2e;
+    // residue of this lane; value waves take the key of their position
+    const int j = w >= 2 ? key_of_pos<T>(lane) : lane;
+    const int i = J * kTileN + j, ic = i < L ? i : L - 1;
+    const bool valid = i < L && (a.mask == nullptr || a.mask[rb + ic] != 0);
 
-    // ---- stage this head's inputs for the block in LDS ----
-    // All threads copy, consecutive lanes on consecutive elements of the
-    // residues' rows: frames, this head's query/key/value points and its
-    // q/k/v scalars. Trip counts are fixed and every load is unconditional
-    // (rows past L read row L - 1, columns past the row read column 0), so
-    // the loads issue together; values outside the data are zeroed when the
-    // rows are used.
-    __shared__ float sFr[kTileN][12];                  // rotation (9), translation (3)
-    __shared__ float sPt[kTileN][2 * 15 + 3 * kPvSlot];  // q points, k points, v points
+    // frame of the residue and the block centre (mean translation of the
+    // block's valid residues; every wave forms it for itself)
+    float R[9], t[3];
     {
-      const int nq = 3 * Pqk, nv = 3 * Pv;
-      const float rq = 1.f / (float)nq, rv = 1.f / (float)nv;
-      const size_t row0 = (size_t)b * L;
-      auto res = [&](int j) -> size_t { const int i = J * kTileN + j; return row0 + (i < L ? i : L - 1); };
-      constexpr int NR = (kTileN * 9 + 255) / 256, NT = (kTileN * 3 + 255) / 256;
-      constexpr int NQ = (kTileN * 15 + 255) / 256, NV = (kTileN * 3 * kPvSlot + 255) / 256;
-      constexpr int NS = 3 * kTileN * kCSlot / 256;
-      float vr[NR], vt[NT], vq[NQ], vk[NQ], vv[NV], vs[NS];
+      const __attribute__((address_space(1))) float* rp =
+          (const __attribute__((address_space(1))) float*)(a.rot + (rb + ic) * 9);
+      const __attribute__((address_space(1))) float* tp =
+          (const __attribute__((address_space(1))) float*)(a.trans + (rb + ic) * 3);
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const int e = tid + 256 * k, ec = e < kTileN * 9 ? e : 0;
-        vr[k] = ldg<float>(a.rot, res(ec / 9) * 9 + ec % 9);
-      }
+      for (int e = 0; e < 9; ++e) R[e] = rp[e];
 #pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        const int e = tid + 256 * k, ec = e < kTileN * 3 ? e : 0;
-        vt[k] = ldg<float>(a.trans, res(ec / 3) * 3 + ec % 3);
-      }
-      // element e of the block's point rows: residue e / n, component e % n
-      // (quotients from a float reciprocal: e < 1536 and n <= 24 keep
-      // (e + 0.5) / n well clear of an integer)
-#pragma unroll
-      for (int k = 0; k < NQ; ++k) {
-        const int e = tid + 256 * k, ec = e < kTileN * nq ? e : 0;
-        const int j = (int)(((float)ec + 0.5f) * rq), c = ec - j * nq;
-        const size_t o = (res(j) * H + h) * nq + c;
-        vq[k] = Elt<T>::load(a.q_pts, o);
-        vk[k] = Elt<T>::load(a.k_pts, o);
-      }
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const int e = tid + 256 * k, ec = e < kTileN * nv ? e : 0;
-        const int j = (int)(((float)ec + 0.5f) * rv), c = ec - j * nv;
-        vv[k] = Elt<T>::load(a.v_pts, (res(j) * H + h) * nv + c);
-      }
-#pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const int e = tid + 256 * k;
-        const int which = e / (kTileN * kCSlot), j = (e / kCSlot) % kTileN, c = e % kCSlot;
-        const void* src = which == 0 ? a.q : which == 1 ? a.k : a.v;
-        vs[k] = Elt<T>::load(src, (res(j) * H + h) * C + (c < C ? c : 0));
-      }
-      // into LDS
-#pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const int e = tid + 256 * k;
-        if (e < kTileN * 9) sFr[e / 9][e % 9] = vr[k];
-      }
-#pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        const int e = tid + 256 * k;
-        if (e < kTileN * 3) sFr[e / 3][9 + e % 3] = vt[k];
-      }
-#pragma unroll
-      for (int k = 0; k < NQ; ++k) {
-        const int e = tid + 256 * k;
-        if (e < kTileN * nq) {
-          const int j = (int)(((float)e + 0.5f) * rq), c = e - j * nq;
-          sPt[j][c] = vq[k];
-          sPt[j][15 + c] = vk[k];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const int e = tid + 256 * k;
-        if (e < kTileN * nv) {
-          const int j = (int)(((float)e + 0.5f) * rv), c = e - j * nv;
-          sPt[j][30 + c] = vv[k];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const int e = tid + 256 * k;
-        const int which = e / (kTileN * kCSlot), j = (e / kCSlot) % kTileN, c = e % kCSlot;
-        sS[which][j][c] = (sValid[j] && c < C) ? vs[k] : 0.f;
-      }
+      for (int x = 0; x < 3; ++x) t[x] = tp[x];
     }
-    __syncthreads();
+    const float vf = valid ? 1.f : 0.f;
+    const float cn = wave_sum(vf);
+    const float cinv = cn > 0.f ? 1.f / cn : 0.f;
+    const float cx = wave_sum(t[0] * vf) * cinv, cy = wave_sum(t[1] * vf) * cinv, cz = wave_sum(t[2] * vf) * cinv;
+    if (h == 0 && w == 0 && lane == 0)
+      reinterpret_cast<float4*>(a.ws + ly.off_cen)[(size_t)b * nJ + J] = make_float4(cx, cy, cz, cn);
+    const float tc[3] = {t[0] - cx, t[1] - cy, t[2] - cz};
 
-    // wave 0: frames and points of one residue per lane, from LDS
-    if (tid < 64) {
-      const int j = tid, i = J * kTileN + j;
-      const bool v = sValid[j];
-      float R[9], tc[3];
+    // this head's input rows of the residue, through buffer resources over
+    // batch b (32-bit offsets; the range check never faults)
+    auto in_rsrc = [&](const void* p, int per_row) {
+      return make_rsrc(static_cast<const unsigned char*>(p) + rb * H * per_row * ES,
+                       (uint32_t)((size_t)L * H * per_row * ES));
+    };
+    const int row = ic * H + h;   // (residue, head) row within the batch
+
+    const size_t o = ((size_t)b * H + h) * Lp + i;  // row of the per-(b, h) arrays
+    const float alpha = a.w_L * rsqrtf((float)C) * kLog2e;
+    const float kap = a.w_L * a.gamma[h] * a.w_C * 0.5f * kLog2e;
+
+    if (w <= 1) {
+      // ---- query (wave 0) or key (wave 1) head row ----
+      const __amdgpu_buffer_rsrc_t rs = in_rsrc(w == 0 ? a.q : a.k, C);
+      const __amdgpu_buffer_rsrc_t rp = in_rsrc(w == 0 ? a.q_pts : a.k_pts, 3 * Pqk);
+      float sc[kCSlot], pt[kPtSlot];
 #pragma unroll
-      for (int e = 0; e < 9; ++e) R[e] = sFr[j][e];
+      for (int c = 0; c < kCSlot; ++c) sc[c] = E::load(rs, (row * C + (c < C ? c : 0)) * ES);
 #pragma unroll
-      for (int x = 0; x < 3; ++x) tc[x] = sFr[j][9 + x] - sCen[x];
-      float ax = 0.f, ay = 0.f, az = 0.f, bx = 0.f, by = 0.f, bz = 0.f, bn = 0.f;
+      for (int u = 0; u < kPtSlot; ++u) pt[u] = E::load(rp, (row * 3 * Pqk + (u < 3 * Pqk ? u : 0)) * ES);
+      // global, centred points
+      float P[kPtSlot];
+#pragma unroll
+      for (int p = 0; p < 5; ++p)
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+          const float g = R[3 * x] * pt[3 * p] + R[3 * x + 1] * pt[3 * p + 1] + R[3 * x + 2] * pt[3 * p + 2] + tc[x];
+          P[3 * p + x] = (valid && p < Pqk) ? g : 0.f;
+        }
+      S rowv[kHeadW];
+#pragma unroll
+      for (int c = 0; c < kCSlot; ++c) {
+        const float s = (valid && c < C) ? sc[c] : 0.f;
+        rowv[c] = E::pack(w == 0 ? alpha * s : s);
+      }
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int u = 0; u < kPtSlot; ++u) {
+          S hi, lo;
+          E::split(w == 0 ? 2.f * kap * P[u] : P[u], hi, lo);
+          // query [hi | hi | lo], key [hi | lo | hi]
+          rowv[kCSlot + u] = hi;
+          rowv[kCSlot + kPtSlot + u] = w == 0 ? hi : lo;
+          rowv[kCSlot + 2 * kPtSlot + u] = w == 0 ? lo : hi;
+        }
+#pragma unroll
+        for (int f = kCSlot + 3 * kPtSlot; f < kHeadW; ++f) rowv[f] = 0;
+      } else {
+        // fp32: key points at kCSlot.., unscaled query points at kFpQPts..;
+        // the attention kernel forms the point term from explicit
+        // differences, so they must not meet in the product
+#pragma unroll
+        for (int f = kCSlot; f < kHeadW; ++f) rowv[f] = 0.f;
+        if (w == 0) {
+#pragma unroll
+          for (int u = 0; u < kPtSlot; ++u) rowv[kFpQPts + u] = P[u];
+        } else {
+#pragma unroll
+          for (int u = 0; u < kPtSlot; ++u) rowv[kCSlot + u] = P[u];
+        }
+      }
+      uint32_t wv[kHeadW * ES / 4];
+      pack_words(rowv, wv);
+      // rows J*64 .. J*64 + 63 of (b, h) are contiguous; lane j holds row j
+      unsigned char* dst = a.ws + (w == 0 ? ly.off_qh : ly.off_kh) +
+                           (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW * ES;
+      ST::rows(xb, lane, wv, dst);
+      float sx = 0.f, sy = 0.f, sz = 0.f, sn = 0.f;
 #pragma unroll
       for (int p = 0; p < 5; ++p) {
-        float A[3] = {0.f, 0.f, 0.f}, Bk[3] = {0.f, 0.f, 0.f};
-        if (v && p < Pqk) {
-          const float q0 = sPt[j][3 * p], q1 = sPt[j][3 * p + 1], q2 = sPt[j][3 * p + 2];
-          const float k0 = sPt[j][15 + 3 * p], k1 = sPt[j][15 + 3 * p + 1], k2 = sPt[j][15 + 3 * p + 2];
+        sx += P[3 * p]; sy += P[3 * p + 1]; sz += P[3 * p + 2];
+        sn += P[3 * p] * P[3 * p] + P[3 * p + 1] * P[3 * p + 1] + P[3 * p + 2] * P[3 * p + 2];
+      }
+      if (w == 0) {
+        reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = make_float4(sx, sy, sz, 0.f);
+      } else {
+        // fp32 takes the whole point term from explicit differences
+        reinterpret_cast<float4*>(a.ws + ly.off_kcol)[o] =
+            !valid ? make_float4(0.f, 0.f, 0.f, -INFINITY)
+                   : (sizeof(T) == 2 ? make_float4(sx, sy, sz, -kap * sn) : make_float4(0.f, 0.f, 0.f, 0.f));
+      }
+    } else {
+      // ---- value head block, feature-major [64 features][64 positions];
+      //      wave 2 writes features 0..31, wave 3 features 32..63 ----
+      const __amdgpu_buffer_rsrc_t rs = in_rsrc(a.v, C);
+      const __amdgpu_buffer_rsrc_t rp = in_rsrc(a.v_pts, 3 * Pv);
+      float G[3][kPvSlot];
+      {
+        float pv[3 * kPvSlot];
+#pragma unroll
+        for (int u = 0; u < 3 * kPvSlot; ++u) pv[u] = E::load(rp, (row * 3 * Pv + (u < 3 * Pv ? u : 0)) * ES);
+#pragma unroll
+        for (int p = 0; p < kPvSlot; ++p)
 #pragma unroll
           for (int x = 0; x < 3; ++x) {
-            A[x] = R[3 * x] * q0 + R[3 * x + 1] * q1 + R[3 * x + 2] * q2 + tc[x];
-            Bk[x] = R[3 * x] * k0 + R[3 * x + 1] * k1 + R[3 * x + 2] * k2 + tc[x];
+            const float g = R[3 * x] * pv[3 * p] + R[3 * x + 1] * pv[3 * p + 1] + R[3 * x + 2] * pv[3 * p + 2] + tc[x];
+            G[x][p] = (valid && p < Pv) ? g : 0.f;
           }
+      }
+      S out[32];
+      if (w == 2) {
+        // v (16), G'hi x (8), G'hi y (8)
+#pragma unroll
+        for (int c = 0; c < kCSlot; ++c) {
+          const float s = E::load(rs, (row * C + (c < C ? c : 0)) * ES);
+          out[c] = E::pack((valid && c < C) ? s : 0.f);
         }
 #pragma unroll
-        for (int x = 0; x < 3; ++x) { sA[j][3 * p + x] = A[x]; sB[j][3 * p + x] = Bk[x]; }
-        ax += A[0]; ay += A[1]; az += A[2];
-        bx += Bk[0]; by += Bk[1]; bz += Bk[2];
-        bn += Bk[0] * Bk[0] + Bk[1] * Bk[1] + Bk[2] * Bk[2];
-      }
-      sA[j][15] = 0.f; sB[j][15] = 0.f;
-#pragma unroll
-      for (int p = 0; p < kPvSlot; ++p) {
-        float G[3] = {0.f, 0.f, 0.f};
-        if (v && p < Pv) {
-          const float v0 = sPt[j][30 + 3 * p], v1 = sPt[j][30 + 3 * p + 1], v2 = sPt[j][30 + 3 * p + 2];
-#pragma unroll
-          for (int x = 0; x < 3; ++x) G[x] = R[3 * x] * v0 + R[3 * x + 1] * v1 + R[3 * x + 2] * v2 + tc[x];
+        for (int p = 0; p < kPvSlot; ++p) {
+          S hi, lo;
+          E::split(G[0][p], hi, lo); out[16 + p] = hi;
+          E::split(G[1][p], hi, lo); out[24 + p] = hi;
         }
+      } else {
+        // G'hi z (8), G'lo x, y, z (8 each)
 #pragma unroll
-        for (int x = 0; x < 3; ++x) sG[j][kPvSlot * x + p] = G[x];
-      }
-      const size_t o = ((size_t)b * H + h) * Lp + i;
-      // fp32 takes the whole point term from explicit differences
-      reinterpret_cast<float4*>(a.ws + ly.off_kcol)[o] =
-          !v ? make_float4(0.f, 0.f, 0.f, -INFINITY)
-             : (sizeof(T) == 2 ? make_float4(bx, by, bz, -kap * bn) : make_float4(0.f, 0.f, 0.f, 0.f));
-      reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = make_float4(ax, ay, az, 0.f);
-    }
-    __syncthreads();
-
-    // --- query / key head rows: 64 rows x 64 features ---
-    S* qh = reinterpret_cast<S*>(a.ws + ly.off_qh) + (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW;
-    S* kh = reinterpret_cast<S*>(a.ws + ly.off_kh) + (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW;
-    const int G3 = 3 * Pqk;
-    // u / G3 for u < 48: (u + 0.5) / G3 stays well clear of an integer, so
-    // the float reciprocal gives the exact quotient without an integer divide
-    const float rG3 = 1.f / (float)G3;
-    for (int ch = tid; ch < kTileN * (kHeadW / EPC); ch += 256) {
-      const int j = ch / (kHeadW / EPC), f0 = (ch % (kHeadW / EPC)) * EPC;
-      S qv[EPC], kv[EPC];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const int f = f0 + e;
-        float qo = 0.f, ko = 0.f;
-        if (f < kCSlot) {
-          qo = alpha * sS[0][j][f];
-          ko = sS[1][j][f];
-        } else if constexpr (sizeof(T) == 2) {
-          const int u = f - kCSlot, grp = (int)(((float)u + 0.5f) * rG3), w = u - grp * G3;
-          if (grp < 3) {
-            float hi, lo;
-            Elt<T>::split(2.f * kap * sA[j][w], hi, lo);
-            qo = (grp == 2) ? lo : hi;
-            Elt<T>::split(sB[j][w], hi, lo);
-            ko = (grp == 1) ? lo : hi;
-          }
-        } else {
-          // fp32: centred key points at 16.., centred query points (unscaled)
-          // at 32..; the attention kernel takes the squared distance from
-          // their explicit differences, so they must not meet in the product
-          const int u = f - kCSlot;
-          if (u < G3) ko = sB[j][u];
-          if (f >= kFpQPts && f - kFpQPts < G3) qo = sA[j][f - kFpQPts];
+        for (int p = 0; p < kPvSlot; ++p) {
+          S hx, lx, hy, ly2, hz, lz;
+          E::split(G[0][p], hx, lx);
+          E::split(G[1][p], hy, ly2);
+          E::split(G[2][p], hz, lz);
+          out[p] = hz;
+          out[8 + p] = lx;
+          out[16 + p] = ly2;
+          out[24 + p] = lz;
         }
-        qv[e] = Elt<T>::pack(qo);
-        kv[e] = Elt<T>::pack(ko);
       }
-      store16(qh + (size_t)j * kHeadW + f0, qv);
-      store16(kh + (size_t)j * kHeadW + f0, kv);
-    }
-
-    // --- value head block, feature-major [64 features][64 key positions] ---
-    S* vth = reinterpret_cast<S*>(a.ws + ly.off_vth) + (((size_t)b * H + h) * ly.nJ + J) * (kHeadW * kTileN);
-    for (int ch = tid; ch < kHeadW * (kTileN / EPC); ch += 256) {
-      const int f = ch / (kTileN / EPC), p0 = (ch % (kTileN / EPC)) * EPC;
-      S vv[EPC];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const int j = key_of_pos<T>(p0 + e);
-        float o = 0.f;
-        if (f < kCSlot) {
-          o = sS[2][j][f];
-        } else {
-          const int u = f - kCSlot;             // 0..47
-          const int half = u / (3 * kPvSlot);   // 0 = hi, 1 = lo
-          const int w = u - half * 3 * kPvSlot;
-          float hi, lo;
-          Elt<T>::split(sG[j][w], hi, lo);
-          o = half ? lo : hi;
-        }
-        vv[e] = Elt<T>::pack(o);
-      }
-      store16(vth + (size_t)f * kTileN + p0, vv);
+      const size_t blk = ((size_t)b * H + h) * nJ + J;   // value block of (b, h, J)
+      store_cols(xb, lane, out, a.ws + ly.off_vth + (blk * kHeadW + (w - 2) * 32) * kTileN * ES);
     }
   } else {
     // ================= pair workgroup: one 64-wide panel of z2 =================
+    if (w == 3) return;
     const int P = y - H;
-    __shared__ float sZ[kTileN][64 + 1];
-    {
-      constexpr int NE = kTileN * 64 / 256;
-      float val[NE];
+    const int j = w == 0 ? lane : key_of_pos<T>(lane);
+    const int i = J * kTileN + j, ic = i < L ? i : L - 1;
+    const bool valid = i < L && (a.mask == nullptr || a.mask[rb + ic] != 0);
+    // z2 row segment u = 64 P .. 64 P + 63 of the residue (16-byte loads:
+    // R Cz is a multiple of 8, so rows and panels are 16-byte aligned; a
+    // segment past the end of the batch reads zeros)
+    const __amdgpu_buffer_rsrc_t rz =
+        make_rsrc(static_cast<const unsigned char*>(a.z2) + rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
+    float z[64];
 #pragma unroll
-      for (int k = 0; k < NE; ++k) {
-        const int e = tid + 256 * k;
-        const int j = e / 64, u = P * 64 + e % 64;
-        const int i = J * kTileN + j, ic = i < L ? i : L - 1;
-        val[k] = Elt<T>::load(a.z2, ((size_t)b * L + ic) * RCz + (u < RCz ? u : 0));
-      }
+    for (int c = 0; c < 64 * ES / 16; ++c) {
+      const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rz, (ic * RCz + 64 * P) * ES + 16 * c, 0, 0);
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int k = 0; k < NE; ++k) {
-        const int e = tid + 256 * k;
-        const int j = e / 64, uu = e % 64;
-        sZ[j][uu] = (sValid[j] && P * 64 + uu < RCz) ? val[k] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          z[8 * c + 2 * e] = __uint_as_float(r[e] << 16);
+          z[8 * c + 2 * e + 1] = __uint_as_float(r[e] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[4 * c + e] = __uint_as_float(r[e]);
       }
     }
-    __syncthreads();
-    S* kz = reinterpret_cast<S*>(a.ws + ly.off_kz) + (((size_t)b * ly.nJ + J) * (PW / 64) + P) * (64 * kTileN);
-    for (int ch = tid; ch < kTileN * (64 / EPC); ch += 256) {
-      const int j = ch / (64 / EPC), u0 = (ch % (64 / EPC)) * EPC;
-      S zv[EPC];
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) zv[e] = Elt<T>::pack_pair(sZ[j][u0 + e]);
-      store16(kz + (size_t)j * 64 + u0, zv);
-    }
-    S* vtz = reinterpret_cast<S*>(a.ws + ly.off_vtz) + (((size_t)b * ly.nJ + J) * PW + P * 64) * kTileN;
-    for (int ch = tid; ch < 64 * (kTileN / EPC); ch += 256) {
-      const int uu = ch / (kTileN / EPC), p0 = (ch % (kTileN / EPC)) * EPC;
-      S zv[EPC];
+    for (int u = 0; u < 64; ++u) z[u] = (valid && 64 * P + u < RCz) ? z[u] : 0.f;
+    if (w == 0) {
+      // key pair row of residue j: [64 features] in panel P
+      S rowv[64];
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) zv[e] = Elt<T>::pack(sZ[key_of_pos<T>(p0 + e)][uu]);
-      store16(vtz + (size_t)uu * kTileN + p0, zv);
+      for (int u = 0; u < 64; ++u) rowv[u] = E::pack_pair(z[u]);
+      uint32_t wv[64 * ES / 4];
+      pack_words(rowv, wv);
+      ST::rows(xb, lane, wv, a.ws + ly.off_kz + ((((size_t)b * nJ + J) * (PW / 64) + P) * (64 * kTileN)) * ES);
+    } else {
+      // value pair block, feature-major: wave 1 features 0..31, wave 2 32..63
+      const size_t blk = ((size_t)b * nJ + J) * PW + 64 * P;   // first feature row
+      S out[32];
+      if (w == 1) {
+#pragma unroll
+        for (int f = 0; f < 32; ++f) out[f] = E::pack(z[f]);
+      } else {
+#pragma unroll
+        for (int f = 0; f < 32; ++f) out[f] = E::pack(z[32 + f]);
+      }
+      store_cols(xb, lane, out, a.ws + ly.off_vtz + (blk + (w - 1) * 32) * kTileN * ES);
     }
   }
 }
