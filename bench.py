@@ -17,6 +17,7 @@ baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -45,6 +46,42 @@ def algo_bytes(d: dict, elem: int = 2) -> float:
     per_res_in = elem * (3 * H * C + H * 3 * (2 * Pqk + Pv) + 2 * R * Cz) + 4 * 12 + 1
     per_res_out = 4 * H * (C + 3 * Pv + Pv + Cz)
     return float(B * L * (per_res_in + per_res_out) + 4 * (Cz * H + H))
+
+
+# Hardware byte counters of the dominant kernel, taken with rocprofv3 (one
+# FETCH_SIZE pass, one WRITE_SIZE pass) and committed as a summary together
+# with the hash of the kernel source they were taken on.
+PROFILE_PMC = os.path.join(ROOT, "profiles", "ipa_attend_long_chain_2048_pmc.md")
+KERNEL_SOURCES = ("ipa_attn.hip", "ipa_internal.h", "ipa_api.cpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "geometric_invariant_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes of one ipa_attend launch from the committed counter summary
+    (each counter scaled by what it reads for a plain copy of known size), or
+    None when the summary was taken on another workload or on kernel source
+    that has changed since."""
+    try:
+        with open(PROFILE_PMC) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        if line.startswith("traffic-record: "):
+            rec = json.loads(line[len("traffic-record: "):])
+            if rec.get("workload") != workload or rec.get("kernel_source_sha256") != kernel_source_hash():
+                return None
+            read_b = rec["fetch_kib_per_launch"] * 1024 * rec["fetch_scale"]
+            write_b = rec["write_kib_per_launch"] * 1024 * rec["write_scale"]
+            return {"bytes": read_b + write_b, "read_bytes": read_b, "write_bytes": write_b}
+    return None
 
 
 def to_device(inp, dev):
@@ -214,6 +251,7 @@ def main(argv=None) -> int:
     value = pairs / (ms_step * 1e-3)
     tflops = flops / (ms_step * 1e-3) / 1e12
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
 
     result = {
         "metric": METRIC,
@@ -235,10 +273,13 @@ def main(argv=None) -> int:
         "kernels_ms": {"ipa_lift": lift_ms, "ipa_attend": attn_ms},
         "roofline": {"kernel": "ipa_attend", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / PEAK_MFMA_TFLOPS, "traffic": None,
+                     "frac": attn_tflops / PEAK_MFMA_TFLOPS,
+                     "traffic": traffic["bytes"] if traffic else None,
                      "algorithmic_flops": flops},
         "lift_GBs_algorithmic": algo_bytes(d) / (lift_ms * 1e-3) / 1e9,
     }
+    if traffic:
+        result["attend_hbm_GBs_counters"] = traffic["bytes"] / (attn_ms * 1e-3) / 1e9
     print(f"[bench] {w.name}: {ms_step * 1e3:.1f} us/step (lift {lift_ms * 1e3:.1f} us, "
           f"attend {attn_ms * 1e3:.1f} us), {tflops:.1f} TFLOP/s, {value:.3e} pairs/s", file=sys.stderr, flush=True)
 
