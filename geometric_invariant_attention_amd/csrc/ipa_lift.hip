@@ -49,7 +49,8 @@
 // pair panel. Rows are assembled in registers and written with 16-byte
 // stores (value blocks: one coalesced row of 64 positions per store); all
 // loads are unconditional buffer loads (rows past L read row L - 1) whose
-// values invalid residues drop.
+// values invalid residues drop, each lane reading its input rows with
+// 16-byte loads where their length and alignment allow.
 
 #include "ipa_internal.h"
 
@@ -82,9 +83,6 @@ template <typename T> struct Elt;
 template <> struct Elt<uint16_t> {
   using S = uint16_t;
   static constexpr int kES = 2;
-  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0));
-  }
   static __device__ __forceinline__ S pack(float x) { return f32_to_bf16(x); }
   // hi/lo split: hi = bf16(x), lo = bf16(x - hi)
   static __device__ __forceinline__ void split(float x, S& hi, S& lo) {
@@ -99,9 +97,6 @@ template <> struct Elt<uint16_t> {
 template <> struct Elt<float> {
   using S = float;
   static constexpr int kES = 4;
-  static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
-  }
   static __device__ __forceinline__ S pack(float x) { return x; }
   static __device__ __forceinline__ void split(float x, S& hi, S& lo) { hi = x; lo = 0.f; }
   static __device__ __forceinline__ S pack_pair(float x) { return x; }
@@ -109,6 +104,51 @@ template <> struct Elt<float> {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
   }
 };
+
+// Elements 0 .. NS-1 of the input row that starts `off` bytes into a buffer
+// resource, `wide` bytes per load: 16 when the row length and the base keep
+// 16-byte alignment, else 4, else one element. A lane reads its whole row
+// with a few wide loads instead of one load per element (each load touches
+// one cache line per lane, so the count of loads sets the cost). Elements
+// past the row's end come from whatever follows it, or are zero past the
+// end of the buffer; callers drop them.
+template <typename T, int NS>
+__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t r, int off, int wide, float (&out)[NS]) {
+  if constexpr (sizeof(T) == 2) {
+    if (wide == 16) {
+#pragma unroll
+      for (int k = 0; k < (NS + 7) / 8; ++k) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (8 * k + e < NS) out[8 * k + e] = __uint_as_float(e & 1 ? v[e / 2] & 0xFFFF0000u : v[e / 2] << 16);
+      }
+    } else if (wide == 4) {
+#pragma unroll
+      for (int k = 0; k < (NS + 1) / 2; ++k) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * k, 0, 0);
+        out[2 * k] = __uint_as_float(v << 16);
+        if (2 * k + 1 < NS) out[2 * k + 1] = __uint_as_float(v & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) out[k] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * k, 0, 0));
+    }
+  } else {
+    if (wide == 16) {
+#pragma unroll
+      for (int k = 0; k < (NS + 3) / 4; ++k) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * k + e < NS) out[4 * k + e] = __uint_as_float(v[e]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) out[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * k, 0, 0));
+    }
+  }
+}
 
 // Key stored at position `pos` of a 64-key value block. The order matches
 // the probability registers of the attention kernel's 32x32 products: for
@@ -241,6 +281,14 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       return make_rsrc(static_cast<const unsigned char*>(p) + rb * H * per_row * ES,
                        (uint32_t)((size_t)L * H * per_row * ES));
     };
+    // widest load that every row of this input keeps aligned
+    auto width_of = [&](const void* p, int per_row) -> int {
+      const uintptr_t base = reinterpret_cast<uintptr_t>(p) + rb * H * per_row * ES;
+      const int rowb = per_row * ES;
+      if (rowb % 16 == 0 && base % 16 == 0) return 16;
+      if (rowb % 4 == 0 && base % 4 == 0) return 4;
+      return ES;
+    };
     const int row = ic * H + h;   // (residue, head) row within the batch
 
     const size_t o = ((size_t)b * H + h) * Lp + i;  // row of the per-(b, h) arrays
@@ -252,10 +300,8 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       const __amdgpu_buffer_rsrc_t rs = in_rsrc(w == 0 ? a.q : a.k, C);
       const __amdgpu_buffer_rsrc_t rp = in_rsrc(w == 0 ? a.q_pts : a.k_pts, 3 * Pqk);
       float sc[kCSlot], pt[kPtSlot];
-#pragma unroll
-      for (int c = 0; c < kCSlot; ++c) sc[c] = E::load(rs, (row * C + (c < C ? c : 0)) * ES);
-#pragma unroll
-      for (int u = 0; u < kPtSlot; ++u) pt[u] = E::load(rp, (row * 3 * Pqk + (u < 3 * Pqk ? u : 0)) * ES);
+      load_row<T>(rs, row * C * ES, width_of(w == 0 ? a.q : a.k, C), sc);
+      load_row<T>(rp, row * 3 * Pqk * ES, width_of(w == 0 ? a.q_pts : a.k_pts, 3 * Pqk), pt);
       // global, centred points
       float P[kPtSlot];
 #pragma unroll
@@ -323,10 +369,11 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       const __amdgpu_buffer_rsrc_t rs = in_rsrc(a.v, C);
       const __amdgpu_buffer_rsrc_t rp = in_rsrc(a.v_pts, 3 * Pv);
       float G[3][kPvSlot];
+      float vs[kCSlot];
+      if (w == 2) load_row<T>(rs, row * C * ES, width_of(a.v, C), vs);
       {
         float pv[3 * kPvSlot];
-#pragma unroll
-        for (int u = 0; u < 3 * kPvSlot; ++u) pv[u] = E::load(rp, (row * 3 * Pv + (u < 3 * Pv ? u : 0)) * ES);
+        load_row<T>(rp, row * 3 * Pv * ES, width_of(a.v_pts, 3 * Pv), pv);
 #pragma unroll
         for (int p = 0; p < kPvSlot; ++p)
 #pragma unroll
@@ -339,10 +386,7 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       if (w == 2) {
         // v (16), G'hi x (8), G'hi y (8)
 #pragma unroll
-        for (int c = 0; c < kCSlot; ++c) {
-          const float s = E::load(rs, (row * C + (c < C ? c : 0)) * ES);
-          out[c] = E::pack((valid && c < C) ? s : 0.f);
-        }
+        for (int c = 0; c < kCSlot; ++c) out[c] = E::pack((valid && c < C) ? vs[c] : 0.f);
 #pragma unroll
         for (int p = 0; p < kPvSlot; ++p) {
           S hi, lo;
