@@ -67,14 +67,10 @@ __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
 template <typename T> struct Mma;
 template <> struct Mma<uint16_t> {
   static constexpr int kStep = 16;   // reduction length of one product
-  static constexpr int kPad = 8;     // LDS row padding (elements)
-  static constexpr int kEpc = 8;     // elements per 16-byte chunk
   using Frag = bf16x8;               // per-lane operand of one product
 };
 template <> struct Mma<float> {
   static constexpr int kStep = 2;
-  static constexpr int kPad = 4;
-  static constexpr int kEpc = 4;
   using Frag = float;
 };
 
@@ -203,7 +199,6 @@ void ipa_attn_kernel(FwdArgs a) {
   constexpr int NKH = kHeadW / M::kStep;   // of which cover the head part
   constexpr int NFB = D / 32;              // 32-feature blocks of O^T
   constexpr int NP = SM::kNP;
-  constexpr int EPC = M::kEpc;
   constexpr int NST = kKT / M::kStep;      // products per O^T block per tile
   constexpr int ES = (int)sizeof(T);
 
@@ -730,110 +725,201 @@ void ipa_attn_kernel(FwdArgs a) {
   const float gz_c = ocz + __shfl_xor(ocz, 32, 64);
   const bool ok = row_valid && l_tot > 0.f;
   const float inv = ok ? 1.f / l_tot : 0.f;
-  const bool in_range = i < L;
-  const size_t rowh = ((size_t)b * L + i) * H + h;
 
-  if (in_range) {
-    // scalar channels: features 8k + 4g + e (k = 0, 1) of the first block
+  // Every global access of the epilogue moves whole rows through this
+  // wave's own staging block, one of the tile buffers (the loop's last
+  // barrier follows every wave's last read of them and every copy into
+  // them): row-major inputs are fetched with consecutive lanes on
+  // consecutive pieces of consecutive rows, and outputs leave the same way,
+  // rather than one cache line per lane per access in the register layout.
+  // A wave's LDS operations execute in order, so the block is reused without
+  // barriers; wave_sync only keeps the compiler from reordering them.
+  unsigned char* const xs = w == 0 ? K0 : w == 1 ? K1 : w == 2 ? V0 : V1;
+  static_assert(SM::kVBuf == SM::kKBuf && SM::kKBuf == 32 * D * ES, "staging block size");
+  const int nrow = L - qw < 32 ? L - qw : 32;   // rows of this wave inside L (none if <= 0)
+  auto wave_sync = [] {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+
+  // (1) z1 rows qw .. qw + 31 as [32][R Cz] (chunk c of row r in slot
+  //     c ^ (r & zm): the 8 rows that 8 lanes read at once fall on distinct
+  //     banks), then the frames of the same rows as [32][9] rotations and
+  //     [32][3] translations. Rows past L read zeros.
+  const int RB = RCz * ES;                      // bytes per z1 row, a multiple of 16
+  const int CPR = RB / 16;                      // 16-byte chunks per row
+  const int zm = (CPR & 7) == 0 ? 7 : (CPR & 3) == 0 ? 3 : (CPR & 1) == 0 ? 1 : 0;
+  float* const fr = reinterpret_cast<float*>(xs + 32 * RB);
+  {
+    const __amdgpu_buffer_rsrc_t rZ =
+        make_rsrc(static_cast<const unsigned char*>(a.z1) + (size_t)b * L * RB, (uint32_t)L * RB);
+    const __amdgpu_buffer_rsrc_t rR = make_rsrc(a.rot + (size_t)b * L * 9, (uint32_t)L * 36);
+    const __amdgpu_buffer_rsrc_t rT = make_rsrc(a.trans + (size_t)b * L * 3, (uint32_t)L * 12);
+    constexpr int NZL = (SM::kPW * ES / 16 + 1) / 2;   // loads for the widest z1 row
+    u32x4 zv[NZL];
+    int zo[NZL];
+    // chunk 64 s + lane of the block: row zr, chunk zc (stepped, no division
+    // in the loop)
+    int zr = lane / CPR, zc = lane - zr * CPR;
+    const int dr = 64 / CPR, dc = 64 - dr * CPR;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int s = 0; s < NZL; ++s) {
+      if (64 * s < 32 * CPR) zv[s] = __builtin_amdgcn_raw_buffer_load_b128(rZ, (qw + zr) * RB + 16 * zc, 0, 0);
+      zo[s] = zr * RB + 16 * (zc ^ (zr & zm));
+      zr += dr;
+      zc += dc;
+      if (zc >= CPR) { zc -= CPR; ++zr; }
+    }
+    float rv[5], tv[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int f = 8 * k + 4 * g + e;
-        if (f < C) a.out_s[rowh * C + f] = ok ? oacc[0][4 * k + e] * inv : 0.f;
-      }
-    // value points 4g + e: hi x/y/z in registers (0,8+e) (0,12+e) (1,e),
-    // lo x/y/z in (1,4+e) (1,8+e) (1,12+e)
-    float R[9], tr[3];
+    for (int s = 0; s < 5; ++s) rv[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rR, (qw * 9 + 64 * s + lane) * 4, 0, 0));
 #pragma unroll
-    for (int e = 0; e < 9; ++e) R[e] = ok ? a.rot[((size_t)b * L + i) * 9 + e] : 0.f;
+    for (int s = 0; s < 2; ++s) tv[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rT, (qw * 3 + 64 * s + lane) * 4, 0, 0));
 #pragma unroll
-    for (int e = 0; e < 3; ++e) tr[e] = ok ? a.trans[((size_t)b * L + i) * 3 + e] : 0.f;
+    for (int s = 0; s < NZL; ++s)
+      if (64 * s + lane < 32 * CPR) *reinterpret_cast<u32x4*>(xs + zo[s]) = zv[s];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int p = 4 * g + e;
-      if (p < Pv) {
-        float lx = 0.f, lyv = 0.f, lz = 0.f, nr = 0.f;
-        if (ok) {
-          const float gx = (oacc[0][8 + e] + oacc[1][4 + e] + gx_c) * inv - tr[0];
-          const float gy = (oacc[0][12 + e] + oacc[1][8 + e] + gy_c) * inv - tr[1];
-          const float gz = (oacc[1][e] + oacc[1][12 + e] + gz_c) * inv - tr[2];
-          lx = R[0] * gx + R[3] * gy + R[6] * gz;
-          lyv = R[1] * gx + R[4] * gy + R[7] * gz;
-          lz = R[2] * gx + R[5] * gy + R[8] * gz;
-          nr = sqrtf(lx * lx + lyv * lyv + lz * lz);
-        }
-        float* op = a.out_pts + (rowh * Pv + p) * 3;
-        op[0] = lx; op[1] = lyv; op[2] = lz;
-        a.out_pts_norm[rowh * Pv + p] = nr;
-      }
+    for (int s = 0; s < 5; ++s)
+      if (64 * s + lane < 32 * 9) fr[64 * s + lane] = rv[s];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (64 * s + lane < 32 * 3) fr[32 * 9 + 64 * s + lane] = tv[s];
+  }
+  wave_sync();
+
+  // (2) this lane's z1 groups 8 q + 4 g .. + 3 of row n (kept packed until
+  //     used) and its frame
+  constexpr int NG = (NFB - 2) * 4;              // pair feature groups per lane
+  constexpr int ZW = sizeof(T) == 2 ? 2 : 4;     // 32-bit words per group
+  uint32_t zp[NG][ZW];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(xs + n * RB + 16 * (q ^ (n & zm)) + 8 * g);
+      zp[q][0] = v[0]; zp[q][1] = v[1];
+    } else {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + n * RB + 16 * ((2 * q + g) ^ (n & zm)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zp[q][e] = v[e];
     }
   }
+  auto zval = [&](int q, int e) -> float {
+    if constexpr (sizeof(T) == 2)
+      return __uint_as_float(e & 1 ? zp[q][e >> 1] & 0xFFFF0000u : zp[q][e >> 1] << 16);
+    else
+      return __uint_as_float(zp[q][e]);
+  };
+  float R[9], tr[3];
+#pragma unroll
+  for (int e = 0; e < 9; ++e) R[e] = fr[9 * n + e];
+#pragma unroll
+  for (int e = 0; e < 3; ++e) tr[e] = fr[32 * 9 + 3 * n + e];
+
+  // (3) scalar channels, points (T_i^-1 of the averaged global points) and
+  //     their norms of row n, staged as [32][kCSlot + 1], [32][3 kPvSlot + 1]
+  //     and [32][kPvSlot + 1] floats (columns past C, 3 Pv, Pv are never
+  //     stored) and written out row-contiguously
+  constexpr int PS = kCSlot + 1, PP = 3 * kPvSlot + 1, PN = kPvSlot + 1;
+  float* const so = reinterpret_cast<float*>(xs);
+  float* const sp = so + 32 * PS;
+  float* const sn = sp + 32 * PP;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) so[n * PS + 8 * k + 4 * g + e] = ok ? oacc[0][4 * k + e] * inv : 0.f;
+  // value points 4g + e: hi x/y/z in registers (0,8+e) (0,12+e) (1,e),
+  // lo x/y/z in (1,4+e) (1,8+e) (1,12+e)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int p = 4 * g + e;
+    const float gx = (oacc[0][8 + e] + oacc[1][4 + e] + gx_c) * inv - tr[0];
+    const float gy = (oacc[0][12 + e] + oacc[1][8 + e] + gy_c) * inv - tr[1];
+    const float gz = (oacc[1][e] + oacc[1][12 + e] + gz_c) * inv - tr[2];
+    const float lx = R[0] * gx + R[3] * gy + R[6] * gz;
+    const float lyv = R[1] * gx + R[4] * gy + R[7] * gz;
+    const float lz = R[2] * gx + R[5] * gy + R[8] * gz;
+    const float nr = sqrtf(lx * lx + lyv * lyv + lz * lz);
+    float* const pp = sp + n * PP + 3 * p;
+    pp[0] = ok ? lx : 0.f;
+    pp[1] = ok ? lyv : 0.f;
+    pp[2] = ok ? lz : 0.f;
+    sn[n * PN + p] = ok ? nr : 0.f;
+  }
+  wave_sync();
+  // [32][cols] block staged at src (row pitch SP > cols) -> rows `pitch`
+  // floats apart from dst; consecutive lanes take consecutive floats. Every
+  // staged value is read first (rows clamped into the block), then the
+  // stores go out back to back; the store resource ends after row nrow - 1,
+  // so rows past L are dropped by its range check.
+  auto store_rows = [&](auto sp_c, const float* src, int cols, float* dst, int pitch) {
+    constexpr int SP = decltype(sp_c)::value;
+    constexpr int NIT = 32 * (SP - 1) / 64;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, nrow > 0 ? (uint32_t)(((nrow - 1) * pitch + cols) * 4) : 0u);
+    float v[NIT];
+    int off[NIT];
+    int r = lane / cols, c = lane - r * cols;
+    const int dr = 64 / cols, dc = 64 - dr * cols;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      v[it] = src[(r < 32 ? r : 31) * SP + c];
+      off[it] = (r * pitch + c) * 4;
+      r += dr;
+      c += dc;
+      if (c >= cols) { c -= cols; ++r; }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[it]), rs, off[it], 0, 0);
+  };
+  const size_t row0 = ((size_t)b * L + qw) * H + h;   // (b, qw, h) output row
+  store_rows(std::integral_constant<int, PS>{}, so, C, a.out_s + row0 * C, H * C);
+  store_rows(std::integral_constant<int, PP>{}, sp, 3 * Pv, a.out_pts + row0 * 3 * Pv, H * 3 * Pv);
+  store_rows(std::integral_constant<int, PN>{}, sn, Pv, a.out_pts_norm + row0 * Pv, H * Pv);
 
   // ---- pair channels: o_pair[c] = sum_r z1[r Cz + c] O[r Cz + c] / l ----
   // Lane (n, g) holds O at features 32 fb + 8 k + 4 g + e of query n: 4-wide
   // groups at feature 8 q + 4 g (q = 4 (fb - 2) + k). Cz is a multiple of 8,
   // so every rank component of a channel lands in the same lane.
-  // (1) every z1 group this lane needs is loaded at once, through the global
-  //     address space so that the loads are not ordered behind the LDS
-  //     traffic below; (2) the products are formed in registers; (3) they
-  //     are summed over r into a padded per-wave LDS block, two waves at a
-  //     time; (4) the block is written out row by row.
-  constexpr int NG = (NFB - 2) * 4;   // pair feature groups per lane
-  float z[NG][4];
-  {
-    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(static_cast<const T*>(a.z1) + (size_t)b * L * RCz,
-                                                (uint32_t)L * RCz * ES);
-    const int vz = (ic * RCz + 4 * g) * ES;
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      // unconditional loads so that they all issue back to back; groups past
-      // R Cz, and rows that output zeros, drop them
-      if constexpr (sizeof(T) == 2) {
-        const u32x2 zr = __builtin_amdgcn_raw_buffer_load_b64(rZ, vz + 16 * q, 0, 0);
-        z[q][0] = __uint_as_float(zr[0] << 16); z[q][1] = __uint_as_float(zr[0] & 0xFFFF0000u);
-        z[q][2] = __uint_as_float(zr[1] << 16); z[q][3] = __uint_as_float(zr[1] & 0xFFFF0000u);
-      } else {
-        const u32x4 zr = __builtin_amdgcn_raw_buffer_load_b128(rZ, vz + 32 * q, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[q][e] = __uint_as_float(zr[e]);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      const bool use = ok && 8 * q + 4 * g < RCz;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) z[q][e] = use ? z[q][e] : 0.f;
-    }
-  }
-
+  //
   // Cz a multiple of 32: rank component r of channel c = 32 m + 8 k + 4 g + e
   // is register 4 k + e of tile 2 + m + r Cz / 32, so the sum over r is
-  // formed in registers (one specialisation per Cz / 32) and each lane
-  // stores its channels directly. Other Cz go through LDS below.
+  // formed in registers (one specialisation per Cz / 32). Each 32-channel
+  // group of the 32 rows is staged as [32][32] floats (chunk c of row r in
+  // slot c ^ (r & 7)), two groups alternating, and stored as 128-byte row
+  // pieces. Other Cz go through LDS below.
   bool pair_done = false;
   auto pair_regs = [&](auto sc) {
     constexpr int S = decltype(sc)::value;
     if constexpr (S * 32 <= SM::kCzMax) {
       constexpr int RMAX = (NFB - 2) / S;
-      float* orow = a.out_pair + rowh * Cz;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(a.out_pair + row0 * Cz, nrow > 0 ? (uint32_t)(((nrow - 1) * H * Cz + Cz) * 4) : 0u);
 #pragma unroll
-      for (int m = 0; m < S; ++m)
+      for (int m = 0; m < S; ++m) {
+        unsigned char* const pb = xs + (m & 1) * 4096;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
+          // only groups of rank components r < R (features < R Cz) are read
           float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int r = 0; r < RMAX; ++r) {
             if (r < ly.R) {
               const int fb = 2 + m + r * S, q = 4 * (m + r * S) + k;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) acc[e] = fmaf(z[q][e], oacc[fb][4 * k + e], acc[e]);
+              for (int e = 0; e < 4; ++e) acc[e] = fmaf(zval(q, e), oacc[fb][4 * k + e], acc[e]);
             }
           }
-          if (in_range)
-            *reinterpret_cast<float4*>(orow + 32 * m + 8 * k + 4 * g) =
-                make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+          // rows that output zeros write +0.0
+          *reinterpret_cast<float4*>(pb + n * 128 + 16 * ((2 * k + g) ^ (n & 7))) =
+              ok ? make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        wave_sync();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = (lane >> 3) + 8 * j, c = lane & 7;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(pb + r * 128 + 16 * (c ^ (r & 7)));
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, (r * H * Cz + 32 * m + 4 * c) * 4, 0, 0);
+        }
+      }
       pair_done = true;
     }
   };
@@ -848,12 +934,15 @@ void ipa_attn_kernel(FwdArgs a) {
   }
   if (pair_done) return;
 
-  // general Cz: products into registers, then summed over r in LDS
+  // general Cz: products into registers (groups past R Cz and rows that
+  // output zeros take z = 0), then summed over r in a padded per-wave LDS
+  // block, two waves at a time, and written out row by row
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     const int fb = 2 + q / 4, k = q % 4;
+    const bool use = ok && 8 * q + 4 * g < RCz;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) oacc[fb][4 * k + e] *= z[q][e] * inv;
+    for (int e = 0; e < 4; ++e) oacc[fb][4 * k + e] *= (use ? zval(q, e) : 0.f) * inv;
   }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
