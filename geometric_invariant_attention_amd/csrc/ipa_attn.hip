@@ -25,8 +25,12 @@
 //   row_i = -k (2 delta . sum A'_i + Pqk |delta|^2)  (float32, per query)
 //   delta = c_I - c_J (query and key block centres).
 // The running max is only moved when a tile's max exceeds it by more than
-// kLazy (base-2) units; probabilities can then reach 2^kLazy, which bf16 and
-// float32 hold exactly, and the final division by the row sum is unchanged.
+// kLazy (base-2) units. Probabilities can then reach 2^kLazy; floating point
+// is scale-free, so only overflow bounds kLazy: with 2^64, up to 2^16 keys
+// and value entries below 2^16 in magnitude the accumulators stay under
+// 2^96, far inside bf16/float32 range, and the final division by the row
+// sum is unchanged. In practice the max then moves once, on the first tile
+// with a valid key, and the output accumulators are never rescaled.
 // Probabilities are rounded to bf16 once and the same rounded values feed
 // the value product, the row sum and the block-centre correction, so the
 // output is a convex combination of the value rows.
@@ -43,19 +47,17 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kLazy = 8.0f;
+constexpr float kLazy = 64.0f;
 // Keys per tile of the key loop (the centring blocks stay 64 residues).
 constexpr int kKT = 32;
 // Operand fragments read ahead of the matrix-core products that use them.
 constexpr int kLook = 6;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
 // Round to nearest even fp16, saturating at the largest finite value.
 __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
   f = fminf(fmaxf(f, -65504.f), 65504.f);
@@ -99,7 +101,6 @@ __device__ __forceinline__ void step_fence() { asm volatile("" ::: "memory"); }
 // product whose result passes through it stays in its step. No instruction
 // is emitted and no register is read.
 __device__ __forceinline__ void pin_step(f32x16& acc) { asm volatile("" : "+a"(acc)); }
-__device__ __forceinline__ void pin_step(f32x16&, int) {}
 
 // o *= al for one 32x32 accumulator tile, in place in the accumulation
 // registers, so that the output accumulators never leave them (plain vector
@@ -336,6 +337,46 @@ void ipa_attn_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rVh = make_rsrc(Vth, (uint32_t)nJ * 4096 * ES);
   const __amdgpu_buffer_rsrc_t rVz = make_rsrc(Vtz, (uint32_t)nJ * (NP - 1) * 4096 * ES);
   const __amdgpu_buffer_rsrc_t rKc = make_rsrc(kcol, (uint32_t)Lp * 16);
+
+  // Running-max seed (bf16 path): the row's own logit s_ii, from its query
+  // operand and its own key row (lane and partner lane l ^ 32 each hold half
+  // of every 16-wide slice) plus the key's column term (the block offset is
+  // zero). A real logit, so a lower bound of the row max, and close to it:
+  // the query's own residue is the key nearest in space. With the lazy
+  // threshold the first key tiles then leave the max where it is instead of
+  // each nearer tile moving it and rescaling the output.
+  float m_seed = -INFINITY;
+  if constexpr (sizeof(T) == 2) {
+    const int J = i / kTileN, jj = i % kTileN;
+    u32x4 kr[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      if (s < NKH) {
+        kr[s] = __builtin_amdgcn_raw_buffer_load_b128(rKh, (i * kHeadW + 16 * s + 8 * g) * ES, 0, 0);
+      } else {
+        const int u = s - NKH;   // pair slice: panel u / 4, features 16 (u % 4) + 8 g
+        kr[s] = __builtin_amdgcn_raw_buffer_load_b128(
+            rKz, (((J * (NP - 1) + u / 4) * kTileN + jj) * 64 + 16 * (u % 4) + 8 * g) * ES, 0, 0);
+      }
+    }
+    const float kci_w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rKc, i * 16 + 12, 0, 0));
+    float d = 0.f;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const u32x4 qv = __builtin_bit_cast(u32x4, qf[s]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // words copied out first: a bit cast straight from a vector element
+        // would read element 0
+        const uint32_t qw2 = qv[e], kw2 = kr[s][e];
+        if (s < NKH)
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw2), __builtin_bit_cast(bf16x2, kw2), d, false);
+        else
+          d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw2), __builtin_bit_cast(f16x2, kw2), d, false);
+      }
+    }
+    m_seed = d + __shfl_xor(d, 32, 64) + kci_w;
+  }
   const uint32_t voK = KS::voff(lane, w, 64 * ES);
   const uint32_t voV = VS::voff(lane, w, 64 * ES);
   // Key tiles are visited starting at this block's own diagonal tile; tiles
@@ -364,7 +405,7 @@ void ipa_attn_kernel(FwdArgs a) {
   f32x16 oacc[NFB];
 #pragma unroll
   for (int fb = 0; fb < NFB; ++fb) oacc[fb] = f32x16{};
-  float m_run = -INFINITY, l_own = 0.f;
+  float m_run = m_seed, l_own = 0.f;
   float ocx = 0.f, ocy = 0.f, ocz = 0.f;
 
   // Column data of tile t (key lane & 31), read straight into registers one
@@ -559,37 +600,25 @@ void ipa_attn_kernel(FwdArgs a) {
   if (nseq > 0) {
     int sq = 0;                                   // sequence position of this iteration
     int t0 = tile_at(0), t1 = tile_at(1), t2 = tile_at(2);
-    // The running max of each wave is seeded from the scores of seq[w],
-    // which is the wave's own diagonal tile when its block has valid keys:
-    // the nearest keys, whose logits the shared visiting order would
-    // otherwise reach only after up to three tiles, each overtaking the
-    // running max and forcing an output rescale. The keys of seq[2] and
-    // seq[3] are staged in V1 and pbuf, both unused until the key loop.
-    unsigned char* const PB = reinterpret_cast<unsigned char*>(&pbuf[0][0][0]);
-    static_assert(sizeof(pbuf) >= SM::kKBuf && SM::kVBuf >= SM::kKBuf, "seed buffers");
-    const int tw = tile_at(w);
     copy_k(t0, K0);
     copy_v(t0, V0);
     copy_k(t1, K1);
-    copy_k(t2, V1);
-    copy_k(tile_at(3), PB);
     const float4 kc0 = load_kc(t0);
     float4 kc_n = load_kc(t1);                    // column data of t1
-    const float4 kcw = load_kc(tw);
     float4 cJ0 = cenS[t0 >> 1], cJ1 = cenS[t1 >> 1];
-    const float4 cJw = cenS[tw >> 1];
     wait_vmem();
     __syncthreads();
-    {
-      const unsigned char* Kw = w == 0 ? K0 : w == 1 ? K1 : w == 2 ? V1 : PB;
-      const float rw = col_prep(kcw, cJw);
-      const f32x16 sw = phase_a(cJw, Kw, col_vals(), [](int) {});
-      m_run = row_max(sw) + rw;
-    }
     float rterm = col_prep(kc0, cJ0);
-    f32x16 sacc = phase_a(cJ0, K0, col_vals(), [](int) {});
+    // the column term is added by vector code, as in the loop, so that the
+    // score tile enters the loop in the registers the loop carries it in
+    f32x16 sacc = phase_a(cJ0, K0, f32x16{}, [](int) {});
+    {
+      const f32x16 cv = col_vals();
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[v] += cv[v];
+    }
     float mx = row_max(sacc);
-    __syncthreads();   // K0, V1 and pbuf are refilled from iteration 0 on
+    __syncthreads();   // K0 is refilled from iteration 0 on
 
     // Iteration sq holds the scores of t0 = seq[sq] (sacc, row max mx) and
     //   1. moves the running max if those scores call for it,
