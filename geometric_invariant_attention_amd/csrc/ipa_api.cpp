@@ -38,6 +38,7 @@ bool make_layout(const int32_t d[8], int esize, Layout* o) {
   ly.off_kcol = take((size_t)B * H * Lp * 16);
   ly.off_qrow = take((size_t)B * H * Lp * 16);
   ly.off_cen = take((size_t)B * ly.nJ * 16);
+  ly.off_pdiag = take((size_t)B * H * Lp * 16);
   ly.total = off;
   return true;
 }

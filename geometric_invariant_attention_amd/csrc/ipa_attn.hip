@@ -47,7 +47,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -338,44 +337,21 @@ void ipa_attn_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rVz = make_rsrc(Vtz, (uint32_t)nJ * (NP - 1) * 4096 * ES);
   const __amdgpu_buffer_rsrc_t rKc = make_rsrc(kcol, (uint32_t)Lp * 16);
 
-  // Running-max seed (bf16 path): the row's own logit s_ii, from its query
-  // operand and its own key row (lane and partner lane l ^ 32 each hold half
-  // of every 16-wide slice) plus the key's column term (the block offset is
-  // zero). A real logit, so a lower bound of the row max, and close to it:
-  // the query's own residue is the key nearest in space. With the lazy
-  // threshold the first key tiles then leave the max where it is instead of
-  // each nearer tile moving it and rescaling the output.
+  // Running-max seed (bf16 path): the row's own logit s_ii, assembled by
+  // the lift kernel (head part plus the key's column term in the row term's
+  // w, the pair part per 64-wide panel; the block offset is zero). A real
+  // logit, so a lower bound of the row max, and close to it: the query's own
+  // residue is the key nearest in space. With the lazy threshold the first
+  // key tiles then leave the max where it is instead of each nearer tile
+  // moving it and rescaling the output.
   float m_seed = -INFINITY;
   if constexpr (sizeof(T) == 2) {
-    const int J = i / kTileN, jj = i % kTileN;
-    u32x4 kr[NKS];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      if (s < NKH) {
-        kr[s] = __builtin_amdgcn_raw_buffer_load_b128(rKh, (i * kHeadW + 16 * s + 8 * g) * ES, 0, 0);
-      } else {
-        const int u = s - NKH;   // pair slice: panel u / 4, features 16 (u % 4) + 8 g
-        kr[s] = __builtin_amdgcn_raw_buffer_load_b128(
-            rKz, (((J * (NP - 1) + u / 4) * kTileN + jj) * 64 + 16 * (u % 4) + 8 * g) * ES, 0, 0);
-      }
-    }
-    const float kci_w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rKc, i * 16 + 12, 0, 0));
-    float d = 0.f;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      const u32x4 qv = __builtin_bit_cast(u32x4, qf[s]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // words copied out first: a bit cast straight from a vector element
-        // would read element 0
-        const uint32_t qw2 = qv[e], kw2 = kr[s][e];
-        if (s < NKH)
-          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw2), __builtin_bit_cast(bf16x2, kw2), d, false);
-        else
-          d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw2), __builtin_bit_cast(f16x2, kw2), d, false);
-      }
-    }
-    m_seed = d + __shfl_xor(d, 32, 64) + kci_w;
+    const float4 pd = reinterpret_cast<const float4*>(a.ws + ly.off_pdiag)[bh * Lp + i];
+    float sd = qr.w + pd.x;
+    if constexpr (NP - 1 > 1) sd += pd.y;
+    if constexpr (NP - 1 > 2) sd += pd.z;
+    if constexpr (NP - 1 > 3) sd += pd.w;
+    m_seed = sd;
   }
   const uint32_t voK = KS::voff(lane, w, 64 * ES);
   const uint32_t voV = VS::voff(lane, w, 64 * ES);

@@ -45,8 +45,9 @@ struct Layout {
   size_t off_vth;   // [B][H][nJ][kHeadW][64]    value head part, feature-major
   size_t off_vtz;   // [B][nJ][PW][64]           value pair part (z2), feature-major
   size_t off_kcol;  // [B][H][Lp] float4         per-key column terms
-  size_t off_qrow;  // [B][H][Lp] float4         per-query row terms
+  size_t off_qrow;  // [B][H][Lp] float4         per-query row terms (w: own-key head logit)
   size_t off_cen;   // [B][nJ] float4            block centre xyz, valid count
+  size_t off_pdiag; // [B][H][Lp] float4        per-panel pair bias of the query's own key (seed)
   size_t total;
 };
 

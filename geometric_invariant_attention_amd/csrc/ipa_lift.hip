@@ -41,16 +41,23 @@
 // term of -inf, so padding garbage never reaches a valid output.
 //
 // Work split. Grid (block J, head h or pair panel, batch b), 4 waves, one
-// residue per lane and no LDS: in a head workgroup wave 0 writes the query
-// rows, wave 1 the key rows and the key column terms, waves 2 and 3 the two
-// halves of the value block (lane = key position); every wave forms the
-// block centre itself with cross-lane sums. In a pair workgroup wave 0
-// writes the key pair panel and waves 1 and 2 the two halves of the value
-// pair panel. Rows are assembled in registers and written with 16-byte
-// stores (value blocks: one coalesced row of 64 positions per store); all
-// loads are unconditional buffer loads (rows past L read row L - 1) whose
-// values invalid residues drop, each lane reading its input rows with
-// 16-byte loads where their length and alignment allow.
+// residue per lane: in a head workgroup wave 0 writes the query rows, wave 1
+// the key rows and the key column terms, waves 2 and 3 the two halves of the
+// value block (lane = key position); every wave forms the block centre
+// itself with cross-lane sums. In a pair workgroup wave 0 writes the key
+// pair panel and waves 1 and 2 the two halves of the value pair panel. Rows
+// are assembled in registers and written through per-wave LDS staging with
+// 16-byte stores (value blocks: one coalesced row of 64 positions per
+// store); all loads are unconditional buffer loads (rows past L read row
+// L - 1) whose values invalid residues drop, each lane reading its input
+// rows with 16-byte loads where their length and alignment allow.
+//
+// On the bf16 path the kernel also assembles, for every query and head, the
+// logit of the query with its own key, which the attention kernel takes as
+// the start of its running max: the head part (the key wave hands its rows
+// to the query wave through LDS) plus the key's column term in the w of the
+// query row term, and the pair part per 64-wide panel from the pair
+// workgroups (all four waves, heads split between them).
 
 #include "ipa_internal.h"
 
@@ -60,6 +67,7 @@ namespace {
 constexpr int kPtSlot = 15;   // query/key point coordinates per group (3 Pqk <= 15)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -245,6 +253,14 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
   using ST = Stage<ES>;
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[4][ST::kBytes];
   unsigned char* xb = xbuf[w];
+  // bf16 path: the key wave's lifted head rows and column terms, handed to
+  // the query wave for the logit of each query with its own key
+  constexpr int XR = sizeof(T) == 2 ? kTileN : 1;
+  __shared__ uint32_t kxr[XR][kHeadW / 2 + 1];
+  __shared__ float kxc[XR];
+  // bf16 path, pair workgroups: per wave, W_b weights of four heads over the
+  // 64 columns of the panel
+  __shared__ __attribute__((aligned(16))) float wtab[4][sizeof(T) == 2 ? 4 * 64 : 4];
 
   if (y < H) {
     // ================= head workgroup =================
@@ -295,6 +311,8 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     const float alpha = a.w_L * rsqrtf((float)C) * kLog2e;
     const float kap = a.w_L * a.gamma[h] * a.w_C * 0.5f * kLog2e;
 
+    uint32_t own[kHeadW * ES / 4];   // query wave: its packed head row
+    float4 qrow_v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (w <= 1) {
       // ---- query (wave 0) or key (wave 1) head row ----
       const __amdgpu_buffer_rsrc_t rs = in_rsrc(w == 0 ? a.q : a.k, C);
@@ -356,12 +374,19 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
         sn += P[3 * p] * P[3 * p] + P[3 * p + 1] * P[3 * p + 1] + P[3 * p + 2] * P[3 * p + 2];
       }
       if (w == 0) {
-        reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = make_float4(sx, sy, sz, 0.f);
+        qrow_v = make_float4(sx, sy, sz, 0.f);
+#pragma unroll
+        for (int e = 0; e < kHeadW * ES / 4; ++e) own[e] = wv[e];
       } else {
         // fp32 takes the whole point term from explicit differences
-        reinterpret_cast<float4*>(a.ws + ly.off_kcol)[o] =
-            !valid ? make_float4(0.f, 0.f, 0.f, -INFINITY)
-                   : (sizeof(T) == 2 ? make_float4(sx, sy, sz, -kap * sn) : make_float4(0.f, 0.f, 0.f, 0.f));
+        const float4 kc = !valid ? make_float4(0.f, 0.f, 0.f, -INFINITY)
+                                 : (sizeof(T) == 2 ? make_float4(sx, sy, sz, -kap * sn) : make_float4(0.f, 0.f, 0.f, 0.f));
+        reinterpret_cast<float4*>(a.ws + ly.off_kcol)[o] = kc;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < kHeadW / 2; ++e) kxr[lane][e] = wv[e];
+          kxc[lane] = kc.w;
+        }
       }
     } else {
       // ---- value head block, feature-major [64 features][64 positions];
@@ -410,11 +435,30 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       const size_t blk = ((size_t)b * H + h) * nJ + J;   // value block of (b, h, J)
       store_cols(xb, lane, out, a.ws + ly.off_vth + (blk * kHeadW + (w - 2) * 32) * kTileN * ES);
     }
+    // query row term; on the bf16 path its w holds the head part of the
+    // logit of the query with its own key (lifted rows as the attention
+    // products see them, plus the key's column term: the block offset is
+    // zero), the running-max seed of the attention kernel
+    if constexpr (sizeof(T) == 2) {
+      __syncthreads();   // kxr, kxc
+      if (w == 0) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < kHeadW / 2; ++e) {
+          const uint32_t qe = own[e], ke = kxr[lane][e];
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qe), __builtin_bit_cast(bf16x2, ke), d, false);
+        }
+        qrow_v.w = d + kxc[lane];
+      }
+    }
+    if (w == 0) reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = qrow_v;
   } else {
     // ================= pair workgroup: one 64-wide panel of z2 =================
-    if (w == 3) return;
+    // waves 0-2 write the panel; on the bf16 path wave 3 joins the pair
+    // bias work below
+    if (sizeof(T) == 4 && w == 3) return;
     const int P = y - H;
-    const int j = w == 0 ? lane : key_of_pos<T>(lane);
+    const int j = (w == 0 || w == 3) ? lane : key_of_pos<T>(lane);
     const int i = J * kTileN + j, ic = i < L ? i : L - 1;
     const bool valid = i < L && (a.mask == nullptr || a.mask[rb + ic] != 0);
     // z2 row segment u = 64 P .. 64 P + 63 of the residue (16-byte loads:
@@ -422,10 +466,37 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     // segment past the end of the batch reads zeros)
     const __amdgpu_buffer_rsrc_t rz =
         make_rsrc(static_cast<const unsigned char*>(a.z2) + rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
+    // bf16 path: the z1 segment and the first head group's W_b weights for
+    // the pair bias below, issued together with the z2 loads
+    constexpr int NZ1 = sizeof(T) == 2 ? 8 : 1;
+    u32x4 z1r[NZ1];
+    float wl0[4];
+    const int uu = 64 * P + lane, cu = uu % ly.Cz;
+    const float wsc = a.w_L * kLog2e;
+    auto weights = [&](int h0, float (&wl)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int hc = h0 + 4 * c < H ? h0 + 4 * c : H - 1;
+        wl[c] = wsc * a.w_b[(size_t)cu * H + hc];
+      }
+    };
+    if constexpr (sizeof(T) == 2) {
+      const __amdgpu_buffer_rsrc_t r1 =
+          make_rsrc(static_cast<const unsigned char*>(a.z1) + rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
+#pragma unroll
+      for (int c = 0; c < 8; ++c) z1r[c] = __builtin_amdgcn_raw_buffer_load_b128(r1, (ic * RCz + 64 * P) * ES + 16 * c, 0, 0);
+      weights(w, wl0);
+    }
     float z[64];
+    u32x4 z2r[64 * ES / 16];
+#pragma unroll
+    for (int c = 0; c < 64 * ES / 16; ++c) z2r[c] = __builtin_amdgcn_raw_buffer_load_b128(rz, (ic * RCz + 64 * P) * ES + 16 * c, 0, 0);
+    // keeps every load above in flight together (the compiler would
+    // otherwise issue the z1 and weight loads only after the z2 work)
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int c = 0; c < 64 * ES / 16; ++c) {
-      const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rz, (ic * RCz + 64 * P) * ES + 16 * c, 0, 0);
+      const u32x4 r = z2r[c];
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -439,6 +510,56 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 64; ++u) z[u] = (valid && 64 * P + u < RCz) ? z[u] : 0.f;
+    // bf16 path: this panel's share of each residue's pair bias with itself,
+    // sum_u w_L log2(e) W_b[u mod Cz, h] z1[u] z2[u], for every head: the
+    // pair part of the attention kernel's running-max seed. Wave w takes
+    // heads w, w + 4, ... in groups of four: lane u loads the weights of
+    // panel column u for the whole group at once, and they are broadcast
+    // through this wave's LDS block.
+    if constexpr (sizeof(T) == 2) {
+      float zz[64];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 r = z1r[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          zz[8 * c + 2 * e] = __uint_as_float(r[e] << 16) * z[8 * c + 2 * e];
+          zz[8 * c + 2 * e + 1] = __uint_as_float(r[e] & 0xFFFF0000u) * z[8 * c + 2 * e + 1];
+        }
+      }
+      float* const wt = wtab[w];
+      float4* const pd = reinterpret_cast<float4*>(a.ws + ly.off_pdiag);
+      for (int h0 = w; h0 < H; h0 += 16) {
+        float wl[4];
+        if (h0 == w) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) wl[c] = wl0[c];
+        } else {
+          weights(h0, wl);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wt[64 * c + lane] = uu < RCz ? wl[c] : 0.f;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float acc = 0.f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(wt + 64 * c + 4 * q);
+            acc = fmaf(v.x, zz[4 * q], acc);
+            acc = fmaf(v.y, zz[4 * q + 1], acc);
+            acc = fmaf(v.z, zz[4 * q + 2], acc);
+            acc = fmaf(v.w, zz[4 * q + 3], acc);
+          }
+          const int h = h0 + 4 * c;
+          if (h < H) reinterpret_cast<float*>(pd + ((size_t)b * H + h) * Lp + i)[P] = acc;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+      if (w == 3) return;
+    }
     if (w == 0) {
       // key pair row of residue j: [64 features] in panel P
       S rowv[64];
