@@ -12,11 +12,18 @@ Pinning status of each function (see the tests under ``tests/``):
                   closed form, permutation equivariance, mask semantics.
   ipa_bruteforce  pinned against the same closed forms on tiny inputs.
   ipa_lifted      pinned to ipa_forward (exact algebra, 1e-12 relative).
+  frames_from_atoms  pinned: orthonormal right-handed frames, local atom
+                  coordinates, SE(3) equivariance, hand-worked closed forms.
+  meet_attention  pinned: textbook attention (library SDPA) at s = 0, the
+                  MEET lifting identity through library SDPA, rigid
+                  invariance, two-residue closed form, mask rules, agreement
+                  with ipa_forward configured to the same logit.
 """
 
 from .ipa_oracle import ipa_forward, ipa_logits, to_global
 from .bruteforce import ipa_bruteforce
 from .lifted import ipa_lifted, block_centres
+from .geometry import frames_from_atoms, meet_attention
 
 __all__ = ["ipa_forward", "ipa_logits", "to_global", "ipa_bruteforce",
-           "ipa_lifted", "block_centres"]
+           "ipa_lifted", "block_centres", "frames_from_atoms", "meet_attention"]

@@ -193,3 +193,122 @@ def stress_pair(inp: dict) -> dict:
         a = inp[name].astype(np.float32) * np.float32(math.sqrt(Cz))
         out[name] = round_to_bf16(a) if inp["dtype"] == "bf16" else a
     return out
+
+
+# ----------------------------------------------------------------------------
+# backbone atoms (input of the frame construction)
+# ----------------------------------------------------------------------------
+
+def make_backbone(B: int, L: int, seed: int = 0, step: float = 3.8) -> dict:
+    """Seeded backbone atoms N, C-alpha, C as float32 [B, L, 3] arrays.
+
+    C-alpha atoms follow the same centred chain as the frame translations
+    (fixed steps of ``step`` A in uniformly random directions). Around each
+    C-alpha, C sits 1.52 A away in a uniformly random direction and N 1.46 A
+    away at an angle of 111 degrees to it, turned by a uniformly random
+    angle about the C-alpha -> C axis (protein-like bond lengths and angle;
+    never collinear). Draw order: chain steps, C directions, N turn angles.
+    """
+    rng = np.random.default_rng(seed)
+    steps = rng.standard_normal((B, L, 3))
+    cdir = rng.standard_normal((B, L, 3))
+    turn = rng.uniform(0.0, 2.0 * math.pi, size=(B, L))
+    g = steps / np.linalg.norm(steps, axis=-1, keepdims=True)
+    ca = np.zeros((B, L, 3))
+    ca[:, 1:] = np.cumsum(step * g[:, 1:], axis=1)
+    ca -= ca.mean(axis=1, keepdims=True)
+    u = cdir / np.linalg.norm(cdir, axis=-1, keepdims=True)
+    # two unit vectors orthogonal to u
+    a = np.where(np.abs(u[..., :1]) < 0.9, np.array([1.0, 0.0, 0.0]), np.array([0.0, 1.0, 0.0]))
+    p = np.cross(u, a)
+    p /= np.linalg.norm(p, axis=-1, keepdims=True)
+    r = np.cross(u, p)
+    ang = math.radians(111.0)
+    ndir = math.cos(ang) * u + math.sin(ang) * (np.cos(turn)[..., None] * p + np.sin(turn)[..., None] * r)
+    c = ca + 1.52 * u
+    n = ca + 1.46 * ndir
+    return dict(n=n.astype(np.float32), ca=ca.astype(np.float32), c=c.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
+# distance-penalised attention over one point per residue
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MeetWorkload:
+    name: str
+    B: int
+    L: int
+    H: int
+    C: int = 16
+    dtype: str = "bf16"          # storage of q, k, v
+    step: float = 3.8
+    ragged: tuple | None = None
+    seed: int = 0
+
+    def dims(self) -> dict:
+        return dict(B=self.B, L=self.L, H=self.H, C=self.C)
+
+    def with_(self, **kw) -> "MeetWorkload":
+        d = asdict(self)
+        d.update(kw)
+        return MeetWorkload(**d)
+
+
+MEET_WORKLOADS = {
+    "meet_tiny_fp32": MeetWorkload("meet_tiny_fp32", B=1, L=64, H=4, dtype="fp32"),
+    "meet_chain_512": MeetWorkload("meet_chain_512", B=1, L=512, H=12),
+    "meet_chain_2048": MeetWorkload("meet_chain_2048", B=1, L=2048, H=12),
+    "meet_ragged": MeetWorkload("meet_ragged", B=8, L=128, H=8, ragged=(40, 128)),
+}
+
+
+def make_meet_inputs(w: MeetWorkload, seed: int | None = None) -> dict:
+    """Draw one seeded input set for a distance-attention workload.
+
+    Draw order: chain steps, q, k, v, rho logits, s logits, lengths, padding
+    garbage. x is the centred chain of the IPA recipe; q, k, v ~ N(0, 1);
+    rho_h = softplus(N(0, 1)) / sqrt(C); s_h = 0.2 softplus(N(0, 1)) (per
+    A). Ragged batches get a prefix mask and finite garbage in padded rows.
+    bf16 workloads round q, k, v to bfloat16 here; x, rho, s stay float32.
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    B, L, H, C = w.B, w.L, w.H, w.C
+    steps = rng.standard_normal((B, L, 3))
+    q = rng.standard_normal((B, L, H, C))
+    k = rng.standard_normal((B, L, H, C))
+    v = rng.standard_normal((B, L, H, C))
+    rho = _softplus(rng.standard_normal(H)) / math.sqrt(C)
+    s = 0.2 * _softplus(rng.standard_normal(H))
+    if w.ragged is not None:
+        lo, hi = w.ragged
+        lengths = rng.integers(lo, hi + 1, size=B)
+    else:
+        lengths = np.full(B, L, dtype=np.int64)
+    x = np.zeros((B, L, 3))
+    mask = np.zeros((B, L), dtype=np.uint8)
+    for b in range(B):
+        n = int(lengths[b])
+        mask[b, :n] = 1
+        g = steps[b, :n] / np.linalg.norm(steps[b, :n], axis=-1, keepdims=True)
+        xb = np.zeros((n, 3))
+        if n > 1:
+            xb[1:] = np.cumsum(w.step * g[1:], axis=0)
+        x[b, :n] = xb - xb.mean(axis=0)
+    if w.ragged is not None:
+        pad = mask == 0
+        npad = int(pad.sum())
+        if npad:
+            q[pad] = 10.0 * rng.standard_normal((npad, H, C))
+            k[pad] = 10.0 * rng.standard_normal((npad, H, C))
+            v[pad] = 10.0 * rng.standard_normal((npad, H, C))
+            x[pad] = rng.uniform(-1e3, 1e3, size=(npad, 3))
+    feats = {}
+    for name, a in (("q", q), ("k", k), ("v", v)):
+        a32 = a.astype(np.float32)
+        feats[name] = round_to_bf16(a32) if w.dtype == "bf16" else a32
+    out = dict(feats)
+    out.update(x=x.astype(np.float32), rho=rho.astype(np.float32), s=s.astype(np.float32),
+               mask=mask, lengths=lengths.astype(np.int64), dtype=w.dtype, dims=w.dims(),
+               workload=w.name, has_mask=w.ragged is not None)
+    return out
