@@ -31,6 +31,10 @@ class IpaDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "H", "C", "Pqk", "Pv", "R", "Cz")]
 
 
+class IpaMeetDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "H", "C")]
+
+
 class IPAError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -57,6 +61,12 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     for fn in (lib.ipa_forward, lib.ipa_lift, lib.ipa_attend):
         fn.argtypes = [ctypes.POINTER(IpaDims), i32] + [vp] * 13 + [f32, f32] + [vp] * 5 + [sz, vp]
         fn.restype = i32
+    lib.ipa_frames_from_atoms.argtypes = [i32, i32] + [vp] * 5 + [vp]
+    lib.ipa_frames_from_atoms.restype = i32
+    lib.ipa_meet_workspace_bytes.argtypes = [ctypes.POINTER(IpaMeetDims), i32]
+    lib.ipa_meet_workspace_bytes.restype = sz
+    lib.ipa_meet_forward.argtypes = [ctypes.POINTER(IpaMeetDims), i32] + [vp] * 9 + [sz, vp]
+    lib.ipa_meet_forward.restype = i32
     lib.ipa_status_string.argtypes = [i32]
     lib.ipa_status_string.restype = ctypes.c_char_p
     lib.ipa_version.argtypes = []
@@ -203,3 +213,96 @@ def ipa_forward(q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma,
     out = plan(q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma,
                mask=mask, w_L=w_L, w_C=w_C)
     return out
+
+
+def frames_from_atoms(n: torch.Tensor, ca: torch.Tensor, c: torch.Tensor,
+                      stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Residue frames (rot [B,L,3,3], trans [B,L,3], float32) from backbone
+    atoms n, ca, c [B,L,3] float32 on one device (ipa_frames_from_atoms)."""
+    if n.dim() != 3 or n.shape[-1] != 3 or ca.shape != n.shape or c.shape != n.shape:
+        raise ValueError(f"atoms must share a [B,L,3] shape, got {tuple(n.shape)}, "
+                         f"{tuple(ca.shape)}, {tuple(c.shape)}")
+    dev = n.device
+    n, ca, c = (_prep(t, torch.float32, dev, name) for t, name in ((n, "n"), (ca, "ca"), (c, "c")))
+    B, L = n.shape[0], n.shape[1]
+    rot = torch.empty(B, L, 3, 3, dtype=torch.float32, device=dev)
+    trans = torch.empty(B, L, 3, dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = load_library().ipa_frames_from_atoms(B, L, n.data_ptr(), ca.data_ptr(), c.data_ptr(),
+                                              rot.data_ptr(), trans.data_ptr(),
+                                              ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise IPAError(rc, status_string(rc))
+    return rot, trans
+
+
+def meet_workspace_bytes(B: int, L: int, H: int, C: int, dtype: int) -> int:
+    d = IpaMeetDims(B, L, H, C)
+    return int(load_library().ipa_meet_workspace_bytes(ctypes.byref(d), int(dtype)))
+
+
+class MeetForward:
+    """Reusable plan of the distance-penalised attention (ipa_meet_forward):
+    validated shapes, preallocated workspace and output on one device."""
+
+    def __init__(self, B, L, H, C, dtype=torch.bfloat16, device=None):
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("dtype must be torch.bfloat16 or torch.float32")
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.dims = IpaMeetDims(B, L, H, C)
+        self.shape = dict(B=B, L=L, H=H, C=C)
+        self.dtype = dtype
+        self.code = IPA_BF16 if dtype == torch.bfloat16 else IPA_F32
+        self.lib = load_library()
+        self.ws_bytes = int(self.lib.ipa_meet_workspace_bytes(ctypes.byref(self.dims), self.code))
+        if self.ws_bytes == 0:
+            raise IPAError(-6, f"unsupported dims {self.shape} for {dtype}")
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.out = torch.empty(B, L, H, C, dtype=torch.float32, device=self.device)
+
+    def bind(self, q, k, v, x, rho, s, mask=None, stream=None) -> tuple:
+        B, L, H, C = (self.shape[n] for n in ("B", "L", "H", "C"))
+        dev, dt = self.device, self.dtype
+        expect = {"q": ((B, L, H, C), dt), "k": ((B, L, H, C), dt), "v": ((B, L, H, C), dt),
+                  "x": ((B, L, 3), torch.float32), "rho": ((H,), torch.float32), "s": ((H,), torch.float32)}
+        args = dict(q=q, k=k, v=v, x=x, rho=rho, s=s)
+        for name, (shp, want) in expect.items():
+            t = args[name]
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+            args[name] = _prep(t, want, dev, name)
+        m = None
+        if mask is not None:
+            if tuple(mask.shape) != (B, L):
+                raise ValueError(f"mask has shape {tuple(mask.shape)}, expected {(B, L)}")
+            if mask.device != dev:
+                raise ValueError(f"mask is on {mask.device}, expected {dev}")
+            m = (mask.to(torch.uint8) if mask.dtype != torch.uint8 else mask).contiguous()
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        self.bound = (args, m)
+        return (ctypes.byref(self.dims), self.code,
+                *(args[n].data_ptr() for n in ("q", "k", "v", "x", "rho", "s")),
+                _dev_ptr(m), self.out.data_ptr(), self.workspace.data_ptr(),
+                ctypes.c_size_t(self.ws_bytes), ctypes.c_void_p(stream.cuda_stream))
+
+    def forward_raw(self, raw: tuple) -> torch.Tensor:
+        rc = self.lib.ipa_meet_forward(*raw)
+        if rc != 0:
+            raise IPAError(rc, status_string(rc))
+        return self.out
+
+    def __call__(self, *args, **kw) -> torch.Tensor:
+        return self.forward_raw(self.bind(*args, **kw))
+
+
+def meet_attention(q, k, v, x, rho, s, mask=None) -> torch.Tensor:
+    """Distance-penalised attention on the device of ``q``: per head h,
+    softmax_j(rho_h (q_i . k_j - s_h^2 |x_i - x_j|^2)) applied to v.
+    Returns a freshly allocated float32 [B,L,H,C] tensor."""
+    B, L, H, C = q.shape
+    plan = MeetForward(B, L, H, C, dtype=q.dtype, device=q.device)
+    return plan(q, k, v, x, rho, s, mask=mask)

@@ -103,6 +103,7 @@ int32_t run(int stages, const ipa_dims* dims, int32_t dtype,
   a.mask = mask; a.w_L = w_L; a.w_C = w_C;
   a.out_s = out_s; a.out_pts = out_pts; a.out_pts_norm = out_pts_norm; a.out_pair = out_pair;
   a.ws = static_cast<unsigned char*>(workspace);
+  a.meet_rho = nullptr; a.meet_s = nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((stages & kLift) && ipa::launch_lift(a, bf16, s) != hipSuccess) return IPA_ERR_HIP;
@@ -137,6 +138,69 @@ size_t ipa_workspace_bytes(const ipa_dims* dims, int32_t dtype) {
 int32_t ipa_forward(IPA_ARGS_DECL) { return run(kBoth, IPA_ARGS_PASS); }
 int32_t ipa_lift(IPA_ARGS_DECL) { return run(kLift, IPA_ARGS_PASS); }
 int32_t ipa_attend(IPA_ARGS_DECL) { return run(kAttend, IPA_ARGS_PASS); }
+
+int32_t ipa_frames_from_atoms(int32_t B, int32_t L, const float* n, const float* ca, const float* c,
+                              float* rot_out, float* trans_out, void* stream) {
+  if (B < 1 || L < 1 || (int64_t)B * L >= (int64_t(1) << 31)) return IPA_ERR_DIMS;
+  const void* req[] = {n, ca, c, rot_out, trans_out};
+  for (const void* p : req)
+    if (!p) return IPA_ERR_NULL;
+  for (const void* p : req)
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return IPA_ERR_ALIGN;
+  if (ipa::launch_frames(B * L, n, ca, c, rot_out, trans_out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return IPA_ERR_HIP;
+  return IPA_OK;
+}
+
+// The distance attention runs on the IPA kernels with one (zero) local
+// point per head for queries, keys and values and one all-zero pair panel.
+static bool meet_ipa_dims(const ipa_meet_dims* d, int32_t out[8]) {
+  if (!d) return false;
+  out[0] = d->B; out[1] = d->L; out[2] = d->H; out[3] = d->C;
+  out[4] = 1; out[5] = 1; out[6] = 1; out[7] = 32;
+  return true;
+}
+
+size_t ipa_meet_workspace_bytes(const ipa_meet_dims* dims, int32_t dtype) {
+  int32_t v[8];
+  if (!meet_ipa_dims(dims, v) || !basic_dims_ok(v)) return 0;
+  if (dtype != IPA_F32 && dtype != IPA_BF16) return 0;
+  ipa::Layout ly;
+  if (!ipa::make_layout(v, dtype == IPA_BF16 ? 2 : 4, &ly)) return 0;
+  return ly.total;
+}
+
+int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype, const void* q, const void* k,
+                         const void* v, const float* x, const float* rho, const float* s,
+                         const uint8_t* mask, float* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  int32_t dv[8];
+  if (!meet_ipa_dims(dims, dv)) return IPA_ERR_NULL;
+  if (!basic_dims_ok(dv)) return IPA_ERR_DIMS;
+  if (dtype != IPA_F32 && dtype != IPA_BF16) return IPA_ERR_DTYPE;
+  const void* req[] = {q, k, v, x, rho, s, out, workspace};
+  for (const void* p : req)
+    if (!p) return IPA_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return IPA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return IPA_ERR_ALIGN;
+
+  ipa::FwdArgs a;
+  const bool bf16 = dtype == IPA_BF16;
+  if (!ipa::make_layout(dv, bf16 ? 2 : 4, &a.lay)) return IPA_ERR_UNSUPPORTED;
+  if (workspace_bytes < a.lay.total) return IPA_ERR_WORKSPACE;
+  a.q = q; a.k = k; a.v = v;
+  a.q_pts = nullptr; a.k_pts = nullptr; a.v_pts = nullptr;
+  a.rot = nullptr; a.trans = x; a.z1 = nullptr; a.z2 = nullptr; a.w_b = nullptr; a.gamma = nullptr;
+  a.mask = mask; a.w_L = 0.f; a.w_C = 0.f;
+  a.out_s = out; a.out_pts = nullptr; a.out_pts_norm = nullptr; a.out_pair = nullptr;
+  a.ws = static_cast<unsigned char*>(workspace);
+  a.meet_rho = rho; a.meet_s = s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ipa::launch_lift(a, bf16, st) != hipSuccess) return IPA_ERR_HIP;
+  if (ipa::launch_attn(a, bf16, st) != hipSuccess) return IPA_ERR_HIP;
+  return IPA_OK;
+}
 
 const char* ipa_status_string(int32_t status) {
   switch (status) {

@@ -129,6 +129,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Resource over `bytes` bytes `off` bytes into `p`, or an empty resource
+// (every load reads zero, every store is dropped) when `p` is NULL; no
+// offset is ever applied to a NULL pointer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_or_empty(const void* p, size_t off, uint32_t bytes) {
+  return p ? make_rsrc(static_cast<const unsigned char*>(p) + off, bytes) : make_rsrc(nullptr, 0u);
+}
+
 // Wait until every vector-memory load of this wave (the direct-to-LDS tile
 // loads) has completed; a builtin, so the compiler's own bookkeeping knows.
 __device__ __forceinline__ void wait_vmem() {
@@ -200,6 +207,8 @@ void ipa_attn_kernel(FwdArgs a) {
   constexpr int NFB = D / 32;              // 32-feature blocks of O^T
   constexpr int NP = SM::kNP;
   constexpr int NST = kKT / M::kStep;      // products per O^T block per tile
+  // the probabilities of a tile are formed two per score step (bf16)
+  static_assert(sizeof(T) == 4 || NKS >= 8, "at least 8 score steps per tile");
   constexpr int ES = (int)sizeof(T);
 
   // key rows: 64 elements of one panel; value rows: 32 keys
@@ -254,11 +263,13 @@ void ipa_attn_kernel(FwdArgs a) {
     const float4* cen = reinterpret_cast<const float4*>(a.ws + ly.off_cen) + (size_t)b * nJ;
     for (int e = tid; e < nJ; e += 256) cenS[e] = cen[e];
     const float ws = a.w_L * kLog2e;
-    for (int e = tid; e < Cz; e += 256) wbS[e] = ws * a.w_b[(size_t)e * H + h];
+    for (int e = tid; e < Cz; e += 256) wbS[e] = a.w_b ? ws * a.w_b[(size_t)e * H + h] : 0.f;
   }
   __syncthreads();  // cenS, wbS
 
-  const float kap = a.w_L * a.gamma[h] * a.w_C * 0.5f * kLog2e;
+  // point weight (base 2): w_L gamma_h w_C / 2, or rho_h s_h^2 for the
+  // distance attention
+  const float kap = (a.meet_rho ? a.meet_rho[h] * a.meet_s[h] * a.meet_s[h] : a.w_L * a.gamma[h] * a.w_C * 0.5f) * kLog2e;
   const bool row_valid = (i < L) && (a.mask == nullptr || a.mask[(size_t)b * L + i] != 0);
 
   // ---- query operand (B operand of S^T = K Q^T), held for the whole loop ----
@@ -268,8 +279,7 @@ void ipa_attn_kernel(FwdArgs a) {
   const int ic = i < L ? i : 0;
   if constexpr (sizeof(T) == 2) {
     const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.ws + ly.off_qh + bh * Lp * kHeadW * ES, (uint32_t)Lp * kHeadW * ES);
-    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(static_cast<const uint16_t*>(a.z1) + (size_t)b * L * RCz,
-                                                (uint32_t)L * RCz * ES);
+    const __amdgpu_buffer_rsrc_t rZ = rsrc_or_empty(a.z1, (size_t)b * L * RCz * ES, (uint32_t)L * RCz * ES);
     const int vq = (i * kHeadW + 8 * g) * ES;
     const int vz = (ic * RCz + 8 * g) * ES;
 #pragma unroll
@@ -312,7 +322,7 @@ void ipa_attn_kernel(FwdArgs a) {
         v = Qh[f];
       } else {
         const int uu = f - kHeadW;
-        if (uu < RCz && i < L) v = static_cast<const float*>(a.z1)[((size_t)b * L + i) * RCz + uu] * wbS[uu % Cz];
+        if (a.z1 && uu < RCz && i < L) v = static_cast<const float*>(a.z1)[((size_t)b * L + i) * RCz + uu] * wbS[uu % Cz];
       }
       qf[s] = v;
     }
@@ -530,30 +540,39 @@ void ipa_attn_kernel(FwdArgs a) {
       }
     }
   };
-  // Direct-to-LDS copy op k of a tile pair: ops 0 .. NP VJ - 1 copy value
-  // tile tv into Vd, the next NP KJ ops key tile tk into Kd.
+  // Source offsets of tile t: the head part (h) and the first pair panel
+  // (z) of its key rows or value block; every copy op adds a constant of its
+  // own (panel and wave), which the compiler keeps out of the loop.
+  struct TileOff { uint32_t h, z; };
+  auto key_off = [&](int t) -> TileOff {
+    return {(uint32_t)t * (kKT * 64 * ES), (uint32_t)((t >> 1) * (NP - 1) * 64 + 32 * (t & 1)) * 64 * ES};
+  };
+  auto val_off = [&](int t) -> TileOff {
+    return {(uint32_t)(t >> 1) * 4096 * ES + (uint32_t)(32 * (t & 1) * ES),
+            (uint32_t)(t >> 1) * (NP - 1) * 4096 * ES + (uint32_t)(32 * (t & 1) * ES)};
+  };
+  // Direct-to-LDS copy op k of a tile pair: ops 0 .. NP VJ - 1 copy the
+  // value tile at vo into Vd, the next NP KJ ops the key tile at ko into Kd.
   constexpr int NDMA = NP * (VJ + KJ);
-  auto dma_op = [&](int k, int tv, unsigned char* Vd, int tk, unsigned char* Kd) {
+  auto dma_op = [&](int k, TileOff vo, unsigned char* Vd, TileOff ko, unsigned char* Kd) {
     if (k < NP * VJ) {
-      const int P = k / VJ, j = k % VJ, J = tv >> 1, half = tv & 1;
-      const uint32_t vbase = (P == 0 ? (uint32_t)J * 4096 * ES : (uint32_t)(J * (NP - 1) + P - 1) * 4096 * ES) +
-                             (uint32_t)(32 * half * ES);
+      const int P = k / VJ, j = k % VJ;
       const int kk = w + 4 * j;
-      dma16(P == 0 ? rVh : rVz, voV, vbase + (uint32_t)(kk * VS::kRPL * 64 * ES), Vd + P * SM::kVPanel + kk * 1024);
+      const uint32_t c = (P == 0 ? 0u : (uint32_t)(P - 1) * 4096 * ES) + (uint32_t)(kk * VS::kRPL * 64 * ES);
+      dma16(P == 0 ? rVh : rVz, voV, (P == 0 ? vo.h : vo.z) + c, Vd + P * SM::kVPanel + kk * 1024);
     } else {
       const int q = k - NP * VJ;
-      const int P = q / KJ, j = q % KJ, J = tk >> 1, half = tk & 1;
-      const uint32_t kbase = P == 0 ? (uint32_t)(J * 64 + 32 * half) * 64 * ES
-                                    : (uint32_t)((J * (NP - 1) + P - 1) * 64 + 32 * half) * 64 * ES;
+      const int P = q / KJ, j = q % KJ;
       const int kk = w + 4 * j;
-      dma16(P == 0 ? rKh : rKz, voK, kbase + (uint32_t)(kk * KS::kRPL * 64 * ES), Kd + P * SM::kKPanel + kk * 1024);
+      const uint32_t c = (P == 0 ? 0u : (uint32_t)(P - 1) * 64 * 64 * ES) + (uint32_t)(kk * KS::kRPL * 64 * ES);
+      dma16(P == 0 ? rKh : rKz, voK, (P == 0 ? ko.h : ko.z) + c, Kd + P * SM::kKPanel + kk * 1024);
     }
   };
   // The copy ops of one iteration, spread evenly over its NKS + NB product
   // steps (op k at step k (NKS + NB) / NDMA): the address unit then drains
   // them alongside the products instead of holding the wave up in a burst.
   constexpr int NSTEP = NKS + NFB * NST;
-  auto dma_at = [&](int step, int tv, unsigned char* Vd, int tk, unsigned char* Kd) {
+  auto dma_at = [&](int step, TileOff tv, unsigned char* Vd, TileOff tk, unsigned char* Kd) {
 #pragma unroll
     for (int k = 0; k < NDMA; ++k)
       if (k * NSTEP / NDMA == step) dma_op(k, tv, Vd, tk, Kd);
@@ -645,6 +664,7 @@ void ipa_attn_kernel(FwdArgs a) {
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       float4 kc_nn;
       float rterm_n;
+      const TileOff vo1 = val_off(t1), ko2 = key_off(t2);
       f32x16 sacc_n = phase_a(cJ1, Kcur, f32x16{}, [&](int st) {
         if constexpr (sizeof(T) == 2) {
           if (st < 8) {
@@ -654,7 +674,7 @@ void ipa_attn_kernel(FwdArgs a) {
             lt = __builtin_amdgcn_fdot2_f32_bf16(pk[st], ones, lt, false);
           }
         }
-        dma_at(st, t1, Vfill, t2, Kfill);
+        dma_at(st, vo1, Vfill, ko2, Kfill);
         if (st == NKS - 3) kc_nn = load_kc(t2);
         if (st == NKS - 2) rterm_n = col_prep(kc_n, cJ1);
       });
@@ -681,22 +701,36 @@ void ipa_attn_kernel(FwdArgs a) {
       float mxn = -INFINITY;
       int t3raw = 0;
       float4 cJ2;
+      // (the side work is placed by step number, clamped to the phase: the
+      // value phase has NB = 2 NFB products, 8 for the narrowest rows)
+      constexpr int NB = NFB * NST;
+      constexpr int kColEnd = NB < 10 ? NB : 10;         // column adds in steps 2 .. kColEnd - 1
+      constexpr int kStCen = NB - 2 < 10 ? NB - 2 : 10;  // centre of t2
+      constexpr int kStSeq = NB - 1 < 11 ? NB - 1 : 11;  // visiting order, seq[sq + 3]
       phase_b(Vcur, pf, [&](int st) {
         if constexpr (sizeof(T) == 2) {
-          if (st >= 2 && st < 10) {
+          if (st >= 2 && st < kColEnd) {
             const int v = 2 * (st - 2);
             sacc_n[v] += cv[v];
             sacc_n[v + 1] += cv[v + 1];
             mxn = fmaxf(fmaxf(mxn, sacc_n[v]), sacc_n[v + 1]);
           }
         }
-        dma_at(NKS + st, t1, Vfill, t2, Kfill);
-        if (st == 10) cJ2 = cenS[t2 >> 1];
+        dma_at(NKS + st, vo1, Vfill, ko2, Kfill);
+        if (st == kStCen) cJ2 = cenS[t2 >> 1];
         // a plain LDS read here; it is made wave-uniform after the loop, so
         // that waiting for it does not stall the operand reads
-        if (st == 11) t3raw = seqS[sq + 3 < nseq ? sq + 3 : nseq - 1];
+        if (st == kStSeq) t3raw = seqS[sq + 3 < nseq ? sq + 3 : nseq - 1];
       });
       const int t3 = __builtin_amdgcn_readfirstlane(t3raw);
+      if constexpr (sizeof(T) == 2) {
+        // column adds the phase had no steps left for
+#pragma unroll
+        for (int v = 2 * (kColEnd - 2); v < 16; ++v) {
+          sacc_n[v] += cv[v];
+          mxn = fmaxf(mxn, sacc_n[v]);
+        }
+      }
       if constexpr (sizeof(T) == 4) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -756,10 +790,9 @@ void ipa_attn_kernel(FwdArgs a) {
   const int zm = (CPR & 7) == 0 ? 7 : (CPR & 3) == 0 ? 3 : (CPR & 1) == 0 ? 1 : 0;
   float* const fr = reinterpret_cast<float*>(xs + 32 * RB);
   {
-    const __amdgpu_buffer_rsrc_t rZ =
-        make_rsrc(static_cast<const unsigned char*>(a.z1) + (size_t)b * L * RB, (uint32_t)L * RB);
-    const __amdgpu_buffer_rsrc_t rR = make_rsrc(a.rot + (size_t)b * L * 9, (uint32_t)L * 36);
-    const __amdgpu_buffer_rsrc_t rT = make_rsrc(a.trans + (size_t)b * L * 3, (uint32_t)L * 12);
+    const __amdgpu_buffer_rsrc_t rZ = rsrc_or_empty(a.z1, (size_t)b * L * RB, (uint32_t)L * RB);
+    const __amdgpu_buffer_rsrc_t rR = rsrc_or_empty(a.rot, (size_t)b * L * 36, (uint32_t)L * 36);
+    const __amdgpu_buffer_rsrc_t rT = rsrc_or_empty(a.trans, (size_t)b * L * 12, (uint32_t)L * 12);
     constexpr int NZL = (SM::kPW * ES / 16 + 1) / 2;   // loads for the widest z1 row
     u32x4 zv[NZL];
     int zo[NZL];
@@ -856,10 +889,12 @@ void ipa_attn_kernel(FwdArgs a) {
   // staged value is read first (rows clamped into the block), then the
   // stores go out back to back; the store resource ends after row nrow - 1,
   // so rows past L are dropped by its range check.
-  auto store_rows = [&](auto sp_c, const float* src, int cols, float* dst, int pitch) {
+  // (an absent output gets an empty resource: nothing is written)
+  auto store_rows = [&](auto sp_c, const float* src, int cols, float* out, size_t first, int pitch) {
     constexpr int SP = decltype(sp_c)::value;
     constexpr int NIT = 32 * (SP - 1) / 64;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, nrow > 0 ? (uint32_t)(((nrow - 1) * pitch + cols) * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t rs =
+        rsrc_or_empty(out, first * 4, nrow > 0 ? (uint32_t)(((nrow - 1) * pitch + cols) * 4) : 0u);
     float v[NIT];
     int off[NIT];
     int r = lane / cols, c = lane - r * cols;
@@ -876,9 +911,9 @@ void ipa_attn_kernel(FwdArgs a) {
     for (int it = 0; it < NIT; ++it) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[it]), rs, off[it], 0, 0);
   };
   const size_t row0 = ((size_t)b * L + qw) * H + h;   // (b, qw, h) output row
-  store_rows(std::integral_constant<int, PS>{}, so, C, a.out_s + row0 * C, H * C);
-  store_rows(std::integral_constant<int, PP>{}, sp, 3 * Pv, a.out_pts + row0 * 3 * Pv, H * 3 * Pv);
-  store_rows(std::integral_constant<int, PN>{}, sn, Pv, a.out_pts_norm + row0 * Pv, H * Pv);
+  store_rows(std::integral_constant<int, PS>{}, so, C, a.out_s, row0 * C, H * C);
+  store_rows(std::integral_constant<int, PP>{}, sp, 3 * Pv, a.out_pts, row0 * 3 * Pv, H * 3 * Pv);
+  store_rows(std::integral_constant<int, PN>{}, sn, Pv, a.out_pts_norm, row0 * Pv, H * Pv);
 
   // ---- pair channels: o_pair[c] = sum_r z1[r Cz + c] O[r Cz + c] / l ----
   // Lane (n, g) holds O at features 32 fb + 8 k + 4 g + e of query n: 4-wide
@@ -897,7 +932,7 @@ void ipa_attn_kernel(FwdArgs a) {
     if constexpr (S * 32 <= SM::kCzMax) {
       constexpr int RMAX = (NFB - 2) / S;
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(a.out_pair + row0 * Cz, nrow > 0 ? (uint32_t)(((nrow - 1) * H * Cz + Cz) * 4) : 0u);
+          rsrc_or_empty(a.out_pair, row0 * Cz * 4, nrow > 0 ? (uint32_t)(((nrow - 1) * H * Cz + Cz) * 4) : 0u);
 #pragma unroll
       for (int m = 0; m < S; ++m) {
         unsigned char* const pb = xs + (m & 1) * 4096;
@@ -976,7 +1011,7 @@ void ipa_attn_kernel(FwdArgs a) {
       int nn = lane / Cz, c = lane - nn * Cz;
       for (int e = lane; e < 32 * Cz; e += 64) {
         const int ii = qw + nn;
-        if (ii < L) a.out_pair[(((size_t)b * L + ii) * H + h) * Cz + c] = pb[nn * SM::kPRow + c];
+        if (a.out_pair && ii < L) a.out_pair[(((size_t)b * L + ii) * H + h) * Cz + c] = pb[nn * SM::kPRow + c];
         nn += dq;
         c += dr;
         if (c >= Cz) { c -= Cz; ++nn; }

@@ -65,10 +65,18 @@ struct FwdArgs {
   float w_L, w_C;
   float* out_s; float* out_pts; float* out_pts_norm; float* out_pair;
   unsigned char* ws;
+  // Distance-attention configuration (both NULL for the IPA forward): per
+  // head, scalar weight rho_h replaces w_L / sqrt(C) and point weight
+  // rho_h s_h^2 replaces w_L gamma_h w_C / 2. In that configuration the
+  // points, rotations, pair factors, W_b and all outputs but out_s may be
+  // NULL: missing inputs read as zeros, missing outputs are not written.
+  const float* meet_rho; const float* meet_s;
 };
 
 // Kernel launchers (return the hipError_t of the launch).
 hipError_t launch_lift(const FwdArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_attn(const FwdArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_frames(int n, const float* atom_n, const float* atom_ca, const float* atom_c,
+                         float* rot, float* trans, hipStream_t s);
 
 }  // namespace ipa

@@ -86,6 +86,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Resource over `bytes` bytes `off` bytes into `p`, or an empty resource
+// (every load reads zero, every store is dropped) when `p` is NULL; no
+// offset is ever applied to a NULL pointer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_or_empty(const void* p, size_t off, uint32_t bytes) {
+  return p ? make_rsrc(static_cast<const unsigned char*>(p) + off, bytes) : make_rsrc(nullptr, 0u);
+}
+
 // Element-type policy of the lifted rows.
 template <typename T> struct Elt;
 template <> struct Elt<uint16_t> {
@@ -274,12 +281,19 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     // block's valid residues; every wave forms it for itself)
     float R[9], t[3];
     {
-      const __attribute__((address_space(1))) float* rp =
-          (const __attribute__((address_space(1))) float*)(a.rot + (rb + ic) * 9);
       const __attribute__((address_space(1))) float* tp =
           (const __attribute__((address_space(1))) float*)(a.trans + (rb + ic) * 3);
+      // no rotations (distance attention): every local point is zero, so
+      // the rotation never matters
+      if (a.rot) {
+        const __attribute__((address_space(1))) float* rp =
+            (const __attribute__((address_space(1))) float*)(a.rot + (rb + ic) * 9);
 #pragma unroll
-      for (int e = 0; e < 9; ++e) R[e] = rp[e];
+        for (int e = 0; e < 9; ++e) R[e] = rp[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 9; ++e) R[e] = 0.f;
+      }
 #pragma unroll
       for (int x = 0; x < 3; ++x) t[x] = tp[x];
     }
@@ -293,9 +307,9 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
 
     // this head's input rows of the residue, through buffer resources over
     // batch b (32-bit offsets; the range check never faults)
+    // (an absent input gets an empty range: its loads read zeros)
     auto in_rsrc = [&](const void* p, int per_row) {
-      return make_rsrc(static_cast<const unsigned char*>(p) + rb * H * per_row * ES,
-                       (uint32_t)((size_t)L * H * per_row * ES));
+      return rsrc_or_empty(p, rb * H * per_row * ES, (uint32_t)((size_t)L * H * per_row * ES));
     };
     // widest load that every row of this input keeps aligned
     auto width_of = [&](const void* p, int per_row) -> int {
@@ -308,8 +322,10 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     const int row = ic * H + h;   // (residue, head) row within the batch
 
     const size_t o = ((size_t)b * H + h) * Lp + i;  // row of the per-(b, h) arrays
-    const float alpha = a.w_L * rsqrtf((float)C) * kLog2e;
-    const float kap = a.w_L * a.gamma[h] * a.w_C * 0.5f * kLog2e;
+    // scalar and point weights (base 2): w_L / sqrt(C) and w_L gamma_h w_C / 2,
+    // or rho_h and rho_h s_h^2 for the distance attention
+    const float alpha = (a.meet_rho ? a.meet_rho[h] : a.w_L * rsqrtf((float)C)) * kLog2e;
+    const float kap = (a.meet_rho ? a.meet_rho[h] * a.meet_s[h] * a.meet_s[h] : a.w_L * a.gamma[h] * a.w_C * 0.5f) * kLog2e;
 
     uint32_t own[kHeadW * ES / 4];   // query wave: its packed head row
     float4 qrow_v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -464,8 +480,7 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     // z2 row segment u = 64 P .. 64 P + 63 of the residue (16-byte loads:
     // R Cz is a multiple of 8, so rows and panels are 16-byte aligned; a
     // segment past the end of the batch reads zeros)
-    const __amdgpu_buffer_rsrc_t rz =
-        make_rsrc(static_cast<const unsigned char*>(a.z2) + rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
+    const __amdgpu_buffer_rsrc_t rz = rsrc_or_empty(a.z2, rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
     // bf16 path: the z1 segment and the first head group's W_b weights for
     // the pair bias below, issued together with the z2 loads
     constexpr int NZ1 = sizeof(T) == 2 ? 8 : 1;
@@ -477,12 +492,11 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int hc = h0 + 4 * c < H ? h0 + 4 * c : H - 1;
-        wl[c] = wsc * a.w_b[(size_t)cu * H + hc];
+        wl[c] = a.w_b ? wsc * a.w_b[(size_t)cu * H + hc] : 0.f;
       }
     };
     if constexpr (sizeof(T) == 2) {
-      const __amdgpu_buffer_rsrc_t r1 =
-          make_rsrc(static_cast<const unsigned char*>(a.z1) + rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
+      const __amdgpu_buffer_rsrc_t r1 = rsrc_or_empty(a.z1, rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
 #pragma unroll
       for (int c = 0; c < 8; ++c) z1r[c] = __builtin_amdgcn_raw_buffer_load_b128(r1, (ic * RCz + 64 * P) * ES + 16 * c, 0, 0);
       weights(w, wl0);

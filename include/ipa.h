@@ -154,6 +154,54 @@ int32_t ipa_attend(const ipa_dims* dims, int32_t dtype,
                    void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Residue frames from backbone atoms.
+ * "Flash Invariant Point Attention", Figure 1: the C-alpha atom is the
+ * centre of a residue's frame, the vectors from C-alpha to N and to C span
+ * it, and Gram-Schmidt completes it. Here
+ *   e1 = (C - CA) / |C - CA|
+ *   e2 = unit component of (N - CA) orthogonal to e1
+ *   e3 = e1 x e2                      (right-handed)
+ *   rot_out = [e1 e2 e3] (the axes as columns: local -> global), trans_out = CA,
+ * the `rot` / `trans` convention of ipa_forward.
+ *   n, ca, c    [B,L,3]   float32 atom positions
+ *   rot_out     [B,L,3,3] float32
+ *   trans_out   [B,L,3]   float32
+ * Pointers must be non-NULL and 4-byte aligned; B, L >= 1 and B*L < 2^31.
+ * Residues whose C coincides with C-alpha, or whose N lies on the
+ * C-alpha -> C line, have no frame: their outputs are not finite. */
+int32_t ipa_frames_from_atoms(int32_t B, int32_t L, const float* n, const float* ca,
+                              const float* c, float* rot_out, float* trans_out,
+                              void* stream);
+
+/* Distance-penalised attention over one point per residue.
+ * MEET ("Scalable peptide design with memory-efficient equivariant
+ * transformers"), section 2.2, eq. 6-8: per head h,
+ *   S_ijh = rho_h * ( q_ih . k_jh - s_h^2 * |x_i - x_j|^2 )
+ *   a_ijh = softmax over allowed j,   out[b,i,h,:] = sum_j a v_jh.
+ * It runs on the IPA kernels as a configuration of ipa_forward's logit:
+ * identity frames at the points x, one zero local point per head, no pair
+ * term, scalar weight rho_h in place of w_L / sqrt(C) and point weight
+ * rho_h * s_h^2 in place of w_L * gamma_h * w_C / 2. Masks, padding and
+ * status codes behave as in ipa_forward.
+ *   dims      B, L, H, C (every dim >= 1, C <= 16, L <= 65536)
+ *   q, k, v   [B,L,H,C] dtype storage
+ *   x         [B,L,3]   float32 points in one global frame
+ *   rho, s    [H]       float32 per-head weights (finite)
+ *   mask      [B,L]     uint8, 1 = valid residue; NULL = all valid
+ *   out       [B,L,H,C] float32, every element overwritten
+ *   workspace ipa_meet_workspace_bytes(dims, dtype) bytes, 256-byte aligned.
+ * Tensor pointers must be 16-byte aligned. */
+typedef struct {
+  int32_t B, L, H, C;
+} ipa_meet_dims;
+size_t ipa_meet_workspace_bytes(const ipa_meet_dims* dims, int32_t dtype);
+int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype,
+                         const void* q, const void* k, const void* v,
+                         const float* x, const float* rho, const float* s,
+                         const uint8_t* mask, float* out,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* ipa_status_string(int32_t status);
 

@@ -29,8 +29,9 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["ipa_attend", "ipa_forward", "ipa_lift", "ipa_status_string", "ipa_version",
-                     "ipa_workspace_bytes"]
+    assert names == ["ipa_attend", "ipa_forward", "ipa_frames_from_atoms", "ipa_lift",
+                     "ipa_meet_forward", "ipa_meet_workspace_bytes", "ipa_status_string",
+                     "ipa_version", "ipa_workspace_bytes"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -115,3 +116,53 @@ def test_forward_rejects_before_launch(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         bd.load_library(tmp_path / "missing.so")
+
+
+def test_frames_reject_before_launch(lib):
+    f = lib.ipa_frames_from_atoms
+    good = [0x100000 + 4096 * i for i in range(5)]
+    assert f(0, 4, *good, None) == -2                              # IPA_ERR_DIMS
+    assert f(1, 0, *good, None) == -2
+    assert f(1 << 16, 1 << 15, *good, None) == -2                  # B*L >= 2^31
+    for idx in range(5):
+        bad = list(good)
+        bad[idx] = 0
+        assert f(1, 4, *bad, None) == -1                           # IPA_ERR_NULL
+        bad = list(good)
+        bad[idx] += 2
+        assert f(1, 4, *bad, None) == -5                           # IPA_ERR_ALIGN
+
+
+def _meet_call(lib, dims, dtype=bd.IPA_BF16, null_idx=None, misalign_idx=None, ws_bytes=1 << 40, ws_ptr=None):
+    """ipa_meet_forward with fake device pointers; every case fails validation."""
+    ptrs = [0x100000 + 4096 * i for i in range(7)]     # q, k, v, x, rho, s, out
+    if null_idx is not None:
+        ptrs[null_idx] = 0
+    if misalign_idx is not None:
+        ptrs[misalign_idx] += 4
+    ws = 0x40000000 if ws_ptr is None else ws_ptr
+    d = ctypes.byref(dims) if dims is not None else None
+    return lib.ipa_meet_forward(d, dtype, *ptrs[:6], 0, ptrs[6], ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_meet_rejects_before_launch(lib):
+    d = bd.IpaMeetDims(1, 512, 12, 16)
+    assert _meet_call(lib, None) == -1
+    assert _meet_call(lib, bd.IpaMeetDims(1, 0, 12, 16)) == -2
+    assert _meet_call(lib, d, dtype=5) == -3
+    for idx in range(7):
+        assert _meet_call(lib, d, null_idx=idx) == -1
+        assert _meet_call(lib, d, misalign_idx=idx) == -5
+    assert _meet_call(lib, d, ws_ptr=0x40000000 + 16) == -5
+    assert _meet_call(lib, bd.IpaMeetDims(1, 512, 12, 17)) == -6
+    need = bd.meet_workspace_bytes(1, 512, 12, 16, bd.IPA_BF16)
+    assert need > 0
+    assert _meet_call(lib, d, ws_bytes=need - 1) == -4
+
+
+def test_meet_workspace_linear_in_L(lib):
+    sizes = {L: bd.meet_workspace_bytes(1, L, 8, 16, bd.IPA_BF16) for L in (1024, 2048, 4096, 8192)}
+    per = (sizes[8192] - sizes[4096]) / 4096
+    for L, v in sizes.items():
+        assert abs(v - sizes[1024] - per * (L - 1024)) < 4096, (L, v)
+    assert bd.meet_workspace_bytes(1, 64, 4, 0, bd.IPA_F32) == 0

@@ -110,6 +110,15 @@ def test_bf16_pair_widths(device, Cz, R):
     _check(w, device, TOL_BF16, seed=Cz)
 
 
+@pytest.mark.parametrize("Cz,R", [(32, 1), (64, 1), (8, 1), (32, 2), (40, 1)])
+def test_bf16_narrowest_rows(device, Cz, R):
+    """R Cz <= 64: lifted rows of 128 columns, the narrowest the kernel
+    runs (its value phase has the fewest product steps to schedule its
+    side work into)."""
+    w = WORKLOADS["single_chain"].with_(L=200, H=2, Cz=Cz, R=R)
+    _check(w, device, TOL_BF16, seed=Cz + R)
+
+
 def test_fp32_pair_width_32(device):
     w = WORKLOADS["tiny_fp32"].with_(L=140, H=2, Cz=32, R=2)
     _check(w, device, TOL_F32, seed=32)
