@@ -172,6 +172,97 @@ def cpu_baseline(inp, gpu_out, budget_s: float):
     }, errs, done
 
 
+def bench_meet(dev, steps: int, warmup: int, cpu: bool) -> dict:
+    """Distance-penalised attention (ipa_meet_forward) on the 2048-residue
+    chain: the forward timed like the IPA step, the fp64 oracle beside it on
+    the whole workload (it is small enough), and parity on that output."""
+    import numpy as np
+    import torch
+    from geometric_invariant_attention_amd import MeetForward
+    from workloads import MEET_WORKLOADS, make_meet_inputs
+    w = MEET_WORKLOADS["meet_chain_2048"]
+    inp = make_meet_inputs(w)
+    d = w.dims()
+    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(torch.bfloat16).to(dev) for k in ("q", "k", "v")}
+    for k in ("x", "rho", "s"):
+        t[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.float32)).to(dev)
+    plan = MeetForward(**d, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    raw = plan.bind(t["q"], t["k"], t["v"], t["x"], t["rho"], t["s"], stream=stream)
+    for _ in range(warmup):
+        plan.forward_raw(raw)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.forward_raw(raw)
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    pairs = d["B"] * d["L"] * d["L"]
+    # algorithmic count of the pages' lifted form (MEET eq. 7-8): the query
+    # and key rows carry C + 9 columns, the value rows C
+    flops = 2.0 * d["H"] * (2 * d["C"] + 9) * pairs
+    out = {"workload": w.name, "config": {**d, "storage": "bf16"}, "ms_per_call": ms,
+           "pairs_per_s": pairs / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
+           "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS,
+           "executed_note": "runs on the IPA kernels with 128-wide lifted rows"}
+    if cpu:
+        from oracle import meet_attention
+        c0, w0 = time.process_time(), time.perf_counter()
+        ref = meet_attention(inp["q"], inp["k"], inp["v"], inp["x"], inp["rho"], inp["s"])
+        wall = time.perf_counter() - w0
+        cores = max(1, round((time.process_time() - c0) / max(wall, 1e-9)))
+        gpu = plan.out.cpu().numpy()
+        out["cpu_baseline"] = {"value": pairs / wall, "unit": "pairs/s", "cores": cores, "kind": "oracle",
+                               "sample": f"the whole {w.name} workload ({d['L']} x {d['L']} pairs, {d['H']} heads)"}
+        out["parity_max_abs_err"] = float(np.abs(gpu.astype(np.float64) - ref).max())
+    return out
+
+
+def bench_frames(dev, steps: int, warmup: int, cpu: bool) -> dict:
+    """Frames from backbone atoms (ipa_frames_from_atoms) over 16 chains of
+    16384 residues: bytes moved per residue (36 read, 48 written) against
+    the HBM peak, and the fp64 oracle on the same atoms."""
+    import numpy as np
+    import torch
+    from geometric_invariant_attention_amd import load_library
+    from workloads import make_backbone
+    import ctypes
+    B, L = 16, 16384
+    bb = make_backbone(B, L, seed=0)
+    t = {k: torch.from_numpy(v).to(dev) for k, v in bb.items()}
+    rot = torch.empty(B, L, 3, 3, dtype=torch.float32, device=dev)
+    trans = torch.empty(B, L, 3, dtype=torch.float32, device=dev)
+    lib = load_library()
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (B, L, t["n"].data_ptr(), t["ca"].data_ptr(), t["c"].data_ptr(), rot.data_ptr(), trans.data_ptr(), sp)
+    for _ in range(warmup):
+        lib.ipa_frames_from_atoms(*args)
+    torch.cuda.synchronize(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        rc = lib.ipa_frames_from_atoms(*args)
+    ev[1].record()
+    torch.cuda.synchronize(dev)
+    assert rc == 0
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    nbytes = B * L * (36 + 48)
+    out = {"workload": f"backbone B={B} L={L}", "ms_per_call": ms, "residues_per_s": B * L / (ms * 1e-3),
+           "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "algorithmic_bytes": nbytes}}
+    if cpu:
+        from oracle import frames_from_atoms
+        c0, w0 = time.process_time(), time.perf_counter()
+        r_ref, _ = frames_from_atoms(bb["n"], bb["ca"], bb["c"])
+        wall = time.perf_counter() - w0
+        cores = max(1, round((time.process_time() - c0) / max(wall, 1e-9)))
+        out["cpu_baseline"] = {"value": B * L / wall, "unit": "residues/s", "cores": cores, "kind": "oracle",
+                               "sample": f"the whole workload ({B * L} residues)"}
+        out["parity_max_abs_err"] = float(np.abs(rot.cpu().numpy().astype(np.float64) - r_ref).max())
+    return out
+
+
 def memory_sweep(dev, Ls, H=12, Cz=128):
     """Peak device memory (inputs + outputs + workspace) of one forward."""
     import torch
@@ -301,6 +392,13 @@ def main(argv=None) -> int:
               file=sys.stderr, flush=True)
     else:
         result["cpu_baseline"] = None
+
+    result["meet"] = bench_meet(dev, args.steps, args.warmup, args.cpu_budget > 0)
+    print(f"[bench] distance attention: {result['meet']['ms_per_call'] * 1e3:.1f} us/call, "
+          f"{result['meet']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    result["frames"] = bench_frames(dev, args.steps, 20, args.cpu_budget > 0)
+    print(f"[bench] frames: {result['frames']['ms_per_call'] * 1e3:.1f} us/call, "
+          f"{result['frames']['roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
 
     if not args.no_mem_sweep:
         result["memory_vs_L"] = memory_sweep(dev, [512, 1024, 2048, 4096, 8192, 16384])
