@@ -568,14 +568,18 @@ void ipa_attn_kernel(FwdArgs a) {
       dma16(P == 0 ? rKh : rKz, voK, (P == 0 ? ko.h : ko.z) + c, Kd + P * SM::kKPanel + kk * 1024);
     }
   };
-  // The copy ops of one iteration, spread evenly over its NKS + NB product
-  // steps (op k at step k (NKS + NB) / NDMA): the address unit then drains
-  // them alongside the products instead of holding the wave up in a burst.
-  constexpr int NSTEP = NKS + NFB * NST;
+  // The copy ops of one iteration, spread evenly over its first NKS +
+  // 0.7 NB product steps (op k at step k NSPAN / NDMA): the address unit
+  // drains them alongside the products instead of holding the wave up in a
+  // burst, and the last one still has about a third of the value phase to
+  // land before the iteration's wait. (Measured at L = 2048: spreading over
+  // the whole iteration left ~200 cycles of that wait per tile, and packing
+  // them into the score phase cost as much in issue slots.)
+  constexpr int NSPAN = NKS + 7 * NFB * NST / 10;
   auto dma_at = [&](int step, TileOff tv, unsigned char* Vd, TileOff tk, unsigned char* Kd) {
 #pragma unroll
     for (int k = 0; k < NDMA; ++k)
-      if (k * NSTEP / NDMA == step) dma_op(k, tv, Vd, tk, Kd);
+      if (k * NSPAN / NDMA == step) dma_op(k, tv, Vd, tk, Kd);
   };
   auto copy_v = [&](int t, unsigned char* Vd) {
     const int J = t >> 1, half = t & 1;
