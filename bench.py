@@ -122,18 +122,23 @@ def run_timed(w, steps: int, warmup: int, dev):
         plan.attend_raw(raw)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    # per-kernel durations: the same `steps` forwards again, each kernel
-    # bracketed by HIP events on its own stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for s in range(steps):
-        ev[s][0].record(stream)
+    # per-kernel durations: each kernel launched `steps` times back to back
+    # between two HIP events on its own stream (both kernels only read what
+    # the lift wrote from the inputs, so repeating either is the same work);
+    # an event record between two dependent kernels would add the dispatch
+    # latency of the second to its measured duration
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(stream)
+    for _ in range(steps):
         plan.lift_raw(raw)
-        ev[s][1].record(stream)
+    ev[1].record(stream)
+    ev[2].record(stream)
+    for _ in range(steps):
         plan.attend_raw(raw)
-        ev[s][2].record(stream)
+    ev[3].record(stream)
     torch.cuda.synchronize(dev)
-    lift_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    lift_ms = ev[0].elapsed_time(ev[1]) / steps
+    attn_ms = ev[2].elapsed_time(ev[3]) / steps
     out = {k: v.detach().cpu().numpy() for k, v in plan.out.items()}
     return inp, wall, lift_ms, attn_ms, out
 
