@@ -18,12 +18,19 @@ Pinning status of each function (see the tests under ``tests/``):
                   MEET lifting identity through library SDPA, rigid
                   invariance, two-residue closed form, mask rules, agreement
                   with ipa_forward configured to the same logit.
+  dirdist_attention  pinned: scalar-loop brute force, textbook attention
+                  (library SDPA) when the distance term vanishes, closed forms
+                  for the unsquared distance and the value transport, rigid
+                  invariance, permutation equivariance, mask and readout rules.
+  dirdist_bruteforce pinned by the same closed forms on tiny inputs.
 """
 
 from .ipa_oracle import ipa_forward, ipa_logits, to_global
-from .bruteforce import ipa_bruteforce
+from .bruteforce import ipa_bruteforce, dirdist_bruteforce
 from .lifted import ipa_lifted, block_centres
 from .geometry import frames_from_atoms, meet_attention
+from .dirdist import dirdist_attention
 
 __all__ = ["ipa_forward", "ipa_logits", "to_global", "ipa_bruteforce",
-           "ipa_lifted", "block_centres", "frames_from_atoms", "meet_attention"]
+           "ipa_lifted", "block_centres", "frames_from_atoms", "meet_attention",
+           "dirdist_attention", "dirdist_bruteforce"]

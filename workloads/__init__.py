@@ -312,3 +312,109 @@ def make_meet_inputs(w: MeetWorkload, seed: int | None = None) -> dict:
                mask=mask, lengths=lengths.astype(np.int64), dtype=w.dtype, dims=w.dims(),
                workload=w.name, has_mask=w.ragged is not None)
     return out
+
+
+# ----------------------------------------------------------------------------
+# direction-and-distance attention
+# ----------------------------------------------------------------------------
+@dataclass(frozen=True)
+class DirDistWorkload:
+    name: str
+    B: int
+    N: int
+    H: int
+    M: int = 8                   # value vectors per head
+    Cout: int = 384
+    step: float = 3.8
+    ragged: tuple | None = None
+    pair_mask: str | None = None  # None, "full" [B,H,N,N], "per_head" [1,H,N,N], "shared" [N,N]
+    bias: bool = True
+    seed: int = 0
+
+    def dims(self) -> dict:
+        return dict(B=self.B, N=self.N, H=self.H, M=self.M, Cout=self.Cout)
+
+    def with_(self, **kw) -> "DirDistWorkload":
+        d = asdict(self)
+        d.update(kw)
+        return DirDistWorkload(**d)
+
+
+DIRDIST_WORKLOADS = {
+    "dd_tiny_fp32": DirDistWorkload("dd_tiny_fp32", B=2, N=37, H=3, M=2, Cout=5,
+                                    ragged=(20, 37), pair_mask="full"),
+    "dd_chain_512": DirDistWorkload("dd_chain_512", B=1, N=512, H=12),
+    "dd_chain_2048": DirDistWorkload("dd_chain_2048", B=1, N=2048, H=12),
+    "dd_ragged": DirDistWorkload("dd_ragged", B=8, N=128, H=8, M=4, Cout=64,
+                                 ragged=(40, 128), pair_mask="per_head"),
+}
+
+
+def make_dirdist_inputs(w: DirDistWorkload, seed: int | None = None) -> dict:
+    """Draw one seeded input set for a direction-and-distance workload.
+
+    Draw order: quaternions, chain steps, q_direction, k_direction, q_point,
+    k_point, values, direction_scale, distance_scale, output_weight,
+    output_bias, lengths, pair mask, padding garbage. Frames follow the IPA
+    recipe (Haar rotations, centred chain of fixed step); local directions,
+    points and values ~ N(0, 1); the two per-head scales are raw N(0, 1)
+    logits (softplus is part of the method); output_weight ~
+    N(0, 1) / sqrt(3 H M), output_bias ~ N(0, 1); a pair mask keeps each edge
+    with probability 0.9. All arrays float32; masks uint8.
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    B, N, H, M, Cout = w.B, w.N, w.H, w.M, w.Cout
+    quat = rng.standard_normal((B, N, 4))
+    steps = rng.standard_normal((B, N, 3))
+    qdir = rng.standard_normal((B, N, H, 3))
+    kdir = rng.standard_normal((B, N, H, 3))
+    qpt = rng.standard_normal((B, N, H, 3))
+    kpt = rng.standard_normal((B, N, H, 3))
+    val = rng.standard_normal((B, N, H, M, 3))
+    dsc = rng.standard_normal(H)
+    ssc = rng.standard_normal(H)
+    W = rng.standard_normal((H * M * 3, Cout)) / math.sqrt(3 * H * M)
+    bias = rng.standard_normal(Cout)
+    if w.ragged is not None:
+        lo, hi = w.ragged
+        lengths = rng.integers(lo, hi + 1, size=B)
+    else:
+        lengths = np.full(B, N, dtype=np.int64)
+    pm = None
+    if w.pair_mask == "full":
+        pm = (rng.random((B, H, N, N)) < 0.9).astype(np.uint8)
+    elif w.pair_mask == "per_head":
+        pm = (rng.random((1, H, N, N)) < 0.9).astype(np.uint8)
+    elif w.pair_mask == "shared":
+        pm = (rng.random((N, N)) < 0.9).astype(np.uint8)
+    rot = _quat_to_rot(quat)
+    trans = np.zeros((B, N, 3))
+    fmask = np.zeros((B, N), dtype=np.uint8)
+    for b in range(B):
+        n = int(lengths[b])
+        fmask[b, :n] = 1
+        g = steps[b, :n] / np.linalg.norm(steps[b, :n], axis=-1, keepdims=True)
+        x = np.zeros((n, 3))
+        if n > 1:
+            x[1:] = np.cumsum(w.step * g[1:], axis=0)
+        trans[b, :n] = x - x.mean(axis=0)
+    if w.ragged is not None:
+        pad = fmask == 0
+        npad = int(pad.sum())
+        if npad:
+            qdir[pad] = 10.0 * rng.standard_normal((npad, H, 3))
+            kdir[pad] = 10.0 * rng.standard_normal((npad, H, 3))
+            qpt[pad] = 10.0 * rng.standard_normal((npad, H, 3))
+            kpt[pad] = 10.0 * rng.standard_normal((npad, H, 3))
+            val[pad] = 10.0 * rng.standard_normal((npad, H, M, 3))
+            rot[pad] = rng.standard_normal((npad, 3, 3))
+            trans[pad] = rng.uniform(-1e3, 1e3, size=(npad, 3))
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return dict(
+        rot=f32(rot), trans=f32(trans), q_direction=f32(qdir), k_direction=f32(kdir),
+        q_point=f32(qpt), k_point=f32(kpt), values=f32(val),
+        direction_scale=f32(dsc), distance_scale=f32(ssc),
+        output_weight=f32(W), output_bias=f32(bias) if w.bias else None,
+        frame_mask=fmask, pair_mask=pm, lengths=lengths.astype(np.int64),
+        dims=w.dims(), workload=w.name,
+    )
