@@ -35,6 +35,10 @@ class IpaMeetDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "L", "H", "C")]
 
 
+class IpaDirDistDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "N", "H", "M", "Cout")]
+
+
 class IPAError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -67,6 +71,10 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ipa_meet_workspace_bytes.restype = sz
     lib.ipa_meet_forward.argtypes = [ctypes.POINTER(IpaMeetDims), i32] + [vp] * 9 + [sz, vp]
     lib.ipa_meet_forward.restype = i32
+    lib.ipa_dirdist_workspace_bytes.argtypes = [ctypes.POINTER(IpaDirDistDims)]
+    lib.ipa_dirdist_workspace_bytes.restype = sz
+    lib.ipa_dirdist_forward.argtypes = [ctypes.POINTER(IpaDirDistDims)] + [vp] * 18 + [sz, vp]
+    lib.ipa_dirdist_forward.restype = i32
     lib.ipa_status_string.argtypes = [i32]
     lib.ipa_status_string.restype = ctypes.c_char_p
     lib.ipa_version.argtypes = []
@@ -306,3 +314,107 @@ def meet_attention(q, k, v, x, rho, s, mask=None) -> torch.Tensor:
     B, L, H, C = q.shape
     plan = MeetForward(B, L, H, C, dtype=q.dtype, device=q.device)
     return plan(q, k, v, x, rho, s, mask=mask)
+
+
+# ---------------------------------------------------------------------------
+# direction-and-distance attention (ipa_dirdist_forward)
+# ---------------------------------------------------------------------------
+def dirdist_workspace_bytes(B: int, N: int, H: int, M: int, Cout: int) -> int:
+    d = IpaDirDistDims(B, N, H, M, Cout)
+    return int(load_library().ipa_dirdist_workspace_bytes(ctypes.byref(d)))
+
+
+class DirDistForward:
+    """Reusable plan of the direction-and-distance attention
+    (ipa_dirdist_forward): validated shapes, preallocated workspace and
+    outputs on one device. Inputs may be non-contiguous (contiguous copies
+    are passed on; the caller's tensors are never written)."""
+
+    def __init__(self, B, N, H, M, Cout, device=None, attention=False):
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.dims = IpaDirDistDims(B, N, H, M, Cout)
+        self.shape = dict(B=B, N=N, H=H, M=M, Cout=Cout)
+        self.lib = load_library()
+        self.ws_bytes = int(self.lib.ipa_dirdist_workspace_bytes(ctypes.byref(self.dims)))
+        if self.ws_bytes == 0:
+            raise IPAError(-6, f"unsupported dims {self.shape}")
+        dev = self.device
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.vectors = torch.empty(B, N, H, M, 3, dtype=torch.float32, device=dev)
+        self.output = torch.empty(B, N, Cout, dtype=torch.float32, device=dev)
+        self.attention = torch.empty(B, H, N, N, dtype=torch.float32, device=dev) if attention else None
+
+    def bind(self, rot, trans, q_direction, k_direction, q_point, k_point, values,
+             direction_scale, distance_scale, output_weight, output_bias=None,
+             frame_mask=None, pair_mask=None, stream=None) -> tuple:
+        B, N, H, M, Cout = (self.shape[n] for n in ("B", "N", "H", "M", "Cout"))
+        dev, f32 = self.device, torch.float32
+        expect = {"rot": (B, N, 3, 3), "trans": (B, N, 3), "q_direction": (B, N, H, 3),
+                  "k_direction": (B, N, H, 3), "q_point": (B, N, H, 3), "k_point": (B, N, H, 3),
+                  "values": (B, N, H, M, 3), "direction_scale": (H,), "distance_scale": (H,),
+                  "output_weight": (3 * H * M, Cout)}
+        args = dict(rot=rot, trans=trans, q_direction=q_direction, k_direction=k_direction,
+                    q_point=q_point, k_point=k_point, values=values,
+                    direction_scale=direction_scale, distance_scale=distance_scale,
+                    output_weight=output_weight)
+        if output_bias is not None:
+            expect["output_bias"] = (Cout,)
+            args["output_bias"] = output_bias
+        for name, shp in expect.items():
+            t = args[name]
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+            args[name] = _prep(t, f32, dev, name)
+        if frame_mask is None:
+            raise ValueError("frame_mask [B,N] is required")
+        if tuple(frame_mask.shape) != (B, N) or frame_mask.device != dev:
+            raise ValueError(f"frame_mask must be [B,N] = {(B, N)} on {dev}")
+        fm = frame_mask.to(torch.uint8).contiguous()
+        pm, strides = None, None
+        if pair_mask is not None:
+            if pair_mask.device != dev:
+                raise ValueError(f"pair_mask is on {pair_mask.device}, expected {dev}")
+            pm = pair_mask if pair_mask.dtype == torch.uint8 else pair_mask.to(torch.uint8)
+            pm = pm.expand(B, H, N, N)               # broadcast dims get stride 0
+            strides = (ctypes.c_int64 * 4)(*pm.stride())
+            pm_ptr = pm.data_ptr()
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        self.bound = (args, fm, pm, strides)
+        return (ctypes.byref(self.dims),
+                *(args[n].data_ptr() for n in ("rot", "trans", "q_direction", "k_direction",
+                                               "q_point", "k_point", "values", "direction_scale",
+                                               "distance_scale", "output_weight")),
+                _dev_ptr(args.get("output_bias")), fm.data_ptr(),
+                pm_ptr if pm is not None else 0,
+                ctypes.cast(strides, ctypes.c_void_p) if strides is not None else None,
+                self.vectors.data_ptr(), self.output.data_ptr(), _dev_ptr(self.attention),
+                self.workspace.data_ptr(), ctypes.c_size_t(self.ws_bytes),
+                ctypes.c_void_p(stream.cuda_stream))
+
+    def forward_raw(self, raw: tuple) -> dict:
+        rc = self.lib.ipa_dirdist_forward(*raw)
+        if rc != 0:
+            raise IPAError(rc, status_string(rc))
+        out = {"vectors": self.vectors, "output": self.output}
+        if self.attention is not None:
+            out["attention"] = self.attention
+        return out
+
+    def __call__(self, *args, **kw) -> dict:
+        return self.forward_raw(self.bind(*args, **kw))
+
+
+def geometric_reasoning_attention(rot, trans, q_direction, k_direction, q_point, k_point, values,
+                                  direction_scale, distance_scale, output_weight, output_bias=None,
+                                  frame_mask=None, pair_mask=None, attention=True) -> dict:
+    """Direction-and-distance attention on the device of ``values``.
+    Returns freshly allocated float32 tensors: "vectors" [B,N,H,M,3],
+    "output" [B,N,Cout] and, if ``attention``, "attention" [B,H,N,N]."""
+    B, N, H, M, _ = values.shape
+    Cout = output_weight.shape[1]
+    plan = DirDistForward(B, N, H, M, Cout, device=values.device, attention=attention)
+    return plan(rot, trans, q_direction, k_direction, q_point, k_point, values, direction_scale,
+                distance_scale, output_weight, output_bias, frame_mask, pair_mask)

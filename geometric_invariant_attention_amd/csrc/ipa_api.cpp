@@ -10,7 +10,7 @@
 
 namespace ipa {
 
-static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool make_layout(const int32_t d[8], int esize, Layout* o) {
   const int64_t B = d[0], L = d[1], H = d[2], C = d[3], Pqk = d[4], Pv = d[5], R = d[6], Cz = d[7];
@@ -202,6 +202,97 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype, const void* q
   return IPA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct DDLayout {
+  size_t off_q, off_k, off_part, off_stats, total;
+  int Np, KW, PW, splits;
+};
+
+bool dd_layout(const ipa_dirdist_dims* d, DDLayout* o) {
+  if (!d) return false;
+  const int64_t B = d->B, N = d->N, H = d->H, M = d->M, Cout = d->Cout;
+  if (B < 1 || N < 1 || H < 1 || M < 1 || Cout < 1) return false;
+  if (M > ipa::kDDMaxM || N > (1 << 24) || H > 65535 || Cout > 65536) return false;
+  if (B * N * H >= (int64_t(1) << 31) || B * N * Cout >= (int64_t(1) << 31) ||
+      B * N * 3 * H * M >= (int64_t(1) << 31) || B * H > 65535)
+    return false;
+  o->Np = ipa::dd_padded_keys((int)N);
+  o->KW = ipa::dd_key_width((int)M);
+  o->PW = ipa::dd_part_width((int)M);
+  o->splits = ipa::dd_splits((int)B, (int)N, (int)H);
+  if (B * o->splits > 65535) return false;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = ipa::align256(off + bytes); return at; };
+  o->off_q = take((size_t)B * H * o->Np * 8 * 4);
+  o->off_k = take((size_t)B * H * o->Np * o->KW * 4);
+  o->off_part = take((size_t)o->splits * B * N * H * o->PW * 4);
+  o->off_stats = take((size_t)B * H * N * 8);
+  o->total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ipa_dirdist_workspace_bytes(const ipa_dirdist_dims* dims) {
+  DDLayout ly;
+  return dd_layout(dims, &ly) ? ly.total : 0;
+}
+
+int32_t ipa_dirdist_forward(const ipa_dirdist_dims* dims, const float* rot, const float* trans,
+                            const float* q_direction, const float* k_direction,
+                            const float* q_point, const float* k_point, const float* values,
+                            const float* direction_scale, const float* distance_scale,
+                            const float* output_weight, const float* output_bias,
+                            const uint8_t* frame_mask, const uint8_t* pair_mask,
+                            const int64_t* pair_mask_strides, float* vectors, float* output,
+                            float* attention, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!dims) return IPA_ERR_NULL;
+  if (dims->B < 1 || dims->N < 1 || dims->H < 1 || dims->M < 1 || dims->Cout < 1) return IPA_ERR_DIMS;
+  const float* fin[] = {rot, trans, q_direction, k_direction, q_point, k_point, values,
+                        direction_scale, distance_scale, output_weight};
+  for (const float* p : fin)
+    if (!p) return IPA_ERR_NULL;
+  if (!frame_mask || !vectors || !output || !workspace) return IPA_ERR_NULL;
+  if (pair_mask && !pair_mask_strides) return IPA_ERR_NULL;
+  const void* al[] = {rot, trans, q_direction, k_direction, q_point, k_point, values,
+                      direction_scale, distance_scale, output_weight, output_bias, vectors,
+                      output, attention};
+  for (const void* p : al)
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return IPA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return IPA_ERR_ALIGN;
+  DDLayout ly;
+  if (!dd_layout(dims, &ly)) return IPA_ERR_UNSUPPORTED;
+  if (workspace_bytes < ly.total) return IPA_ERR_WORKSPACE;
+  ipa::DDArgs a{};
+  if (pair_mask) {
+    for (int e = 0; e < 4; ++e)
+      if (pair_mask_strides[e] < 0) return IPA_ERR_ARG;
+    a.pm_sb = pair_mask_strides[0]; a.pm_sh = pair_mask_strides[1];
+    a.pm_si = pair_mask_strides[2]; a.pm_sj = pair_mask_strides[3];
+  }
+  a.B = dims->B; a.N = dims->N; a.H = dims->H; a.M = dims->M; a.Cout = dims->Cout;
+  a.Np = ly.Np; a.KW = ly.KW; a.PW = ly.PW; a.splits = ly.splits;
+  a.rot = rot; a.trans = trans; a.q_direction = q_direction; a.k_direction = k_direction;
+  a.q_point = q_point; a.k_point = k_point; a.values = values;
+  a.direction_scale = direction_scale; a.distance_scale = distance_scale;
+  a.w_out = output_weight; a.b_out = output_bias;
+  a.frame_mask = frame_mask; a.pair_mask = pair_mask;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.qbuf = reinterpret_cast<float*>(ws + ly.off_q);
+  a.kbuf = reinterpret_cast<float*>(ws + ly.off_k);
+  a.part = reinterpret_cast<float*>(ws + ly.off_part);
+  a.stats = reinterpret_cast<float*>(ws + ly.off_stats);
+  a.vectors = vectors; a.output = output; a.attention = attention;
+  if (ipa::launch_dirdist(a, static_cast<hipStream_t>(stream)) != hipSuccess) return IPA_ERR_HIP;
+  return IPA_OK;
+}
+
 const char* ipa_status_string(int32_t status) {
   switch (status) {
     case IPA_OK: return "ok";
@@ -212,7 +303,7 @@ const char* ipa_status_string(int32_t status) {
     case IPA_ERR_ALIGN: return "a pointer is not 16-byte aligned (workspace: 256-byte)";
     case IPA_ERR_UNSUPPORTED: return "dims outside the supported envelope";
     case IPA_ERR_HIP: return "a HIP kernel launch failed";
-    case IPA_ERR_ARG: return "w_L and w_C must be finite and >= 0";
+    case IPA_ERR_ARG: return "a scalar argument is out of range (w_L, w_C finite and >= 0; strides >= 0)";
     default: return "unknown status";
   }
 }

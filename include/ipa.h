@@ -202,6 +202,59 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Geometric direction-and-distance attention (ESM3-style).
+ * "Geometric direction-and-distance attention" (BioTorch), Required
+ * behavior. Per batch b, head h, query i and key j, with frames (R, t) that
+ * map local column vectors to the global frame:
+ *   qd_i = R_i q_direction_i,          kd_j = R_j k_direction_j
+ *   qp_i = R_i q_point_i + t_i,        kp_j = R_j k_point_j + t_j
+ *   a_ijh = ( softplus(direction_scale_h) (qd_i . kd_j)
+ *             - softplus(distance_scale_h) |qp_i - kp_j| ) / sqrt(3)
+ *   (the distance itself, not squared, no epsilon; softplus stable)
+ *   allowed_ijh = frame_mask_i and frame_mask_j and pair_mask[b,h,i,j]
+ *   A_ijh = softmax over allowed j; a query with no allowed key gets 0
+ *   vectors[b,i,h,m,:] = R_i^T sum_j A_ijh R_j values[b,j,h,m,:]  (no translation)
+ *   output[b,i,:] = flatten_{h,m,xyz}(vectors[b,i]) @ output_weight + output_bias,
+ *                   +0.0 when no head of query i has an allowed key.
+ * Arithmetic is float32 throughout; memory is linear in N unless the
+ * attention matrix is requested.
+ *   dims            B, N, H, M, Cout (every dim >= 1, M <= 8, N <= 2^24, Cout <= 65536,
+ *                   B*H <= 65535, B*N*H*3*M < 2^31, B*N*Cout < 2^31)
+ *   rot             [B,N,3,3] float32 (proper rotations on valid frames)
+ *   trans           [B,N,3]   float32
+ *   q_direction, k_direction, q_point, k_point  [B,N,H,3] float32
+ *   values          [B,N,H,M,3] float32
+ *   direction_scale, distance_scale  [H] float32 raw (pre-softplus) logits
+ *   output_weight   [3*H*M, Cout] float32; output_bias [Cout] or NULL
+ *   frame_mask      [B,N] uint8, 1 = valid frame (required)
+ *   pair_mask       uint8 or NULL (every edge allowed); element (b,h,i,j) is
+ *                   pair_mask[b*s0 + h*s1 + i*s2 + j*s3] with
+ *                   pair_mask_strides = {s0,s1,s2,s3} (>= 0; 0 broadcasts)
+ *   vectors         [B,N,H,M,3] float32, every element overwritten
+ *   output          [B,N,Cout]  float32, every element overwritten
+ *   attention       [B,H,N,N]   float32 or NULL (not computed); O(N^2) bytes
+ *   workspace       ipa_dirdist_workspace_bytes(dims) bytes, 256-byte aligned
+ * Float pointers must be 4-byte aligned. Invalid frames may hold any finite
+ * values; they are never read past the mask. Returns IPA_ERR_UNSUPPORTED
+ * for dims outside the envelope (ipa_dirdist_workspace_bytes then returns
+ * 0) and IPA_ERR_ARG for a negative stride. */
+typedef struct {
+  int32_t B, N, H, M, Cout;
+} ipa_dirdist_dims;
+size_t ipa_dirdist_workspace_bytes(const ipa_dirdist_dims* dims);
+int32_t ipa_dirdist_forward(const ipa_dirdist_dims* dims,
+                            const float* rot, const float* trans,
+                            const float* q_direction, const float* k_direction,
+                            const float* q_point, const float* k_point,
+                            const float* values,
+                            const float* direction_scale, const float* distance_scale,
+                            const float* output_weight, const float* output_bias,
+                            const uint8_t* frame_mask,
+                            const uint8_t* pair_mask, const int64_t* pair_mask_strides,
+                            float* vectors, float* output, float* attention,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* ipa_status_string(int32_t status);
 

@@ -46,8 +46,12 @@ def softplus(x):
 
 def dirdist_attention(rot, trans, q_direction, k_direction, q_point, k_point, values,
                       direction_scale, distance_scale, output_weight, output_bias=None,
-                      frame_mask=None, pair_mask=None):
+                      frame_mask=None, pair_mask=None, rows=None):
     """Direction-and-distance attention in fp64 with explicit [N, N] tensors.
+
+    ``rows`` (optional 1-D int array) restricts the queries to those residues
+    (each query row is independent); the outputs then have N' = len(rows)
+    along the query axis and every key.
 
     rot [B,N,3,3], trans [B,N,3]; q_direction, k_direction, q_point, k_point
     [B,N,H,3]; values [B,N,H,M,3]; direction_scale, distance_scale [H] (raw
@@ -78,12 +82,15 @@ def dirdist_attention(rot, trans, q_direction, k_direction, q_point, k_point, va
     kp = np.einsum("bnxy,bnhy->bnhx", rot, kpt) + trans[:, :, None, :]
     gv = np.einsum("bnxy,bnhmy->bnhmx", rot, val)
 
+    qi = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    qd, qp, rot_q = qd[:, qi], qp[:, qi], rot[:, qi]
+    pm = pm[:, :, qi]
     dots = np.einsum("bihx,bjhx->bhij", qd, kd)
     diff = qp.transpose(0, 2, 1, 3)[:, :, :, None, :] - kp.transpose(0, 2, 1, 3)[:, :, None, :, :]
     dist = np.sqrt(np.sum(diff * diff, axis=-1))                       # [B,H,N,N]
     logit = cd[None, :, None, None] * dots - cs[None, :, None, None] * dist
 
-    allowed = fm[:, None, :, None] & fm[:, None, None, :] & pm          # [B,H,N,N]
+    allowed = fm[:, None, qi, None] & fm[:, None, None, :] & pm         # [B,H,N',N]
     lg = np.where(allowed, logit, -np.inf)
     m = lg.max(axis=-1, keepdims=True)
     m = np.where(np.isfinite(m), m, 0.0)
@@ -92,8 +99,8 @@ def dirdist_attention(rot, trans, q_direction, k_direction, q_point, k_point, va
     att = np.divide(e, den, out=np.zeros_like(e), where=den > 0)
 
     agg = np.einsum("bhij,bjhmx->bihmx", att, gv)                       # global frame
-    vectors = np.einsum("biyx,bihmy->bihmx", rot, agg)                  # R_i^T
-    flat = vectors.reshape(B, N, H * M * 3)
+    vectors = np.einsum("biyx,bihmy->bihmx", rot_q, agg)                # R_i^T
+    flat = vectors.reshape(B, len(qi), H * M * 3)
     out = flat @ W
     if output_bias is not None:
         out = out + np.asarray(output_bias, F64)[None, None, :]

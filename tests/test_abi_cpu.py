@@ -29,7 +29,8 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["ipa_attend", "ipa_forward", "ipa_frames_from_atoms", "ipa_lift",
+    assert names == ["ipa_attend", "ipa_dirdist_forward", "ipa_dirdist_workspace_bytes",
+                     "ipa_forward", "ipa_frames_from_atoms", "ipa_lift",
                      "ipa_meet_forward", "ipa_meet_workspace_bytes", "ipa_status_string",
                      "ipa_version", "ipa_workspace_bytes"]
     for n in names:
@@ -166,3 +167,54 @@ def test_meet_workspace_linear_in_L(lib):
     for L, v in sizes.items():
         assert abs(v - sizes[1024] - per * (L - 1024)) < 4096, (L, v)
     assert bd.meet_workspace_bytes(1, 64, 4, 0, bd.IPA_F32) == 0
+
+
+def _dd_call(lib, dims, ptrs=None, ws_bytes=1 << 30, ws=0x100000, strides=None, pm=0):
+    """ipa_dirdist_forward with fake device pointers; every case fails
+    validation before a launch."""
+    d = bd.IpaDirDistDims(*dims) if dims is not None else None
+    if ptrs is None:
+        ptrs = [0x1000 * (n + 1) for n in range(15)]
+    st = (ctypes.c_int64 * 4)(*strides) if strides is not None else None
+    return lib.ipa_dirdist_forward(ctypes.byref(d) if d is not None else None,
+                                   *ptrs[:11], ptrs[11], pm,
+                                   ctypes.cast(st, ctypes.c_void_p) if st is not None else None,
+                                   ptrs[12], ptrs[13], ptrs[14], ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_dirdist_rejects_before_launch(lib):
+    good = (1, 64, 4, 4, 16)
+    assert _dd_call(lib, None) == -1
+    assert _dd_call(lib, (0, 64, 4, 4, 16)) == -2
+    assert _dd_call(lib, (1, 64, 4, 9, 16)) == -6            # M > 8
+    assert _dd_call(lib, (1, 64, 4, 4, 70000)) == -6         # Cout > 65536
+    for k in range(10):                                      # each required float input
+        p = [0x1000 * (n + 1) for n in range(15)]
+        p[k] = 0
+        assert _dd_call(lib, good, p) == -1, k
+    p = [0x1000 * (n + 1) for n in range(15)]
+    p[11] = 0                                                # frame mask
+    assert _dd_call(lib, good, p) == -1
+    p = [0x1000 * (n + 1) for n in range(15)]
+    p[12] = 0                                                # vectors
+    assert _dd_call(lib, good, p) == -1
+    p = [0x1000 * (n + 1) for n in range(15)]
+    p[3] += 2                                                # misaligned float
+    assert _dd_call(lib, good, p) == -5
+    assert _dd_call(lib, good, ws=0x100010) == -5            # workspace alignment
+    need = lib.ipa_dirdist_workspace_bytes(ctypes.byref(bd.IpaDirDistDims(*good)))
+    assert _dd_call(lib, good, ws_bytes=need - 1) == -4
+    assert _dd_call(lib, good, pm=0x9000) == -1              # mask without strides
+    assert _dd_call(lib, good, pm=0x9000, strides=(0, 0, 64, -1)) == -8
+
+
+def test_dirdist_workspace_linear_in_N(lib):
+    def ws(N):
+        return lib.ipa_dirdist_workspace_bytes(ctypes.byref(bd.IpaDirDistDims(1, N, 8, 4, 64)))
+    # linear once the chip is full without splitting the keys (N >= 8192 here)
+    a, b, c = ws(8192), ws(16384), ws(32768)
+    assert a > 0 and abs((c - b) - 2 * (b - a)) <= 4 * 256
+    # and bounded by a multiple of N below that (the key splits add partials)
+    per = [ws(n) / n for n in (64, 256, 1024, 2048, 4096, 8192)]
+    assert max(per) <= 3 * per[-1]
+    assert lib.ipa_dirdist_workspace_bytes(ctypes.byref(bd.IpaDirDistDims(1, 64, 4, 9, 16))) == 0

@@ -320,3 +320,13 @@ def test_planted_mistake_is_caught(monkeypatch, mistake):
 
 def test_unplanted_copy_passes(monkeypatch):
     assert _caught(monkeypatch) == 0
+
+
+def test_row_subset_matches_full():
+    inp = make_dirdist_inputs(TINY.with_(N=9, ragged=(6, 9), pair_mask="full"), seed=9)
+    full = run(inp)
+    rows = np.array([0, 3, 4, 8])
+    sub = dd.dirdist_attention(**{k: inp[k] for k in ARGS}, rows=rows)
+    assert np.array_equal(sub["vectors"], full["vectors"][:, rows])
+    assert np.array_equal(sub["attention"], full["attention"][:, :, rows])
+    assert np.abs(sub["output"] - full["output"][:, rows]).max() < 1e-14

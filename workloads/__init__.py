@@ -377,6 +377,8 @@ def make_dirdist_inputs(w: DirDistWorkload, seed: int | None = None) -> dict:
     bias = rng.standard_normal(Cout)
     if w.ragged is not None:
         lo, hi = w.ragged
+        if not 1 <= lo <= hi <= N:
+            raise ValueError(f"ragged lengths {w.ragged} must lie in [1, N={N}]")
         lengths = rng.integers(lo, hi + 1, size=B)
     else:
         lengths = np.full(B, N, dtype=np.int64)
