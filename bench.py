@@ -30,6 +30,9 @@ if ROOT not in sys.path:
 
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+# MI355X fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed
+# fp32) x 2.4 GHz. Code built without packed fp32 issues at most half of it.
+PEAK_FP32_VECTOR_TFLOPS = 157.3
 METRIC = "IPA fwd pairs/s & TFLOP/s (% bf16 MFMA peak) at L=2048; peak HBM GB vs L"
 
 
@@ -268,6 +271,85 @@ def bench_frames(dev, steps: int, warmup: int, cpu: bool) -> dict:
     return out
 
 
+def dirdist_flops_per_triple(M: int) -> int:
+    """Algorithmic fp32 operations per (query, key, head) of the
+    direction-and-distance attention, each operation counted once: direction
+    dot 5, point difference 3, squared norm 5, square root 1, the logit's
+    scale-and-subtract 2, running-max compare 1, subtract + exponential +
+    sum 3, weighted rotated values 2 * 3M."""
+    return 20 + 6 * M
+
+
+def bench_dirdist(dev, steps: int, warmup: int, cpu: bool) -> dict:
+    """Direction-and-distance attention (ipa_dirdist_forward) on the
+    2048-residue chain, vectors and readout (no attention matrix): the whole
+    forward timed like the IPA step, its ALU roofline, the fp64 oracle on a
+    bounded sample of query rows beside it, and parity on that sample."""
+    import numpy as np
+    import torch
+    from geometric_invariant_attention_amd import DirDistForward
+    from workloads import DIRDIST_WORKLOADS, make_dirdist_inputs
+    w = DIRDIST_WORKLOADS["dd_chain_2048"]
+    inp = make_dirdist_inputs(w)
+    d = w.dims()
+    names = ("rot", "trans", "q_direction", "k_direction", "q_point", "k_point", "values",
+             "direction_scale", "distance_scale", "output_weight", "output_bias")
+    t = {k: torch.from_numpy(inp[k]).to(dev) for k in names}
+    fm = torch.from_numpy(inp["frame_mask"]).to(dev)
+    plan = DirDistForward(**d, device=dev, attention=False)
+    stream = torch.cuda.current_stream(dev)
+    raw = plan.bind(*(t[k] for k in names), frame_mask=fm, stream=stream)
+    for _ in range(warmup):
+        plan.forward_raw(raw)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.forward_raw(raw)
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        plan.forward_raw(raw)
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    ev_ms = ev[0].elapsed_time(ev[1]) / steps
+    triples = d["B"] * d["N"] * d["N"] * d["H"]
+    flops = dirdist_flops_per_triple(d["M"]) * triples
+    ach = flops / (ev_ms * 1e-3) / 1e12
+    out = {"workload": w.name, "config": {**d, "storage": "fp32"}, "ms_per_call": ms,
+           "ms_per_call_events": ev_ms, "pairs_per_s": d["B"] * d["N"] * d["N"] / (ms * 1e-3),
+           "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK_FP32_VECTOR_TFLOPS,
+                        "unit": "TFLOP/s", "frac": ach / PEAK_FP32_VECTOR_TFLOPS,
+                        "flops_per_call": flops,
+                        "note": "whole forward (lift, loop, merge, readout) timed; flops of the loop"}}
+    if cpu:
+        from oracle import dirdist_attention
+        vec = plan.vectors.cpu().numpy()
+        outp = plan.output.cpu().numpy()
+        rng = np.random.default_rng(7)
+        order = rng.permutation(d["N"])
+        done, spent, spent_cpu, n, err = 0, 0.0, 0.0, 16, 0.0
+        scale = None
+        while done < d["N"] and spent < 10.0:
+            rows = np.sort(order[done:done + n])
+            c0, w0 = time.process_time(), time.perf_counter()
+            ref = dirdist_attention(**{k: inp[k] for k in names}, frame_mask=inp["frame_mask"], rows=rows)
+            spent += time.perf_counter() - w0
+            spent_cpu += time.process_time() - c0
+            scale = max(1.0, float(np.abs(ref["output"]).max()))
+            err = max(err, float(np.abs(vec[:, rows] - ref["vectors"]).max()),
+                      float(np.abs(outp[:, rows] - ref["output"]).max()) / scale)
+            done += len(rows)
+            n = min(2 * n, 256)
+        out["cpu_baseline"] = {"value": d["B"] * done * d["N"] / spent, "unit": "pairs/s",
+                               "cores": max(1, round(spent_cpu / max(spent, 1e-9))), "kind": "oracle",
+                               "sample": f"{done} of {d['N']} query rows x {d['N']} keys, all {d['H']} heads, "
+                                         f"fp64 numpy, {spent:.1f} s wall"}
+        out["parity_max_err"] = err
+    return out
+
+
 def memory_sweep(dev, Ls, H=12, Cz=128):
     """Peak device memory (inputs + outputs + workspace) of one forward."""
     import torch
@@ -402,6 +484,8 @@ def main(argv=None) -> int:
     print(f"[bench] distance attention: {result['meet']['ms_per_call'] * 1e3:.1f} us/call, "
           f"{result['meet']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     result["frames"] = bench_frames(dev, args.steps, 20, args.cpu_budget > 0)
+    print("[bench] direction-and-distance attention", file=sys.stderr, flush=True)
+    result["dirdist"] = bench_dirdist(dev, args.steps, args.warmup, args.cpu_budget > 0)
     print(f"[bench] frames: {result['frames']['ms_per_call'] * 1e3:.1f} us/call, "
           f"{result['frames']['roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
 

@@ -207,8 +207,8 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype, const void* q
 namespace {
 
 struct DDLayout {
-  size_t off_q, off_k, off_part, off_stats, total;
-  int Np, KW, PW, splits;
+  size_t off_q, off_klog, off_kval, off_part, off_stats, total;
+  int Np, PW, splits;
 };
 
 bool dd_layout(const ipa_dirdist_dims* d, DDLayout* o) {
@@ -217,17 +217,18 @@ bool dd_layout(const ipa_dirdist_dims* d, DDLayout* o) {
   if (B < 1 || N < 1 || H < 1 || M < 1 || Cout < 1) return false;
   if (M > ipa::kDDMaxM || N > (1 << 24) || H > 65535 || Cout > 65536) return false;
   if (B * N * H >= (int64_t(1) << 31) || B * N * Cout >= (int64_t(1) << 31) ||
-      B * N * 3 * H * M >= (int64_t(1) << 31) || B * H > 65535)
+      B * N * 3 * H * M >= (int64_t(1) << 31) || B * H > 65535 ||
+      3 * H * M * Cout >= (int64_t(1) << 29))
     return false;
   o->Np = ipa::dd_padded_keys((int)N);
-  o->KW = ipa::dd_key_width((int)M);
   o->PW = ipa::dd_part_width((int)M);
   o->splits = ipa::dd_splits((int)B, (int)N, (int)H);
   if (B * o->splits > 65535) return false;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = ipa::align256(off + bytes); return at; };
   o->off_q = take((size_t)B * H * o->Np * 8 * 4);
-  o->off_k = take((size_t)B * H * o->Np * o->KW * 4);
+  o->off_klog = take((size_t)B * H * o->Np * ipa::kKeyLog * 4);
+  o->off_kval = take((size_t)B * H * o->Np * ipa::kValW * 4);
   o->off_part = take((size_t)o->splits * B * N * H * o->PW * 4);
   o->off_stats = take((size_t)B * H * N * 8);
   o->total = off;
@@ -277,7 +278,7 @@ int32_t ipa_dirdist_forward(const ipa_dirdist_dims* dims, const float* rot, cons
     a.pm_si = pair_mask_strides[2]; a.pm_sj = pair_mask_strides[3];
   }
   a.B = dims->B; a.N = dims->N; a.H = dims->H; a.M = dims->M; a.Cout = dims->Cout;
-  a.Np = ly.Np; a.KW = ly.KW; a.PW = ly.PW; a.splits = ly.splits;
+  a.Np = ly.Np; a.PW = ly.PW; a.splits = ly.splits;
   a.rot = rot; a.trans = trans; a.q_direction = q_direction; a.k_direction = k_direction;
   a.q_point = q_point; a.k_point = k_point; a.values = values;
   a.direction_scale = direction_scale; a.distance_scale = distance_scale;
@@ -285,7 +286,8 @@ int32_t ipa_dirdist_forward(const ipa_dirdist_dims* dims, const float* rot, cons
   a.frame_mask = frame_mask; a.pair_mask = pair_mask;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.qbuf = reinterpret_cast<float*>(ws + ly.off_q);
-  a.kbuf = reinterpret_cast<float*>(ws + ly.off_k);
+  a.klog = reinterpret_cast<float*>(ws + ly.off_klog);
+  a.kval = reinterpret_cast<float*>(ws + ly.off_kval);
   a.part = reinterpret_cast<float*>(ws + ly.off_part);
   a.stats = reinterpret_cast<float*>(ws + ly.off_stats);
   a.vectors = vectors; a.output = output; a.attention = attention;

@@ -12,21 +12,26 @@
 //
 // The distance is not squared, so unlike the squared-distance logits of IPA
 // and MEET it cannot be folded into a dot product of lifted rows: every
-// (i, j, h) needs its own square root. The loop is plain fp32 vector
-// arithmetic, bound by the VALU issue rate, and laid out for it:
-//   * one query row per lane, 64 rows per wave, all of a wave's key data
-//     wave-uniform, so it is read with scalar loads into SGPRs and used as
-//     the scalar operand of each vector instruction (no LDS traffic, no
-//     VGPRs for keys);
-//   * per key and row: 3 FMA for the direction dot, 6 for the squared
-//     distance, one square root, one FMA to combine, the online-softmax
-//     exponential and 3M FMA for the rotated values;
+// (i, j, h) needs its own square root. The logits are fp32 vector work, the
+// weighted sum of the values a small dense product:
+//   * logits: one query row per lane, 64 rows per wave; the 8 floats of a
+//     key's logit data (global direction, validity bias, global point) are
+//     wave-uniform, read with scalar loads a chunk of 8 keys at a time and
+//     used as the scalar operand of each vector instruction; per key and
+//     row: 3 FMA for the direction dot, 6 for the squared distance, one
+//     square root, one FMA to combine, the online-softmax exponential;
+//   * P.V on fp32 matrix cores (v_mfma_f32_32x32x2f32): each product
+//     contracts two keys for 32 query rows and 32 value columns (3M used).
+//     One lane-half swap (v_permlane32_swap) turns the row-per-lane P of
+//     two keys into the A operands of both 32-row blocks; the B operand is
+//     the rotated values of the two keys, one column per lane, loaded with
+//     plain vector loads a chunk ahead;
 //   * exponentials in base 2 (log2 e folded into the scales), the running
 //     maximum raised lazily (only when a chunk's maximum exceeds it by more
 //     than 2^8), so most chunks skip the rescale.
 // Stages (one stream, all sizes linear in B * N):
 //   dd_lift    per (b, n, h): global directions (the query one pre-scaled),
-//              global points, rotated values, key validity -> qbuf, kbuf.
+//              global points, rotated values, key validity -> qbuf, klog, kval.
 //   dd_attn    per (b, h, 64 queries, key split): 4 waves take 4 key ranges,
 //              merge their (m, l, acc) through LDS, write one partial.
 //   dd_finish  per (b, i, h): merge the partials, divide, rotate back by
@@ -44,6 +49,9 @@ namespace {
 constexpr float kSqrt3Inv = 0.57735026918962576f;
 constexpr float kLazy = 8.f;   // a chunk maximum this far above the running one forces a rescale
 constexpr int kChunk = 8;      // keys per online-softmax chunk (the key axis is padded to it)
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float softplus_dev(float x) {
   return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
@@ -63,22 +71,25 @@ __device__ __forceinline__ void rotate(const float* R, float x, float y, float z
 // ---------------------------------------------------------------------------
 // dd_lift
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void dd_lift_kernel(DDArgs a) {
+__global__ __launch_bounds__(64) void dd_lift_kernel(DDArgs a) {
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int H = a.H, M = a.M, Np = a.Np, N = a.N, KW = a.KW;
+  const int H = a.H, M = a.M, Np = a.Np, N = a.N;
   const long long total = (long long)a.B * Np * H;
   if (t >= total) return;
   const int h = (int)(t % H);
   const int n = (int)((t / H) % Np);
   const int b = (int)(t / ((long long)H * Np));
-  float* qo = a.qbuf + (((size_t)b * H + h) * Np + n) * 8;
-  float* ko = a.kbuf + (((size_t)b * H + h) * Np + n) * KW;
+  const size_t row = ((size_t)b * H + h) * Np + n;
+  float4* qo = reinterpret_cast<float4*>(a.qbuf + row * 8);
+  float4* ko = reinterpret_cast<float4*>(a.klog + row * kKeyLog);
+  float4* vo = reinterpret_cast<float4*>(a.kval + row * kValW);
   const bool valid = n < N && a.frame_mask[(size_t)b * N + n] != 0;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
   if (!valid) {
     // padded keys and invalid frames: no contribution (bias -inf), zero data
-    for (int c = 0; c < 8; ++c) qo[c] = 0.f;
-    for (int c = 0; c < KW; ++c) ko[c] = 0.f;
-    ko[3] = -INFINITY;
+    qo[0] = z4; qo[1] = z4;
+    ko[0] = make_float4(0.f, 0.f, 0.f, -INFINITY); ko[1] = z4;
+    for (int c = 0; c < kValW / 4; ++c) vo[c] = z4;
     return;
   }
   const size_t bn = (size_t)b * N + n;
@@ -87,21 +98,24 @@ __global__ __launch_bounds__(256) void dd_lift_kernel(DDArgs a) {
   const float* T = a.trans + bn * 3;
   const size_t v3 = (bn * H + h) * 3;
   const float cd = softplus_dev(a.direction_scale[h]) * kSqrt3Inv * kLog2e;
-  float o[3];
+  float o[3], p[3];
   rotate(R, a.q_direction[v3], a.q_direction[v3 + 1], a.q_direction[v3 + 2], o);
-  qo[0] = cd * o[0]; qo[1] = cd * o[1]; qo[2] = cd * o[2]; qo[3] = 0.f;
-  rotate(R, a.q_point[v3], a.q_point[v3 + 1], a.q_point[v3 + 2], o);
-  qo[4] = o[0] + T[0]; qo[5] = o[1] + T[1]; qo[6] = o[2] + T[2]; qo[7] = 0.f;
+  rotate(R, a.q_point[v3], a.q_point[v3 + 1], a.q_point[v3 + 2], p);
+  qo[0] = make_float4(cd * o[0], cd * o[1], cd * o[2], 0.f);
+  qo[1] = make_float4(p[0] + T[0], p[1] + T[1], p[2] + T[2], 0.f);
   rotate(R, a.k_direction[v3], a.k_direction[v3 + 1], a.k_direction[v3 + 2], o);
-  ko[0] = o[0]; ko[1] = o[1]; ko[2] = o[2]; ko[3] = 0.f;
-  rotate(R, a.k_point[v3], a.k_point[v3 + 1], a.k_point[v3 + 2], o);
-  ko[4] = o[0] + T[0]; ko[5] = o[1] + T[1]; ko[6] = o[2] + T[2]; ko[7] = 0.f;
+  rotate(R, a.k_point[v3], a.k_point[v3 + 1], a.k_point[v3 + 2], p);
+  ko[0] = make_float4(o[0], o[1], o[2], 0.f);
+  ko[1] = make_float4(p[0] + T[0], p[1] + T[1], p[2] + T[2], 0.f);
   const float* vv = a.values + (bn * H + h) * (size_t)M * 3;
-  for (int m = 0; m < M; ++m) {
-    rotate(R, vv[3 * m], vv[3 * m + 1], vv[3 * m + 2], o);
-    ko[8 + 3 * m] = o[0]; ko[9 + 3 * m] = o[1]; ko[10 + 3 * m] = o[2];
-  }
-  for (int c = 8 + 3 * M; c < KW; ++c) ko[c] = 0.f;
+  float g[kValW];
+#pragma unroll
+  for (int c = 0; c < kValW; ++c) g[c] = 0.f;
+#pragma unroll
+  for (int m = 0; m < kDDMaxM; ++m)
+    if (m < M) rotate(R, vv[3 * m], vv[3 * m + 1], vv[3 * m + 2], g + 3 * m);
+#pragma unroll
+  for (int c = 0; c < kValW / 4; ++c) vo[c] = make_float4(g[4 * c], g[4 * c + 1], g[4 * c + 2], g[4 * c + 3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -110,9 +124,8 @@ __global__ __launch_bounds__(256) void dd_lift_kernel(DDArgs a) {
 template <int M, bool PM>
 __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
   constexpr int V = 3 * M;
-  constexpr int KW = dd_key_width(M);
   constexpr int PW = dd_part_width(M);
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.H, N = a.N, Np = a.Np, S = a.splits;
   const int h = blockIdx.y;
@@ -125,29 +138,56 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
   const int c0 = (int)((long long)nchunk * part / parts);
   const int c1 = (int)((long long)nchunk * (part + 1) / parts);
 
-  const float4* qrow = reinterpret_cast<const float4*>(a.qbuf + (((size_t)b * H + h) * Np + ic) * 8);
+  const size_t bh = (size_t)b * H + h;
+  const float4* qrow = reinterpret_cast<const float4*>(a.qbuf + (bh * Np + ic) * 8);
   const float4 qd = qrow[0], qp = qrow[1];
   const float cs = dist_coef(a.distance_scale, h);
-  const float* __restrict__ kb = a.kbuf + ((size_t)b * H + h) * Np * KW;
+  const float* __restrict__ klog = a.klog + bh * Np * kKeyLog;
+  // this lane's B element: value column l32 of key (2u + half) of a chunk
+  const float* __restrict__ kval = a.kval + bh * Np * kValW + half * kValW + l32;
   const uint8_t* pmrow = nullptr;
-  if constexpr (PM)
-    pmrow = a.pair_mask + (size_t)b * a.pm_sb + (size_t)h * a.pm_sh + (size_t)ic * a.pm_si;
+  if constexpr (PM) pmrow = a.pair_mask + (size_t)b * a.pm_sb + (size_t)h * a.pm_sh + (size_t)ic * a.pm_si;
 
-  float m_run = -INFINITY, l = 0.f;
-  float acc[V];
+  float bnext[4] = {0.f, 0.f, 0.f, 0.f};
+  auto load_b = [&](int ch) {
 #pragma unroll
-  for (int c = 0; c < V; ++c) acc[c] = 0.f;
+    for (int u = 0; u < 4; ++u) bnext[u] = kval[(size_t)(ch * kChunk + 2 * u) * kValW];
+  };
+  if (c0 < c1) load_b(c0);
+
+  // Logit data of a chunk (8 keys x 8 floats) is staged through a per-wave
+  // double buffer in LDS: lane l fetches float l of the chunk (one coalesced
+  // 256-byte load), the wave writes it, and every lane then reads each key
+  // as two broadcast float4. The global load runs two chunks ahead, the LDS
+  // reads return in order, so neither waits for a full memory round trip.
+  __shared__ float kls[4][2][kChunk * kKeyLog];
+  float* kls_w = &kls[w][0][0];
+  const float* __restrict__ klog_lane = klog + lane;
+  float gnext = 0.f;
+  if (c0 < c1) kls_w[lane] = klog_lane[(size_t)c0 * kChunk * kKeyLog];
+  if (c0 + 1 < c1) gnext = klog_lane[(size_t)(c0 + 1) * kChunk * kKeyLog];
+  asm volatile("" ::: "memory");
+
+  floatx16 acc0 = {}, acc1 = {};   // rows 0-31 and 32-63 of the wave, 32 value columns
+  float m_run = -INFINITY, l = 0.f;
 
   for (int ch = c0; ch < c1; ++ch) {
-    const float* __restrict__ kc = kb + (size_t)ch * kChunk * KW;
+    const int buf = (ch - c0) & 1;
+    const float bcur[4] = {bnext[0], bnext[1], bnext[2], bnext[3]};
+    if (ch + 1 < c1) {
+      load_b(ch + 1);
+      kls_w[(buf ^ 1) * kChunk * kKeyLog + lane] = gnext;
+    }
+    if (ch + 2 < c1) gnext = klog_lane[(size_t)(ch + 2) * kChunk * kKeyLog];
+    const float4* kc = reinterpret_cast<const float4*>(kls_w + buf * kChunk * kKeyLog);
     float sv[kChunk];
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const float* kk = kc + k * KW;
-      const float dot = qd.x * kk[0] + qd.y * kk[1] + qd.z * kk[2];
-      const float dx = qp.x - kk[4], dy = qp.y - kk[5], dz = qp.z - kk[6];
+      const float4 ka = kc[2 * k], kb = kc[2 * k + 1];
+      const float dot = qd.x * ka.x + qd.y * ka.y + qd.z * ka.z;
+      const float dx = qp.x - kb.x, dy = qp.y - kb.y, dz = qp.z - kb.z;
       const float d = __builtin_amdgcn_sqrtf(dx * dx + dy * dy + dz * dz);
-      float lg = fmaf(-cs, d, dot) + kk[3];
+      float lg = fmaf(-cs, d, dot) + ka.w;
       if constexpr (PM) {
         // padded keys (j >= N) already carry a -inf bias and have no mask entry
         const int j = ch * kChunk + k;
@@ -162,38 +202,62 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
       const float mn = fmaxf(m_run, cm);
       const float f = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
       l *= f;
-#pragma unroll
-      for (int c = 0; c < V; ++c) acc[c] *= f;
       m_run = mn;
+      // the factor of each accumulator row, fetched from the lane that owns
+      // the row: register e of a 32-row block holds row 8 (e/4) + 4 half + e%4
+      const int fi = __float_as_int(f);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int src = 8 * (e >> 2) + 4 * half + (e & 3);
+        acc0[e] *= __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, fi));
+        acc1[e] *= __int_as_float(__builtin_amdgcn_ds_bpermute((32 + src) << 2, fi));
+      }
     }
     const float ms = m_run == -INFINITY ? 0.f : m_run;
+    float p[kChunk];
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const float* kk = kc + k * KW;
-      const float p = __builtin_amdgcn_exp2f(sv[k] - ms);
-      l += p;
-#pragma unroll
-      for (int c = 0; c < V; ++c) acc[c] = fmaf(p, kk[8 + c], acc[c]);
+      p[k] = __builtin_amdgcn_exp2f(sv[k] - ms);
+      l += p[k];
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // lanes 0-31 take key 2u of rows 0-31 / 32-63, lanes 32-63 key 2u+1
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2 * u]),
+                                                       __float_as_uint(p[2 * u + 1]), false, false);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(sw[0]), bcur[u], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(sw[1]), bcur[u], acc1, 0, 0, 0);
+    }
+    // the next iteration reads the buffer written above and rewrites this
+    // one: LDS operations of a wave complete in order, only the compiler
+    // must keep them in program order
+    asm volatile("" ::: "memory");
   }
 
   // merge the four waves' key ranges through LDS
-  constexpr int LS = V + 3;   // odd row pitch: conflict-free per-lane rows
-  __shared__ float red[4][64][LS];
-  red[w][lane][0] = m_run;
-  red[w][lane][1] = l;
+  constexpr int LS = V + 1;   // odd row pitch: conflict-free per-lane rows
+  __shared__ float red_ml[4][64][2];
+  __shared__ float red_acc[4][64][LS];
+  red_ml[w][lane][0] = m_run;
+  red_ml[w][lane][1] = l;
+  if (l32 < V) {
 #pragma unroll
-  for (int c = 0; c < V; ++c) red[w][lane][2 + c] = acc[c];
+    for (int e = 0; e < 16; ++e) {
+      const int r = 8 * (e >> 2) + 4 * half + (e & 3);
+      red_acc[w][r][l32] = acc0[e];
+      red_acc[w][32 + r][l32] = acc1[e];
+    }
+  }
   __syncthreads();
   if (w != 0 || i >= N) return;
-  float mm = red[0][lane][0];
-  for (int u = 1; u < 4; ++u) mm = fmaxf(mm, red[u][lane][0]);
+  float mm = red_ml[0][lane][0];
+  for (int u = 1; u < 4; ++u) mm = fmaxf(mm, red_ml[u][lane][0]);
   float fu[4];
   float lt = 0.f;
   for (int u = 0; u < 4; ++u) {
-    const float mu = red[u][lane][0];
+    const float mu = red_ml[u][lane][0];
     fu[u] = mu == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mu - mm);
-    lt = fmaf(red[u][lane][1], fu[u], lt);
+    lt = fmaf(red_ml[u][lane][1], fu[u], lt);
   }
   float* po = a.part + ((((size_t)s * a.B + b) * N + i) * H + h) * PW;
   po[0] = mm;
@@ -201,107 +265,152 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
 #pragma unroll
   for (int c = 0; c < V; ++c) {
     float v = 0.f;
-    for (int u = 0; u < 4; ++u) v = fmaf(red[u][lane][2 + c], fu[u], v);
+    for (int u = 0; u < 4; ++u) v = fmaf(red_acc[u][lane][c], fu[u], v);
     po[2 + c] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-// dd_finish
+// dd_finish: one thread per (b, i, h, m): merge the key splits' partials,
+// divide by the softmax sum, rotate back by R_i^T. The m = 0 thread of each
+// (b, i, h) also writes the row statistics.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dd_finish_kernel(DDArgs a) {
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int H = a.H, M = a.M, N = a.N, S = a.splits, PW = a.PW;
-  if (t >= (long long)a.B * N * H) return;
-  const int h = (int)(t % H);
-  const int i = (int)((t / H) % N);
-  const int b = (int)(t / ((long long)H * N));
-  const size_t bi = (size_t)b * N + i;
-  float* vo = a.vectors + (bi * H + h) * (size_t)M * 3;
+  if (t >= (long long)a.B * N * H * M) return;
+  const int m = (int)(t % M);
+  const long long bih = t / M;             // (b * N + i) * H + h
+  const int h = (int)(bih % H);
+  const long long bi = bih / H;
+  const int i = (int)(bi % N), b = (int)(bi / N);
+  float* vo = a.vectors + (size_t)t * 3;
   float2* st = reinterpret_cast<float2*>(a.stats) + ((size_t)b * H + h) * N + i;
   if (!a.frame_mask[bi]) {
-    for (int c = 0; c < 3 * M; ++c) vo[c] = 0.f;
-    *st = make_float2(0.f, 0.f);
+    vo[0] = 0.f; vo[1] = 0.f; vo[2] = 0.f;
+    if (m == 0) *st = make_float2(0.f, 0.f);
     return;
   }
   const size_t pstride = (size_t)a.B * N * H * PW;
-  const float* p0 = a.part + (bi * H + h) * PW;
-  float mm = -INFINITY;
-  for (int s = 0; s < S; ++s) mm = fmaxf(mm, p0[s * pstride]);
-  float l = 0.f;
-  float fs[kMaxSplits];
+  const float* p0 = a.part + (size_t)bih * PW;
+  // running merge over the splits: (mm, l, g) rescaled whenever a split
+  // brings a larger maximum
+  float mm = -INFINITY, l = 0.f, gx = 0.f, gy = 0.f, gz = 0.f;
   for (int s = 0; s < S; ++s) {
-    const float ms = p0[s * pstride];
-    fs[s] = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mm);
-    l = fmaf(p0[s * pstride + 1], fs[s], l);
+    const float* ps = p0 + s * pstride;
+    const float msp = ps[0];
+    if (msp == -INFINITY) continue;   // an empty split adds nothing
+    const float mn = fmaxf(mm, msp);
+    const float fo = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm - mn);
+    const float fn = __builtin_amdgcn_exp2f(msp - mn);
+    l = fmaf(ps[1], fn, l * fo);
+    gx = fmaf(ps[2 + 3 * m], fn, gx * fo);
+    gy = fmaf(ps[3 + 3 * m], fn, gy * fo);
+    gz = fmaf(ps[4 + 3 * m], fn, gz * fo);
+    mm = mn;
   }
-  *st = make_float2(mm == -INFINITY ? 0.f : mm, l);
+  if (m == 0) *st = make_float2(mm == -INFINITY ? 0.f : mm, l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float R[9];
-  for (int c = 0; c < 9; ++c) R[c] = a.rot[bi * 9 + c];
-  for (int m = 0; m < M; ++m) {
-    float g[3];
-    for (int x = 0; x < 3; ++x) {
-      float v = 0.f;
-      for (int s = 0; s < S; ++s) v = fmaf(p0[s * pstride + 2 + 3 * m + x], fs[s], v);
-      g[x] = v * inv;
-    }
-    // R_i^T g: column x of R dotted with g
-    for (int x = 0; x < 3; ++x) vo[3 * m + x] = (R[x] * g[0] + R[3 + x] * g[1] + R[6 + x] * g[2]) + 0.f;
-  }
+  gx *= inv; gy *= inv; gz *= inv;
+  const float* R = a.rot + bi * 9;
+  // R_i^T g: column x of R dotted with g
+  vo[0] = (R[0] * gx + R[3] * gy + R[6] * gz) + 0.f;
+  vo[1] = (R[1] * gx + R[4] * gy + R[7] * gz) + 0.f;
+  vo[2] = (R[2] * gx + R[5] * gy + R[8] * gz) + 0.f;
 }
 
 // ---------------------------------------------------------------------------
 // dd_readout: out[r][c] = sum_k vec[r][k] W[k][c] + bias[c] on
-// v_mfma_f32_32x32x2f32, one wave per 32 x 32 output tile. Lanes 0-31 feed
-// reduction slot 0 and lanes 32-63 slot 1 of each product; the reduction
-// index is permuted (slot 0 takes k = 8t..8t+3, slot 1 k = 8t+4..8t+7 over
-// four products) so each lane reads its A row as one float4 per four steps.
+// v_mfma_f32_32x32x2f32. A workgroup of four waves owns a 32 x 32 output
+// tile and splits the reduction in four; each wave issues all of its
+// operand loads at once (buffer loads straight into registers), runs its
+// products, and the four partial tiles are summed through LDS. Lane l feeds
+// row / column l % 32 and reduction slot l / 32 of each product; the
+// reduction index is permuted (slot 0 takes k = 8t..8t+3, slot 1
+// k = 8t+4..8t+7 over four products) so a lane reads its vector row as one
+// float4 per four products.
 // ---------------------------------------------------------------------------
-typedef float floatx16 __attribute__((ext_vector_type(16)));
+constexpr int kRoTile = 32, kRoWaves = 4, kRoMaxK8 = 12;   // up to 96 reduction steps per wave
 
-__global__ __launch_bounds__(64) void dd_readout_kernel(DDArgs a) {
-  const int lane = threadIdx.x;
-  const int rows = a.B * a.N, K = 3 * a.H * a.M, Cout = a.Cout;
-  const int r0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
+template <bool V4>   // K % 4 == 0: each lane reads its 4 vector elements as one 16-byte load
+__global__ __launch_bounds__(64 * kRoWaves) void dd_readout_kernel(DDArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int half = lane >> 5, li = lane & 31;
-  const int ar = r0 + li < rows ? r0 + li : rows - 1;   // A row of this lane
-  const int bc = c0 + li;                               // B column of this lane
-  const bool bcol = bc < Cout;
-  const float* arow = a.vectors + (size_t)ar * K;
+  const int rows = a.B * a.N, K = 3 * a.H * a.M, Cout = a.Cout;
+  const int r0 = blockIdx.x * kRoTile, c0 = blockIdx.y * kRoTile;
+  const int nk8 = (K + 7) / 8;                       // groups of 8 reduction steps
+  // buffer loads: an offset past the end of the resource reads 0, so the
+  // ragged edges (rows past B*N, k past K, columns past Cout) need no branch
+  constexpr uint32_t kOut = 0x80000000u;
+  const int nr = rows - r0 < kRoTile ? rows - r0 : kRoTile;
+  const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.vectors) + (size_t)r0 * K, (short)0, (int)((size_t)nr * K * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.w_out) + c0, (short)0, (int)(((size_t)K * Cout - c0) * 4), 0x00020000);
+  const bool row_ok = li < nr, col_ok = c0 + li < Cout;
   floatx16 c = {};
-  for (int k8 = 0; k8 < K; k8 += 8) {
-    const int kb = k8 + 4 * half;
-    float av[4], bv[4];
+  // this wave's share of the k8 groups, processed kRoMaxK8 at a time
+  const int g0 = nk8 * wv / kRoWaves, g1 = nk8 * (wv + 1) / kRoWaves;
+  for (int gb = g0; gb < g1; gb += kRoMaxK8) {
+    float av[kRoMaxK8][4], bv[kRoMaxK8][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = kb + u;
-      av[u] = k < K ? arow[k] : 0.f;
-      bv[u] = (k < K && bcol) ? a.w_out[(size_t)k * Cout + bc] : 0.f;
+    for (int t = 0; t < kRoMaxK8; ++t) {
+      const int kb = 8 * (gb + t) + 4 * half;          // first k of this lane's float4
+      const bool in = gb + t < g1;
+      if constexpr (V4) {
+        // kb % 4 == 0 and K % 4 == 0: the four elements are in range together
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+            ra_rs, (in && kb < K && row_ok) ? (uint32_t)(li * K + kb) * 4u : kOut, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) av[t][u] = __uint_as_float(v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = kb + u;
+        const bool ok = in && k < K;
+        if constexpr (!V4)
+          av[t][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              ra_rs, (ok && row_ok) ? (uint32_t)(li * K + k) * 4u : kOut, 0, 0));
+        bv[t][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rw_rs, (ok && col_ok) ? (uint32_t)(k * Cout + li) * 4u : kOut, 0, 0));
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first product
 #pragma unroll
-    for (int u = 0; u < 4; ++u) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[u], c, 0, 0, 0);
+    for (int t = 0; t < kRoMaxK8; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[t][u], bv[t][u], c, 0, 0, 0);
   }
-  // which of this tile's rows have an allowed key in some head
-  __shared__ int row_any[32];
-  if (lane < 32) {
+  // sum the four waves' partial tiles
+  __shared__ float red[kRoWaves - 1][16][64];
+  __shared__ int row_any[kRoTile];
+  if (wv > 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[wv - 1][e][lane] = c[e];
+  }
+  if (tid < kRoTile) {
     int any = 0;
-    const int r = r0 + lane;
+    const int r = r0 + tid;
     if (r < rows) {
       const int b = r / a.N, i = r - b * a.N;
       const float2* st = reinterpret_cast<const float2*>(a.stats);
       for (int h = 0; h < a.H && !any; ++h) any = st[((size_t)b * a.H + h) * a.N + i].y > 0.f;
     }
-    row_any[lane] = any;
+    row_any[tid] = any;
   }
   __syncthreads();
-  if (!bcol) return;
-  const float bias = a.b_out ? a.b_out[bc] : 0.f;
+  if (wv != 0) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    for (int u = 0; u < kRoWaves - 1; ++u) c[e] += red[u][e][lane];
+  const int col = c0 + li;
+  if (col >= Cout) return;
+  const float bias = a.b_out ? a.b_out[col] : 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int rr = 8 * (e >> 2) + 4 * half + (e & 3);
     const int r = r0 + rr;
-    if (r < rows) a.output[(size_t)r * Cout + bc] = row_any[rr] ? c[e] + bias : 0.f;
+    if (r < rows) a.output[(size_t)r * Cout + col] = row_any[rr] ? c[e] + bias : 0.f;
   }
 }
 
@@ -312,12 +421,12 @@ __global__ __launch_bounds__(64) void dd_readout_kernel(DDArgs a) {
 constexpr int kProbRows = 4;
 
 __global__ __launch_bounds__(256) void dd_probs_kernel(DDArgs a) {
-  const int H = a.H, N = a.N, Np = a.Np, KW = a.KW;
+  const int H = a.H, N = a.N, Np = a.Np;
   const int bh = blockIdx.z, b = bh / H, h = bh - b * H;
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= N) return;
   const float cs = dist_coef(a.distance_scale, h);
-  const float4* kr = reinterpret_cast<const float4*>(a.kbuf + (((size_t)b * H + h) * Np + j) * KW);
+  const float4* kr = reinterpret_cast<const float4*>(a.klog + ((size_t)bh * Np + j) * kKeyLog);
   const float4 kd = kr[0], kp = kr[1];
   const float2* st = reinterpret_cast<const float2*>(a.stats) + (size_t)bh * N;
   for (int i0 = blockIdx.y * kProbRows; i0 < N; i0 += gridDim.y * kProbRows)
@@ -370,7 +479,7 @@ int dd_padded_keys(int N) { return (N + kChunk - 1) / kChunk * kChunk; }
 hipError_t launch_dirdist(const DDArgs& a, hipStream_t s) {
   {
     const long long total = (long long)a.B * a.Np * a.H;
-    hipLaunchKernelGGL(dd_lift_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(dd_lift_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   hipError_t e;
@@ -387,13 +496,16 @@ hipError_t launch_dirdist(const DDArgs& a, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   {
-    const long long total = (long long)a.B * a.N * a.H;
+    const long long total = (long long)a.B * a.N * a.H * a.M;
     hipLaunchKernelGGL(dd_finish_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   {
-    const dim3 grid((a.B * a.N + 31) / 32, (a.Cout + 31) / 32);
-    hipLaunchKernelGGL(dd_readout_kernel, grid, dim3(64), 0, s, a);
+    const dim3 grid((a.B * a.N + kRoTile - 1) / kRoTile, (a.Cout + kRoTile - 1) / kRoTile);
+    if ((3 * a.H * a.M) % 4 == 0)
+      hipLaunchKernelGGL(dd_readout_kernel<true>, grid, dim3(64 * kRoWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL(dd_readout_kernel<false>, grid, dim3(64 * kRoWaves), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (a.attention) {

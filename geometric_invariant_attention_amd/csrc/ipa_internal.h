@@ -84,15 +84,17 @@ hipError_t launch_frames(int n, const float* atom_n, const float* atom_ca, const
 // ---------------------------------------------------------------------------
 constexpr int kDDMaxM = 8;        // value vectors per head
 constexpr int kMaxSplits = 16;    // key splits across workgroups
-// floats per lifted key row: direction + validity bias, point, 3M rotated values
-constexpr int dd_key_width(int M) { return (8 + 3 * M + 3) / 4 * 4; }
+// floats per key: logit part (global direction, validity bias, global point,
+// pad) and rotated-value part (3M values, zero padded to one 32-column block)
+constexpr int kKeyLog = 8;
+constexpr int kValW = 32;
 // floats per partial row: running max, sum, 3M accumulators
 constexpr int dd_part_width(int M) { return (2 + 3 * M + 3) / 4 * 4; }
 
 struct DDArgs {
   int B, N, H, M, Cout;
   int Np;       // N rounded up to the key chunk
-  int KW, PW;   // dd_key_width(M), dd_part_width(M)
+  int PW;       // dd_part_width(M)
   int splits;   // key splits across workgroups (1..kMaxSplits)
   const float* rot; const float* trans;
   const float* q_direction; const float* k_direction;
@@ -103,8 +105,9 @@ struct DDArgs {
   const uint8_t* frame_mask;
   const uint8_t* pair_mask;                  // NULL: every edge allowed
   long long pm_sb, pm_sh, pm_si, pm_sj;      // element strides (0 = broadcast)
-  float* qbuf;    // [B][H][Np][8]    scaled global direction, global point
-  float* kbuf;    // [B][H][Np][KW]   global direction, bias, point, values
+  float* qbuf;    // [B][H][Np][8]        scaled global direction, global point
+  float* klog;    // [B][H][Np][kKeyLog]  global direction, bias, global point
+  float* kval;    // [B][H][Np][kValW]    rotated values
   float* part;    // [splits][B][N][H][PW]
   float* stats;   // [B][H][N] float2 (running max, sum)
   float* vectors; float* output; float* attention;

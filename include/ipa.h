@@ -219,7 +219,8 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype,
  * Arithmetic is float32 throughout; memory is linear in N unless the
  * attention matrix is requested.
  *   dims            B, N, H, M, Cout (every dim >= 1, M <= 8, N <= 2^24, Cout <= 65536,
- *                   B*H <= 65535, B*N*H*3*M < 2^31, B*N*Cout < 2^31)
+ *                   B*H <= 65535, B*N*H*3*M < 2^31, B*N*Cout < 2^31,
+ *                   3*H*M*Cout < 2^29)
  *   rot             [B,N,3,3] float32 (proper rotations on valid frames)
  *   trans           [B,N,3]   float32
  *   q_direction, k_direction, q_point, k_point  [B,N,H,3] float32
