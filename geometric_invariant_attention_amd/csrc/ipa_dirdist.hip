@@ -20,12 +20,15 @@
 //     used as the scalar operand of each vector instruction; per key and
 //     row: 3 FMA for the direction dot, 6 for the squared distance, one
 //     square root, one FMA to combine, the online-softmax exponential;
-//   * P.V on fp32 matrix cores (v_mfma_f32_32x32x2f32): each product
-//     contracts two keys for 32 query rows and 32 value columns (3M used).
-//     One lane-half swap (v_permlane32_swap) turns the row-per-lane P of
-//     two keys into the A operands of both 32-row blocks; the B operand is
-//     the rotated values of the two keys, one column per lane, loaded with
-//     plain vector loads a chunk ahead;
+//   * P.V on bf16 matrix cores (v_mfma_f32_32x32x16_bf16) in three
+//     products per 16-key chunk and 32-row block, Ph Vh + Ph Vl + Pl Vh,
+//     with P and V split into bf16 hi + lo pairs (16 significant bits, so
+//     the product keeps fp32-level accuracy at a fifth of the matrix-core
+//     time of fp32 products). 32 value columns: 3M values and a column of
+//     ones that accumulates the softmax sum. A lane-half swap
+//     (v_permlane32_swap) turns the row-per-lane P into the A operands of
+//     both 32-row blocks; the B operand is the rotated values of 8 keys in
+//     one column per lane, loaded with plain vector loads a chunk ahead;
 //   * exponentials in base 2 (log2 e folded into the scales), the running
 //     maximum raised lazily (only when a chunk's maximum exceeds it by more
 //     than 2^8), so most chunks skip the rescale.
@@ -48,10 +51,48 @@ namespace {
 
 constexpr float kSqrt3Inv = 0.57735026918962576f;
 constexpr float kLazy = 8.f;   // a chunk maximum this far above the running one forces a rescale
-constexpr int kChunk = 8;      // keys per online-softmax chunk (the key axis is padded to it)
+constexpr int kChunk = 16;     // keys per online-softmax chunk (the key axis is padded to it)
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as bf16 pairs hi + lo: hi keeps the top 16 bits of each
+// (truncation), lo is the exact fp32 remainder rounded to bf16. hi + lo
+// carries 16 significant bits: |x - hi - lo| <= 2^-16 |x|. The first value
+// goes to the low half of each register.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t t0 = __float_as_uint(x0) & 0xffff0000u, t1 = __float_as_uint(x1) & 0xffff0000u;
+  const f32x2 r = {x0 - __uint_as_float(t0), x1 - __uint_as_float(t1)};
+  hi = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
+
+// Value column whose entry is 1 for every valid key: the product P V then
+// carries the softmax sum of each row in that column (3M <= 24 < 31).
+constexpr int kSumCol = kValW - 1;
+
+// acc[e] *= f[e] in place in the accumulation registers: plain vector code
+// on the tile would move it to architectural registers and back on every
+// iteration of the loop. The caller lets the matrix-core writes settle
+// before (acc_settle) and after.
+__device__ __forceinline__ void scale_acc(floatx16& acc, const float (&f)[16]) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(acc[e]), "=&v"(t)
+        : "v"(f[e]));
+  }
+}
+// 32 wait states: more than any matrix-core result or accumulation-register
+// write needs before the next access to the same registers.
+__device__ __forceinline__ void acc_settle() { asm volatile("s_nop 15\n\ts_nop 15"); }
 
 __device__ __forceinline__ float softplus_dev(float x) {
   return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
@@ -114,6 +155,7 @@ __global__ __launch_bounds__(64) void dd_lift_kernel(DDArgs a) {
 #pragma unroll
   for (int m = 0; m < kDDMaxM; ++m)
     if (m < M) rotate(R, vv[3 * m], vv[3 * m + 1], vv[3 * m + 2], g + 3 * m);
+  g[kSumCol] = 1.f;   // P times this column is the softmax sum
 #pragma unroll
   for (int c = 0; c < kValW / 4; ++c) vo[c] = make_float4(g[4 * c], g[4 * c + 1], g[4 * c + 2], g[4 * c + 3]);
 }
@@ -143,15 +185,16 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
   const float4 qd = qrow[0], qp = qrow[1];
   const float cs = dist_coef(a.distance_scale, h);
   const float* __restrict__ klog = a.klog + bh * Np * kKeyLog;
-  // this lane's B element: value column l32 of key (2u + half) of a chunk
-  const float* __restrict__ kval = a.kval + bh * Np * kValW + half * kValW + l32;
+  // this lane's B elements: value column l32 of keys 8 half .. 8 half + 7 of a chunk
+  const float* __restrict__ kval = a.kval + bh * Np * kValW + half * 8 * kValW + l32;
   const uint8_t* pmrow = nullptr;
   if constexpr (PM) pmrow = a.pair_mask + (size_t)b * a.pm_sb + (size_t)h * a.pm_sh + (size_t)ic * a.pm_si;
 
-  float bnext[4] = {0.f, 0.f, 0.f, 0.f};
+  static_assert(kChunk == 16, "one 32x32x16 product per chunk and operand split");
+  float bnext[8];
   auto load_b = [&](int ch) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) bnext[u] = kval[(size_t)(ch * kChunk + 2 * u) * kValW];
+    for (int j = 0; j < 8; ++j) bnext[j] = kval[(size_t)(ch * kChunk + j) * kValW];
   };
   if (c0 < c1) load_b(c0);
 
@@ -162,23 +205,41 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
   // reads return in order, so neither waits for a full memory round trip.
   __shared__ float kls[4][2][kChunk * kKeyLog];
   float* kls_w = &kls[w][0][0];
+  constexpr int NG = kChunk * kKeyLog / 64;   // floats per lane per chunk
   const float* __restrict__ klog_lane = klog + lane;
-  float gnext = 0.f;
-  if (c0 < c1) kls_w[lane] = klog_lane[(size_t)c0 * kChunk * kKeyLog];
-  if (c0 + 1 < c1) gnext = klog_lane[(size_t)(c0 + 1) * kChunk * kKeyLog];
+  float gnext[NG];
+  if (c0 < c1) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) kls_w[64 * g + lane] = klog_lane[(size_t)c0 * kChunk * kKeyLog + 64 * g];
+  }
+  if (c0 + 1 < c1) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) gnext[g] = klog_lane[(size_t)(c0 + 1) * kChunk * kKeyLog + 64 * g];
+  }
   asm volatile("" ::: "memory");
 
-  floatx16 acc0 = {}, acc1 = {};   // rows 0-31 and 32-63 of the wave, 32 value columns
-  float m_run = -INFINITY, l = 0.f;
+  // rows 0-31 and 32-63 of the wave, 32 value columns (the last one the
+  // softmax sum)
+  floatx16 acc0 = {}, acc1 = {};
+  float m_run = -INFINITY;
 
   for (int ch = c0; ch < c1; ++ch) {
     const int buf = (ch - c0) & 1;
-    const float bcur[4] = {bnext[0], bnext[1], bnext[2], bnext[3]};
+    // B = the chunk's values as bf16 hi + lo (hi: the top 16 bits, lo: the
+    // exact fp32 remainder rounded to bf16; together 16 significant bits)
+    uint32_t bh4[4], bl4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split_pair(bnext[2 * j], bnext[2 * j + 1], bh4[j], bl4[j]);
+    const u32x4 bhi = {bh4[0], bh4[1], bh4[2], bh4[3]}, blo = {bl4[0], bl4[1], bl4[2], bl4[3]};
     if (ch + 1 < c1) {
       load_b(ch + 1);
-      kls_w[(buf ^ 1) * kChunk * kKeyLog + lane] = gnext;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) kls_w[(buf ^ 1) * kChunk * kKeyLog + 64 * g + lane] = gnext[g];
     }
-    if (ch + 2 < c1) gnext = klog_lane[(size_t)(ch + 2) * kChunk * kKeyLog];
+    if (ch + 2 < c1) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) gnext[g] = klog_lane[(size_t)(ch + 2) * kChunk * kKeyLog + 64 * g];
+    }
     const float4* kc = reinterpret_cast<const float4*>(kls_w + buf * kChunk * kKeyLog);
     float sv[kChunk];
 #pragma unroll
@@ -201,33 +262,53 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
     if (__builtin_amdgcn_ballot_w64(cm > m_run + kLazy)) {
       const float mn = fmaxf(m_run, cm);
       const float f = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-      l *= f;
       m_run = mn;
       // the factor of each accumulator row, fetched from the lane that owns
       // the row: register e of a 32-row block holds row 8 (e/4) + 4 half + e%4
       const int fi = __float_as_int(f);
+      float f0[16], f1[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int src = 8 * (e >> 2) + 4 * half + (e & 3);
-        acc0[e] *= __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, fi));
-        acc1[e] *= __int_as_float(__builtin_amdgcn_ds_bpermute((32 + src) << 2, fi));
+        f0[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, fi));
+        f1[e] = __int_as_float(__builtin_amdgcn_ds_bpermute((32 + src) << 2, fi));
       }
+      acc_settle();
+      scale_acc(acc0, f0);
+      scale_acc(acc1, f1);
+      acc_settle();
     }
     const float ms = m_run == -INFINITY ? 0.f : m_run;
     float p[kChunk];
 #pragma unroll
-    for (int k = 0; k < kChunk; ++k) {
-      p[k] = __builtin_amdgcn_exp2f(sv[k] - ms);
-      l += p[k];
-    }
+    for (int k = 0; k < kChunk; ++k) p[k] = __builtin_amdgcn_exp2f(sv[k] - ms);
+    // P split the same way, two keys per register; one lane-half swap per
+    // register pair gives the A operands of both 32-row blocks: block 0
+    // takes keys 0-7 of rows 0-31 in lanes 0-31 and keys 8-15 of the same
+    // rows in lanes 32-63, block 1 likewise for rows 32-63
+    uint32_t phi[8], plo[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      // lanes 0-31 take key 2u of rows 0-31 / 32-63, lanes 32-63 key 2u+1
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2 * u]),
-                                                       __float_as_uint(p[2 * u + 1]), false, false);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(sw[0]), bcur[u], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(sw[1]), bcur[u], acc1, 0, 0, 0);
+    for (int j = 0; j < 8; ++j) split_pair(p[2 * j], p[2 * j + 1], phi[j], plo[j]);
+    uint32_t a0h4[4], a1h4[4], a0l4[4], a1l4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto sh = __builtin_amdgcn_permlane32_swap(phi[j], phi[4 + j], false, false);
+      const auto sl = __builtin_amdgcn_permlane32_swap(plo[j], plo[4 + j], false, false);
+      a0h4[j] = sh[0]; a1h4[j] = sh[1];
+      a0l4[j] = sl[0]; a1l4[j] = sl[1];
     }
+    const u32x4 a0h = {a0h4[0], a0h4[1], a0h4[2], a0h4[3]}, a1h = {a1h4[0], a1h4[1], a1h4[2], a1h4[3]};
+    const u32x4 a0l = {a0l4[0], a0l4[1], a0l4[2], a0l4[3]}, a1l = {a1l4[0], a1l4[1], a1l4[2], a1l4[3]};
+    const bf16x8 Bh = __builtin_bit_cast(bf16x8, bhi), Bl = __builtin_bit_cast(bf16x8, blo);
+    const bf16x8 A0h = __builtin_bit_cast(bf16x8, a0h), A0l = __builtin_bit_cast(bf16x8, a0l);
+    const bf16x8 A1h = __builtin_bit_cast(bf16x8, a1h), A1l = __builtin_bit_cast(bf16x8, a1l);
+    // P V ~ Ph Vh + Ph Vl + Pl Vh (the dropped Pl Vl is below 2^-16 relative)
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0h, Bh, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1h, Bh, acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0h, Bl, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1h, Bl, acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0l, Bh, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1l, Bh, acc1, 0, 0, 0);
     // the next iteration reads the buffer written above and rewrites this
     // one: LDS operations of a wave complete in order, only the compiler
     // must keep them in program order
@@ -239,13 +320,19 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
   __shared__ float red_ml[4][64][2];
   __shared__ float red_acc[4][64][LS];
   red_ml[w][lane][0] = m_run;
-  red_ml[w][lane][1] = l;
   if (l32 < V) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = 8 * (e >> 2) + 4 * half + (e & 3);
       red_acc[w][r][l32] = acc0[e];
       red_acc[w][32 + r][l32] = acc1[e];
+    }
+  } else if (l32 == kSumCol) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = 8 * (e >> 2) + 4 * half + (e & 3);
+      red_ml[w][r][1] = acc0[e];
+      red_ml[w][32 + r][1] = acc1[e];
     }
   }
   __syncthreads();
