@@ -22,9 +22,9 @@
 //     square root, one FMA to combine, the online-softmax exponential;
 //   * P.V on bf16 matrix cores (v_mfma_f32_32x32x16_bf16) in three
 //     products per 16-key chunk and 32-row block, Ph Vh + Ph Vl + Pl Vh,
-//     with P and V split into bf16 hi + lo pairs (16 significant bits, so
-//     the product keeps fp32-level accuracy at a fifth of the matrix-core
-//     time of fp32 products). 32 value columns: 3M values and a column of
+//     with P and V split into bf16 hi + lo pairs (the dropped lo * lo term
+//     is below 2^-18 relative, so the product keeps near-fp32 accuracy at a
+//     fifth of the matrix-core time of fp32 products). 32 value columns: 3M values and a column of
 //     ones that accumulates the softmax sum. A lane-half swap
 //     (v_permlane32_swap) turns the row-per-lane P into the A operands of
 //     both 32-row blocks; the B operand is the rotated values of 8 keys in
@@ -59,14 +59,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Two fp32 values as bf16 pairs hi + lo: hi keeps the top 16 bits of each
-// (truncation), lo is the exact fp32 remainder rounded to bf16. hi + lo
-// carries 16 significant bits: |x - hi - lo| <= 2^-16 |x|. The first value
-// goes to the low half of each register.
+// Two fp32 values as bf16 pairs hi + lo: hi is each value rounded to bf16
+// (nearest even), lo the exact fp32 remainder rounded to bf16, so
+// |x - hi - lo| <= 2^-18 |x| and |lo| <= 2^-9 |x|: in a product of two
+// split operands the dropped lo * lo term is below 2^-18 relative. The
+// first value goes to the low half of each register.
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t t0 = __float_as_uint(x0) & 0xffff0000u, t1 = __float_as_uint(x1) & 0xffff0000u;
-  const f32x2 r = {x0 - __uint_as_float(t0), x1 - __uint_as_float(t1)};
-  hi = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+  const f32x2 x = {x0, x1};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  const f32x2 r = {x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u)};
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
 
@@ -225,8 +226,7 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
 
   for (int ch = c0; ch < c1; ++ch) {
     const int buf = (ch - c0) & 1;
-    // B = the chunk's values as bf16 hi + lo (hi: the top 16 bits, lo: the
-    // exact fp32 remainder rounded to bf16; together 16 significant bits)
+    // B = the chunk's values as bf16 hi + lo pairs
     uint32_t bh4[4], bl4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) split_pair(bnext[2 * j], bnext[2 * j + 1], bh4[j], bl4[j]);
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void dd_attn_kernel(DDArgs a) {
     const bf16x8 Bh = __builtin_bit_cast(bf16x8, bhi), Bl = __builtin_bit_cast(bf16x8, blo);
     const bf16x8 A0h = __builtin_bit_cast(bf16x8, a0h), A0l = __builtin_bit_cast(bf16x8, a0l);
     const bf16x8 A1h = __builtin_bit_cast(bf16x8, a1h), A1l = __builtin_bit_cast(bf16x8, a1l);
-    // P V ~ Ph Vh + Ph Vl + Pl Vh (the dropped Pl Vl is below 2^-16 relative)
+    // P V ~ Ph Vh + Ph Vl + Pl Vh (the dropped Pl Vl is below 2^-18 relative)
     acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0h, Bh, acc0, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1h, Bh, acc1, 0, 0, 0);
     acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0h, Bl, acc0, 0, 0, 0);

@@ -158,3 +158,12 @@ def test_inputs_are_not_modified(device):
         assert torch.equal(before[k], t[k]), k
     ref = _oracle(inp)
     assert np.abs(out["vectors"].cpu().numpy() - ref["vectors"]).max() < TOL
+
+
+
+def test_wide_value_rows(device):
+    """24 heads of 8 value vectors (576 flattened values per query row):
+    the readout's reduction spans several of its load batches."""
+    w = DIRDIST_WORKLOADS["dd_tiny_fp32"].with_(B=2, N=70, H=24, M=8, Cout=40, ragged=(30, 70),
+                                                pair_mask="per_head")
+    _run(w, device, seed=5)
