@@ -23,6 +23,10 @@ Pinning status of each function (see the tests under ``tests/``):
                   for the unsquared distance and the value transport, rigid
                   invariance, permutation equivariance, mask and readout rules.
   dirdist_bruteforce pinned by the same closed forms on tiny inputs.
+  ipa_backward    pinned: central finite differences of ipa_forward along
+                  random directions for every input, its restated forward
+                  equals ipa_forward, rigid-motion identities of the frame
+                  gradients, masked rows and keys.
 """
 
 from .ipa_oracle import ipa_forward, ipa_logits, to_global
@@ -30,7 +34,8 @@ from .bruteforce import ipa_bruteforce, dirdist_bruteforce
 from .lifted import ipa_lifted, block_centres
 from .geometry import frames_from_atoms, meet_attention
 from .dirdist import dirdist_attention
+from .ipa_grad import ipa_backward
 
 __all__ = ["ipa_forward", "ipa_logits", "to_global", "ipa_bruteforce",
            "ipa_lifted", "block_centres", "frames_from_atoms", "meet_attention",
-           "dirdist_attention", "dirdist_bruteforce"]
+           "dirdist_attention", "dirdist_bruteforce", "ipa_backward"]

@@ -1,0 +1,88 @@
+"""Pins of the IPA gradient oracle (CPU only).
+
+The gradient oracle (oracle/ipa_grad.py) restates the forward in torch and
+differentiates it with autograd. It is pinned to things other than itself:
+  * its restated forward equals the numpy forward oracle;
+  * central finite differences of the numpy forward oracle, along random
+    directions, match <gradient, direction> for every input tensor;
+  * rigid-motion invariance of the loss: moving every frame by one global
+    rotation and translation changes no output, so the gradients of the
+    frames satisfy sum_i dtrans_i = 0 and sum_i (drot_i R_i^T + dtrans_i t_i^T)
+    is symmetric;
+  * masked rows pass no gradient, masked keys receive none.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import ipa_forward
+from oracle.ipa_grad import INPUTS, ipa_backward, ipa_forward_torch
+from workloads import WORKLOADS, make_inputs
+
+TINY = WORKLOADS["tiny_fp32"].with_(L=7, H=2, C=4, Pqk=2, Pv=3, R=2, Cz=8)
+RAGGED = WORKLOADS["ragged_batch"].with_(B=2, L=9, H=2, C=4, Pqk=2, Pv=2, R=1, Cz=8,
+                                         ragged=(5, 9), dtype="fp32")
+
+
+def _grads(inp, seed):
+    d = inp["dims"]
+    rng = np.random.default_rng(seed)
+    B, L, H = d["B"], d["L"], d["H"]
+    return {"s": rng.standard_normal((B, L, H, d["C"])),
+            "pts": rng.standard_normal((B, L, H, d["Pv"], 3)),
+            "pts_norm": rng.standard_normal((B, L, H, d["Pv"])),
+            "pair": rng.standard_normal((B, L, H, d["Cz"]))}
+
+
+def _loss(inp, g):
+    out = ipa_forward(inp)
+    return sum(float(np.sum(out[k] * g[k])) for k in ("s", "pts", "pts_norm", "pair"))
+
+
+@pytest.mark.parametrize("w", [TINY, RAGGED])
+def test_restated_forward_matches_numpy_oracle(w):
+    inp = make_inputs(w, seed=3)
+    a, b = ipa_forward(inp), ipa_forward_torch(inp)
+    for k in a:
+        assert np.abs(a[k] - b[k]).max() < 1e-12, k
+
+
+@pytest.mark.parametrize("w,seed", [(TINY, 0), (TINY, 1), (RAGGED, 2)])
+def test_finite_differences_every_input(w, seed):
+    inp = make_inputs(w, seed=seed)
+    for n in INPUTS:
+        inp[n] = inp[n].astype(np.float64)
+    g = _grads(inp, seed + 10)
+    grad = ipa_backward(inp, g)
+    rng = np.random.default_rng(seed + 20)
+    for n in INPUTS:
+        v = rng.standard_normal(inp[n].shape)
+        eps = 1e-6
+        plus, minus = dict(inp), dict(inp)
+        plus[n] = inp[n] + eps * v
+        minus[n] = inp[n] - eps * v
+        fd = (_loss(plus, g) - _loss(minus, g)) / (2 * eps)
+        an = float(np.sum(grad[n] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (n, fd, an)
+
+
+def test_rigid_motion_invariance_of_frame_gradients():
+    inp = make_inputs(TINY.with_(B=1, L=6), seed=5)
+    g = _grads(inp, 6)
+    grad = ipa_backward(inp, g)
+    R = inp["rot"].astype(np.float64)[0]
+    t = inp["trans"].astype(np.float64)[0]
+    dR, dt = grad["rot"][0], grad["trans"][0]
+    assert np.abs(dt.sum(axis=0)).max() < 1e-9
+    M = np.einsum("lab,lcb->ac", dR, R) + np.einsum("la,lc->ac", dt, t)
+    assert np.abs(M - M.T).max() < 1e-9 * max(1.0, np.abs(M).max())
+
+
+def test_masked_rows_and_keys():
+    inp = make_inputs(RAGGED, seed=7)
+    g = _grads(inp, 8)
+    grad = ipa_backward(inp, g)
+    pad = inp["mask"] == 0
+    assert pad.any()
+    for n in ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2"):
+        assert np.all(grad[n][pad] == 0), n
