@@ -9,10 +9,12 @@ from ._binding import (  # noqa: F401
     ipa_forward, load_library, make_dims, status_string, workspace_bytes,
     frames_from_atoms, meet_attention, MeetForward, IpaMeetDims, meet_workspace_bytes,
     DirDistForward, IpaDirDistDims, dirdist_workspace_bytes, geometric_reasoning_attention,
+    IPABackward, backward_workspace_bytes,
 )
 
 __all__ = ["ipa_forward", "IPAForward", "IPAError", "load_library", "workspace_bytes",
            "status_string", "make_dims", "IpaDims", "default_weights", "IPA_F32",
            "IPA_BF16", "LIB_PATH", "frames_from_atoms", "meet_attention", "MeetForward",
            "IpaMeetDims", "meet_workspace_bytes", "DirDistForward", "IpaDirDistDims",
-           "dirdist_workspace_bytes", "geometric_reasoning_attention"]
+           "dirdist_workspace_bytes", "geometric_reasoning_attention", "IPABackward",
+           "backward_workspace_bytes"]

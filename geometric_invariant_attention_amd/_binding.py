@@ -75,6 +75,10 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ipa_dirdist_workspace_bytes.restype = sz
     lib.ipa_dirdist_forward.argtypes = [ctypes.POINTER(IpaDirDistDims)] + [vp] * 18 + [sz, vp]
     lib.ipa_dirdist_forward.restype = i32
+    lib.ipa_backward_workspace_bytes.argtypes = [ctypes.POINTER(IpaDims)]
+    lib.ipa_backward_workspace_bytes.restype = sz
+    lib.ipa_backward.argtypes = [ctypes.POINTER(IpaDims)] + [vp] * 13 + [f32, f32] + [vp] * 20 + [sz, vp]
+    lib.ipa_backward.restype = i32
     lib.ipa_status_string.argtypes = [i32]
     lib.ipa_status_string.restype = ctypes.c_char_p
     lib.ipa_version.argtypes = []
@@ -418,3 +422,79 @@ def geometric_reasoning_attention(rot, trans, q_direction, k_direction, q_point,
     plan = DirDistForward(B, N, H, M, Cout, device=values.device, attention=attention)
     return plan(rot, trans, q_direction, k_direction, q_point, k_point, values, direction_scale,
                 distance_scale, output_weight, output_bias, frame_mask, pair_mask)
+
+
+# ---------------------------------------------------------------------------
+# gradient of the forward (ipa_backward, float32)
+# ---------------------------------------------------------------------------
+BACKWARD_INPUTS = ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2", "w_b", "gamma")
+
+
+def backward_workspace_bytes(B, L, H, C, Pqk, Pv, R, Cz) -> int:
+    d = make_dims(B, L, H, C, Pqk, Pv, R, Cz)
+    return int(load_library().ipa_backward_workspace_bytes(ctypes.byref(d)))
+
+
+class IPABackward:
+    """Reusable plan of the IPA gradient (ipa_backward, float32): validated
+    shapes, preallocated workspace and gradient tensors on one device."""
+
+    def __init__(self, B, L, H, C, Pqk, Pv, R, Cz, device=None):
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.dims = make_dims(B, L, H, C, Pqk, Pv, R, Cz)
+        self.shape = dict(B=B, L=L, H=H, C=C, Pqk=Pqk, Pv=Pv, R=R, Cz=Cz)
+        self.lib = load_library()
+        self.ws_bytes = int(self.lib.ipa_backward_workspace_bytes(ctypes.byref(self.dims)))
+        if self.ws_bytes == 0:
+            raise IPAError(-6, f"unsupported dims {self.shape}")
+        dev, f32 = self.device, torch.float32
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.shapes = {"q": (B, L, H, C), "k": (B, L, H, C), "v": (B, L, H, C),
+                       "q_pts": (B, L, H, Pqk, 3), "k_pts": (B, L, H, Pqk, 3), "v_pts": (B, L, H, Pv, 3),
+                       "rot": (B, L, 3, 3), "trans": (B, L, 3), "z1": (B, L, R, Cz), "z2": (B, L, R, Cz),
+                       "w_b": (Cz, H), "gamma": (H,)}
+        self.grads = {n: torch.empty(shp, dtype=f32, device=dev) for n, shp in self.shapes.items()}
+
+    def bind(self, inputs: dict, outputs: dict, cotangents: dict, mask=None, w_L=None, w_C=None,
+             stream=None) -> tuple:
+        B, L, H, C, Pv, Cz = (self.shape[n] for n in ("B", "L", "H", "C", "Pv", "Cz"))
+        dev, f32 = self.device, torch.float32
+        if w_L is None or w_C is None:
+            dl, dc = default_weights(self.shape["Pqk"])
+            w_L = dl if w_L is None else w_L
+            w_C = dc if w_C is None else w_C
+        t = {}
+        for n, shp in self.shapes.items():
+            x = inputs[n]
+            if tuple(x.shape) != shp:
+                raise ValueError(f"{n} has shape {tuple(x.shape)}, expected {shp}")
+            t[n] = _prep(x, f32, dev, n)
+        oshapes = {"s": (B, L, H, C), "pts": (B, L, H, Pv, 3), "pts_norm": (B, L, H, Pv), "pair": (B, L, H, Cz)}
+        o = {n: _prep(outputs[n], f32, dev, "out_" + n) for n in ("s", "pts", "pair")}
+        g = {}
+        for n, shp in oshapes.items():
+            x = cotangents[n]
+            if tuple(x.shape) != shp:
+                raise ValueError(f"cotangent {n} has shape {tuple(x.shape)}, expected {shp}")
+            g[n] = _prep(x, f32, dev, "g_" + n)
+        m = None
+        if mask is not None:
+            m = (mask.to(torch.uint8) if mask.dtype != torch.uint8 else mask).contiguous()
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        self.bound = (t, o, g, m)
+        return (ctypes.byref(self.dims), *(t[n].data_ptr() for n in BACKWARD_INPUTS), _dev_ptr(m),
+                ctypes.c_float(w_L), ctypes.c_float(w_C),
+                o["s"].data_ptr(), o["pts"].data_ptr(), o["pair"].data_ptr(),
+                g["s"].data_ptr(), g["pts"].data_ptr(), g["pts_norm"].data_ptr(), g["pair"].data_ptr(),
+                *(self.grads[n].data_ptr() for n in BACKWARD_INPUTS),
+                self.workspace.data_ptr(), ctypes.c_size_t(self.ws_bytes), ctypes.c_void_p(stream.cuda_stream))
+
+    def backward_raw(self, raw: tuple) -> dict:
+        rc = self.lib.ipa_backward(*raw)
+        if rc != 0:
+            raise IPAError(rc, status_string(rc))
+        return self.grads
+
+    def __call__(self, *args, **kw) -> dict:
+        return self.backward_raw(self.bind(*args, **kw))

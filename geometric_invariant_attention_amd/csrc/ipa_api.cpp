@@ -295,6 +295,89 @@ int32_t ipa_dirdist_forward(const ipa_dirdist_dims* dims, const float* rot, cons
   return IPA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct BwdLayout {
+  size_t off[17];
+  size_t total;
+};
+
+bool bwd_layout(const ipa_dims* d, BwdLayout* o) {
+  if (!d) return false;
+  const int64_t B = d->B, L = d->L, H = d->H, C = d->C, P = d->Pqk, Pv = d->Pv, R = d->R, Cz = d->Cz;
+  if (B < 1 || L < 1 || H < 1 || C < 1 || P < 1 || Pv < 1 || R < 1 || Cz < 1) return false;
+  if (C > 16 || P > 5 || Pv > 8 || R * Cz > 256) return false;
+  if (B * H > 65535 || B * L * H * 296 >= (int64_t(1) << 31) || B * L * (Cz * H + H) >= (int64_t(1) << 31))
+    return false;
+  const size_t rows = (size_t)(B * H * L), DA = (size_t)(C + R * Cz), DV = (size_t)(C + 3 * Pv + R * Cz);
+  const size_t sizes[17] = {rows * DA, rows * DA, rows * DV, rows * DV, rows * 3 * P, rows * 3 * P, rows,
+                            rows * DA, rows * R * Cz, rows * 3 * P, rows, rows,
+                            rows * DA, rows * DV, rows * 3 * P,
+                            (size_t)(B * L * H) * 12, (size_t)(B * L) * (size_t)(Cz * H + H)};
+  size_t off = 0;
+  for (int e = 0; e < 17; ++e) {
+    o->off[e] = off;
+    off = ipa::align256(off + sizes[e] * 4);
+  }
+  o->total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ipa_backward_workspace_bytes(const ipa_dims* dims) {
+  BwdLayout ly;
+  return bwd_layout(dims, &ly) ? ly.total : 0;
+}
+
+int32_t ipa_backward(const ipa_dims* dims, const float* q, const float* k, const float* v,
+                     const float* q_pts, const float* k_pts, const float* v_pts,
+                     const float* rot, const float* trans, const float* z1, const float* z2,
+                     const float* w_b, const float* gamma, const uint8_t* mask, float w_L, float w_C,
+                     const float* out_s, const float* out_pts, const float* out_pair,
+                     const float* g_s, const float* g_pts, const float* g_pts_norm, const float* g_pair,
+                     float* dq, float* dk, float* dv, float* dq_pts, float* dk_pts, float* dv_pts,
+                     float* drot, float* dtrans, float* dz1, float* dz2, float* dw_b, float* dgamma,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dims) return IPA_ERR_NULL;
+  if (dims->B < 1 || dims->L < 1 || dims->H < 1 || dims->C < 1 || dims->Pqk < 1 || dims->Pv < 1 ||
+      dims->R < 1 || dims->Cz < 1)
+    return IPA_ERR_DIMS;
+  const void* ptrs[] = {q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma,
+                        out_s, out_pts, out_pair, g_s, g_pts, g_pts_norm, g_pair,
+                        dq, dk, dv, dq_pts, dk_pts, dv_pts, drot, dtrans, dz1, dz2, dw_b, dgamma, workspace};
+  for (const void* p : ptrs) {
+    if (!p) return IPA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return IPA_ERR_ALIGN;
+  }
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return IPA_ERR_ALIGN;
+  if (!std::isfinite(w_L) || !std::isfinite(w_C) || w_L < 0.f || w_C < 0.f) return IPA_ERR_ARG;
+  BwdLayout ly;
+  if (!bwd_layout(dims, &ly)) return IPA_ERR_UNSUPPORTED;
+  if (workspace_bytes < ly.total) return IPA_ERR_WORKSPACE;
+  ipa::BwdArgs a{};
+  a.B = dims->B; a.L = dims->L; a.H = dims->H; a.C = dims->C; a.Pqk = dims->Pqk; a.Pv = dims->Pv;
+  a.R = dims->R; a.Cz = dims->Cz;
+  a.DA = a.C + a.R * a.Cz; a.DV = a.C + 3 * a.Pv + a.R * a.Cz; a.P3 = 3 * a.Pqk;
+  a.w_L = w_L; a.w_C = w_C;
+  a.q = q; a.k = k; a.v = v; a.q_pts = q_pts; a.k_pts = k_pts; a.v_pts = v_pts;
+  a.rot = rot; a.trans = trans; a.z1 = z1; a.z2 = z2; a.w_b = w_b; a.gamma = gamma; a.mask = mask;
+  a.o_s = out_s; a.o_pts = out_pts; a.o_pair = out_pair;
+  a.g_s = g_s; a.g_pts = g_pts; a.g_norm = g_pts_norm; a.g_pair = g_pair;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dq_pts = dq_pts; a.dk_pts = dk_pts; a.dv_pts = dv_pts;
+  a.drot = drot; a.dtrans = dtrans; a.dz1 = dz1; a.dz2 = dz2; a.dw_b = dw_b; a.dgamma = dgamma;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float** slots[17] = {&a.QA, &a.KA, &a.VA, &a.GA, &a.QP, &a.KP, &a.Dv, &a.dQA, &a.U, &a.dQP, &a.gam,
+                       &a.LSE, &a.dKA, &a.dVA, &a.dKP, &a.fpart, &a.share};
+  for (int e = 0; e < 17; ++e) *slots[e] = reinterpret_cast<float*>(ws + ly.off[e]);
+  if (ipa::launch_backward(a, static_cast<hipStream_t>(stream)) != hipSuccess) return IPA_ERR_HIP;
+  return IPA_OK;
+}
+
 const char* ipa_status_string(int32_t status) {
   switch (status) {
     case IPA_OK: return "ok";

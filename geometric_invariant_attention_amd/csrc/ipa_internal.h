@@ -113,6 +113,31 @@ struct DDArgs {
   float* vectors; float* output; float* attention;
 };
 
+// ---------------------------------------------------------------------------
+// Gradient of the IPA forward (ipa_bwd.hip), float32
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+  int B, L, H, C, Pqk, Pv, R, Cz;
+  int DA, DV, P3;   // C + R Cz, C + 3 Pv + R Cz, 3 Pqk
+  float w_L, w_C;
+  const float* q; const float* k; const float* v;
+  const float* q_pts; const float* k_pts; const float* v_pts;
+  const float* rot; const float* trans;
+  const float* z1; const float* z2; const float* w_b; const float* gamma;
+  const uint8_t* mask;
+  const float* o_s; const float* o_pts; const float* o_pair;   // forward outputs
+  const float* g_s; const float* g_pts; const float* g_norm; const float* g_pair;
+  float* dq; float* dk; float* dv; float* dq_pts; float* dk_pts; float* dv_pts;
+  float* drot; float* dtrans; float* dz1; float* dz2; float* dw_b; float* dgamma;
+  // workspace, rows [B][H][L][...]
+  float* QA; float* KA; float* VA; float* GA; float* QP; float* KP; float* Dv;
+  float* dQA; float* U; float* dQP; float* gam; float* LSE;
+  float* dKA; float* dVA; float* dKP;
+  float* fpart;   // [B][L][H][12]  per-head frame gradient shares
+  float* share;   // [B][L][Cz H + H] per-residue shares of dW_b and dgamma
+};
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+
 int dd_splits(int B, int N, int H);
 int dd_padded_keys(int N);
 hipError_t launch_dirdist(const DDArgs& a, hipStream_t s);

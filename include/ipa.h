@@ -202,6 +202,42 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Gradient of ipa_forward (float32 path).
+ * Training goes through this attention ("Flash Invariant Point Attention",
+ * abstract: training at previously unattainable lengths). For output
+ * cotangents g_s, g_pts, g_pts_norm, g_pair this returns the gradient of
+ *   sum <g_s, out_s> + <g_pts, out_pts> + <g_pts_norm, out_pts_norm> + <g_pair, out_pair>
+ * with respect to every input of ipa_forward, computed FlashAttention-2
+ * style on the lifted rows (nothing of size L x L is stored):
+ *   inputs        as ipa_forward (IPA_F32 storage only), mask may be NULL
+ *   out_s, out_pts, out_pair   the forward's outputs for these inputs
+ *   g_*           cotangents, shaped like the outputs
+ *   dq, dk, dv [B,L,H,C]; dq_pts, dk_pts [B,L,H,Pqk,3]; dv_pts [B,L,H,Pv,3];
+ *   drot [B,L,3,3]; dtrans [B,L,3]; dz1, dz2 [B,L,R,Cz]; dw_b [Cz,H];
+ *   dgamma [H]: every element overwritten (float32).
+ * The derivative of |out_pts| at 0 is taken as 0. Rows whose mask entry is
+ * 0 pass no gradient and receive none. Supported envelope: C <= 16,
+ * Pqk <= 5, Pv <= 8, R*Cz <= 256, B*H <= 65535. Pointers 4-byte aligned,
+ * workspace ipa_backward_workspace_bytes(dims) bytes, 256-byte aligned.
+ * Deterministic: repeated calls give identical bits. */
+size_t ipa_backward_workspace_bytes(const ipa_dims* dims);
+int32_t ipa_backward(const ipa_dims* dims,
+                     const float* q, const float* k, const float* v,
+                     const float* q_pts, const float* k_pts, const float* v_pts,
+                     const float* rot, const float* trans,
+                     const float* z1, const float* z2,
+                     const float* w_b, const float* gamma,
+                     const uint8_t* mask, float w_L, float w_C,
+                     const float* out_s, const float* out_pts, const float* out_pair,
+                     const float* g_s, const float* g_pts, const float* g_pts_norm,
+                     const float* g_pair,
+                     float* dq, float* dk, float* dv,
+                     float* dq_pts, float* dk_pts, float* dv_pts,
+                     float* drot, float* dtrans, float* dz1, float* dz2,
+                     float* dw_b, float* dgamma,
+                     void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* Geometric direction-and-distance attention (ESM3-style).
  * "Geometric direction-and-distance attention" (BioTorch), Required
  * behavior. Per batch b, head h, query i and key j, with frames (R, t) that

@@ -29,7 +29,8 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["ipa_attend", "ipa_dirdist_forward", "ipa_dirdist_workspace_bytes",
+    assert names == ["ipa_attend", "ipa_backward", "ipa_backward_workspace_bytes",
+                     "ipa_dirdist_forward", "ipa_dirdist_workspace_bytes",
                      "ipa_forward", "ipa_frames_from_atoms", "ipa_lift",
                      "ipa_meet_forward", "ipa_meet_workspace_bytes", "ipa_status_string",
                      "ipa_version", "ipa_workspace_bytes"]
@@ -218,3 +219,35 @@ def test_dirdist_workspace_linear_in_N(lib):
     per = [ws(n) / n for n in (64, 256, 1024, 2048, 4096, 8192)]
     assert max(per) <= 3 * per[-1]
     assert lib.ipa_dirdist_workspace_bytes(ctypes.byref(bd.IpaDirDistDims(1, 64, 4, 9, 16))) == 0
+
+
+def test_backward_rejects_before_launch(lib):
+    good = bd.make_dims(1, 64, 4, 16, 4, 8, 2, 16)
+    ptrs = [0x1000 * (n + 1) for n in range(33)]
+
+    def call(dims, p=ptrs, mask=0, wl=1.0, wc=1.0, ws_bytes=1 << 34, ws=0x100000):
+        return lib.ipa_backward(ctypes.byref(dims) if dims is not None else None, *p[:12], mask,
+                                ctypes.c_float(wl), ctypes.c_float(wc), *p[12:31], ws,
+                                ctypes.c_size_t(ws_bytes), None)
+    assert call(None) == -1
+    assert call(bd.make_dims(1, 0, 4, 16, 4, 8, 2, 16)) == -2
+    assert call(bd.make_dims(1, 64, 4, 32, 4, 8, 2, 16)) == -6       # C > 16
+    assert call(bd.make_dims(1, 64, 4, 16, 4, 8, 4, 128)) == -6      # R Cz > 256
+    for k in range(31):
+        p = list(ptrs)
+        p[k] = 0
+        assert call(good, p) == -1, k
+    p = list(ptrs)
+    p[5] += 2
+    assert call(good, p) == -5
+    assert call(good, ws=0x100010) == -5
+    assert call(good, wl=float("nan")) == -8
+    need = lib.ipa_backward_workspace_bytes(ctypes.byref(good))
+    assert need > 0 and call(good, ws_bytes=need - 1) == -4
+
+
+def test_backward_workspace_linear_in_L(lib):
+    def ws(L):
+        return lib.ipa_backward_workspace_bytes(ctypes.byref(bd.make_dims(1, L, 12, 16, 4, 8, 2, 128)))
+    a, b, c = ws(1024), ws(2048), ws(4096)
+    assert a > 0 and abs((c - b) - 2 * (b - a)) <= 17 * 256

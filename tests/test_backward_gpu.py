@@ -1,0 +1,105 @@
+"""GPU parity of the IPA gradient (ipa_backward, float32) against the fp64
+gradient oracle, through the C ABI.
+
+The forward outputs handed to the backward are the GPU forward's own
+(float32 path), as in training. Tolerance per gradient tensor: max-abs
+error <= 2e-4 x max(1, max |reference|). The float32 path rounds the
+forward outputs (which enter D_i = dO . O) and every dot product of ~300
+terms at about 1e-6 relative; the softmax derivative subtracts D_i from
+dP_ij, terms of similar size, which can lose one or two more digits.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ipa_backward as oracle_backward
+from workloads import WORKLOADS, make_inputs, stress_pair
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+NAMES = ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2", "w_b", "gamma")
+
+
+def _cotangents(inp, seed):
+    d = inp["dims"]
+    rng = np.random.default_rng(seed)
+    B, L, H = d["B"], d["L"], d["H"]
+    return {"s": rng.standard_normal((B, L, H, d["C"])).astype(np.float32),
+            "pts": rng.standard_normal((B, L, H, d["Pv"], 3)).astype(np.float32),
+            "pts_norm": rng.standard_normal((B, L, H, d["Pv"])).astype(np.float32),
+            "pair": rng.standard_normal((B, L, H, d["Cz"])).astype(np.float32)}
+
+
+def _gpu_backward(inp, g, device):
+    from geometric_invariant_attention_amd import IPABackward, IPAForward
+    d = inp["dims"]
+    t = {n: torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).to(device) for n in NAMES}
+    m = torch.from_numpy(inp["mask"]).to(device) if inp.get("has_mask") else None
+    fwd = IPAForward(**d, dtype=torch.float32, device=device)
+    out = fwd(*(t[n] for n in NAMES), mask=m, w_L=inp["w_L"], w_C=inp["w_C"])
+    gt = {k: torch.from_numpy(v).to(device) for k, v in g.items()}
+    bwd = IPABackward(**d, device=device)
+    grads = bwd(t, {"s": out["s"], "pts": out["pts"], "pair": out["pair"]}, gt, mask=m,
+                w_L=inp["w_L"], w_C=inp["w_C"])
+    torch.cuda.synchronize()
+    return {n: grads[n].cpu().numpy().copy() for n in NAMES}
+
+
+def _check(w, device, seed=0, stress=False):
+    print(f"[backward] {w.name} dims={w.dims()} seed={seed} stress={stress}", flush=True)
+    inp = make_inputs(w, seed=seed)
+    if stress:
+        inp = stress_pair(inp)
+    g = _cotangents(inp, seed + 100)
+    got = _gpu_backward(inp, g, device)
+    ref = oracle_backward(inp, g)
+    errs = {}
+    for n in NAMES:
+        assert np.isfinite(got[n]).all(), n
+        scale = max(1.0, float(np.abs(ref[n]).max()))
+        errs[n] = float(np.abs(got[n] - ref[n]).max()) / scale
+    print("  rel errors", {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
+    assert max(errs.values()) < TOL, errs
+    return inp, got, ref
+
+
+@pytest.mark.parametrize("L", [1, 7, 16, 33, 64])
+def test_backward_small(device, L):
+    _check(WORKLOADS["tiny_fp32"].with_(L=L, H=3), device, seed=L)
+
+
+def test_backward_tiny_full_heads(device):
+    _check(WORKLOADS["tiny_fp32"], device)
+
+
+def test_backward_pair_stress(device):
+    _check(WORKLOADS["tiny_fp32"].with_(L=48, H=4), device, seed=3, stress=True)
+
+
+def test_backward_ragged_batch(device):
+    inp, got, ref = _check(WORKLOADS["ragged_batch"].with_(B=4, L=40, H=3, Cz=16, ragged=(17, 40),
+                                                           dtype="fp32"), device, seed=4)
+    pad = inp["mask"] == 0
+    for n in ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2"):
+        assert np.all(got[n][pad] == 0), n
+
+
+@pytest.mark.parametrize("dims", [dict(C=8, Pqk=3, Pv=5, R=1, Cz=24), dict(C=16, Pqk=5, Pv=8, R=2, Cz=64)])
+def test_backward_other_shapes(device, dims):
+    _check(WORKLOADS["tiny_fp32"].with_(L=37, H=2, **dims), device, seed=9)
+
+
+def test_backward_chain_256(device):
+    _check(WORKLOADS["tiny_fp32"].with_(L=256, H=4), device, seed=11)
+
+
+def test_backward_deterministic(device):
+    w = WORKLOADS["tiny_fp32"].with_(L=40, H=3)
+    inp = make_inputs(w, seed=1)
+    g = _cotangents(inp, 2)
+    a = _gpu_backward(inp, g, device)
+    b = _gpu_backward(inp, g, device)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), n
