@@ -350,6 +350,84 @@ def bench_dirdist(dev, steps: int, warmup: int, cpu: bool) -> dict:
     return out
 
 
+def backward_flops_per_pair(d: dict) -> int:
+    """Algorithmic fp32 operations of the gradient per (query, key, head):
+    both passes recompute the logit (2 DA for the lifted dot, 3 per point
+    coordinate for difference, square and sum) and dP (2 DV); the dQ pass
+    accumulates dS KA (2 DA), A z2 (2 R Cz), the point differences (3 per
+    coordinate) and the gamma term (2); the dK/dV pass accumulates dS QA
+    (2 DA), A dO (2 DV) and the point differences (3 per coordinate)."""
+    DA = d["C"] + d["R"] * d["Cz"]
+    DV = d["C"] + 3 * d["Pv"] + d["R"] * d["Cz"]
+    P3 = 3 * d["Pqk"]
+    logit = 2 * DA + 3 * P3 + 2 * DV
+    return 2 * logit + (2 * DA + 2 * d["R"] * d["Cz"] + 3 * P3 + 2) + (2 * DA + 2 * DV + 3 * P3)
+
+
+def bench_backward(dev, steps: int, warmup: int, cpu: bool) -> dict:
+    """Gradient of the IPA forward (ipa_backward, float32) at the
+    long_chain_2048 dimensions: the forward outputs come from the forward
+    kernels on the same inputs (float32 copies of the bf16 workload), the
+    cotangents are N(0, 1). Timed between HIP events over back-to-back
+    calls; the fp64 oracle is timed on a 256-residue chain of the same
+    dimensions and scaled per pair."""
+    import numpy as np
+    import torch
+    from geometric_invariant_attention_amd import IPABackward, IPAForward
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["long_chain_2048"]
+    inp = make_inputs(w)
+    d = w.dims()
+    names = ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2", "w_b", "gamma")
+    t = {n: torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).to(dev) for n in names}
+    fwd = IPAForward(**d, dtype=torch.bfloat16, device=dev)
+    out = fwd(*(t[n].to(torch.bfloat16) if n not in ("rot", "trans", "w_b", "gamma") else t[n] for n in names),
+              w_L=inp["w_L"], w_C=inp["w_C"])
+    rng = np.random.default_rng(5)
+    g = {"s": (d["B"], d["L"], d["H"], d["C"]), "pts": (d["B"], d["L"], d["H"], d["Pv"], 3),
+         "pts_norm": (d["B"], d["L"], d["H"], d["Pv"]), "pair": (d["B"], d["L"], d["H"], d["Cz"])}
+    g = {k: torch.from_numpy(rng.standard_normal(v).astype(np.float32)).to(dev) for k, v in g.items()}
+    bwd = IPABackward(**d, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    raw = bwd.bind(t, {"s": out["s"], "pts": out["pts"], "pair": out["pair"]}, g,
+                   w_L=inp["w_L"], w_C=inp["w_C"], stream=stream)
+    nw = max(2, warmup // 20)
+    for _ in range(nw):
+        bwd.backward_raw(raw)
+    torch.cuda.synchronize(dev)
+    n = max(2, steps // 10)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(n):
+        bwd.backward_raw(raw)
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    ms = ev[0].elapsed_time(ev[1]) / n
+    pairs = d["B"] * d["L"] * d["L"]
+    flops = backward_flops_per_pair(d) * pairs * d["H"]
+    ach = flops / (ms * 1e-3) / 1e12
+    res = {"workload": w.name, "config": {**d, "storage": "fp32"}, "calls": n, "ms_per_call": ms,
+           "pairs_per_s": pairs / (ms * 1e-3),
+           "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                        "frac": ach / PEAK_FP32_VECTOR_TFLOPS, "flops_per_call": flops,
+                        "note": "whole gradient (7 kernels) timed"}}
+    if cpu:
+        from oracle import ipa_backward as oracle_backward
+        ws = w.with_(L=256)
+        ci = make_inputs(ws)
+        cg = {k: np.random.default_rng(1).standard_normal(
+            (ws.B, ws.L) + tuple(v.shape[2:])) for k, v in g.items()}
+        c0, w0 = time.process_time(), time.perf_counter()
+        oracle_backward(ci, cg)
+        wall = time.perf_counter() - w0
+        res["cpu_baseline"] = {"value": ws.B * ws.L * ws.L / wall, "unit": "pairs/s",
+                               "cores": max(1, round((time.process_time() - c0) / max(wall, 1e-9))),
+                               "kind": "oracle",
+                               "sample": f"fp64 autograd oracle on a {ws.L}-residue chain with the same H, C, "
+                                         f"points and pair factors, {wall:.1f} s wall, scaled per pair"}
+    return res
+
+
 def memory_sweep(dev, Ls, H=12, Cz=128):
     """Peak device memory (inputs + outputs + workspace) of one forward."""
     import torch
@@ -484,6 +562,8 @@ def main(argv=None) -> int:
     print(f"[bench] distance attention: {result['meet']['ms_per_call'] * 1e3:.1f} us/call, "
           f"{result['meet']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     result["frames"] = bench_frames(dev, args.steps, 20, args.cpu_budget > 0)
+    print("[bench] backward", file=sys.stderr, flush=True)
+    result["backward"] = bench_backward(dev, args.steps, args.warmup, args.cpu_budget > 0)
     print("[bench] direction-and-distance attention", file=sys.stderr, flush=True)
     result["dirdist"] = bench_dirdist(dev, args.steps, args.warmup, args.cpu_budget > 0)
     print(f"[bench] frames: {result['frames']['ms_per_call'] * 1e3:.1f} us/call, "
