@@ -33,6 +33,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # MI355X fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed
 # fp32) x 2.4 GHz. Code built without packed fp32 issues at most half of it.
 PEAK_FP32_VECTOR_TFLOPS = 157.3
+PEAK_FP32_MFMA_TFLOPS = 157.3    # MI355X dense fp32 matrix peak
 METRIC = "IPA fwd pairs/s & TFLOP/s (% bf16 MFMA peak) at L=2048; peak HBM GB vs L"
 
 
@@ -351,17 +352,16 @@ def bench_dirdist(dev, steps: int, warmup: int, cpu: bool) -> dict:
 
 
 def backward_flops_per_pair(d: dict) -> int:
-    """Algorithmic fp32 operations of the gradient per (query, key, head):
-    both passes recompute the logit (2 DA for the lifted dot, 3 per point
-    coordinate for difference, square and sum) and dP (2 DV); the dQ pass
-    accumulates dS KA (2 DA), A z2 (2 R Cz), the point differences (3 per
-    coordinate) and the gamma term (2); the dK/dV pass accumulates dS QA
-    (2 DA), A dO (2 DV) and the point differences (3 per coordinate)."""
+    """Algorithmic fp32 operations of the gradient per (query, key, head),
+    each product or sum counted once: the logit's lifted dot (2 DA) and point
+    term (3 per coordinate + 2), dP (2 DV), the softmax and dS (4), then
+    dS KA' (2 (DA + 3Pqk)), A z2 (2 R Cz), dS^T QA' (2 (DA + 3Pqk + 1)),
+    A^T GA (2 DV) and the gamma term (2)."""
     DA = d["C"] + d["R"] * d["Cz"]
     DV = d["C"] + 3 * d["Pv"] + d["R"] * d["Cz"]
     P3 = 3 * d["Pqk"]
-    logit = 2 * DA + 3 * P3 + 2 * DV
-    return 2 * logit + (2 * DA + 2 * d["R"] * d["Cz"] + 3 * P3 + 2) + (2 * DA + 2 * DV + 3 * P3)
+    return (2 * DA + 3 * P3 + 2 + 2 * DV + 4 + 2 * (DA + P3) + 2 * d["R"] * d["Cz"]
+            + 2 * (DA + P3 + 1) + 2 * DV + 2)
 
 
 def bench_backward(dev, steps: int, warmup: int, cpu: bool) -> dict:
@@ -408,9 +408,10 @@ def bench_backward(dev, steps: int, warmup: int, cpu: bool) -> dict:
     ach = flops / (ms * 1e-3) / 1e12
     res = {"workload": w.name, "config": {**d, "storage": "fp32"}, "calls": n, "ms_per_call": ms,
            "pairs_per_s": pairs / (ms * 1e-3),
-           "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
-                        "frac": ach / PEAK_FP32_VECTOR_TFLOPS, "flops_per_call": flops,
-                        "note": "whole gradient (7 kernels) timed"}}
+           "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                        "frac": ach / PEAK_FP32_MFMA_TFLOPS, "flops_per_call": flops,
+                        "note": "whole gradient timed (preparation, 6 fp32 matrix-core GEMMs and a row "
+                                "kernel per query chunk, chain rule)"}}
     if cpu:
         from oracle import ipa_backward as oracle_backward
         ws = w.with_(L=256)

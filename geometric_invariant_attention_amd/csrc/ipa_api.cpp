@@ -302,7 +302,16 @@ namespace {
 struct BwdLayout {
   size_t off[17];
   size_t total;
+  int QC;
 };
+
+// query rows per chunk: the two score buffers hold at most 2^26 floats each
+int bwd_chunk(int64_t BH, int64_t L) {
+  int64_t qc = (int64_t(1) << 26) / (BH * L);
+  if (qc >= L) return (int)L;
+  qc = qc / 64 * 64;
+  return (int)(qc < 64 ? 64 : qc);
+}
 
 bool bwd_layout(const ipa_dims* d, BwdLayout* o) {
   if (!d) return false;
@@ -311,11 +320,15 @@ bool bwd_layout(const ipa_dims* d, BwdLayout* o) {
   if (C > 16 || P > 5 || Pv > 8 || R * Cz > 256) return false;
   if (B * H > 65535 || B * L * H * 296 >= (int64_t(1) << 31) || B * L * (Cz * H + H) >= (int64_t(1) << 31))
     return false;
+  const int QC = bwd_chunk(B * H, L);
+  if (B * H * (int64_t)QC * L >= (int64_t(1) << 31)) return false;
+  o->QC = QC;
   const size_t rows = (size_t)(B * H * L), DA = (size_t)(C + R * Cz), DV = (size_t)(C + 3 * Pv + R * Cz);
-  const size_t sizes[17] = {rows * DA, rows * DA, rows * DV, rows * DV, rows * 3 * P, rows * 3 * P, rows,
-                            rows * DA, rows * R * Cz, rows * 3 * P, rows, rows,
-                            rows * DA, rows * DV, rows * 3 * P,
-                            (size_t)(B * L * H) * 12, (size_t)(B * L) * (size_t)(Cz * H + H)};
+  const size_t P3 = (size_t)(3 * P), DAQ = DA + P3 + 1, DAK = DA + P3, xs = (size_t)(B * H) * QC * L;
+  const size_t sizes[17] = {rows * DAQ, rows * DAK, rows * DV, rows * DV, rows * P3, rows * P3, rows,
+                            rows * DAK, rows * R * Cz, rows, rows,
+                            rows * DAQ, rows * DV,
+                            (size_t)(B * L * H) * 12, (size_t)(B * L) * (size_t)(Cz * H + H), xs, xs};
   size_t off = 0;
   for (int e = 0; e < 17; ++e) {
     o->off[e] = off;
@@ -363,6 +376,7 @@ int32_t ipa_backward(const ipa_dims* dims, const float* q, const float* k, const
   a.B = dims->B; a.L = dims->L; a.H = dims->H; a.C = dims->C; a.Pqk = dims->Pqk; a.Pv = dims->Pv;
   a.R = dims->R; a.Cz = dims->Cz;
   a.DA = a.C + a.R * a.Cz; a.DV = a.C + 3 * a.Pv + a.R * a.Cz; a.P3 = 3 * a.Pqk;
+  a.DAQ = a.DA + a.P3 + 1; a.DAK = a.DA + a.P3; a.QC = ly.QC;
   a.w_L = w_L; a.w_C = w_C;
   a.q = q; a.k = k; a.v = v; a.q_pts = q_pts; a.k_pts = k_pts; a.v_pts = v_pts;
   a.rot = rot; a.trans = trans; a.z1 = z1; a.z2 = z2; a.w_b = w_b; a.gamma = gamma; a.mask = mask;
@@ -371,8 +385,8 @@ int32_t ipa_backward(const ipa_dims* dims, const float* q, const float* k, const
   a.dq = dq; a.dk = dk; a.dv = dv; a.dq_pts = dq_pts; a.dk_pts = dk_pts; a.dv_pts = dv_pts;
   a.drot = drot; a.dtrans = dtrans; a.dz1 = dz1; a.dz2 = dz2; a.dw_b = dw_b; a.dgamma = dgamma;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float** slots[17] = {&a.QA, &a.KA, &a.VA, &a.GA, &a.QP, &a.KP, &a.Dv, &a.dQA, &a.U, &a.dQP, &a.gam,
-                       &a.LSE, &a.dKA, &a.dVA, &a.dKP, &a.fpart, &a.share};
+  float** slots[17] = {&a.QA, &a.KA, &a.VA, &a.GA, &a.QP, &a.KP, &a.Dv, &a.dQA, &a.U, &a.gam,
+                       &a.rsum, &a.dKA, &a.dVA, &a.fpart, &a.share, &a.X, &a.Y};
   for (int e = 0; e < 17; ++e) *slots[e] = reinterpret_cast<float*>(ws + ly.off[e]);
   if (ipa::launch_backward(a, static_cast<hipStream_t>(stream)) != hipSuccess) return IPA_ERR_HIP;
   return IPA_OK;

@@ -11,7 +11,7 @@
 //   O_i   = sum_j A_ij VA_j,   VA_j = [ v_j | Vg_jp | z2_jr ]
 // and the four outputs are o_s = O_s, o_pts = R_i^T (O_pts - t_i),
 // |o_pts|, o_pair = sum_r z1_ir * O_pair_r. The backward is that of a
-// softmax attention (FlashAttention-2 style, nothing O(L^2) is stored):
+// softmax attention, taken query chunk by query chunk:
 //   GA_i  = [ g_s | R_i g_tot_ip | z1_ir * g_pair ]     (dO of the lifted rows,
 //           g_tot = g_pts + g_norm o_pts / |o_pts|, 0 at o_pts = 0)
 //   D_i   = GA_i . O_i  = g_s.o_s + sum_p (R g_tot).(R o_pts + t) + g_pair.o_pair
@@ -22,32 +22,35 @@
 //   U_i   = sum_j A_ij z2_jr   (the pair output before z1, for dz1)
 // then the chain rule through the lifting and the frames, per residue.
 //
-// Stages (one stream; workspace linear in B * L):
-//   bwd_prep    per (b, i, h): QA, KA, VA, GA, Qg, Kg rows and D_i.
-//   bwd_dq      per (b, h, 16 queries): over key tiles, S and dP for a
-//               16 x 16 tile (one pair per thread), the running maximum and
-//               sum of the softmax (online, as in the forward), and the
-//               accumulations dQA, U, the query point term and the gamma
-//               term, rescaled with the running maximum; writes them and
-//               the row log-sum-exp.
-//   bwd_dkv     per (b, h, 16 keys): over query tiles, A from the saved
-//               log-sum-exp, dS, and the accumulations dKA, dVA and the key
-//               point term.
+// Stages (one stream):
+//   bwd_prep    per (b, i, h): the lifted rows QA' = [QA | Qg | 1],
+//               KA' = [KA | Kg], VA, GA, the points and D_i.
+//   per chunk of QC query rows (QC bounds the two score buffers to
+//   2 x 2^26 floats, so memory stays linear in L):
+//     gemm      S = QA KA^T and dP = GA VA^T (fp32 matrix cores)
+//     bwd_rows  per query row: the point term -kappa |Qg_i - Kg_j|^2 from
+//               explicit differences, the masked softmax A, dS, and the
+//               row sums of dS and of dS |Qg_i - Kg_j|^2
+//     gemm      dQA' = dS KA' (with sum_j dS Kg_j), U = A z2,
+//               dKA' += dS^T QA' (with sum_i dS Qg_i and the column sum),
+//               dVA += A^T GA
 //   bwd_post    per (b, i, h): dq, dk, dv, the point gradients through R,
 //               and this head's share of the frame gradient.
 //   bwd_z       per (b, i, c): dz1, dz2 (summed over heads) and the
 //               residue's share of dW_b and dgamma.
 //   bwd_frames  per (b, i): drot, dtrans (summed over heads).
 //   bwd_reduce  column sums of the shares: dW_b, dgamma (fixed order).
-// Float32 vector arithmetic throughout; the tiles live in LDS.
+// The point sums of dS against Qg, Kg come from the GEMMs and the
+// corrections Qg_i sum_j dS_ij, Kg_j sum_i dS_ij; the coordinates are a
+// few hundred A at most and the dS sums vanish up to rounding, so the
+// products lose no significant digits at float32.
 
 #include "ipa_internal.h"
 
 namespace ipa {
 namespace {
 
-constexpr int kT = 16;     // queries x keys per tile
-constexpr int kMaxDA = 272, kMaxDV = 296, kMaxP3 = 15;
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ void rot3(const float* R, const float* x, float* o) {
   o[0] = R[0] * x[0] + R[1] * x[1] + R[2] * x[2];
@@ -79,8 +82,8 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(BwdArgs a) {
   for (int c = 0; c < 9; ++c) R[c] = a.rot[bi * 9 + c];
   for (int c = 0; c < 3; ++c) T[c] = a.trans[bi * 3 + c];
   const float alpha = a.w_L / sqrtf((float)C);
-  float* qa = a.QA + row * a.DA;
-  float* ka = a.KA + row * a.DA;
+  float* qa = a.QA + row * a.DAQ;
+  float* ka = a.KA + row * a.DAK;
   float* va = a.VA + row * a.DV;
   float* ga = a.GA + row * a.DV;
   float* qp = a.QP + row * a.P3;
@@ -99,10 +102,11 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(BwdArgs a) {
   for (int p = 0; p < P; ++p) {
     float o[3];
     rot3(R, a.q_pts + (bih * P + p) * 3, o);
-    for (int x = 0; x < 3; ++x) qp[3 * p + x] = o[x] + T[x];
+    for (int x = 0; x < 3; ++x) qp[3 * p + x] = qa[a.DA + 3 * p + x] = o[x] + T[x];
     rot3(R, a.k_pts + (bih * P + p) * 3, o);
-    for (int x = 0; x < 3; ++x) kp[3 * p + x] = o[x] + T[x];
+    for (int x = 0; x < 3; ++x) kp[3 * p + x] = ka[a.DA + 3 * p + x] = o[x] + T[x];
   }
+  qa[a.DA + a.P3] = 1.f;   // dS^T times this column: the column sums of dS
   for (int p = 0; p < Pv; ++p) {
     float o[3];
     rot3(R, a.v_pts + (bih * Pv + p) * 3, o);
@@ -144,250 +148,161 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Shared tile evaluation: thread (r, c) of a 16 x 16 tile computes, for its
-// query row qi and key row kj, the logit S, the distance sum d and dP.
-struct PairOut { float s, d, dp; };
+// Batched fp32 GEMM on v_mfma_f32_32x32x2f32:
+//   C[z](m, n) = sum_k A[z](m, k) B[z](k, n)  (+ C[z](m, n) when acc)
+// with A(m, k) at A + z sAb + m am + k ak, B(k, n) at B + z sBb + k bk + n bn,
+// C(m, n) at C + z sCb + m cm + n. A workgroup of four waves owns a 64 x 64
+// tile (a 32 x 32 quadrant per wave); the reduction runs in steps of 16,
+// each step's A and B slices staged in LDS with loads along whichever of
+// their two strides is 1, the next step's loads in flight in registers
+// while this step's 8 products per wave run.
+// ---------------------------------------------------------------------------
+struct Gemm {
+  int M, N, K;
+  const float* A; long long sAb, am, ak;
+  const float* B; long long sBb, bk, bn;
+  float* C; long long sCb, cm;
+  int acc;
+};
 
-__device__ __forceinline__ PairOut pair_eval(const float* qa, const float* ka, const float* qp,
-                                             const float* kp, const float* ga, const float* va,
-                                             int DA, int DV, int P3, float kappa) {
-  float s = 0.f, d = 0.f, dp = 0.f;
-  for (int c = 0; c < DA; ++c) s = fmaf(qa[c], ka[c], s);
-  for (int c = 0; c < P3; ++c) {
-    const float e = qp[c] - kp[c];
-    d = fmaf(e, e, d);
+__global__ __launch_bounds__(256) void gemm_kernel(Gemm g) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wn = w >> 1, half = lane >> 5, l32 = lane & 31;
+  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64, z = blockIdx.z;
+  const float* A = g.A + (size_t)z * g.sAb;
+  const float* B = g.B + (size_t)z * g.sBb;
+  __shared__ float As[16][64 + 4], Bs[16][64 + 4];
+  // element u of this thread's share of the A slice (64 m x 16 k) and of
+  // the B slice (16 k x 64 n), chosen so that consecutive threads read
+  // consecutive addresses
+  const bool a_k1 = g.ak == 1, b_n1 = g.bn == 1;
+  auto a_mk = [&](int u, int& m, int& k) {
+    const int e = tid + 256 * u;
+    if (a_k1) { k = e & 15; m = e >> 4; } else { m = e & 63; k = e >> 6; }
+  };
+  auto b_kn = [&](int u, int& k, int& n) {
+    const int e = tid + 256 * u;
+    if (b_n1) { n = e & 63; k = e >> 6; } else { k = e & 15; n = e >> 4; }
+  };
+  float ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int m, k;
+      a_mk(u, m, k);
+      const int gm = m0 + m, gk = k0 + k;
+      ra[u] = (gm < g.M && gk < g.K) ? A[(size_t)gm * g.am + (size_t)gk * g.ak] : 0.f;
+      int kb, n;
+      b_kn(u, kb, n);
+      const int gkb = k0 + kb, gn = n0 + n;
+      rb[u] = (gkb < g.K && gn < g.N) ? B[(size_t)gkb * g.bk + (size_t)gn * g.bn] : 0.f;
+    }
+  };
+  gload(0);
+  floatx16 c = {};
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int m, k, kb, n;
+      a_mk(u, m, k);
+      b_kn(u, kb, n);
+      As[k][m] = ra[u];
+      Bs[kb][n] = rb[u];
+    }
+    __syncthreads();
+    if (k0 + 16 < g.K) gload(k0 + 16);
+    __builtin_amdgcn_sched_barrier(0);   // the next step's loads go out before the products
+    float av[8], bv[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      av[s2] = As[2 * s2 + half][32 * wm + l32];
+      bv[s2] = Bs[2 * s2 + half][32 * wn + l32];
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s2], bv[s2], c, 0, 0, 0);
+    __syncthreads();
   }
-  for (int c = 0; c < DV; ++c) dp = fmaf(ga[c], va[c], dp);
-  return {fmaf(-kappa, d, s), d, dp};
+  float* C = g.C + (size_t)z * g.sCb;
+  const int n = n0 + 32 * wn + l32;
+  if (n >= g.N) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int m = m0 + 32 * wm + 8 * (e >> 2) + 4 * half + (e & 3);
+    if (m < g.M) {
+      float* dst = C + (size_t)m * g.cm + n;
+      *dst = g.acc ? *dst + c[e] : c[e];
+    }
+  }
+}
+
+hipError_t gemm(const Gemm& g, int batch, hipStream_t s) {
+  const dim3 grid((g.M + 63) / 64, (g.N + 63) / 64, batch);
+  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, g);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
-  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
-  const int H = a.H, L = a.L, DA = a.DA, DV = a.DV, P3 = a.P3, C = a.C, RCz = a.R * a.Cz;
-  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
-  const int i0 = blockIdx.x * kT;
-  const float kappa = a.w_L * a.gamma[h] * a.w_C * 0.5f;
-  __shared__ float qa[kT][kMaxDA + 1], ga[kT][kMaxDV + 1], qp[kT][kMaxP3 + 1];
-  __shared__ float ka[kT][kMaxDA + 1], va[kT][kMaxDV + 1], kp[kT][kMaxP3 + 1];
-  __shared__ float st[kT][kT + 1], dpt[kT][kT + 1], dd[kT][kT + 1], ps[kT][kT + 1], dsd[kT][kT + 1];
-  __shared__ float frow[kT], Dq[kT];
-  __shared__ int qv[kT], kv[kT];
-  const size_t base = (size_t)bh * L;
-  for (int e = tid; e < kT * DA; e += 256) {
-    const int r = e / DA, c = e - r * DA, i = i0 + r;
-    qa[r][c] = i < L ? a.QA[(base + i) * DA + c] : 0.f;
-  }
-  for (int e = tid; e < kT * DV; e += 256) {
-    const int r = e / DV, c = e - r * DV, i = i0 + r;
-    ga[r][c] = i < L ? a.GA[(base + i) * DV + c] : 0.f;
-  }
-  for (int e = tid; e < kT * P3; e += 256) {
-    const int r = e / P3, c = e - r * P3, i = i0 + r;
-    qp[r][c] = i < L ? a.QP[(base + i) * P3 + c] : 0.f;
-  }
-  if (tid < kT) {
-    const int i = i0 + tid;
-    qv[tid] = i < L && row_valid(a, b, i);
-    Dq[tid] = i < L ? a.Dv[base + i] : 0.f;
-  }
-  // accumulators of row tr: dQA channels tc + 16 k, U channels tc + 16 k,
-  // point channel tc (tc < P3), gamma term (tc == 15)
-  float accA[(kMaxDA + 15) / 16], accU[256 / 16], accP = 0.f, accG = 0.f;
-  for (int k = 0; k < (kMaxDA + 15) / 16; ++k) accA[k] = 0.f;
-  for (int k = 0; k < 16; ++k) accU[k] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;   // used by threads tid < 16 (row tid)
-  for (int j0 = 0; j0 < L; j0 += kT) {
-    __syncthreads();
-    for (int e = tid; e < kT * DA; e += 256) {
-      const int r = e / DA, c = e - r * DA, j = j0 + r;
-      ka[r][c] = j < L ? a.KA[(base + j) * DA + c] : 0.f;
-    }
-    for (int e = tid; e < kT * DV; e += 256) {
-      const int r = e / DV, c = e - r * DV, j = j0 + r;
-      va[r][c] = j < L ? a.VA[(base + j) * DV + c] : 0.f;
-    }
-    for (int e = tid; e < kT * P3; e += 256) {
-      const int r = e / P3, c = e - r * P3, j = j0 + r;
-      kp[r][c] = j < L ? a.KP[(base + j) * P3 + c] : 0.f;
-    }
-    if (tid < kT) {
-      const int j = j0 + tid;
-      kv[tid] = j < L && row_valid(a, b, j);
-    }
-    __syncthreads();
-    {
-      const PairOut po = pair_eval(qa[tr], ka[tc], qp[tr], kp[tc], ga[tr], va[tc], DA, DV, P3, kappa);
-      st[tr][tc] = (qv[tr] && kv[tc]) ? po.s : -INFINITY;
-      dd[tr][tc] = po.d;
-      dpt[tr][tc] = po.dp;
-    }
-    __syncthreads();
-    if (tid < kT) {
-      float cm = -INFINITY;
-      for (int j = 0; j < kT; ++j) cm = fmaxf(cm, st[tid][j]);
-      const float mn = fmaxf(m_run, cm);
-      const float f = m_run == -INFINITY ? 0.f : expf(m_run - mn);
-      float ls = 0.f;
-      for (int j = 0; j < kT; ++j) {
-        const float p = st[tid][j] == -INFINITY ? 0.f : expf(st[tid][j] - mn);
-        ps[tid][j] = p;
-        dsd[tid][j] = p * (dpt[tid][j] - Dq[tid]);
-        ls += p;
-      }
-      l_run = fmaf(l_run, f, ls);
-      m_run = mn;
-      frow[tid] = f;
-    }
-    __syncthreads();
-    const float f = frow[tr];
-    for (int k = 0; k < (kMaxDA + 15) / 16; ++k) {
-      const int c = tc + 16 * k;
-      if (c < DA) {
-        float v = accA[k] * f;
-        for (int j = 0; j < kT; ++j) v = fmaf(dsd[tr][j], ka[j][c], v);
-        accA[k] = v;
-      }
-    }
-    for (int k = 0; k < 16; ++k) {
-      const int c = tc + 16 * k;
-      if (c < RCz) {
-        float v = accU[k] * f;
-        for (int j = 0; j < kT; ++j) v = fmaf(ps[tr][j], ka[j][C + c], v);
-        accU[k] = v;
-      }
-    }
-    if (tc < P3) {
-      float v = accP * f;
-      for (int j = 0; j < kT; ++j) v = fmaf(dsd[tr][j], qp[tr][tc] - kp[j][tc], v);
-      accP = v;
-    }
-    if (tc == 15) {
-      float v = accG * f;
-      for (int j = 0; j < kT; ++j) v = fmaf(dsd[tr][j], dd[tr][j], v);
-      accG = v;
-    }
-  }
-  __syncthreads();
-  if (tid < kT) {
-    frow[tid] = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int i = i0 + tid;
-    if (i < L) a.LSE[base + i] = l_run > 0.f ? m_run + logf(l_run) : INFINITY;
-  }
-  __syncthreads();
-  const int i = i0 + tr;
-  if (i >= L) return;
-  const float inv = frow[tr];
-  const size_t row = base + i;
-  for (int k = 0; k < (kMaxDA + 15) / 16; ++k) {
-    const int c = tc + 16 * k;
-    if (c < DA) a.dQA[row * DA + c] = accA[k] * inv;
-  }
-  for (int k = 0; k < 16; ++k) {
-    const int c = tc + 16 * k;
-    if (c < RCz) a.U[row * RCz + c] = accU[k] * inv;
-  }
-  if (tc < P3) a.dQP[row * P3 + tc] = accP * inv;
-  if (tc == 15) a.gam[row] = accG * inv;
-}
-
+// bwd_rows: one wave per query row of the chunk. X holds S (without the
+// point term) and becomes A; Y holds dP and becomes dS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs a) {
-  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
-  const int H = a.H, L = a.L, DA = a.DA, DV = a.DV, P3 = a.P3;
-  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
-  const int j0 = blockIdx.x * kT;
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc) {
+  const int lane = threadIdx.x & 63, r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= qc) return;
+  const int bh = blockIdx.y, H = a.H, L = a.L, P3 = a.P3;
+  const int b = bh / H, h = bh - b * H, i = q0 + r;
   const float kappa = a.w_L * a.gamma[h] * a.w_C * 0.5f;
-  __shared__ float qa[kT][kMaxDA + 1], ga[kT][kMaxDV + 1], qp[kT][kMaxP3 + 1];
-  __shared__ float ka[kT][kMaxDA + 1], va[kT][kMaxDV + 1], kp[kT][kMaxP3 + 1];
-  __shared__ float pt[kT][kT + 1], dst[kT][kT + 1];
-  __shared__ float lse[kT], Dq[kT];
-  __shared__ int qv[kT], kv[kT];
-  const size_t base = (size_t)bh * L;
-  for (int e = tid; e < kT * DA; e += 256) {
-    const int r = e / DA, c = e - r * DA, j = j0 + r;
-    ka[r][c] = j < L ? a.KA[(base + j) * DA + c] : 0.f;
+  const size_t qrow = (size_t)bh * L + i;
+  float* X = a.X + ((size_t)bh * a.QC + r) * L;
+  float* Y = a.Y + ((size_t)bh * a.QC + r) * L;
+  const bool qv = row_valid(a, b, i);
+  float qp[15];
+  for (int c = 0; c < 15; ++c) qp[c] = c < P3 ? a.QP[qrow * P3 + c] : 0.f;
+  const float* KP = a.KP + (size_t)bh * L * P3;
+  auto dist = [&](int j) {
+    float d = 0.f;
+    for (int c = 0; c < P3; ++c) {
+      const float e = qp[c] - KP[(size_t)j * P3 + c];
+      d = fmaf(e, e, d);
+    }
+    return d;
+  };
+  // pass 1: running maximum and sum per lane
+  float m = -INFINITY, l = 0.f;
+  for (int j = lane; j < L; j += 64) {
+    if (!(qv && row_valid(a, b, j))) continue;
+    const float sj = fmaf(-kappa, dist(j), X[j]);
+    if (sj > m) { l = l * expf(m - sj) + 1.f; m = sj; }
+    else l += expf(sj - m);
   }
-  for (int e = tid; e < kT * DV; e += 256) {
-    const int r = e / DV, c = e - r * DV, j = j0 + r;
-    va[r][c] = j < L ? a.VA[(base + j) * DV + c] : 0.f;
+  // combine the lanes
+  float mw = m;
+  for (int o = 32; o > 0; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+  l = m == -INFINITY ? 0.f : l * expf(m - mw);
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float D = a.Dv[qrow];
+  // pass 2: A, dS and the row sums
+  float rs = 0.f, gs = 0.f;
+  for (int j = lane; j < L; j += 64) {
+    float p = 0.f, ds = 0.f;
+    if (qv && row_valid(a, b, j)) {
+      const float d = dist(j);
+      p = expf(fmaf(-kappa, d, X[j]) - mw) * inv;
+      ds = p * (Y[j] - D);
+      rs += ds;
+      gs = fmaf(ds, d, gs);
+    }
+    X[j] = p;
+    Y[j] = ds;
   }
-  for (int e = tid; e < kT * P3; e += 256) {
-    const int r = e / P3, c = e - r * P3, j = j0 + r;
-    kp[r][c] = j < L ? a.KP[(base + j) * P3 + c] : 0.f;
+  for (int o = 32; o > 0; o >>= 1) {
+    rs += __shfl_xor(rs, o);
+    gs += __shfl_xor(gs, o);
   }
-  if (tid < kT) {
-    const int j = j0 + tid;
-    kv[tid] = j < L && row_valid(a, b, j);
+  if (lane == 0) {
+    a.rsum[qrow] = rs;
+    a.gam[qrow] = gs;
   }
-  // accumulators of key row tr: dKA channels tc + 16 k, dVA channels tc + 16 k,
-  // point channel tc (tc < P3)
-  float accK[(kMaxDA + 15) / 16], accV[(kMaxDV + 15) / 16], accP = 0.f;
-  for (int k = 0; k < (kMaxDA + 15) / 16; ++k) accK[k] = 0.f;
-  for (int k = 0; k < (kMaxDV + 15) / 16; ++k) accV[k] = 0.f;
-  for (int i0 = 0; i0 < L; i0 += kT) {
-    __syncthreads();
-    for (int e = tid; e < kT * DA; e += 256) {
-      const int r = e / DA, c = e - r * DA, i = i0 + r;
-      qa[r][c] = i < L ? a.QA[(base + i) * DA + c] : 0.f;
-    }
-    for (int e = tid; e < kT * DV; e += 256) {
-      const int r = e / DV, c = e - r * DV, i = i0 + r;
-      ga[r][c] = i < L ? a.GA[(base + i) * DV + c] : 0.f;
-    }
-    for (int e = tid; e < kT * P3; e += 256) {
-      const int r = e / P3, c = e - r * P3, i = i0 + r;
-      qp[r][c] = i < L ? a.QP[(base + i) * P3 + c] : 0.f;
-    }
-    if (tid < kT) {
-      const int i = i0 + tid;
-      qv[tid] = i < L && row_valid(a, b, i);
-      lse[tid] = i < L ? a.LSE[base + i] : INFINITY;
-      Dq[tid] = i < L ? a.Dv[base + i] : 0.f;
-    }
-    __syncthreads();
-    {
-      // thread (tr, tc): key row tr, query row tc
-      const PairOut po = pair_eval(qa[tc], ka[tr], qp[tc], kp[tr], ga[tc], va[tr], DA, DV, P3, kappa);
-      const float p = (qv[tc] && kv[tr]) ? expf(po.s - lse[tc]) : 0.f;
-      pt[tr][tc] = p;
-      dst[tr][tc] = p * (po.dp - Dq[tc]);
-    }
-    __syncthreads();
-    for (int k = 0; k < (kMaxDA + 15) / 16; ++k) {
-      const int c = tc + 16 * k;
-      if (c < DA) {
-        float v = accK[k];
-        for (int i = 0; i < kT; ++i) v = fmaf(dst[tr][i], qa[i][c], v);
-        accK[k] = v;
-      }
-    }
-    for (int k = 0; k < (kMaxDV + 15) / 16; ++k) {
-      const int c = tc + 16 * k;
-      if (c < DV) {
-        float v = accV[k];
-        for (int i = 0; i < kT; ++i) v = fmaf(pt[tr][i], ga[i][c], v);
-        accV[k] = v;
-      }
-    }
-    if (tc < P3) {
-      float v = accP;
-      for (int i = 0; i < kT; ++i) v = fmaf(dst[tr][i], qp[i][tc] - kp[tr][tc], v);
-      accP = v;
-    }
-  }
-  const int j = j0 + tr;
-  if (j >= L) return;
-  const size_t row = base + j;
-  for (int k = 0; k < (kMaxDA + 15) / 16; ++k) {
-    const int c = tc + 16 * k;
-    if (c < DA) a.dKA[row * DA + c] = accK[k];
-  }
-  for (int k = 0; k < (kMaxDV + 15) / 16; ++k) {
-    const int c = tc + 16 * k;
-    if (c < DV) a.dVA[row * DV + c] = accV[k];
-  }
-  if (tc < P3) a.dKP[row * P3 + tc] = accP;
 }
 
 // ---------------------------------------------------------------------------
@@ -414,10 +329,12 @@ __global__ __launch_bounds__(64) void bwd_post_kernel(BwdArgs a) {
   const float alpha = a.w_L / sqrtf((float)C);
   const float kappa = a.w_L * a.gamma[h] * a.w_C * 0.5f;
   for (int c = 0; c < C; ++c) {
-    a.dq[bih * C + c] = alpha * a.dQA[row * a.DA + c];
-    a.dk[bih * C + c] = a.dKA[row * a.DA + c];
+    a.dq[bih * C + c] = alpha * a.dQA[row * a.DAK + c];
+    a.dk[bih * C + c] = a.dKA[row * a.DAQ + c];
     a.dv[bih * C + c] = a.dVA[row * a.DV + c];
   }
+  // sum_j dS_ij (Qg_i - Kg_j) and sum_i dS_ij (Qg_i - Kg_j) per coordinate
+  const float rsum = a.rsum[row], csum = a.dKA[row * a.DAQ + a.DA + a.P3];
   float dR[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, dT[3] = {0.f, 0.f, 0.f};
   // global-frame point gradient u of local point x: d(local) = R^T u,
   // dR += u x^T, dt += u
@@ -430,10 +347,16 @@ __global__ __launch_bounds__(64) void bwd_post_kernel(BwdArgs a) {
   };
   for (int p = 0; p < P; ++p) {
     float u[3], dl[3];
-    for (int x = 0; x < 3; ++x) u[x] = -2.f * kappa * a.dQP[row * a.P3 + 3 * p + x];
+    for (int x = 0; x < 3; ++x) {
+      const int c = 3 * p + x;
+      u[x] = -2.f * kappa * (a.QP[row * a.P3 + c] * rsum - a.dQA[row * a.DAK + a.DA + c]);
+    }
     through_frame(u, a.q_pts + (bih * P + p) * 3, dl);
     for (int x = 0; x < 3; ++x) a.dq_pts[(bih * P + p) * 3 + x] = dl[x];
-    for (int x = 0; x < 3; ++x) u[x] = 2.f * kappa * a.dKP[row * a.P3 + 3 * p + x];
+    for (int x = 0; x < 3; ++x) {
+      const int c = 3 * p + x;
+      u[x] = 2.f * kappa * (a.dKA[row * a.DAQ + a.DA + c] - a.KP[row * a.P3 + c] * csum);
+    }
     through_frame(u, a.k_pts + (bih * P + p) * 3, dl);
     for (int x = 0; x < 3; ++x) a.dk_pts[(bih * P + p) * 3 + x] = dl[x];
   }
@@ -482,11 +405,11 @@ __global__ __launch_bounds__(64) void bwd_z_kernel(BwdArgs a) {
     float d1 = 0.f, d2 = 0.f;
     for (int h = 0; h < H; ++h) {
       const size_t row = ((size_t)b * H + h) * L + i;
-      const float e = a.dQA[row * a.DA + C + rc];   // sum_j dS_ij z2_j
+      const float e = a.dQA[row * a.DAK + C + rc];   // sum_j dS_ij z2_j
       const float wb = a.w_b[(size_t)c * H + h];
       d1 = fmaf(a.w_L * wb, e, d1);
       d1 = fmaf(a.g_pair[((size_t)bi * H + h) * Cz + c], a.U[row * RCz + rc], d1);
-      d2 += a.dKA[row * a.DA + C + rc] + a.dVA[row * a.DV + C + 3 * Pv + rc];
+      d2 += a.dKA[row * a.DAQ + C + rc] + a.dVA[row * a.DV + C + 3 * Pv + rc];
       // dW_b[c, h] share: w_L z1_irc e_ihrc, summed over r
       if (r == 0) share[c * H + h] = 0.f;
       share[c * H + h] = fmaf(a.w_L * z1, e, share[c * H + h]);
@@ -538,11 +461,51 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   const unsigned g64 = (unsigned)((bih + 63) / 64);
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(g64), dim3(64), 0, s, a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  const dim3 gt((a.L + kT - 1) / kT, a.B * a.H);
-  hipLaunchKernelGGL(bwd_dq_kernel, gt, dim3(256), 0, s, a);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL(bwd_dkv_kernel, gt, dim3(256), 0, s, a);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  const int BH = a.B * a.H, L = a.L, RCz = a.R * a.Cz;
+  const long long rowsQ = (long long)L * a.DAQ, rowsK = (long long)L * a.DAK, rowsV = (long long)L * a.DV;
+  const long long xs = (long long)a.QC * L;
+  for (int q0 = 0; q0 < L; q0 += a.QC) {
+    const int qc = L - q0 < a.QC ? L - q0 : a.QC;
+    // S = QA KA^T (the first DA columns of both)
+    Gemm g{};
+    g.M = qc; g.N = L; g.K = a.DA;
+    g.A = a.QA + (size_t)q0 * a.DAQ; g.sAb = rowsQ; g.am = a.DAQ; g.ak = 1;
+    g.B = a.KA; g.sBb = rowsK; g.bk = 1; g.bn = a.DAK;
+    g.C = a.X; g.sCb = xs; g.cm = L; g.acc = 0;
+    if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+    // dP = GA VA^T
+    g.K = a.DV;
+    g.A = a.GA + (size_t)q0 * a.DV; g.sAb = rowsV; g.am = a.DV;
+    g.B = a.VA; g.sBb = rowsV; g.bk = 1; g.bn = a.DV;
+    g.C = a.Y;
+    if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(bwd_rows_kernel, dim3((qc + 3) / 4, BH), dim3(256), 0, s, a, q0, qc);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    // dQA' = dS KA' (rows q0 .. q0 + qc)
+    g.M = qc; g.N = a.DAK; g.K = L;
+    g.A = a.Y; g.sAb = xs; g.am = L; g.ak = 1;
+    g.B = a.KA; g.sBb = rowsK; g.bk = a.DAK; g.bn = 1;
+    g.C = a.dQA + (size_t)q0 * a.DAK; g.sCb = rowsK; g.cm = a.DAK; g.acc = 0;
+    if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+    // U = A z2
+    g.N = RCz;
+    g.A = a.X;
+    g.B = a.KA + a.C;
+    g.C = a.U + (size_t)q0 * RCz; g.sCb = (long long)L * RCz; g.cm = RCz;
+    if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+    // dKA' += dS^T QA' (all keys)
+    g.M = L; g.N = a.DAQ; g.K = qc;
+    g.A = a.Y; g.sAb = xs; g.am = 1; g.ak = L;
+    g.B = a.QA + (size_t)q0 * a.DAQ; g.sBb = rowsQ; g.bk = a.DAQ; g.bn = 1;
+    g.C = a.dKA; g.sCb = rowsQ; g.cm = a.DAQ; g.acc = q0 > 0;
+    if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+    // dVA += A^T GA
+    g.N = a.DV;
+    g.A = a.X;
+    g.B = a.GA + (size_t)q0 * a.DV; g.sBb = rowsV; g.bk = a.DV; g.bn = 1;
+    g.C = a.dVA; g.sCb = rowsV; g.cm = a.DV;
+    if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+  }
   hipLaunchKernelGGL(bwd_post_kernel, dim3(g64), dim3(64), 0, s, a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const long long biz = (long long)a.B * a.L * a.Cz;

@@ -119,6 +119,8 @@ struct DDArgs {
 struct BwdArgs {
   int B, L, H, C, Pqk, Pv, R, Cz;
   int DA, DV, P3;   // C + R Cz, C + 3 Pv + R Cz, 3 Pqk
+  int DAQ, DAK;     // DA + P3 + 1 (QA' = [QA | Qg | 1]), DA + P3 (KA' = [KA | Kg])
+  int QC;           // query rows per chunk of the score buffers
   float w_L, w_C;
   const float* q; const float* k; const float* v;
   const float* q_pts; const float* k_pts; const float* v_pts;
@@ -131,8 +133,9 @@ struct BwdArgs {
   float* drot; float* dtrans; float* dz1; float* dz2; float* dw_b; float* dgamma;
   // workspace, rows [B][H][L][...]
   float* QA; float* KA; float* VA; float* GA; float* QP; float* KP; float* Dv;
-  float* dQA; float* U; float* dQP; float* gam; float* LSE;
-  float* dKA; float* dVA; float* dKP;
+  float* dQA; float* U; float* gam; float* rsum;
+  float* dKA; float* dVA;
+  float* X; float* Y;   // [B H][QC][L] score buffers: S then A, dP then dS
   float* fpart;   // [B][L][H][12]  per-head frame gradient shares
   float* share;   // [B][L][Cz H + H] per-residue shares of dW_b and dgamma
 };

@@ -207,8 +207,9 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype,
  * abstract: training at previously unattainable lengths). For output
  * cotangents g_s, g_pts, g_pts_norm, g_pair this returns the gradient of
  *   sum <g_s, out_s> + <g_pts, out_pts> + <g_pts_norm, out_pts_norm> + <g_pair, out_pair>
- * with respect to every input of ipa_forward, computed FlashAttention-2
- * style on the lifted rows (nothing of size L x L is stored):
+ * with respect to every input of ipa_forward, computed on the lifted rows
+ * one chunk of query rows at a time (the chunk's scores, at most 2^26
+ * floats per buffer, are the only quadratic-size data):
  *   inputs        as ipa_forward (IPA_F32 storage only), mask may be NULL
  *   out_s, out_pts, out_pair   the forward's outputs for these inputs
  *   g_*           cotangents, shaped like the outputs

@@ -247,7 +247,16 @@ def test_backward_rejects_before_launch(lib):
 
 
 def test_backward_workspace_linear_in_L(lib):
+    """The per-row arrays grow linearly in L; the two score buffers of a
+    query chunk are capped at 2^26 floats each, so past the cap the whole
+    workspace grows at most linearly."""
     def ws(L):
         return lib.ipa_backward_workspace_bytes(ctypes.byref(bd.make_dims(1, L, 12, 16, 4, 8, 2, 128)))
-    a, b, c = ws(1024), ws(2048), ws(4096)
-    assert a > 0 and abs((c - b) - 2 * (b - a)) <= 17 * 256
+    sizes = {L: ws(L) for L in (1024, 4096, 8192, 16384, 32768, 65536)}
+    assert all(v > 0 for v in sizes.values())
+    for L in (4096, 8192, 16384, 32768):
+        assert sizes[2 * L] <= 2 * sizes[L]
+    # the score buffers never exceed 2 x 2^26 floats: past the cap, doubling
+    # L adds less than the per-row arrays of L more rows plus the buffers
+    grow = sizes[65536] - sizes[32768]
+    assert sizes[65536] <= 2 * grow + 2 * 4 * (1 << 26) + 17 * 256
