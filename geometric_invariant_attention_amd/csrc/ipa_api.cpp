@@ -300,7 +300,7 @@ int32_t ipa_dirdist_forward(const ipa_dirdist_dims* dims, const float* rot, cons
 namespace {
 
 struct BwdLayout {
-  size_t off[17];
+  size_t off[18];
   size_t total;
   int QC;
 };
@@ -325,12 +325,13 @@ bool bwd_layout(const ipa_dims* d, BwdLayout* o) {
   o->QC = QC;
   const size_t rows = (size_t)(B * H * L), DA = (size_t)(C + R * Cz), DV = (size_t)(C + 3 * Pv + R * Cz);
   const size_t P3 = (size_t)(3 * P), DAQ = DA + P3 + 1, DAK = DA + P3, xs = (size_t)(B * H) * QC * L;
-  const size_t sizes[17] = {rows * DAQ, rows * DAK, rows * DV, rows * DV, rows * P3, rows * P3, rows,
+  const size_t sizes[18] = {rows * DAQ, rows * DAK, rows * DV, rows * DV, rows * P3, rows * P3, rows,
                             rows * DAK, rows * R * Cz, rows, rows,
                             rows * DAQ, rows * DV,
-                            (size_t)(B * L * H) * 12, (size_t)(B * L) * (size_t)(Cz * H + H), xs, xs};
+                            (size_t)(B * L * H) * 12, (size_t)(B * L) * (size_t)(Cz * H + H), xs, xs,
+                            (size_t)((B * L + 127) / 128) * (size_t)(Cz * H + H)};
   size_t off = 0;
-  for (int e = 0; e < 17; ++e) {
+  for (int e = 0; e < 18; ++e) {
     o->off[e] = off;
     off = ipa::align256(off + sizes[e] * 4);
   }
@@ -385,9 +386,9 @@ int32_t ipa_backward(const ipa_dims* dims, const float* q, const float* k, const
   a.dq = dq; a.dk = dk; a.dv = dv; a.dq_pts = dq_pts; a.dk_pts = dk_pts; a.dv_pts = dv_pts;
   a.drot = drot; a.dtrans = dtrans; a.dz1 = dz1; a.dz2 = dz2; a.dw_b = dw_b; a.dgamma = dgamma;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float** slots[17] = {&a.QA, &a.KA, &a.VA, &a.GA, &a.QP, &a.KP, &a.Dv, &a.dQA, &a.U, &a.gam,
-                       &a.rsum, &a.dKA, &a.dVA, &a.fpart, &a.share, &a.X, &a.Y};
-  for (int e = 0; e < 17; ++e) *slots[e] = reinterpret_cast<float*>(ws + ly.off[e]);
+  float** slots[18] = {&a.QA, &a.KA, &a.VA, &a.GA, &a.QP, &a.KP, &a.Dv, &a.dQA, &a.U, &a.gam,
+                       &a.rsum, &a.dKA, &a.dVA, &a.fpart, &a.share, &a.X, &a.Y, &a.red1};
+  for (int e = 0; e < 18; ++e) *slots[e] = reinterpret_cast<float*>(ws + ly.off[e]);
   if (ipa::launch_backward(a, static_cast<hipStream_t>(stream)) != hipSuccess) return IPA_ERR_HIP;
   return IPA_OK;
 }

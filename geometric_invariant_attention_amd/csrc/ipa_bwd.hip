@@ -39,7 +39,7 @@
 //   bwd_z       per (b, i, c): dz1, dz2 (summed over heads) and the
 //               residue's share of dW_b and dgamma.
 //   bwd_frames  per (b, i): drot, dtrans (summed over heads).
-//   bwd_reduce  column sums of the shares: dW_b, dgamma (fixed order).
+//   bwd_reduce1/2  column sums of the shares: dW_b, dgamma (fixed order).
 // The point sums of dS against Qg, Kg come from the GEMMs and the
 // corrections Qg_i sum_j dS_ij, Kg_j sum_i dS_ij; the coordinates are a
 // few hundred A at most and the dS sums vanish up to rounding, so the
@@ -51,6 +51,7 @@ namespace ipa {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+constexpr int kMaxP3 = 15;   // 3 Pqk
 
 __device__ __forceinline__ void rot3(const float* R, const float* x, float* o) {
   o[0] = R[0] * x[0] + R[1] * x[1] + R[2] * x[2];
@@ -68,8 +69,11 @@ __device__ __forceinline__ bool row_valid(const BwdArgs& a, int b, int i) {
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void bwd_prep_kernel(BwdArgs a) {
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+// bwd_prep: one wave per (b, i, h); lanes over the columns of the lifted
+// rows, so every row is written with coalesced stores.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long t = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int H = a.H, L = a.L, C = a.C, P = a.Pqk, Pv = a.Pv, RCz = a.R * a.Cz, Cz = a.Cz;
   if (t >= (long long)a.B * L * H) return;
   const int h = (int)(t % H);
@@ -78,73 +82,73 @@ __global__ __launch_bounds__(64) void bwd_prep_kernel(BwdArgs a) {
   const size_t bi = (size_t)b * L + i, bih = bi * H + h;
   const size_t row = ((size_t)b * H + h) * L + i;
   const bool valid = row_valid(a, b, i);
-  float R[9], T[3];
-  for (int c = 0; c < 9; ++c) R[c] = a.rot[bi * 9 + c];
-  for (int c = 0; c < 3; ++c) T[c] = a.trans[bi * 3 + c];
+  const float* R = a.rot + bi * 9;
+  const float* T = a.trans + bi * 3;
   const float alpha = a.w_L / sqrtf((float)C);
   float* qa = a.QA + row * a.DAQ;
   float* ka = a.KA + row * a.DAK;
   float* va = a.VA + row * a.DV;
   float* ga = a.GA + row * a.DV;
-  float* qp = a.QP + row * a.P3;
-  float* kp = a.KP + row * a.P3;
-  for (int c = 0; c < C; ++c) {
-    qa[c] = alpha * a.q[bih * C + c];
-    ka[c] = a.k[bih * C + c];
-    va[c] = a.v[bih * C + c];
+  // global point coordinate x of local point pt: R[x] . pt + t[x]
+  auto gpt = [&](const float* pt, int x) {
+    return R[3 * x] * pt[0] + R[3 * x + 1] * pt[1] + R[3 * x + 2] * pt[2] + T[x];
+  };
+  for (int c = lane; c < a.DAQ; c += 64) {
+    float vq, vk = 0.f;
+    if (c < C) {
+      vq = alpha * a.q[bih * C + c];
+      vk = a.k[bih * C + c];
+    } else if (c < a.DA) {
+      const int rc = c - C;
+      vq = a.w_L * a.w_b[(size_t)(rc % Cz) * H + h] * a.z1[bi * RCz + rc];
+      vk = a.z2[bi * RCz + rc];
+    } else if (c < a.DA + a.P3) {
+      const int e = c - a.DA, p = e / 3, x = e - 3 * p;
+      vq = gpt(a.q_pts + (bih * P + p) * 3, x);
+      vk = gpt(a.k_pts + (bih * P + p) * 3, x);
+      a.QP[row * a.P3 + e] = vq;
+      a.KP[row * a.P3 + e] = vk;
+    } else {
+      vq = 1.f;   // dS^T times this column: the column sums of dS
+    }
+    qa[c] = vq;
+    if (c < a.DAK) ka[c] = vk;
   }
-  for (int rc = 0; rc < RCz; ++rc) {
-    const float w = a.w_L * a.w_b[(size_t)(rc % Cz) * H + h];
-    qa[C + rc] = w * a.z1[bi * RCz + rc];
-    ka[C + rc] = a.z2[bi * RCz + rc];
-    va[C + 3 * Pv + rc] = a.z2[bi * RCz + rc];
-  }
-  for (int p = 0; p < P; ++p) {
-    float o[3];
-    rot3(R, a.q_pts + (bih * P + p) * 3, o);
-    for (int x = 0; x < 3; ++x) qp[3 * p + x] = qa[a.DA + 3 * p + x] = o[x] + T[x];
-    rot3(R, a.k_pts + (bih * P + p) * 3, o);
-    for (int x = 0; x < 3; ++x) kp[3 * p + x] = ka[a.DA + 3 * p + x] = o[x] + T[x];
-  }
-  qa[a.DA + a.P3] = 1.f;   // dS^T times this column: the column sums of dS
-  for (int p = 0; p < Pv; ++p) {
-    float o[3];
-    rot3(R, a.v_pts + (bih * Pv + p) * 3, o);
-    for (int x = 0; x < 3; ++x) va[C + 3 * p + x] = o[x] + T[x];
-  }
-  // lifted output cotangent and D_i; rows whose outputs are forced to zero
-  // pass no gradient
+  // VA and the lifted output cotangent GA; rows whose outputs are forced to
+  // zero pass no gradient. D_i = GA_i . O_i, O_i from the outputs.
   float D = 0.f;
-  if (valid) {
-    for (int c = 0; c < C; ++c) {
-      const float g = a.g_s[bih * C + c];
-      ga[c] = g;
-      D = fmaf(g, a.o_s[bih * C + c], D);
-    }
-    for (int p = 0; p < Pv; ++p) {
-      const float* op = a.o_pts + (bih * Pv + p) * 3;
-      const float* gp = a.g_pts + (bih * Pv + p) * 3;
-      const float n2 = op[0] * op[0] + op[1] * op[1] + op[2] * op[2];
-      const float gn = a.g_norm[bih * Pv + p];
-      const float s = n2 > 0.f ? gn / sqrtf(n2) : 0.f;
-      const float gt[3] = {gp[0] + s * op[0], gp[1] + s * op[1], gp[2] + s * op[2]};
-      float dog[3], og[3];
-      rot3(R, gt, dog);
-      rot3(R, op, og);
-      for (int x = 0; x < 3; ++x) {
-        ga[C + 3 * p + x] = dog[x];
-        D = fmaf(dog[x], og[x] + T[x], D);
+  for (int c = lane; c < a.DV; c += 64) {
+    float vv, gv = 0.f;
+    if (c < C) {
+      vv = a.v[bih * C + c];
+      if (valid) {
+        gv = a.g_s[bih * C + c];
+        D = fmaf(gv, a.o_s[bih * C + c], D);
       }
+    } else if (c < C + 3 * Pv) {
+      const int e = c - C, p = e / 3, x = e - 3 * p;
+      vv = gpt(a.v_pts + (bih * Pv + p) * 3, x);
+      if (valid) {
+        const float* op = a.o_pts + (bih * Pv + p) * 3;
+        const float* gp = a.g_pts + (bih * Pv + p) * 3;
+        const float n2 = op[0] * op[0] + op[1] * op[1] + op[2] * op[2];
+        const float s = n2 > 0.f ? a.g_norm[bih * Pv + p] / sqrtf(n2) : 0.f;
+        const float gt[3] = {gp[0] + s * op[0], gp[1] + s * op[1], gp[2] + s * op[2]};
+        gv = R[3 * x] * gt[0] + R[3 * x + 1] * gt[1] + R[3 * x + 2] * gt[2];   // R g_tot
+        D = fmaf(gv, gpt(op, x), D);                                            // . (R o_pts + t)
+      }
+    } else {
+      const int rc = c - C - 3 * Pv;
+      vv = a.z2[bi * RCz + rc];
+      if (valid) gv = a.z1[bi * RCz + rc] * a.g_pair[bih * Cz + rc % Cz];
     }
-    for (int rc = 0; rc < RCz; ++rc) {
-      const float gp = a.g_pair[bih * Cz + rc % Cz];
-      ga[C + 3 * Pv + rc] = a.z1[bi * RCz + rc] * gp;
-    }
-    for (int c = 0; c < Cz; ++c) D = fmaf(a.g_pair[bih * Cz + c], a.o_pair[bih * Cz + c], D);
-  } else {
-    for (int c = 0; c < a.DV; ++c) ga[c] = 0.f;
+    va[c] = vv;
+    ga[c] = gv;
   }
-  a.Dv[row] = D;
+  if (valid)
+    for (int c = lane; c < Cz; c += 64) D = fmaf(a.g_pair[bih * Cz + c], a.o_pair[bih * Cz + c], D);
+  for (int o = 32; o > 0; o >>= 1) D += __shfl_xor(D, o);
+  if (lane == 0) a.Dv[row] = D;
 }
 
 // ---------------------------------------------------------------------------
@@ -242,66 +246,146 @@ hipError_t gemm(const Gemm& g, int batch, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_rows: one wave per query row of the chunk. X holds S (without the
-// point term) and becomes A; Y holds dP and becomes dS.
+// bwd_rows: a workgroup takes kRowsPerWG query rows of one (b, h), a wave
+// one row at a time. X holds S (without the point term) and becomes A; Y
+// holds dP and becomes dS. The head's key points are staged in LDS,
+// coordinate-major, kKeyBlock keys at a time (lane j reads key j: no bank
+// conflicts), so each row reads them from LDS instead of L2.
 // ---------------------------------------------------------------------------
+constexpr int kRowsPerWG = 16, kKeyBlock = 1024, kUnroll = 8;
+
+// e^x for x <= 0 through the hardware base-2 exponential (about 1 ulp)
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc) {
-  const int lane = threadIdx.x & 63, r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= qc) return;
+  __shared__ float kps[kMaxP3][kKeyBlock];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bh = blockIdx.y, H = a.H, L = a.L, P3 = a.P3;
-  const int b = bh / H, h = bh - b * H, i = q0 + r;
+  const int b = bh / H, h = bh - b * H;
   const float kappa = a.w_L * a.gamma[h] * a.w_C * 0.5f;
-  const size_t qrow = (size_t)bh * L + i;
-  float* X = a.X + ((size_t)bh * a.QC + r) * L;
-  float* Y = a.Y + ((size_t)bh * a.QC + r) * L;
-  const bool qv = row_valid(a, b, i);
-  float qp[15];
-  for (int c = 0; c < 15; ++c) qp[c] = c < P3 ? a.QP[qrow * P3 + c] : 0.f;
   const float* KP = a.KP + (size_t)bh * L * P3;
-  auto dist = [&](int j) {
+  const int r0 = blockIdx.x * kRowsPerWG;
+  // per row of this wave: running max and sum (pass 1), then A, dS (pass 2)
+  float m[kRowsPerWG / 4], l[kRowsPerWG / 4], qp[kRowsPerWG / 4][kMaxP3];
+  bool qv[kRowsPerWG / 4];
+#pragma unroll
+  for (int u = 0; u < kRowsPerWG / 4; ++u) {
+    const int r = r0 + w + 4 * u, i = q0 + r;
+    qv[u] = r < qc && row_valid(a, b, i);
+    m[u] = -INFINITY;
+    l[u] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxP3; ++c) qp[u][c] = (r < qc && c < P3) ? a.QP[((size_t)bh * L + i) * P3 + c] : 0.f;
+  }
+  auto stage = [&](int k0, int nk) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < nk * P3; e += 256) {
+      const int j = e / P3, c = e - j * P3;
+      kps[c][j] = KP[(size_t)(k0 + j) * P3 + c];
+    }
+    __syncthreads();
+  };
+  auto dist = [&](const float (&q)[kMaxP3], int jj) {
     float d = 0.f;
-    for (int c = 0; c < P3; ++c) {
-      const float e = qp[c] - KP[(size_t)j * P3 + c];
-      d = fmaf(e, e, d);
+#pragma unroll
+    for (int c = 0; c < kMaxP3; ++c) {
+      if (c < P3) {
+        const float e = q[c] - kps[c][jj];
+        d = fmaf(e, e, d);
+      }
     }
     return d;
   };
-  // pass 1: running maximum and sum per lane
-  float m = -INFINITY, l = 0.f;
-  for (int j = lane; j < L; j += 64) {
-    if (!(qv && row_valid(a, b, j))) continue;
-    const float sj = fmaf(-kappa, dist(j), X[j]);
-    if (sj > m) { l = l * expf(m - sj) + 1.f; m = sj; }
-    else l += expf(sj - m);
-  }
-  // combine the lanes
-  float mw = m;
-  for (int o = 32; o > 0; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
-  l = m == -INFINITY ? 0.f : l * expf(m - mw);
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float D = a.Dv[qrow];
-  // pass 2: A, dS and the row sums
-  float rs = 0.f, gs = 0.f;
-  for (int j = lane; j < L; j += 64) {
-    float p = 0.f, ds = 0.f;
-    if (qv && row_valid(a, b, j)) {
-      const float d = dist(j);
-      p = expf(fmaf(-kappa, d, X[j]) - mw) * inv;
-      ds = p * (Y[j] - D);
-      rs += ds;
-      gs = fmaf(ds, d, gs);
+  // pass 1
+  for (int k0 = 0; k0 < L; k0 += kKeyBlock) {
+    const int nk = L - k0 < kKeyBlock ? L - k0 : kKeyBlock;
+    stage(k0, nk);
+#pragma unroll
+    for (int u = 0; u < kRowsPerWG / 4; ++u) {
+      if (!qv[u]) continue;
+      const float* X = a.X + ((size_t)bh * a.QC + r0 + w + 4 * u) * L;
+      // kUnroll keys per lane at a time: all their loads in flight together
+      for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
+        float xv[kUnroll];
+#pragma unroll
+        for (int t = 0; t < kUnroll; ++t) {
+          const int jj = jb + 64 * t + lane;
+          xv[t] = jj < nk ? X[k0 + jj] : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < kUnroll; ++t) {
+          const int jj = jb + 64 * t + lane;
+          if (jj >= nk || !row_valid(a, b, k0 + jj)) continue;
+          const float sj = fmaf(-kappa, dist(qp[u], jj), xv[t]);
+          if (sj > m[u]) { l[u] = l[u] * fexp(m[u] - sj) + 1.f; m[u] = sj; }
+          else l[u] += fexp(sj - m[u]);
+        }
+      }
     }
-    X[j] = p;
-    Y[j] = ds;
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    rs += __shfl_xor(rs, o);
-    gs += __shfl_xor(gs, o);
+  float inv[kRowsPerWG / 4];
+#pragma unroll
+  for (int u = 0; u < kRowsPerWG / 4; ++u) {
+    float mw = m[u];
+    for (int o = 32; o > 0; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+    float lw = m[u] == -INFINITY ? 0.f : l[u] * fexp(m[u] - mw);
+    for (int o = 32; o > 0; o >>= 1) lw += __shfl_xor(lw, o);
+    m[u] = mw;
+    inv[u] = lw > 0.f ? 1.f / lw : 0.f;
   }
-  if (lane == 0) {
-    a.rsum[qrow] = rs;
-    a.gam[qrow] = gs;
+  // pass 2
+  float rs[kRowsPerWG / 4], gs[kRowsPerWG / 4];
+#pragma unroll
+  for (int u = 0; u < kRowsPerWG / 4; ++u) rs[u] = gs[u] = 0.f;
+  for (int k0 = 0; k0 < L; k0 += kKeyBlock) {
+    const int nk = L - k0 < kKeyBlock ? L - k0 : kKeyBlock;
+    if (k0 > 0 || L > kKeyBlock) stage(k0, nk);
+#pragma unroll
+    for (int u = 0; u < kRowsPerWG / 4; ++u) {
+      const int r = r0 + w + 4 * u;
+      if (r >= qc) continue;
+      const float D = a.Dv[(size_t)bh * L + q0 + r];
+      float* X = a.X + ((size_t)bh * a.QC + r) * L;
+      float* Y = a.Y + ((size_t)bh * a.QC + r) * L;
+      for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
+        float xv[kUnroll], yv[kUnroll];
+#pragma unroll
+        for (int t = 0; t < kUnroll; ++t) {
+          const int jj = jb + 64 * t + lane;
+          xv[t] = jj < nk ? X[k0 + jj] : 0.f;
+          yv[t] = jj < nk ? Y[k0 + jj] : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < kUnroll; ++t) {
+          const int jj = jb + 64 * t + lane;
+          if (jj >= nk) continue;
+          const int j = k0 + jj;
+          float p = 0.f, ds = 0.f;
+          if (qv[u] && row_valid(a, b, j)) {
+            const float d = dist(qp[u], jj);
+            p = fexp(fmaf(-kappa, d, xv[t]) - m[u]) * inv[u];
+            ds = p * (yv[t] - D);
+            rs[u] += ds;
+            gs[u] = fmaf(ds, d, gs[u]);
+          }
+          X[j] = p;
+          Y[j] = ds;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowsPerWG / 4; ++u) {
+    float r1 = rs[u], g1 = gs[u];
+    for (int o = 32; o > 0; o >>= 1) {
+      r1 += __shfl_xor(r1, o);
+      g1 += __shfl_xor(g1, o);
+    }
+    const int r = r0 + w + 4 * u;
+    if (lane == 0 && r < qc) {
+      a.rsum[(size_t)bh * L + q0 + r] = r1;
+      a.gam[(size_t)bh * L + q0 + r] = g1;
+    }
   }
 }
 
@@ -436,20 +520,32 @@ __global__ __launch_bounds__(64) void bwd_frames_kernel(BwdArgs a) {
   for (int c = 0; c < 3; ++c) a.dtrans[(size_t)t * 3 + c] = acc[9 + c];
 }
 
-// column sums of the per-residue shares, in a fixed order: 4 row groups per
-// column, then the groups added in order
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+// column sums of the per-residue shares, in a fixed order: stage 1 sums
+// blocks of kRedRows rows (4 row groups per column, added in order) into
+// partial rows, stage 2 adds the partial rows in order
+constexpr int kRedRows = 128;
+
+__global__ __launch_bounds__(256) void bwd_reduce1_kernel(BwdArgs a) {
   const int ncol = a.Cz * a.H + a.H;
   const int col = blockIdx.x * 64 + (threadIdx.x & 63), g = threadIdx.x >> 6;
-  const long long rows = (long long)a.B * a.L;
+  const long long rows = (long long)a.B * a.L, r0 = (long long)blockIdx.y * kRedRows;
   __shared__ float part[4][64];
   float s = 0.f;
   if (col < ncol)
-    for (long long r = g; r < rows; r += 4) s += a.share[(size_t)r * ncol + col];
+    for (long long r = r0 + g; r < r0 + kRedRows && r < rows; r += 4) s += a.share[(size_t)r * ncol + col];
   part[g][threadIdx.x & 63] = s;
   __syncthreads();
   if (g != 0 || col >= ncol) return;
-  const float v = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+  a.red1[(size_t)blockIdx.y * ncol + col] =
+      ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
+}
+
+__global__ __launch_bounds__(256) void bwd_reduce2_kernel(BwdArgs a, int nblk) {
+  const int ncol = a.Cz * a.H + a.H;
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= ncol) return;
+  float v = 0.f;
+  for (int k = 0; k < nblk; ++k) v += a.red1[(size_t)k * ncol + col];
   if (col < a.Cz * a.H) a.dw_b[col] = v;
   else a.dgamma[col - a.Cz * a.H] = v;
 }
@@ -459,7 +555,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   const long long bih = (long long)a.B * a.L * a.H;
   const unsigned g64 = (unsigned)((bih + 63) / 64);
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(g64), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((bih + 3) / 4)), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const int BH = a.B * a.H, L = a.L, RCz = a.R * a.Cz;
   const long long rowsQ = (long long)L * a.DAQ, rowsK = (long long)L * a.DAK, rowsV = (long long)L * a.DV;
@@ -479,7 +575,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     g.B = a.VA; g.sBb = rowsV; g.bk = 1; g.bn = a.DV;
     g.C = a.Y;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(bwd_rows_kernel, dim3((qc + 3) / 4, BH), dim3(256), 0, s, a, q0, qc);
+    hipLaunchKernelGGL(bwd_rows_kernel, dim3((qc + kRowsPerWG - 1) / kRowsPerWG, BH), dim3(256), 0, s, a, q0, qc);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     // dQA' = dS KA' (rows q0 .. q0 + qc)
     g.M = qc; g.N = a.DAK; g.K = L;
@@ -515,7 +611,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_frames_kernel, dim3((unsigned)((bi + 63) / 64)), dim3(64), 0, s, a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const int ncol = a.Cz * a.H + a.H;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((ncol + 63) / 64), dim3(256), 0, s, a);
+  const int nblk = (int)((bi + kRedRows - 1) / kRedRows);
+  hipLaunchKernelGGL(bwd_reduce1_kernel, dim3((ncol + 63) / 64, nblk), dim3(256), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(bwd_reduce2_kernel, dim3((ncol + 255) / 256), dim3(256), 0, s, a, nblk);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   return hipSuccess;
 }
