@@ -114,6 +114,21 @@ struct DDArgs {
 };
 
 // ---------------------------------------------------------------------------
+// Batched fp32 GEMM (ipa_gemm.hip): C[z](m, n) = sum_k A[z](m, k) B[z](k, n)
+// (+ C[z](m, n) when acc, + bias[n], rows with rowmask[m] == 0 set to 0)
+// ---------------------------------------------------------------------------
+struct Gemm {
+  int M, N, K;
+  const float* A; long long sAb, am, ak;
+  const float* B; long long sBb, bk, bn;
+  float* C; long long sCb, cm;
+  int acc;
+  const float* bias;        // [N] or NULL
+  const uint8_t* rowmask;   // [M] or NULL
+};
+hipError_t gemm(const Gemm& g, int batch, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Gradient of the IPA forward (ipa_bwd.hip), float32
 // ---------------------------------------------------------------------------
 struct BwdArgs {

@@ -27,6 +27,9 @@ Pinning status of each function (see the tests under ``tests/``):
                   random directions for every input, its restated forward
                   equals ipa_forward, rigid-motion identities of the frame
                   gradients, masked rows and keys.
+  ipa_layer       pinned: reduces to ipa_forward plus the readout with
+                  selection weights, readout order by one-hot rows, the
+                  affine maps against a scalar loop, masked rows.
 """
 
 from .ipa_oracle import ipa_forward, ipa_logits, to_global
@@ -35,7 +38,8 @@ from .lifted import ipa_lifted, block_centres
 from .geometry import frames_from_atoms, meet_attention
 from .dirdist import dirdist_attention
 from .ipa_grad import ipa_backward
+from .layer import ipa_layer
 
 __all__ = ["ipa_forward", "ipa_logits", "to_global", "ipa_bruteforce",
            "ipa_lifted", "block_centres", "frames_from_atoms", "meet_attention",
-           "dirdist_attention", "dirdist_bruteforce", "ipa_backward"]
+           "dirdist_attention", "dirdist_bruteforce", "ipa_backward", "ipa_layer"]

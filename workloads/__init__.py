@@ -420,3 +420,35 @@ def make_dirdist_inputs(w: DirDistWorkload, seed: int | None = None) -> dict:
         frame_mask=fmask, pair_mask=pm, lengths=lengths.astype(np.int64),
         dims=w.dims(), workload=w.name,
     )
+
+
+# ----------------------------------------------------------------------------
+# the full layer around the attention
+# ----------------------------------------------------------------------------
+def make_layer_inputs(w: IPAWorkload, c_s: int = 384, seed: int | None = None) -> dict:
+    """Draw one seeded input set for the IPA layer with single-representation
+    width c_s: frames, mask, W_b and gamma as ``make_inputs(w)``; then
+    s ~ N(0, 1) [B,L,c_s]; the input map W_in [c_s, Nin] with columns
+    ~ N(0, 1/c_s) (projected features of unit variance; the pair-factor
+    columns scaled by 1/sqrt(c_z), as in the IPA recipe), b_in ~ N(0, 0.1^2);
+    the readout W_out [Nout, c_s] ~ N(0, 1/Nout), b_out ~ N(0, 1). Column
+    blocks of W_in: q, k, v [H C each], q_pts, k_pts [H Pqk 3], v_pts
+    [H Pv 3], z1, z2 [R c_z]; rows of W_out: o_s [H C], o_pts [H Pv 3],
+    o_norm [H Pv], o_pair [H c_z]. float32 throughout.
+    """
+    base = make_inputs(w, seed=seed)
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 7919)
+    B, L, H, C, Pqk, Pv, R, Cz = w.B, w.L, w.H, w.C, w.Pqk, w.Pv, w.R, w.Cz
+    n_in = 3 * H * C + 3 * H * Pqk * 2 + 3 * H * Pv + 2 * R * Cz
+    n_out = H * (C + 3 * Pv + Pv + Cz)
+    s = rng.standard_normal((B, L, c_s))
+    w_in = rng.standard_normal((c_s, n_in)) / math.sqrt(c_s)
+    w_in[:, n_in - 2 * R * Cz:] /= math.sqrt(Cz)
+    b_in = 0.1 * rng.standard_normal(n_in)
+    w_out = rng.standard_normal((n_out, c_s)) / math.sqrt(n_out)
+    b_out = rng.standard_normal(c_s)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return dict(s=f32(s), rot=base["rot"], trans=base["trans"], mask=base["mask"],
+                has_mask=base["has_mask"], w_in=f32(w_in), b_in=f32(b_in), w_b=base["w_b"],
+                gamma=base["gamma"], w_L=base["w_L"], w_C=base["w_C"], w_out=f32(w_out),
+                b_out=f32(b_out), dims=w.dims(), c_s=c_s, dtype=w.dtype, workload=w.name)
