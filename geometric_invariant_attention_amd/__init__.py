@@ -9,7 +9,7 @@ from ._binding import (  # noqa: F401
     ipa_forward, load_library, make_dims, status_string, workspace_bytes,
     frames_from_atoms, meet_attention, MeetForward, IpaMeetDims, meet_workspace_bytes,
     DirDistForward, IpaDirDistDims, dirdist_workspace_bytes, geometric_reasoning_attention,
-    IPABackward, backward_workspace_bytes,
+    IPABackward, backward_workspace_bytes, IPALayer,
 )
 
 __all__ = ["ipa_forward", "IPAForward", "IPAError", "load_library", "workspace_bytes",
@@ -17,4 +17,4 @@ __all__ = ["ipa_forward", "IPAForward", "IPAError", "load_library", "workspace_b
            "IPA_BF16", "LIB_PATH", "frames_from_atoms", "meet_attention", "MeetForward",
            "IpaMeetDims", "meet_workspace_bytes", "DirDistForward", "IpaDirDistDims",
            "dirdist_workspace_bytes", "geometric_reasoning_attention", "IPABackward",
-           "backward_workspace_bytes"]
+           "backward_workspace_bytes", "IPALayer"]

@@ -79,6 +79,10 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ipa_backward_workspace_bytes.restype = sz
     lib.ipa_backward.argtypes = [ctypes.POINTER(IpaDims)] + [vp] * 13 + [f32, f32] + [vp] * 20 + [sz, vp]
     lib.ipa_backward.restype = i32
+    lib.ipa_layer_workspace_bytes.argtypes = [ctypes.POINTER(IpaDims), i32, i32]
+    lib.ipa_layer_workspace_bytes.restype = sz
+    lib.ipa_layer_forward.argtypes = [ctypes.POINTER(IpaDims), i32, i32] + [vp] * 8 + [f32, f32] + [vp] * 4 + [sz, vp]
+    lib.ipa_layer_forward.restype = i32
     lib.ipa_status_string.argtypes = [i32]
     lib.ipa_status_string.restype = ctypes.c_char_p
     lib.ipa_version.argtypes = []
@@ -498,3 +502,67 @@ class IPABackward:
 
     def __call__(self, *args, **kw) -> dict:
         return self.backward_raw(self.bind(*args, **kw))
+
+
+# ---------------------------------------------------------------------------
+# the full layer (ipa_layer_forward)
+# ---------------------------------------------------------------------------
+class IPALayer:
+    """Reusable plan of the full IPA layer (ipa_layer_forward): projections
+    of the single representation, the attention, the readout."""
+
+    def __init__(self, B, L, H, C, Pqk, Pv, R, Cz, c_s, dtype=torch.bfloat16, device=None):
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("dtype must be torch.bfloat16 or torch.float32")
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.dims = make_dims(B, L, H, C, Pqk, Pv, R, Cz)
+        self.shape = dict(B=B, L=L, H=H, C=C, Pqk=Pqk, Pv=Pv, R=R, Cz=Cz, c_s=c_s)
+        self.code = IPA_BF16 if dtype == torch.bfloat16 else IPA_F32
+        self.lib = load_library()
+        self.ws_bytes = int(self.lib.ipa_layer_workspace_bytes(ctypes.byref(self.dims), c_s, self.code))
+        if self.ws_bytes == 0:
+            raise IPAError(-6, f"unsupported dims {self.shape} for {dtype}")
+        self.n_in = 3 * H * C + 6 * H * Pqk + 3 * H * Pv + 2 * R * Cz
+        self.n_out = H * (C + 4 * Pv + Cz)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.out = torch.empty(B, L, c_s, dtype=torch.float32, device=self.device)
+
+    def bind(self, s, rot, trans, w_in, b_in, w_b, gamma, w_out, b_out, mask=None, w_L=None, w_C=None,
+             stream=None) -> tuple:
+        B, L, H, Cz, c_s = (self.shape[n] for n in ("B", "L", "H", "Cz", "c_s"))
+        dev, f32 = self.device, torch.float32
+        if w_L is None or w_C is None:
+            dl, dc = default_weights(self.shape["Pqk"])
+            w_L = dl if w_L is None else w_L
+            w_C = dc if w_C is None else w_C
+        expect = {"s": (B, L, c_s), "rot": (B, L, 3, 3), "trans": (B, L, 3), "w_in": (c_s, self.n_in),
+                  "w_b": (Cz, H), "gamma": (H,), "w_out": (self.n_out, c_s)}
+        args = dict(s=s, rot=rot, trans=trans, w_in=w_in, w_b=w_b, gamma=gamma, w_out=w_out)
+        for name, shp in expect.items():
+            t = args[name]
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+            args[name] = _prep(t, f32, dev, name)
+        bi = _prep(b_in, f32, dev, "b_in") if b_in is not None else None
+        bo = _prep(b_out, f32, dev, "b_out") if b_out is not None else None
+        m = None
+        if mask is not None:
+            m = (mask.to(torch.uint8) if mask.dtype != torch.uint8 else mask).contiguous()
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        self.bound = (args, bi, bo, m)
+        return (ctypes.byref(self.dims), self.shape["c_s"], self.code,
+                args["s"].data_ptr(), args["rot"].data_ptr(), args["trans"].data_ptr(), _dev_ptr(m),
+                args["w_in"].data_ptr(), _dev_ptr(bi), args["w_b"].data_ptr(), args["gamma"].data_ptr(),
+                ctypes.c_float(w_L), ctypes.c_float(w_C), args["w_out"].data_ptr(), _dev_ptr(bo),
+                self.out.data_ptr(), self.workspace.data_ptr(), ctypes.c_size_t(self.ws_bytes),
+                ctypes.c_void_p(stream.cuda_stream))
+
+    def forward_raw(self, raw: tuple) -> torch.Tensor:
+        rc = self.lib.ipa_layer_forward(*raw)
+        if rc != 0:
+            raise IPAError(rc, status_string(rc))
+        return self.out
+
+    def __call__(self, *args, **kw) -> torch.Tensor:
+        return self.forward_raw(self.bind(*args, **kw))

@@ -393,6 +393,116 @@ int32_t ipa_backward(const ipa_dims* dims, const float* q, const float* k, const
   return IPA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+struct LayerLayout {
+  size_t off_x, off_feat[8], off_ipa, off_out[4], total, ipa_bytes;
+  int n_in, n_out, widths[8];
+};
+
+bool layer_layout(const ipa_dims* d, int32_t c_s, int32_t dtype, LayerLayout* o) {
+  if (!d || c_s < 1 || c_s > 65536) return false;
+  if (dtype != IPA_F32 && dtype != IPA_BF16) return false;
+  const size_t ipa_bytes = ipa_workspace_bytes(d, dtype);
+  if (ipa_bytes == 0) return false;
+  const int64_t B = d->B, L = d->L, H = d->H, C = d->C, P = d->Pqk, Pv = d->Pv, R = d->R, Cz = d->Cz;
+  const int w[8] = {(int)(H * C), (int)(H * C), (int)(H * C), (int)(H * P * 3), (int)(H * P * 3),
+                    (int)(H * Pv * 3), (int)(R * Cz), (int)(R * Cz)};
+  int n_in = 0;
+  for (int e = 0; e < 8; ++e) { o->widths[e] = w[e]; n_in += w[e]; }
+  o->n_in = n_in;
+  o->n_out = (int)(H * (C + 3 * Pv + Pv + Cz));
+  if (B * L * (int64_t)n_in >= (int64_t(1) << 31) || B * L * (int64_t)c_s >= (int64_t(1) << 31)) return false;
+  const size_t rows = (size_t)(B * L), es = dtype == IPA_BF16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = ipa::align256(off + bytes); return at; };
+  o->off_x = take(rows * n_in * 4);
+  for (int e = 0; e < 8; ++e) o->off_feat[e] = take(rows * w[e] * es);
+  o->off_ipa = take(ipa_bytes);
+  o->ipa_bytes = ipa_bytes;
+  const size_t outw[4] = {(size_t)(H * C), (size_t)(H * Pv * 3), (size_t)(H * Pv), (size_t)(H * Cz)};
+  for (int e = 0; e < 4; ++e) o->off_out[e] = take(rows * outw[e] * 4);
+  o->total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ipa_layer_workspace_bytes(const ipa_dims* dims, int32_t c_s, int32_t dtype) {
+  LayerLayout ly;
+  return layer_layout(dims, c_s, dtype, &ly) ? ly.total : 0;
+}
+
+int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype, const float* s,
+                          const float* rot, const float* trans, const uint8_t* mask,
+                          const float* w_in, const float* b_in, const float* w_b, const float* gamma,
+                          float w_L, float w_C, const float* w_out, const float* b_out, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dims) return IPA_ERR_NULL;
+  if (dims->B < 1 || dims->L < 1 || dims->H < 1 || dims->C < 1 || dims->Pqk < 1 || dims->Pv < 1 ||
+      dims->R < 1 || dims->Cz < 1 || c_s < 1)
+    return IPA_ERR_DIMS;
+  if (dtype != IPA_F32 && dtype != IPA_BF16) return IPA_ERR_DTYPE;
+  const void* req[] = {s, rot, trans, w_in, w_b, gamma, w_out, out, workspace};
+  for (const void* p : req)
+    if (!p) return IPA_ERR_NULL;
+  const void* al[] = {s, rot, trans, w_in, b_in, w_b, gamma, w_out, b_out, out};
+  for (const void* p : al)
+    if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return IPA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return IPA_ERR_ALIGN;
+  if (!std::isfinite(w_L) || !std::isfinite(w_C) || w_L < 0.f || w_C < 0.f) return IPA_ERR_ARG;
+  LayerLayout ly;
+  if (!layer_layout(dims, c_s, dtype, &ly)) return IPA_ERR_UNSUPPORTED;
+  if (workspace_bytes < ly.total) return IPA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const long long rows = (long long)dims->B * dims->L;
+  float* x = reinterpret_cast<float*>(ws + ly.off_x);
+  // x = s W_in + b_in
+  ipa::Gemm g{};
+  g.M = (int)rows; g.N = ly.n_in; g.K = c_s;
+  g.A = s; g.am = c_s; g.ak = 1;
+  g.B = w_in; g.bk = ly.n_in; g.bn = 1;
+  g.C = x; g.cm = ly.n_in; g.bias = b_in;
+  if (ipa::gemm(g, 1, st) != hipSuccess) return IPA_ERR_HIP;
+  ipa::LayerSplit sp{};
+  sp.x = x; sp.rows = rows; sp.n_in = ly.n_in; sp.bf16 = dtype == IPA_BF16;
+  int c0 = 0;
+  for (int e = 0; e < 8; ++e) {
+    sp.start[e] = c0;
+    c0 += ly.widths[e];
+    sp.out[e] = ws + ly.off_feat[e];
+  }
+  sp.start[8] = c0;
+  if (ipa::launch_layer_split(sp, st) != hipSuccess) return IPA_ERR_HIP;
+  // the attention
+  float* o[4];
+  for (int e = 0; e < 4; ++e) o[e] = reinterpret_cast<float*>(ws + ly.off_out[e]);
+  const int32_t rc = ipa_forward(dims, dtype, sp.out[0], sp.out[1], sp.out[2], sp.out[3], sp.out[4],
+                                 sp.out[5], rot, trans, sp.out[6], sp.out[7], w_b, gamma, mask, w_L, w_C,
+                                 o[0], o[1], o[2], o[3], ws + ly.off_ipa, ly.ipa_bytes, stream);
+  if (rc != IPA_OK) return rc;
+  // y = [o_s | o_pts | o_norm | o_pair] W_out + b_out, masked rows 0
+  const int H = dims->H, C = dims->C, Pv = dims->Pv, Cz = dims->Cz;
+  const int wo[4] = {H * C, H * Pv * 3, H * Pv, H * Cz};
+  int r0 = 0;
+  for (int e = 0; e < 4; ++e) {
+    ipa::Gemm q{};
+    q.M = (int)rows; q.N = c_s; q.K = wo[e];
+    q.A = o[e]; q.am = wo[e]; q.ak = 1;
+    q.B = w_out + (size_t)r0 * c_s; q.bk = c_s; q.bn = 1;
+    q.C = out; q.cm = c_s; q.acc = e > 0;
+    if (e == 3) { q.bias = b_out; q.rowmask = mask; }
+    if (ipa::gemm(q, 1, st) != hipSuccess) return IPA_ERR_HIP;
+    r0 += wo[e];
+  }
+  return IPA_OK;
+}
+
 const char* ipa_status_string(int32_t status) {
   switch (status) {
     case IPA_OK: return "ok";

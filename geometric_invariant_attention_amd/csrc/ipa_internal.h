@@ -129,6 +129,21 @@ struct Gemm {
 hipError_t gemm(const Gemm& g, int batch, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Full layer (ipa_layer.hip): x [rows][n_in] -> the attention's 8 input
+// arrays (q, k, v, q_pts, k_pts, v_pts, z1, z2), fp32 or bf16 (nearest even)
+// ---------------------------------------------------------------------------
+constexpr int kLayerBlocks = 8;
+struct LayerSplit {
+  const float* x;
+  long long rows;
+  int n_in;
+  int start[kLayerBlocks + 1];   // first column of each block, then n_in
+  void* out[kLayerBlocks];
+  int bf16;
+};
+hipError_t launch_layer_split(const LayerSplit& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Gradient of the IPA forward (ipa_bwd.hip), float32
 // ---------------------------------------------------------------------------
 struct BwdArgs {

@@ -202,6 +202,37 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype,
                          void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* The full IPA layer around ipa_forward.
+ * Reading taken (the pages fix the attention, not its wrap; "Flash
+ * Invariant Point Attention", TL;DR and abstract: per-residue scalar,
+ * point and factorised pair features feed it): one affine map of the
+ * single representation s gives every input feature,
+ *   x = s W_in + b_in = [q | k | v | q_pts | k_pts | v_pts | z1 | z2]
+ * (blocks flattened head-major: q [H,C], q_pts [H,Pqk,3], z1 [R,Cz], ...),
+ * the features are stored in `dtype` (bf16: round to nearest even), the
+ * attention runs as ipa_forward, and its outputs are read out as
+ *   out = [o_s | o_pts | o_norm | o_pair] W_out + b_out
+ * flattened head-major with xyz last; rows whose mask entry is 0 give +0.0.
+ *   dims, dtype   as ipa_forward;  c_s >= 1 the width of s and out
+ *   s      [B,L,c_s] float32      rot, trans, mask, w_b, gamma, w_L, w_C as ipa_forward
+ *   w_in   [c_s, 3HC + 6HPqk + 3HPv + 2RCz] float32, b_in [..] or NULL
+ *   w_out  [H(C + 3Pv + Pv + Cz), c_s] float32, b_out [c_s] or NULL
+ *   out    [B,L,c_s] float32, every element overwritten
+ *   workspace ipa_layer_workspace_bytes(dims, c_s, dtype) bytes, 256-byte aligned
+ * Pointers 16-byte aligned. The projections and the readout run on the
+ * fp32 matrix cores; the attention's envelope and statuses are those of
+ * ipa_forward. */
+size_t ipa_layer_workspace_bytes(const ipa_dims* dims, int32_t c_s, int32_t dtype);
+int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype,
+                          const float* s, const float* rot, const float* trans,
+                          const uint8_t* mask,
+                          const float* w_in, const float* b_in,
+                          const float* w_b, const float* gamma, float w_L, float w_C,
+                          const float* w_out, const float* b_out,
+                          float* out,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Gradient of ipa_forward (float32 path).
  * Training goes through this attention ("Flash Invariant Point Attention",
  * abstract: training at previously unattainable lengths). For output

@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert names == ["ipa_attend", "ipa_backward", "ipa_backward_workspace_bytes",
                      "ipa_dirdist_forward", "ipa_dirdist_workspace_bytes",
-                     "ipa_forward", "ipa_frames_from_atoms", "ipa_lift",
+                     "ipa_forward", "ipa_frames_from_atoms", "ipa_layer_forward",
+                     "ipa_layer_workspace_bytes", "ipa_lift",
                      "ipa_meet_forward", "ipa_meet_workspace_bytes", "ipa_status_string",
                      "ipa_version", "ipa_workspace_bytes"]
     for n in names:
@@ -260,3 +261,27 @@ def test_backward_workspace_linear_in_L(lib):
     # L adds less than the per-row arrays of L more rows plus the buffers
     grow = sizes[65536] - sizes[32768]
     assert sizes[65536] <= 2 * grow + 2 * 4 * (1 << 26) + 17 * 256
+
+
+def test_layer_rejects_before_launch(lib):
+    good = bd.make_dims(1, 64, 4, 16, 4, 8, 2, 16)
+    ptrs = [0x1000 * (n + 1) for n in range(16)]
+
+    def call(dims, c_s=32, dtype=1, p=ptrs, wl=1.0, ws_bytes=1 << 34, ws=0x100000):
+        return lib.ipa_layer_forward(ctypes.byref(dims) if dims is not None else None, c_s, dtype,
+                                     *p[:8], ctypes.c_float(wl), ctypes.c_float(1.0), *p[8:11], ws,
+                                     ctypes.c_size_t(ws_bytes), None)
+    assert call(None) == -1
+    assert call(good, c_s=0) == -2
+    assert call(good, dtype=7) == -3
+    for k in (0, 1, 2, 4, 6, 7, 8, 10):      # s, rot, trans, w_in, w_b, gamma, w_out, out
+        p = list(ptrs)
+        p[k] = 0
+        assert call(good, p=p) == -1, k
+    p = list(ptrs)
+    p[4] += 4
+    assert call(good, p=p) == -5
+    assert call(good, wl=float("inf")) == -8
+    need = lib.ipa_layer_workspace_bytes(ctypes.byref(good), 32, 1)
+    assert need > 0 and call(good, ws_bytes=need - 1) == -4
+    assert lib.ipa_layer_workspace_bytes(ctypes.byref(bd.make_dims(1, 64, 4, 32, 4, 8, 2, 16)), 32, 1) == 0

@@ -1,0 +1,76 @@
+"""GPU parity of the full IPA layer (ipa_layer_forward) against the fp64
+layer oracle, through the C ABI.
+
+Tolerance on the output, relative to its scale (max(1, max |reference|)):
+fp32 storage 1e-4 (fp32 projections and readout, sums of a few hundred
+terms, around the fp32 attention); bf16 storage 3e-2 (the attention's own
+bf16 bound; a projected feature that lands on a bf16 rounding boundary may
+round the other way on the two sides, one bf16 ulp, well inside it).
+Masked rows must be exact +0.0.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ipa_layer
+from workloads import WORKLOADS, make_layer_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(inp, device):
+    from geometric_invariant_attention_amd import IPALayer
+    d = inp["dims"]
+    dt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    t = {k: torch.from_numpy(inp[k]).to(device) for k in ("s", "rot", "trans", "w_in", "b_in", "w_b",
+                                                          "gamma", "w_out", "b_out")}
+    m = torch.from_numpy(inp["mask"]).to(device) if inp.get("has_mask") else None
+    layer = IPALayer(**d, c_s=inp["c_s"], dtype=dt, device=device)
+    y = layer(t["s"], t["rot"], t["trans"], t["w_in"], t["b_in"], t["w_b"], t["gamma"], t["w_out"],
+              t["b_out"], mask=m, w_L=inp["w_L"], w_C=inp["w_C"])
+    torch.cuda.synchronize()
+    return y.cpu().numpy().copy()
+
+
+def _check(w, device, c_s, tol, seed=0):
+    print(f"[layer] {w.name} dims={w.dims()} c_s={c_s} dtype={w.dtype} seed={seed}", flush=True)
+    inp = make_layer_inputs(w, c_s=c_s, seed=seed)
+    got = _gpu(inp, device)
+    ref = ipa_layer(inp)
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref).max()) / max(1.0, float(np.abs(ref).max()))
+    print(f"  rel error {err:.2e}", flush=True)
+    assert err < tol, err
+    return inp, got
+
+
+@pytest.mark.parametrize("L,c_s", [(1, 8), (37, 24), (64, 96)])
+def test_layer_fp32(device, L, c_s):
+    _check(WORKLOADS["tiny_fp32"].with_(L=L, H=4), device, c_s, 1e-4, seed=L)
+
+
+def test_layer_bf16_single_chain(device):
+    _check(WORKLOADS["single_chain"].with_(L=200), device, 384, 3e-2)
+
+
+def test_layer_ragged_batch_masked_rows_zero(device):
+    inp, got = _check(WORKLOADS["ragged_batch"].with_(B=4, L=70, ragged=(30, 70)), device, 128, 3e-2, seed=2)
+    pad = inp["mask"] == 0
+    assert np.all(got[pad] == 0) and not np.signbit(got[pad]).any()
+
+
+def test_layer_no_biases(device):
+    from geometric_invariant_attention_amd import IPALayer
+    w = WORKLOADS["tiny_fp32"].with_(L=33, H=3)
+    inp = make_layer_inputs(w, c_s=16, seed=5)
+    d = inp["dims"]
+    t = {k: torch.from_numpy(inp[k]).to(device) for k in ("s", "rot", "trans", "w_in", "w_b", "gamma", "w_out")}
+    y = IPALayer(**d, c_s=16, dtype=torch.float32, device=device)(
+        t["s"], t["rot"], t["trans"], t["w_in"], None, t["w_b"], t["gamma"], t["w_out"], None,
+        w_L=inp["w_L"], w_C=inp["w_C"])
+    torch.cuda.synchronize()
+    inp["b_in"] = np.zeros_like(inp["b_in"])
+    inp["b_out"] = np.zeros_like(inp["b_out"])
+    ref = ipa_layer(inp)
+    assert np.abs(y.cpu().numpy() - ref).max() / max(1.0, np.abs(ref).max()) < 1e-4
