@@ -429,6 +429,53 @@ def bench_backward(dev, steps: int, warmup: int, cpu: bool) -> dict:
     return res
 
 
+def bench_layer(dev, steps: int, warmup: int, cpu: bool) -> dict:
+    """The full IPA layer (ipa_layer_forward) at the long_chain_2048
+    dimensions with a 384-wide single representation, bf16 attention: the
+    whole layer timed like the IPA step; the projections' and readout's
+    share is the difference to the bare attention step."""
+    import numpy as np
+    import torch
+    from geometric_invariant_attention_amd import IPALayer
+    from workloads import WORKLOADS, make_layer_inputs
+    w = WORKLOADS["long_chain_2048"]
+    c_s = 384
+    inp = make_layer_inputs(w, c_s=c_s)
+    d = w.dims()
+    t = {k: torch.from_numpy(inp[k]).to(dev) for k in ("s", "rot", "trans", "w_in", "b_in", "w_b",
+                                                       "gamma", "w_out", "b_out")}
+    layer = IPALayer(**d, c_s=c_s, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    raw = layer.bind(t["s"], t["rot"], t["trans"], t["w_in"], t["b_in"], t["w_b"], t["gamma"],
+                     t["w_out"], t["b_out"], w_L=inp["w_L"], w_C=inp["w_C"], stream=stream)
+    for _ in range(warmup):
+        layer.forward_raw(raw)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward_raw(raw)
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    rows = d["B"] * d["L"]
+    n_in = layer.n_in
+    gemm_flops = 2.0 * rows * c_s * (n_in + layer.n_out)
+    res = {"workload": w.name, "config": {**d, "c_s": c_s, "storage": "bf16"}, "ms_per_call": ms,
+           "pairs_per_s": d["B"] * d["L"] * d["L"] / (ms * 1e-3),
+           "projection_readout_gflop": gemm_flops / 1e9}
+    if cpu:
+        from oracle import ipa_layer
+        ci = make_layer_inputs(w.with_(L=256), c_s=c_s)
+        c0, w0 = time.process_time(), time.perf_counter()
+        ipa_layer(ci)
+        wall = time.perf_counter() - w0
+        res["cpu_baseline"] = {"value": 256 * 256 / wall, "unit": "pairs/s",
+                               "cores": max(1, round((time.process_time() - c0) / max(wall, 1e-9))),
+                               "kind": "oracle",
+                               "sample": f"fp64 layer oracle on a 256-residue chain with the same dimensions, "
+                                         f"{wall:.2f} s wall, scaled per pair"}
+    return res
+
+
 def memory_sweep(dev, Ls, H=12, Cz=128):
     """Peak device memory (inputs + outputs + workspace) of one forward."""
     import torch
@@ -563,6 +610,8 @@ def main(argv=None) -> int:
     print(f"[bench] distance attention: {result['meet']['ms_per_call'] * 1e3:.1f} us/call, "
           f"{result['meet']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     result["frames"] = bench_frames(dev, args.steps, 20, args.cpu_budget > 0)
+    print("[bench] layer", file=sys.stderr, flush=True)
+    result["layer"] = bench_layer(dev, args.steps, args.warmup, args.cpu_budget > 0)
     print("[bench] backward", file=sys.stderr, flush=True)
     result["backward"] = bench_backward(dev, args.steps, args.warmup, args.cpu_budget > 0)
     print("[bench] direction-and-distance attention", file=sys.stderr, flush=True)

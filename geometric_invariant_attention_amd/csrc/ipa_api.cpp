@@ -397,9 +397,16 @@ int32_t ipa_backward(const ipa_dims* dims, const float* q, const float* k, const
 
 namespace {
 
+// The full layer is four launches around the attention: x = s W_in + b_in
+// as one GEMM whose epilogue writes each column block straight into the
+// attention's input array in its storage type; the attention; a gather of
+// its four outputs into one row-major matrix; and
+// y = [o_s | o_pts | o_norm | o_pair] W_out + b_out as one GEMM with the
+// reduction split across the grid, the partials added in order with the
+// bias by a second kernel that also zeroes masked rows.
 struct LayerLayout {
-  size_t off_x, off_feat[8], off_ipa, off_out[4], total, ipa_bytes;
-  int n_in, n_out, widths[8];
+  size_t off_feat[8], off_ipa, off_out[4], off_cat, off_part, total, ipa_bytes;
+  int n_in, n_out, widths[8], splits;
 };
 
 bool layer_layout(const ipa_dims* d, int32_t c_s, int32_t dtype, LayerLayout* o) {
@@ -414,16 +421,26 @@ bool layer_layout(const ipa_dims* d, int32_t c_s, int32_t dtype, LayerLayout* o)
   for (int e = 0; e < 8; ++e) { o->widths[e] = w[e]; n_in += w[e]; }
   o->n_in = n_in;
   o->n_out = (int)(H * (C + 3 * Pv + Pv + Cz));
-  if (B * L * (int64_t)n_in >= (int64_t(1) << 31) || B * L * (int64_t)c_s >= (int64_t(1) << 31)) return false;
-  const size_t rows = (size_t)(B * L), es = dtype == IPA_BF16 ? 2 : 4;
+  const int64_t rows = B * L;
+  if (rows * (int64_t)n_in >= (int64_t(1) << 31) || rows * (int64_t)c_s >= (int64_t(1) << 31) ||
+      rows * (int64_t)o->n_out >= (int64_t(1) << 31))
+    return false;
+  // readout reduction slices: enough workgroups to fill the chip, >= 64 steps each
+  const int64_t tiles = ((rows + 63) / 64) * ((c_s + 63) / 64);
+  int sp = (int)((1024 + tiles - 1) / tiles);
+  const int cap = (o->n_out + 63) / 64;
+  o->splits = sp < 1 ? 1 : (sp > cap ? cap : sp);
+  if (o->splits * rows * (int64_t)c_s >= (int64_t(1) << 31)) return false;
+  const size_t es = dtype == IPA_BF16 ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = ipa::align256(off + bytes); return at; };
-  o->off_x = take(rows * n_in * 4);
-  for (int e = 0; e < 8; ++e) o->off_feat[e] = take(rows * w[e] * es);
+  for (int e = 0; e < 8; ++e) o->off_feat[e] = take((size_t)rows * w[e] * es);
   o->off_ipa = take(ipa_bytes);
   o->ipa_bytes = ipa_bytes;
   const size_t outw[4] = {(size_t)(H * C), (size_t)(H * Pv * 3), (size_t)(H * Pv), (size_t)(H * Cz)};
-  for (int e = 0; e < 4; ++e) o->off_out[e] = take(rows * outw[e] * 4);
+  for (int e = 0; e < 4; ++e) o->off_out[e] = take((size_t)rows * outw[e] * 4);
+  o->off_cat = take((size_t)rows * o->n_out * 4);
+  o->off_part = take((size_t)o->splits * rows * c_s * 4);
   o->total = off;
   return true;
 }
@@ -461,45 +478,51 @@ int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   const long long rows = (long long)dims->B * dims->L;
-  float* x = reinterpret_cast<float*>(ws + ly.off_x);
-  // x = s W_in + b_in
+  // x = s W_in + b_in, each column block written straight into the
+  // attention's input array in its storage type
+  void* feat[8];
+  for (int e = 0; e < 8; ++e) feat[e] = ws + ly.off_feat[e];
   ipa::Gemm g{};
   g.M = (int)rows; g.N = ly.n_in; g.K = c_s;
   g.A = s; g.am = c_s; g.ak = 1;
   g.B = w_in; g.bk = ly.n_in; g.bn = 1;
-  g.C = x; g.cm = ly.n_in; g.bias = b_in;
-  if (ipa::gemm(g, 1, st) != hipSuccess) return IPA_ERR_HIP;
-  ipa::LayerSplit sp{};
-  sp.x = x; sp.rows = rows; sp.n_in = ly.n_in; sp.bf16 = dtype == IPA_BF16;
+  g.bias = b_in;
+  g.nseg = 8; g.seg_bf16 = dtype == IPA_BF16;
   int c0 = 0;
   for (int e = 0; e < 8; ++e) {
-    sp.start[e] = c0;
+    g.seg_start[e] = c0;
     c0 += ly.widths[e];
-    sp.out[e] = ws + ly.off_feat[e];
+    g.seg_out[e] = feat[e];
   }
-  sp.start[8] = c0;
-  if (ipa::launch_layer_split(sp, st) != hipSuccess) return IPA_ERR_HIP;
+  g.seg_start[8] = c0;
+  if (ipa::gemm(g, 1, st) != hipSuccess) return IPA_ERR_HIP;
   // the attention
   float* o[4];
   for (int e = 0; e < 4; ++e) o[e] = reinterpret_cast<float*>(ws + ly.off_out[e]);
-  const int32_t rc = ipa_forward(dims, dtype, sp.out[0], sp.out[1], sp.out[2], sp.out[3], sp.out[4],
-                                 sp.out[5], rot, trans, sp.out[6], sp.out[7], w_b, gamma, mask, w_L, w_C,
-                                 o[0], o[1], o[2], o[3], ws + ly.off_ipa, ly.ipa_bytes, stream);
+  const int32_t rc = ipa_forward(dims, dtype, feat[0], feat[1], feat[2], feat[3], feat[4], feat[5], rot, trans,
+                                 feat[6], feat[7], w_b, gamma, mask, w_L, w_C, o[0], o[1], o[2], o[3],
+                                 ws + ly.off_ipa, ly.ipa_bytes, stream);
   if (rc != IPA_OK) return rc;
   // y = [o_s | o_pts | o_norm | o_pair] W_out + b_out, masked rows 0
   const int H = dims->H, C = dims->C, Pv = dims->Pv, Cz = dims->Cz;
+  ipa::LayerGather ga{};
   const int wo[4] = {H * C, H * Pv * 3, H * Pv, H * Cz};
   int r0 = 0;
   for (int e = 0; e < 4; ++e) {
-    ipa::Gemm q{};
-    q.M = (int)rows; q.N = c_s; q.K = wo[e];
-    q.A = o[e]; q.am = wo[e]; q.ak = 1;
-    q.B = w_out + (size_t)r0 * c_s; q.bk = c_s; q.bn = 1;
-    q.C = out; q.cm = c_s; q.acc = e > 0;
-    if (e == 3) { q.bias = b_out; q.rowmask = mask; }
-    if (ipa::gemm(q, 1, st) != hipSuccess) return IPA_ERR_HIP;
+    ga.src[e] = o[e];
+    ga.start[e] = r0;
     r0 += wo[e];
   }
+  ga.start[4] = r0;
+  ga.rows = rows; ga.n_out = ly.n_out;
+  ga.cat = reinterpret_cast<float*>(ws + ly.off_cat);
+  if (ipa::launch_layer_gather(ga, st) != hipSuccess) return IPA_ERR_HIP;
+  ipa::Gemm q{};
+  q.M = (int)rows; q.N = c_s; q.K = ly.n_out;
+  q.A = ga.cat; q.am = ly.n_out; q.ak = 1;
+  q.B = w_out; q.bk = c_s; q.bn = 1;
+  q.C = out; q.cm = c_s; q.bias = b_out; q.rowmask = mask;
+  if (ipa::gemm_splitk(q, ly.splits, reinterpret_cast<float*>(ws + ly.off_part), st) != hipSuccess) return IPA_ERR_HIP;
   return IPA_OK;
 }
 

@@ -125,23 +125,30 @@ struct Gemm {
   int acc;
   const float* bias;        // [N] or NULL
   const uint8_t* rowmask;   // [M] or NULL
+  int kpart;                // set by gemm_splitk: reduction slice per grid z
+  int nseg;                 // > 0: segmented output (C unused)
+  int seg_start[9];         // first column of each block, then N
+  void* seg_out[8];         // block b stored [M][width_b]
+  int seg_bf16;             // blocks stored as bf16 (nearest even)
 };
 hipError_t gemm(const Gemm& g, int batch, hipStream_t s);
+// the reduction split into `splits` slices along the grid; partials in
+// `part` ([splits][M][N] floats), then reduced in order into g.C (row
+// stride N) with g.bias and g.rowmask; g.acc must be 0
+hipError_t gemm_splitk(const Gemm& g, int splits, float* part, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Full layer (ipa_layer.hip): x [rows][n_in] -> the attention's 8 input
-// arrays (q, k, v, q_pts, k_pts, v_pts, z1, z2), fp32 or bf16 (nearest even)
+// Full layer (ipa_layer.hip): the attention's four outputs gathered into one
+// row-major matrix [rows][n_out] for the readout
 // ---------------------------------------------------------------------------
-constexpr int kLayerBlocks = 8;
-struct LayerSplit {
-  const float* x;
+struct LayerGather {
+  const float* src[4];   // o_s, o_pts, o_norm, o_pair, each [rows][width]
+  int start[5];          // first column of each block, then n_out
   long long rows;
-  int n_in;
-  int start[kLayerBlocks + 1];   // first column of each block, then n_in
-  void* out[kLayerBlocks];
-  int bf16;
+  int n_out;
+  float* cat;
 };
-hipError_t launch_layer_split(const LayerSplit& a, hipStream_t s);
+hipError_t launch_layer_gather(const LayerGather& g, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Gradient of the IPA forward (ipa_bwd.hip), float32
