@@ -14,112 +14,188 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 //   C[z](m, n) = sum_k A[z](m, k) B[z](k, n)  (+ C[z](m, n) when acc)
 // with A(m, k) at A + z sAb + m am + k ak, B(k, n) at B + z sBb + k bk + n bn,
 // C(m, n) at C + z sCb + m cm + n, then + bias[n] and rows m with
-// rowmask[m] == 0 set to 0 when those are given. A workgroup of four waves owns a 64 x 64
-// tile (a 32 x 32 quadrant per wave); the reduction runs in steps of 32,
-// each step's A and B slices staged in LDS with loads along whichever of
-// their two strides is 1, the next step's loads in flight in registers
-// while this step's 16 products per wave run. Options: the reduction split
-// over the grid's z (partials reduced in order by a second kernel), and a
-// segmented epilogue that writes column blocks to separate arrays (fp32 or
-// bf16).
+// rowmask[m] == 0 set to 0 when those are given.
+//
+// A workgroup of four waves (2 x 2) owns a (64 TM) x (64 TN) tile, each wave
+// TM x TN blocks of 32 x 32. The reduction runs in steps of 32: the step's
+// A and B slices are staged in LDS k-contiguous ([m][k] and [n][k], rows
+// padded to 36 floats), loaded from global memory along whichever of their
+// two strides is 1, the next step's loads in flight in registers while this
+// step's products run. Within a step, product s (0..15) takes reduction
+// indices s (lanes 0-31) and 16 + s (lanes 32-63), so that every lane reads
+// its operands for the whole step as four 16-byte LDS reads per block.
+// Options: the reduction split over the grid's z (partials reduced in order
+// by a second kernel), and a segmented epilogue that writes column blocks to
+// separate arrays (fp32 or bf16).
 // ---------------------------------------------------------------------------
+template <int TM, int TN, bool AK1, bool BK1>
 __global__ __launch_bounds__(256) void gemm_kernel(Gemm g) {
-  constexpr int KS = 32;   // reduction step
+  constexpr int KS = 32;              // reduction step
+  constexpr int PK = KS + 4;          // LDS row pitch (floats)
+  constexpr int BM = 64 * TM, BN = 64 * TN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w & 1, wn = w >> 1, half = lane >> 5, l32 = lane & 31;
-  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64, z = blockIdx.z;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN, z = blockIdx.z;
   // z indexes the batch, or the slice of the reduction when it is split
   const int kbeg = g.kpart ? z * g.kpart : 0;
   const int kend = g.kpart ? (g.K < kbeg + g.kpart ? g.K : kbeg + g.kpart) : g.K;
   const float* A = g.A + (g.kpart ? 0 : (size_t)z * g.sAb);
   const float* B = g.B + (g.kpart ? 0 : (size_t)z * g.sBb);
-  __shared__ float As[KS][64 + 4], Bs[KS][64 + 4];
-  // element u of this thread's share of the A slice (64 m x KS k) and of
-  // the B slice (KS k x 64 n), chosen so that consecutive threads read
-  // consecutive addresses
-  const bool a_k1 = g.ak == 1, b_n1 = g.bn == 1;
+  __shared__ __attribute__((aligned(16))) float As[BM][PK];
+  __shared__ __attribute__((aligned(16))) float Bs[BN][PK];
+  // Element u of this thread's share of the A slice (BM m x KS k) and of
+  // the B slice (KS k x BN n), chosen so that consecutive threads read
+  // consecutive addresses: along k when that stride is 1 (AK1 / BK1),
+  // along m / n otherwise (then that stride is 1).
+  constexpr int NA = BM * KS / 256, NB = BN * KS / 256;
   auto a_mk = [&](int u, int& m, int& k) {
-    const int e = tid + 256 * u;
-    if (a_k1) { k = e & (KS - 1); m = e / KS; } else { m = e & 63; k = e >> 6; }
+    if (AK1) { k = tid & (KS - 1); m = (tid >> 5) + 8 * u; }
+    else { m = tid % BM; k = tid / BM + (256 / BM) * u; }
   };
   auto b_kn = [&](int u, int& k, int& n) {
-    const int e = tid + 256 * u;
-    if (b_n1) { n = e & 63; k = e >> 6; } else { k = e & (KS - 1); n = e / KS; }
+    if (BK1) { k = tid & (KS - 1); n = (tid >> 5) + 8 * u; }
+    else { n = tid % BN; k = tid / BN + (256 / BN) * u; }
   };
-  constexpr int NU = 64 * KS / 256;
-  float ra[NU], rb[NU];
-  auto gload = [&](int k0) {
+  // Offsets (in elements, below 2^31) of each element at reduction index 0;
+  // rows past M and columns past N read row / column M - 1 / N - 1 and are
+  // zeroed. Only a step that runs past kend clamps the reduction index.
+  int oa[NA], ob[NB];
+  bool va[NA], vb[NB];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      int m, k;
-      a_mk(u, m, k);
-      const int gm = m0 + m, gk = k0 + k;
-      ra[u] = (gm < g.M && gk < kend) ? A[(size_t)gm * g.am + (size_t)gk * g.ak] : 0.f;
-      int kb, n;
-      b_kn(u, kb, n);
-      const int gkb = k0 + kb, gn = n0 + n;
-      rb[u] = (gkb < kend && gn < g.N) ? B[(size_t)gkb * g.bk + (size_t)gn * g.bn] : 0.f;
+  for (int u = 0; u < NA; ++u) {
+    int m, k;
+    a_mk(u, m, k);
+    va[u] = m0 + m < g.M;
+    const int mm = va[u] ? m0 + m : g.M - 1;
+    oa[u] = AK1 ? mm * (int)g.am + k : mm + k * (int)g.ak;
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    int k, n;
+    b_kn(u, k, n);
+    vb[u] = n0 + n < g.N;
+    const int nn = vb[u] ? n0 + n : g.N - 1;
+    ob[u] = BK1 ? nn * (int)g.bn + k : nn + k * (int)g.bk;
+  }
+  const int ak = AK1 ? 1 : (int)g.ak, bk = BK1 ? 1 : (int)g.bk;
+  float ra[NA], rb[NB];
+  auto gload = [&](int k0) {
+    if (k0 + KS <= kend) {
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        const float v = A[(unsigned)(oa[u] + k0 * ak)];
+        ra[u] = va[u] ? v : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const float v = B[(unsigned)(ob[u] + k0 * bk)];
+        rb[u] = vb[u] ? v : 0.f;
+      }
+    } else {
+      // last, partial step: indices past kend read index kend - 1, zeroed
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        int m, k;
+        a_mk(u, m, k);
+        const bool in = k0 + k < kend;
+        const int back = in ? 0 : (k0 + k - (kend - 1)) * ak;
+        const float v = A[(unsigned)(oa[u] + k0 * ak - back)];
+        ra[u] = (va[u] && in) ? v : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        int k, n;
+        b_kn(u, k, n);
+        const bool in = k0 + k < kend;
+        const int back = in ? 0 : (k0 + k - (kend - 1)) * bk;
+        const float v = B[(unsigned)(ob[u] + k0 * bk - back)];
+        rb[u] = (vb[u] && in) ? v : 0.f;
+      }
     }
   };
-  gload(kbeg);
-  floatx16 c = {};
+  if (kbeg < kend) gload(kbeg);
+  floatx16 c[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) c[i][j] = floatx16{};
   for (int k0 = kbeg; k0 < kend; k0 += KS) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      int m, k, kb, n;
+    for (int u = 0; u < NA; ++u) {
+      int m, k;
       a_mk(u, m, k);
-      b_kn(u, kb, n);
-      As[k][m] = ra[u];
-      Bs[kb][n] = rb[u];
+      As[m][k] = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      int k, n;
+      b_kn(u, k, n);
+      Bs[n][k] = rb[u];
     }
     __syncthreads();
     if (k0 + KS < kend) gload(k0 + KS);
     __builtin_amdgcn_sched_barrier(0);   // the next step's loads go out before the products
-    float av[KS / 2], bv[KS / 2];
 #pragma unroll
-    for (int s2 = 0; s2 < KS / 2; ++s2) {
-      av[s2] = As[2 * s2 + half][32 * wm + l32];
-      bv[s2] = Bs[2 * s2 + half][32 * wn + l32];
+    for (int q = 0; q < 4; ++q) {
+      float4 av[TM], bv[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        av[i] = *reinterpret_cast<const float4*>(&As[32 * (wm * TM + i) + l32][16 * half + 4 * q]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bv[j] = *reinterpret_cast<const float4*>(&Bs[32 * (wn * TN + j) + l32][16 * half + 4 * q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            c[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][e], bv[j][e], c[i][j], 0, 0, 0);
     }
-#pragma unroll
-    for (int s2 = 0; s2 < KS / 2; ++s2) c = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s2], bv[s2], c, 0, 0, 0);
     __syncthreads();
   }
-  const int n = n0 + 32 * wn + l32;
-  if (n >= g.N) return;
-  if (g.nseg > 0) {
-    // segmented output: column n belongs to block blk of width w, stored
-    // [m][w] in fp32 or bf16 (nearest even)
-    int blk = 0;
-    while (blk + 1 < g.nseg && n >= g.seg_start[blk + 1]) ++blk;
-    const int wd = g.seg_start[blk + 1] - g.seg_start[blk], nc = n - g.seg_start[blk];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = m0 + 32 * wm + 8 * (e >> 2) + 4 * half + (e & 3);
-      if (m >= g.M) continue;
-      float v = c[e];
-      if (g.bias) v += g.bias[n];
-      const size_t at = (size_t)m * wd + nc;
-      if (g.seg_bf16) {
-        const uint32_t u = __float_as_uint(v);
-        reinterpret_cast<uint16_t*>(g.seg_out[blk])[at] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-      } else {
-        reinterpret_cast<float*>(g.seg_out[blk])[at] = v;
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + 32 * (wn * TN + j) + l32;
+    if (n >= g.N) continue;
+    if (g.nseg > 0) {
+      // segmented output: column n belongs to block blk of width wd, stored
+      // [m][wd] in fp32 or bf16 (nearest even)
+      int blk = 0;
+      while (blk + 1 < g.nseg && n >= g.seg_start[blk + 1]) ++blk;
+      const int wd = g.seg_start[blk + 1] - g.seg_start[blk], nc = n - g.seg_start[blk];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 32 * (wm * TM + i) + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (m >= g.M) continue;
+          float v = c[i][j][e];
+          if (g.bias) v += g.bias[n];
+          const size_t at = (size_t)m * wd + nc;
+          if (g.seg_bf16) {
+            const uint32_t u = __float_as_uint(v);
+            reinterpret_cast<uint16_t*>(g.seg_out[blk])[at] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+          } else {
+            reinterpret_cast<float*>(g.seg_out[blk])[at] = v;
+          }
+        }
+      continue;
+    }
+    float* C = g.C + (size_t)z * g.sCb;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * (wm * TM + i) + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (m < g.M) {
+          float* dst = C + (size_t)m * g.cm + n;
+          float v = g.acc ? *dst + c[i][j][e] : c[i][j][e];
+          if (g.bias) v += g.bias[n];
+          if (g.rowmask && !g.rowmask[m]) v = 0.f;
+          *dst = v;
+        }
       }
-    }
-    return;
-  }
-  float* C = g.C + (size_t)z * g.sCb;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int m = m0 + 32 * wm + 8 * (e >> 2) + 4 * half + (e & 3);
-    if (m < g.M) {
-      float* dst = C + (size_t)m * g.cm + n;
-      float v = g.acc ? *dst + c[e] : c[e];
-      if (g.bias) v += g.bias[n];
-      if (g.rowmask && !g.rowmask[m]) v = 0.f;
-      *dst = v;
-    }
   }
 }
 
@@ -138,13 +214,56 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
   out[t] = v;
 }
 
-}  // namespace
+// Tile shape for an M x N product over `z` grid slices: among the shapes
+// that give at least 1.5 workgroups per compute unit, the one with the least
+// padded work per unit of speed (larger tiles reuse each staged operand
+// more often); otherwise the shape with the most workgroups.
+struct TileShape { int tm, tn; };
+TileShape pick_tile(int M, int N, int z) {
+  const TileShape cand[4] = {{2, 2}, {2, 1}, {1, 2}, {1, 1}};
+  const double speed[4] = {1.0, 0.85, 0.85, 0.65};
+  int best = -1, most = 3;
+  double best_cost = 0.0;
+  long long most_wg = 0;
+  for (int c = 0; c < 4; ++c) {
+    const long long gm = (M + 64 * cand[c].tm - 1) / (64 * cand[c].tm), gn = (N + 64 * cand[c].tn - 1) / (64 * cand[c].tn);
+    const long long wg = gm * gn * z;
+    const double cost = (double)(gm * 64 * cand[c].tm) * (double)(gn * 64 * cand[c].tn) / speed[c];
+    if (wg >= 384 && (best < 0 || cost < best_cost)) { best = c; best_cost = cost; }
+    if (wg > most_wg) { most_wg = wg; most = c; }
+  }
+  return cand[best >= 0 ? best : most];
+}
 
-hipError_t gemm(const Gemm& g, int batch, hipStream_t s) {
-  const dim3 grid((g.M + 63) / 64, (g.N + 63) / 64, batch);
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, g);
+template <int TM, int TN>
+void launch_shape(const Gemm& g, dim3 grid, hipStream_t s) {
+  const bool ak1 = g.ak == 1, bk1 = g.bk == 1;
+  if (ak1 && bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, true>), grid, dim3(256), 0, s, g);
+  else if (ak1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, false>), grid, dim3(256), 0, s, g);
+  else if (bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, false, true>), grid, dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gemm_kernel<TM, TN, false, false>), grid, dim3(256), 0, s, g);
+}
+
+hipError_t launch_gemm(const Gemm& g, int z, hipStream_t s) {
+  // one of each operand's two strides is 1, and every element of one
+  // batch slice lies within 2^31 elements of its start
+  if (!(g.ak == 1 || g.am == 1) || !(g.bk == 1 || g.bn == 1)) return hipErrorInvalidValue;
+  if ((double)(g.M - 1) * g.am + (double)(g.K - 1) * g.ak >= 2147483647.0 ||
+      (double)(g.K - 1) * g.bk + (double)(g.N - 1) * g.bn >= 2147483647.0)
+    return hipErrorInvalidValue;
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  const TileShape t = pick_tile(g.M, g.N, z);
+  const dim3 grid((g.M + 64 * t.tm - 1) / (64 * t.tm), (g.N + 64 * t.tn - 1) / (64 * t.tn), z);
+  if (t.tm == 2 && t.tn == 2) launch_shape<2, 2>(g, grid, s);
+  else if (t.tm == 2) launch_shape<2, 1>(g, grid, s);
+  else if (t.tn == 2) launch_shape<1, 2>(g, grid, s);
+  else launch_shape<1, 1>(g, grid, s);
   return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t gemm(const Gemm& g, int batch, hipStream_t s) { return launch_gemm(g, batch, s); }
 
 hipError_t gemm_splitk(const Gemm& g0, int splits, float* part, hipStream_t s) {
   Gemm g = g0;
@@ -152,9 +271,7 @@ hipError_t gemm_splitk(const Gemm& g0, int splits, float* part, hipStream_t s) {
   const int used = (g.K + g.kpart - 1) / g.kpart;
   g.C = part; g.cm = g.N; g.sCb = (long long)g.M * g.N; g.acc = 0;
   g.bias = nullptr; g.rowmask = nullptr; g.nseg = 0;
-  const dim3 grid((g.M + 63) / 64, (g.N + 63) / 64, used);
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, g);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (launch_gemm(g, used, s) != hipSuccess) return hipErrorLaunchFailure;
   const long long total = (long long)g.M * g.N;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                      part, used, g.M, g.N, g0.bias, g0.rowmask, g0.C);
