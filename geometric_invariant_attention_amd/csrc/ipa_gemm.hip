@@ -4,10 +4,18 @@
 
 #include "ipa_internal.h"
 
+#include <type_traits>
+
 namespace ipa {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Compiler fence: memory operations stay on their side of it.
+__device__ __forceinline__ void fence() { asm volatile("" ::: "memory"); }
+// An empty, ordered statement that takes an accumulator tile in place: a
+// product whose result passes through it stays between its fences.
+__device__ __forceinline__ void pin(floatx16& acc) { asm volatile("" : "+a"(acc)); }
 
 // ---------------------------------------------------------------------------
 // Batched fp32 GEMM on v_mfma_f32_32x32x2f32:
@@ -19,9 +27,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // A workgroup of four waves (2 x 2) owns a (64 TM) x (64 TN) tile, each wave
 // TM x TN blocks of 32 x 32. The reduction runs in steps of 32: the step's
 // A and B slices are staged in LDS k-contiguous ([m][k] and [n][k], rows
-// padded to 36 floats), loaded from global memory along whichever of their
-// two strides is 1, the next step's loads in flight in registers while this
-// step's products run. Within a step, product s (0..15) takes reduction
+// padded to 36 floats, two buffers), loaded from global memory along
+// whichever of their two strides is 1; the next step's loads and LDS writes
+// are spread over this step's products. Within a step, product s (0..15) takes reduction
 // indices s (lanes 0-31) and 16 + s (lanes 32-63), so that every lane reads
 // its operands for the whole step as four 16-byte LDS reads per block.
 // Options: the reduction split over the grid's z (partials reduced in order
@@ -29,7 +37,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // separate arrays (fp32 or bf16).
 // ---------------------------------------------------------------------------
 template <int TM, int TN, bool AK1, bool BK1>
-__global__ __launch_bounds__(256) void gemm_kernel(Gemm g) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(Gemm g) {
   constexpr int KS = 32;              // reduction step
   constexpr int PK = KS + 4;          // LDS row pitch (floats)
   constexpr int BM = 64 * TM, BN = 64 * TN;
@@ -41,8 +49,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(Gemm g) {
   const int kend = g.kpart ? (g.K < kbeg + g.kpart ? g.K : kbeg + g.kpart) : g.K;
   const float* A = g.A + (g.kpart ? 0 : (size_t)z * g.sAb);
   const float* B = g.B + (g.kpart ? 0 : (size_t)z * g.sBb);
-  __shared__ __attribute__((aligned(16))) float As[BM][PK];
-  __shared__ __attribute__((aligned(16))) float Bs[BN][PK];
+  // two buffers per operand: step s reads buffer s & 1 while the next
+  // step's slices are written into the other
+  __shared__ __attribute__((aligned(16))) float As[2][BM][PK];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BN][PK];
   // Element u of this thread's share of the A slice (BM m x KS k) and of
   // the B slice (KS k x BN n), chosen so that consecutive threads read
   // consecutive addresses: along k when that stride is 1 (AK1 / BK1),
@@ -79,18 +89,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(Gemm g) {
   }
   const int ak = AK1 ? 1 : (int)g.ak, bk = BK1 ? 1 : (int)g.bk;
   float ra[NA], rb[NB];
+  // element u of a full step: A for u < NA, then B
+  // (rows / columns out of range are zeroed when staged, so that nothing
+  // waits for a load before its LDS write)
+  auto load_one = [&](int k0, int u) {
+    if (u < NA) ra[u] = A[(unsigned)(oa[u] + k0 * ak)];
+    else rb[u - NA] = B[(unsigned)(ob[u - NA] + k0 * bk)];
+  };
+  auto stage_one = [&](int p, int u) {
+    if (u < NA) {
+      int m, k;
+      a_mk(u, m, k);
+      As[p][m][k] = va[u] ? ra[u] : 0.f;
+    } else {
+      int k, n;
+      b_kn(u - NA, k, n);
+      Bs[p][n][k] = vb[u - NA] ? rb[u - NA] : 0.f;
+    }
+  };
   auto gload = [&](int k0) {
     if (k0 + KS <= kend) {
 #pragma unroll
-      for (int u = 0; u < NA; ++u) {
-        const float v = A[(unsigned)(oa[u] + k0 * ak)];
-        ra[u] = va[u] ? v : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const float v = B[(unsigned)(ob[u] + k0 * bk)];
-        rb[u] = vb[u] ? v : 0.f;
-      }
+      for (int u = 0; u < NA + NB; ++u) load_one(k0, u);
     } else {
       // last, partial step: indices past kend read index kend - 1, zeroed
 #pragma unroll
@@ -113,47 +133,71 @@ __global__ __launch_bounds__(256) void gemm_kernel(Gemm g) {
       }
     }
   };
-  if (kbeg < kend) gload(kbeg);
   floatx16 c[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) c[i][j] = floatx16{};
-  for (int k0 = kbeg; k0 < kend; k0 += KS) {
+  if (kbeg < kend) {
+    gload(kbeg);
 #pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      int m, k;
-      a_mk(u, m, k);
-      As[m][k] = ra[u];
-    }
+    for (int u = 0; u < NA + NB; ++u) stage_one(0, u);
+  }
+  __syncthreads();
+  // Each step is a fixed sequence of NM products. The operands of quarter
+  // q + 1 of the step (four products per block pair) are read from LDS
+  // while quarter q runs; the next step's global loads go out one or two per
+  // product over the first half and their LDS writes over the second half,
+  // so both run in the products' shadow. Memory operations are held in
+  // their product step by compiler fences.
+  constexpr int NM = 16 * TM * TN, NU = NA + NB, HALF = NM / 2;
+  auto read_q = [&](int p, int q, float4 (&av)[TM], float4 (&bv)[TN]) {
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      int k, n;
-      b_kn(u, k, n);
-      Bs[n][k] = rb[u];
-    }
-    __syncthreads();
-    if (k0 + KS < kend) gload(k0 + KS);
-    __builtin_amdgcn_sched_barrier(0);   // the next step's loads go out before the products
+    for (int i = 0; i < TM; ++i)
+      av[i] = *reinterpret_cast<const float4*>(&As[p][32 * (wm * TM + i) + l32][16 * half + 4 * q]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bv[j] = *reinterpret_cast<const float4*>(&Bs[p][32 * (wn * TN + j) + l32][16 * half + 4 * q]);
+  };
+  // MODE 0: the next step is a full one (its loads spread over the
+  // products); 1: the next step is the partial last one (its loads up
+  // front); 2: no next step.
+  auto iter = [&](int k0, int p, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    if (MODE == 1) gload(k0 + KS);
+    float4 av[2][TM], bv[2][TN];
+    read_q(p, 0, av[0], bv[0]);
+    fence();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float4 av[TM], bv[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        av[i] = *reinterpret_cast<const float4*>(&As[32 * (wm * TM + i) + l32][16 * half + 4 * q]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bv[j] = *reinterpret_cast<const float4*>(&Bs[32 * (wn * TN + j) + l32][16 * half + 4 * q]);
+      if (q < 3) read_q(p, q + 1, av[(q + 1) & 1], bv[(q + 1) & 1]);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            c[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][e], bv[j][e], c[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j) {
+            const int st = 16 * TM * TN / 4 * q + TM * TN * e + TN * i + j;
+            c[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q & 1][i][e], bv[q & 1][j][e], c[i][j], 0, 0, 0);
+            pin(c[i][j]);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              if (MODE == 0 && u * HALF / NU == st) load_one(k0 + KS, u);
+              if (MODE != 2 && HALF + u * HALF / NU == st) stage_one(p ^ 1, u);
+            }
+            fence();
+          }
     }
     __syncthreads();
+  };
+  int k0 = kbeg, p = 0;
+  for (; k0 + 2 * KS <= kend; k0 += KS, p ^= 1) iter(k0, p, std::integral_constant<int, 0>{});
+  if (k0 + KS < kend) {
+    iter(k0, p, std::integral_constant<int, 1>{});
+    k0 += KS;
+    p ^= 1;
   }
+  if (k0 < kend) iter(k0, p, std::integral_constant<int, 2>{});
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int n = n0 + 32 * (wn * TN + j) + l32;
@@ -214,25 +258,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
   out[t] = v;
 }
 
-// Tile shape for an M x N product over `z` grid slices: among the shapes
-// that give at least 1.5 workgroups per compute unit, the one with the least
-// padded work per unit of speed (larger tiles reuse each staged operand
-// more often); otherwise the shape with the most workgroups.
+// Tile shape for an M x N product over `z` grid slices: the shape with the
+// least work on the busiest compute unit, taking workgroups as dealt out
+// evenly (ceil(workgroups / 256) per unit), each costing its padded tile
+// area over the shape's relative speed (larger tiles reuse each staged
+// operand more often; speeds and the single-workgroup penalty measured on
+// the gradient's and the layer's products).
 struct TileShape { int tm, tn; };
 TileShape pick_tile(int M, int N, int z) {
   const TileShape cand[4] = {{2, 2}, {2, 1}, {1, 2}, {1, 1}};
   const double speed[4] = {1.0, 0.85, 0.85, 0.65};
-  int best = -1, most = 3;
+  int best = 3;
   double best_cost = 0.0;
-  long long most_wg = 0;
   for (int c = 0; c < 4; ++c) {
     const long long gm = (M + 64 * cand[c].tm - 1) / (64 * cand[c].tm), gn = (N + 64 * cand[c].tn - 1) / (64 * cand[c].tn);
-    const long long wg = gm * gn * z;
-    const double cost = (double)(gm * 64 * cand[c].tm) * (double)(gn * 64 * cand[c].tn) / speed[c];
-    if (wg >= 384 && (best < 0 || cost < best_cost)) { best = c; best_cost = cost; }
-    if (wg > most_wg) { most_wg = wg; most = c; }
+    const long long per_cu = (gm * gn * z + 255) / 256;
+    // a unit left with one workgroup runs one wave per SIMD, which hides
+    // less of the load and LDS latency
+    const double cost = (double)per_cu * (64.0 * cand[c].tm) * (64.0 * cand[c].tn) / speed[c] * (per_cu == 1 ? 1.4 : 1.0);
+    if (c == 0 || cost < best_cost) { best = c; best_cost = cost; }
   }
-  return cand[best >= 0 ? best : most];
+  return cand[best];
 }
 
 template <int TM, int TN>
