@@ -156,15 +156,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 // one row at a time. X holds S (without the point term) and becomes A; Y
 // holds dP and becomes dS. The head's key points are staged in LDS,
 // coordinate-major, kKeyBlock keys at a time (lane j reads key j: no bank
-// conflicts), so each row reads them from LDS instead of L2.
+// conflicts), together with a per-key bias (0, or -inf for a masked key),
+// so each row reads them from LDS instead of L2. Pass 1 takes the row max
+// and sum kUnroll keys per lane at a time (one rescale per group, no
+// divergent branches); pass 2 writes A and dS.
 // ---------------------------------------------------------------------------
-constexpr int kRowsPerWG = 16, kKeyBlock = 1024, kUnroll = 8;
+constexpr int kRowsPerWG = 16, kKeyBlock = 512, kUnroll = 8;
 
 // e^x for x <= 0 through the hardware base-2 exponential (about 1 ulp)
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc) {
-  __shared__ float kps[kMaxP3][kKeyBlock];
+  __shared__ float kps[kMaxP3 + 1][kKeyBlock];   // rows 0 .. P3 - 1: points; row kMaxP3: key bias
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bh = blockIdx.y, H = a.H, L = a.L, P3 = a.P3;
   const int b = bh / H, h = bh - b * H;
@@ -189,6 +192,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
       const int j = e / P3, c = e - j * P3;
       kps[c][j] = KP[(size_t)(k0 + j) * P3 + c];
     }
+    for (int j = threadIdx.x; j < kKeyBlock; j += 256)
+      kps[kMaxP3][j] = (j < nk && row_valid(a, b, k0 + j)) ? 0.f : -INFINITY;
     __syncthreads();
   };
   auto dist = [&](const float (&q)[kMaxP3], int jj) {
@@ -209,23 +214,29 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
 #pragma unroll
     for (int u = 0; u < kRowsPerWG / 4; ++u) {
       if (!qv[u]) continue;
-      const float* X = a.X + ((size_t)bh * a.QC + r0 + w + 4 * u) * L;
+      const float* X = a.X + ((size_t)bh * a.QC + r0 + w + 4 * u) * L + k0;
       // kUnroll keys per lane at a time: all their loads in flight together
       for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
-        float xv[kUnroll];
+        float sv[kUnroll];
 #pragma unroll
         for (int t = 0; t < kUnroll; ++t) {
           const int jj = jb + 64 * t + lane;
-          xv[t] = jj < nk ? X[k0 + jj] : 0.f;
+          sv[t] = jj < nk ? X[jj] : 0.f;
         }
+        float mt = m[u];
 #pragma unroll
         for (int t = 0; t < kUnroll; ++t) {
           const int jj = jb + 64 * t + lane;
-          if (jj >= nk || !row_valid(a, b, k0 + jj)) continue;
-          const float sj = fmaf(-kappa, dist(qp[u], jj), xv[t]);
-          if (sj > m[u]) { l[u] = l[u] * fexp(m[u] - sj) + 1.f; m[u] = sj; }
-          else l[u] += fexp(sj - m[u]);
+          sv[t] = jj < nk ? fmaf(-kappa, dist(qp[u], jj), sv[t]) + kps[kMaxP3][jj] : -INFINITY;
+          mt = fmaxf(mt, sv[t]);
         }
+        // every key so far masked: nothing to add yet
+        const float sc = mt == -INFINITY ? 0.f : mt;
+        float acc = l[u] * fexp(m[u] - sc);
+#pragma unroll
+        for (int t = 0; t < kUnroll; ++t) acc += fexp(sv[t] - sc);
+        l[u] = acc;
+        m[u] = mt;
       }
     }
   }
@@ -251,31 +262,32 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
       const int r = r0 + w + 4 * u;
       if (r >= qc) continue;
       const float D = a.Dv[(size_t)bh * L + q0 + r];
-      float* X = a.X + ((size_t)bh * a.QC + r) * L;
-      float* Y = a.Y + ((size_t)bh * a.QC + r) * L;
+      float* X = a.X + ((size_t)bh * a.QC + r) * L + k0;
+      float* Y = a.Y + ((size_t)bh * a.QC + r) * L + k0;
+      // a row with no valid key (or a masked row) writes zeros
+      const float mu = m[u] == -INFINITY ? 0.f : m[u];
       for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
         float xv[kUnroll], yv[kUnroll];
 #pragma unroll
         for (int t = 0; t < kUnroll; ++t) {
           const int jj = jb + 64 * t + lane;
-          xv[t] = jj < nk ? X[k0 + jj] : 0.f;
-          yv[t] = jj < nk ? Y[k0 + jj] : 0.f;
+          xv[t] = jj < nk ? X[jj] : 0.f;
+          yv[t] = jj < nk ? Y[jj] : 0.f;
         }
 #pragma unroll
         for (int t = 0; t < kUnroll; ++t) {
           const int jj = jb + 64 * t + lane;
           if (jj >= nk) continue;
-          const int j = k0 + jj;
           float p = 0.f, ds = 0.f;
-          if (qv[u] && row_valid(a, b, j)) {
+          if (qv[u]) {
             const float d = dist(qp[u], jj);
-            p = fexp(fmaf(-kappa, d, xv[t]) - m[u]) * inv[u];
+            p = fexp(fmaf(-kappa, d, xv[t]) + kps[kMaxP3][jj] - mu) * inv[u];
             ds = p * (yv[t] - D);
             rs[u] += ds;
             gs[u] = fmaf(ds, d, gs[u]);
           }
-          X[j] = p;
-          Y[j] = ds;
+          X[jj] = p;
+          Y[jj] = ds;
         }
       }
     }
