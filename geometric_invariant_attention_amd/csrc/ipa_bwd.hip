@@ -188,12 +188,14 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
   }
   auto stage = [&](int k0, int nk) {
     __syncthreads();
-    for (int e = threadIdx.x; e < nk * P3; e += 256) {
-      const int j = e / P3, c = e - j * P3;
-      kps[c][j] = KP[(size_t)(k0 + j) * P3 + c];
-    }
-    for (int j = threadIdx.x; j < kKeyBlock; j += 256)
+    // thread j copies key j's coordinates (no division by P3)
+    for (int j = threadIdx.x; j < kKeyBlock; j += 256) {
+      const float* src = KP + (size_t)(k0 + j) * P3;
+#pragma unroll
+      for (int c = 0; c < kMaxP3; ++c)
+        if (c < P3 && j < nk) kps[c][j] = src[c];
       kps[kMaxP3][j] = (j < nk && row_valid(a, b, k0 + j)) ? 0.f : -INFINITY;
+    }
     __syncthreads();
   };
   auto dist = [&](const float (&q)[kMaxP3], int jj) {
