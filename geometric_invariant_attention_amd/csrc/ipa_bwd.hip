@@ -399,7 +399,7 @@ __global__ __launch_bounds__(64) void bwd_z_kernel(BwdArgs a) {
   float* share = a.share + (size_t)bi * (Cz * H + H);
   if (!row_valid(a, b, i)) {
     for (int r = 0; r < R; ++r) { a.dz1[bi * RCz + r * Cz + c] = 0.f; a.dz2[bi * RCz + r * Cz + c] = 0.f; }
-    for (int h = 0; h < H; ++h) share[c * H + h] = 0.f;
+    for (int h = 0; h < H; ++h) share[h * Cz + c] = 0.f;
     if (c == 0) for (int h = 0; h < H; ++h) share[Cz * H + h] = 0.f;
     return;
   }
@@ -415,8 +415,8 @@ __global__ __launch_bounds__(64) void bwd_z_kernel(BwdArgs a) {
       d1 = fmaf(a.g_pair[((size_t)bi * H + h) * Cz + c], a.U[row * RCz + rc], d1);
       d2 += a.dKA[row * a.DAQ + C + rc] + a.dVA[row * a.DV + C + 3 * Pv + rc];
       // dW_b[c, h] share: w_L z1_irc e_ihrc, summed over r
-      if (r == 0) share[c * H + h] = 0.f;
-      share[c * H + h] = fmaf(a.w_L * z1, e, share[c * H + h]);
+      // (stored [h][c]: consecutive lanes write consecutive floats)
+      share[h * Cz + c] = r == 0 ? a.w_L * z1 * e : fmaf(a.w_L * z1, e, share[h * Cz + c]);
     }
     a.dz1[bi * RCz + rc] = d1;
     a.dz2[bi * RCz + rc] = d2;
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(256) void bwd_reduce2_kernel(BwdArgs a, int nblk) {
   if (col >= ncol) return;
   float v = 0.f;
   for (int k = 0; k < nblk; ++k) v += a.red1[(size_t)k * ncol + col];
-  if (col < a.Cz * a.H) a.dw_b[col] = v;
+  if (col < a.Cz * a.H) a.dw_b[(size_t)(col % a.Cz) * a.H + col / a.Cz] = v;   // share column h Cz + c
   else a.dgamma[col - a.Cz * a.H] = v;
 }
 

@@ -174,7 +174,7 @@ struct BwdArgs {
   float* dKA; float* dVA;
   float* X; float* Y;   // [B H][QC][L] score buffers: S then A, dP then dS
   float* fpart;   // [B][L][H][12]  per-head frame gradient shares
-  float* share;   // [B][L][Cz H + H] per-residue shares of dW_b and dgamma
+  float* share;   // [B][L][H Cz + H] per-residue shares of dW_b ([h][c]) and dgamma
   float* red1;    // [ceil(B L / 128)][Cz H + H] partial column sums of the shares
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
