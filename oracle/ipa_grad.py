@@ -24,7 +24,7 @@ Pinning status (tests/test_grad_pins.py): central finite differences of
 the numpy oracle ``ipa_forward`` along random directions, for every input;
 the torch forward restated here equals ``ipa_forward``; rigid-motion
 invariance of the loss gives zero gradient along the generators of the
-global motion.
+global motion; the row-restricted form (``rows=``) against the full one.
 """
 
 from __future__ import annotations
@@ -38,39 +38,44 @@ F64 = torch.float64
 INPUTS = ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2", "w_b", "gamma")
 
 
-def _forward_torch(x: dict, mask: torch.Tensor, w_L: float, w_C: float) -> dict:
-    """The IPA forward of ``oracle.ipa_oracle.ipa_forward`` in torch fp64."""
+def _forward_torch(x: dict, mask: torch.Tensor, w_L: float, w_C: float, rows=None) -> dict:
+    """The IPA forward of ``oracle.ipa_oracle.ipa_forward`` in torch fp64.
+
+    ``rows`` (optional index array) restricts the query side to those rows
+    (every key is still attended); outputs then have those rows only.
+    """
     q, k, v = x["q"], x["k"], x["v"]
     rot, trans = x["rot"], x["trans"]
     B, L, H, C = q.shape
+    qi = torch.arange(L) if rows is None else torch.as_tensor(np.asarray(rows, dtype=np.int64))
 
     def glob(pts):          # R_i x + t_i for every head and point
         return torch.einsum("blxy,blhpy->blhpx", rot, pts) + trans[:, :, None, None, :]
 
-    Qg, Kg, Vg = glob(x["q_pts"]), glob(x["k_pts"]), glob(x["v_pts"])
-    Z = torch.einsum("birc,bjrc->bijc", x["z1"], x["z2"])                       # [B,L,L,Cz]
+    Qg, Kg, Vg = glob(x["q_pts"])[:, qi], glob(x["k_pts"]), glob(x["v_pts"])
+    Z = torch.einsum("birc,bjrc->bijc", x["z1"][:, qi], x["z2"])                # [B,L',L,Cz]
     bias = torch.einsum("bijc,ch->bijh", Z, x["w_b"])
-    diff = Qg[:, :, None] - Kg[:, None, :]                                      # [B,L,L,H,P,3]
-    dist = (diff * diff).sum(dim=(-1, -2))                                      # [B,L,L,H]
-    scal = torch.einsum("bihc,bjhc->bijh", q, k) / math.sqrt(C)
+    diff = Qg[:, :, None] - Kg[:, None, :]                                      # [B,L',L,H,P,3]
+    dist = (diff * diff).sum(dim=(-1, -2))                                      # [B,L',L,H]
+    scal = torch.einsum("bihc,bjhc->bijh", q[:, qi], k) / math.sqrt(C)
     S = w_L * (scal + bias - (x["gamma"] * w_C / 2.0) * dist)
-    allowed = (mask[:, :, None] & mask[:, None, :])[..., None]                  # [B,L,L,1]
+    allowed = (mask[:, qi, None] & mask[:, None, :])[..., None]                 # [B,L',L,1]
     S = torch.where(allowed, S, torch.tensor(-math.inf, dtype=F64))
     m = S.amax(dim=2, keepdim=True)
     m = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
     e = torch.where(allowed, torch.exp(S - m), torch.zeros_like(S))
     den = e.sum(dim=2, keepdim=True)
-    a = e / torch.where(den > 0, den, torch.ones_like(den))                     # [B,L,L,H]
+    a = e / torch.where(den > 0, den, torch.ones_like(den))                     # [B,L',L,H]
     o_s = torch.einsum("bijh,bjhc->bihc", a, v)
     og = torch.einsum("bijh,bjhpx->bihpx", a, Vg)
-    rel = og - trans[:, :, None, None, :]
-    o_pts = torch.einsum("biyx,bihpy->bihpx", rot, rel)
+    rel = og - trans[:, qi, None, None, :]
+    o_pts = torch.einsum("biyx,bihpy->bihpx", rot[:, qi], rel)
     # norm with a zero gradient at the origin
     sq = (o_pts * o_pts).sum(-1)
     safe = torch.where(sq > 0, sq, torch.ones_like(sq))
     o_norm = torch.where(sq > 0, torch.sqrt(safe), torch.zeros_like(sq))
     o_pair = torch.einsum("bijh,bijc->bihc", a, Z)
-    keep = mask[:, :, None]
+    keep = mask[:, qi, None]
     zero = torch.zeros((), dtype=F64)
     return {"s": torch.where(keep[..., None], o_s, zero),
             "pts": torch.where(keep[..., None, None], o_pts, zero),
@@ -95,17 +100,23 @@ def _mask(inp: dict) -> torch.Tensor:
     return torch.tensor(np.asarray(m).astype(bool))
 
 
-def ipa_backward(inp: dict, grads: dict) -> dict:
+def ipa_backward(inp: dict, grads: dict, rows=None) -> dict:
     """Gradients of sum_o <grads[o], forward(inp)[o]> for every input.
 
     inp: the forward's input dict (``workloads.make_inputs`` layout);
     grads: "s" [B,L,H,C], "pts" [B,L,H,Pv,3], "pts_norm" [B,L,H,Pv],
     "pair" [B,L,H,Cz]. Returns a dict keyed like INPUTS, float64 numpy.
+
+    With ``rows`` only those query rows' outputs enter the sum (their
+    cotangents are taken from ``grads``). q, q_pts and z1 of residue i enter
+    only row i's outputs, so their gradients on those rows equal the full
+    gradient's there; every other returned array is a partial sum.
     """
     x = {n: torch.tensor(np.asarray(inp[n], dtype=np.float64), requires_grad=True) for n in INPUTS}
     mask = _mask(inp)
-    out = _forward_torch(x, mask, float(inp["w_L"]), float(inp["w_C"]))
-    loss = sum((out[k] * torch.tensor(np.asarray(grads[k], dtype=np.float64))).sum()
+    out = _forward_torch(x, mask, float(inp["w_L"]), float(inp["w_C"]), rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows, dtype=np.int64)
+    loss = sum((out[k] * torch.tensor(np.asarray(grads[k], dtype=np.float64)[:, sel])).sum()
                for k in ("s", "pts", "pts_norm", "pair"))
     g = torch.autograd.grad(loss, [x[n] for n in INPUTS], allow_unused=True)
     return {n: (gi.numpy() if gi is not None else np.zeros_like(x[n].detach().numpy()))

@@ -24,7 +24,7 @@ kernels store them.
 Pinning status (tests/test_layer_pins.py): with selection weights the layer
 reduces to ``ipa_forward`` (itself pinned) plus a known readout; the
 concatenation order is checked with one-hot readout weights; the affine
-maps against a scalar loop.
+maps against a scalar loop; the row-restricted form against the full one.
 """
 
 from __future__ import annotations
@@ -56,12 +56,14 @@ def _bf16(a: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
 
 
-def ipa_layer(inp: dict) -> np.ndarray:
+def ipa_layer(inp: dict, rows=None) -> np.ndarray:
     """The layer in fp64 (bf16-rounded features for bf16 storage).
 
     inp: "s" [B,L,c_s], "rot", "trans", "mask", "w_in" [c_s, Nin],
     "b_in" [Nin], "w_b", "gamma", "w_L", "w_C", "w_out" [Nout, c_s],
-    "b_out" [c_s], "dims", "dtype". Returns y [B,L,c_s] float64.
+    "b_out" [c_s], "dims", "dtype". Returns y [B,L,c_s] float64, or
+    [B,L',c_s] for the query rows ``rows`` only (each output row depends on
+    every residue's features but on its own attention row alone).
     """
     d = inp["dims"]
     B, L = d["B"], d["L"]
@@ -76,9 +78,11 @@ def ipa_layer(inp: dict) -> np.ndarray:
     fwd_in = dict(feats)
     fwd_in.update(rot=inp["rot"], trans=inp["trans"], w_b=inp["w_b"], gamma=inp["gamma"],
                   mask=inp["mask"], w_L=inp["w_L"], w_C=inp["w_C"], dims=d)
-    o = ipa_forward(fwd_in)
-    cat = np.concatenate([o["s"].reshape(B, L, -1), o["pts"].reshape(B, L, -1),
-                          o["pts_norm"].reshape(B, L, -1), o["pair"].reshape(B, L, -1)], axis=-1)
+    sel = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = ipa_forward(fwd_in, rows=None if rows is None else sel)
+    n = len(sel)
+    cat = np.concatenate([o["s"].reshape(B, n, -1), o["pts"].reshape(B, n, -1),
+                          o["pts_norm"].reshape(B, n, -1), o["pair"].reshape(B, n, -1)], axis=-1)
     y = cat @ np.asarray(inp["w_out"], F64) + np.asarray(inp["b_out"], F64)
-    keep = np.asarray(inp["mask"]).astype(bool)
+    keep = np.asarray(inp["mask"]).astype(bool)[:, sel]
     return np.where(keep[..., None], y, 0.0) + 0.0

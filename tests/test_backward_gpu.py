@@ -103,3 +103,53 @@ def test_backward_deterministic(device):
     b = _gpu_backward(inp, g, device)
     for n in NAMES:
         assert np.array_equal(a[n], b[n]), n
+
+
+def test_backward_long_chain_2048_sampled_rows(device):
+    """The gradient at the benchmarked size (L = 2048, H = 12, c_z = 128,
+    R = 2; float32), in the configuration the benchmark times.
+
+    The forward outputs handed over are the bf16 forward's, except on the
+    sampled rows, which get the oracle's: a row's output enters only its own
+    D_i. On those rows dq, dq_pts and dz1 (query-side inputs, which reach
+    no other row's output) are compared with the row-restricted oracle. Over
+    all rows, sum_j dv_j = sum_i g_s,i holds at any size (every row's
+    attention weights sum to 1), tolerance 1e-4 x sum_i |g_s,i|."""
+    from geometric_invariant_attention_amd import IPABackward, IPAForward
+    from oracle import ipa_forward
+    w = WORKLOADS["long_chain_2048"]
+    d = w.dims()
+    print(f"[backward] {w.name} dims={d} sampled rows", flush=True)
+    inp = make_inputs(w, seed=0)
+    L = w.L
+    edges = {i for t in range(0, L + 1, 64) for i in (t - 1, t) if 0 <= i < L}
+    rng = np.random.default_rng(2)
+    rows = np.array(sorted(edges | set(rng.choice(L, 16, replace=False).tolist()))[::3])
+    t = {n: torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).to(device) for n in NAMES}
+    fwd = IPAForward(**d, dtype=torch.bfloat16, device=device)
+    out = fwd(*(t[n].to(torch.bfloat16) if n not in ("rot", "trans", "w_b", "gamma") else t[n] for n in NAMES),
+              w_L=inp["w_L"], w_C=inp["w_C"])
+    ref_o = ipa_forward(inp, rows=rows)
+    o = {k: out[k].float().cpu().numpy().copy() for k in ("s", "pts", "pair")}
+    for k in o:
+        o[k][:, rows] = ref_o[k].astype(np.float32)
+    g = _cotangents(inp, 31)
+    gt = {k: torch.from_numpy(v).to(device) for k, v in g.items()}
+    bwd = IPABackward(**d, device=device)
+    grads = bwd(t, {k: torch.from_numpy(v).to(device) for k, v in o.items()}, gt,
+                w_L=inp["w_L"], w_C=inp["w_C"])
+    torch.cuda.synchronize()
+    got = {n: grads[n].cpu().numpy() for n in NAMES}
+    ref = oracle_backward(inp, g, rows=rows)
+    for n in ("q", "q_pts", "z1"):
+        assert np.isfinite(got[n]).all(), n
+        r = ref[n][:, rows]
+        err = float(np.abs(got[n][:, rows] - r).max()) / max(1.0, float(np.abs(r).max()))
+        print(f"  {n}: {len(rows)} rows, rel error {err:.2e}", flush=True)
+        assert err < TOL, (n, err)
+    sv = got["v"].astype(np.float64).sum(axis=1)            # [B, H, C]
+    sg = g["s"].astype(np.float64).sum(axis=1)
+    scale = np.abs(g["s"]).astype(np.float64).sum(axis=1)
+    dev = float((np.abs(sv - sg) / scale).max())
+    print(f"  sum_j dv_j - sum_i g_s,i: {dev:.2e} of sum |g_s|", flush=True)
+    assert dev < 1e-4, dev

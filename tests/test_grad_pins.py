@@ -86,3 +86,29 @@ def test_masked_rows_and_keys():
     assert pad.any()
     for n in ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2"):
         assert np.all(grad[n][pad] == 0), n
+
+
+@pytest.mark.parametrize("w,rows", [(TINY, [0, 3, 6]), (RAGGED, [1, 5, 8])])
+def test_row_restricted_query_side_matches_full(w, rows):
+    """q, q_pts and z1 of residue i enter only row i's outputs: the
+    row-restricted gradient equals the full one on those rows, and the
+    row-restricted forward equals the numpy oracle's sampled rows."""
+    inp = make_inputs(w, seed=7)
+    for n in INPUTS:
+        inp[n] = inp[n].astype(np.float64)
+    g = _grads(inp, 17)
+    full = ipa_backward(inp, g)
+    part = ipa_backward(inp, g, rows=rows)
+    for n in ("q", "q_pts", "z1"):
+        assert np.abs(part[n][:, rows] - full[n][:, rows]).max() < 1e-12, n
+    # the other rows of a query-side input get nothing from the sampled rows
+    others = [i for i in range(w.L) if i not in rows]
+    assert np.all(part["q"][:, others] == 0)
+    import torch
+    from oracle.ipa_grad import _forward_torch, _mask
+    x = {n: torch.tensor(inp[n]) for n in INPUTS}
+    with torch.no_grad():
+        sub = _forward_torch(x, _mask(inp), float(inp["w_L"]), float(inp["w_C"]), rows=rows)
+    ref = ipa_forward(inp, rows=np.asarray(rows))
+    for k in ref:
+        assert np.abs(sub[k].numpy() - ref[k]).max() < 1e-12, k

@@ -74,3 +74,23 @@ def test_layer_no_biases(device):
     inp["b_out"] = np.zeros_like(inp["b_out"])
     ref = ipa_layer(inp)
     assert np.abs(y.cpu().numpy() - ref).max() / max(1.0, np.abs(ref).max()) < 1e-4
+
+
+def test_layer_long_chain_2048_sampled_rows(device):
+    """The layer at the benchmarked size (L = 2048, H = 12, c_z = 128,
+    c_s = 384, bf16 attention), checked on sampled rows: tile edges and
+    random rows; the oracle computes each output row from every residue's
+    features and that row's attention alone."""
+    w = WORKLOADS["long_chain_2048"]
+    print(f"[layer] {w.name} dims={w.dims()} c_s=384 sampled rows", flush=True)
+    inp = make_layer_inputs(w, c_s=384, seed=0)
+    got = _gpu(inp, device)
+    L = w.L
+    edges = {i for t in range(0, L + 1, 64) for i in (t - 1, t) if 0 <= i < L}
+    rng = np.random.default_rng(1)
+    rows = np.array(sorted(edges | set(rng.choice(L, 16, replace=False).tolist()))[::2])
+    ref = ipa_layer(inp, rows=rows)
+    err = float(np.abs(got[:, rows] - ref).max()) / max(1.0, float(np.abs(ref).max()))
+    print(f"  {len(rows)} rows, rel error {err:.2e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err < 3e-2, err

@@ -100,3 +100,14 @@ def test_masked_rows_are_zero():
     pad = inp["mask"] == 0
     assert pad.any() and np.all(y[pad] == 0) and not np.signbit(y[pad]).any()
     assert np.abs(y[~pad]).max() > 0
+
+
+def test_row_restricted_layer_matches_full():
+    w = WORKLOADS["ragged_batch"].with_(B=2, L=12, H=2, C=3, Pqk=2, Pv=2, R=1, Cz=4, ragged=(6, 12),
+                                        dtype="bf16")
+    inp = make_layer_inputs(w, c_s=6, seed=8)
+    rows = np.array([0, 5, 11])
+    full = ipa_layer(inp)
+    part = ipa_layer(inp, rows=rows)
+    assert part.shape == (2, 3, 6)
+    assert np.abs(part - full[:, rows]).max() < 1e-12
