@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 // and sum kUnroll keys per lane at a time (one rescale per group, no
 // divergent branches); pass 2 writes A and dS.
 // ---------------------------------------------------------------------------
-constexpr int kRowsPerWG = 16, kKeyBlock = 512, kUnroll = 8;
+constexpr int kRowsPerWG = 8, kKeyBlock = 512, kUnroll = 8;
 
 // e^x for x <= 0 through the hardware base-2 exponential (about 1 ulp)
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
