@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 // conflicts), together with a per-key bias (0, or -inf for a masked key),
 // so each row reads them from LDS instead of L2. Pass 1 takes the row max
 // and sum kUnroll keys per lane at a time (one rescale per group, no
-// divergent branches); pass 2 writes A and dS.
+// divergent branches); pass 2 writes A and dS. In both passes a wave
+// handles its two rows side by side so that their loads overlap.
 // ---------------------------------------------------------------------------
 constexpr int kRowsPerWG = 8, kKeyBlock = 512, kUnroll = 8;
 
@@ -209,34 +210,37 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
     }
     return d;
   };
-  // pass 1
+  // pass 1: the wave's rows side by side, so that all their loads of a
+  // group are in flight together
+  constexpr int NR = kRowsPerWG / 4;
   for (int k0 = 0; k0 < L; k0 += kKeyBlock) {
     const int nk = L - k0 < kKeyBlock ? L - k0 : kKeyBlock;
     stage(k0, nk);
+    for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
+      float sv[NR][kUnroll];
 #pragma unroll
-    for (int u = 0; u < kRowsPerWG / 4; ++u) {
-      if (!qv[u]) continue;
-      const float* X = a.X + ((size_t)bh * a.QC + r0 + w + 4 * u) * L + k0;
-      // kUnroll keys per lane at a time: all their loads in flight together
-      for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
-        float sv[kUnroll];
+      for (int u = 0; u < NR; ++u) {
+        const float* X = a.X + ((size_t)bh * a.QC + r0 + w + 4 * u) * L + k0;
 #pragma unroll
         for (int t = 0; t < kUnroll; ++t) {
           const int jj = jb + 64 * t + lane;
-          sv[t] = jj < nk ? X[jj] : 0.f;
+          sv[u][t] = (qv[u] && jj < nk) ? X[jj] : 0.f;
         }
+      }
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
         float mt = m[u];
 #pragma unroll
         for (int t = 0; t < kUnroll; ++t) {
           const int jj = jb + 64 * t + lane;
-          sv[t] = jj < nk ? fmaf(-kappa, dist(qp[u], jj), sv[t]) + kps[kMaxP3][jj] : -INFINITY;
-          mt = fmaxf(mt, sv[t]);
+          sv[u][t] = (qv[u] && jj < nk) ? fmaf(-kappa, dist(qp[u], jj), sv[u][t]) + kps[kMaxP3][jj] : -INFINITY;
+          mt = fmaxf(mt, sv[u][t]);
         }
         // every key so far masked: nothing to add yet
         const float sc = mt == -INFINITY ? 0.f : mt;
         float acc = l[u] * fexp(m[u] - sc);
 #pragma unroll
-        for (int t = 0; t < kUnroll; ++t) acc += fexp(sv[t] - sc);
+        for (int t = 0; t < kUnroll; ++t) acc += fexp(sv[u][t] - sc);
         l[u] = acc;
         m[u] = mt;
       }
@@ -256,26 +260,36 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
   float rs[kRowsPerWG / 4], gs[kRowsPerWG / 4];
 #pragma unroll
   for (int u = 0; u < kRowsPerWG / 4; ++u) rs[u] = gs[u] = 0.f;
+  float Dr[NR], mu[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const int r = r0 + w + 4 * u;
+    Dr[u] = r < qc ? a.Dv[(size_t)bh * L + q0 + r] : 0.f;
+    // a row with no valid key (or a masked row) writes zeros
+    mu[u] = m[u] == -INFINITY ? 0.f : m[u];
+  }
   for (int k0 = 0; k0 < L; k0 += kKeyBlock) {
     const int nk = L - k0 < kKeyBlock ? L - k0 : kKeyBlock;
     if (k0 > 0 || L > kKeyBlock) stage(k0, nk);
+    for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
+      float xv[NR][kUnroll], yv[NR][kUnroll];
 #pragma unroll
-    for (int u = 0; u < kRowsPerWG / 4; ++u) {
-      const int r = r0 + w + 4 * u;
-      if (r >= qc) continue;
-      const float D = a.Dv[(size_t)bh * L + q0 + r];
-      float* X = a.X + ((size_t)bh * a.QC + r) * L + k0;
-      float* Y = a.Y + ((size_t)bh * a.QC + r) * L + k0;
-      // a row with no valid key (or a masked row) writes zeros
-      const float mu = m[u] == -INFINITY ? 0.f : m[u];
-      for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
-        float xv[kUnroll], yv[kUnroll];
+      for (int u = 0; u < NR; ++u) {
+        const size_t row = (size_t)bh * a.QC + r0 + w + 4 * u;
+        const bool rin = r0 + w + 4 * u < qc;
 #pragma unroll
         for (int t = 0; t < kUnroll; ++t) {
           const int jj = jb + 64 * t + lane;
-          xv[t] = jj < nk ? X[jj] : 0.f;
-          yv[t] = jj < nk ? Y[jj] : 0.f;
+          xv[u][t] = (rin && jj < nk) ? a.X[row * L + k0 + jj] : 0.f;
+          yv[u][t] = (rin && jj < nk) ? a.Y[row * L + k0 + jj] : 0.f;
         }
+      }
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int r = r0 + w + 4 * u;
+        if (r >= qc) continue;
+        float* X = a.X + ((size_t)bh * a.QC + r) * L + k0;
+        float* Y = a.Y + ((size_t)bh * a.QC + r) * L + k0;
 #pragma unroll
         for (int t = 0; t < kUnroll; ++t) {
           const int jj = jb + 64 * t + lane;
@@ -283,8 +297,8 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
           float p = 0.f, ds = 0.f;
           if (qv[u]) {
             const float d = dist(qp[u], jj);
-            p = fexp(fmaf(-kappa, d, xv[t]) + kps[kMaxP3][jj] - mu) * inv[u];
-            ds = p * (yv[t] - D);
+            p = fexp(fmaf(-kappa, d, xv[u][t]) + kps[kMaxP3][jj] - mu[u]) * inv[u];
+            ds = p * (yv[u][t] - Dr[u]);
             rs[u] += ds;
             gs[u] = fmaf(ds, d, gs[u]);
           }
