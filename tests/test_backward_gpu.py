@@ -105,9 +105,17 @@ def test_backward_deterministic(device):
         assert np.array_equal(a[n], b[n]), n
 
 
-def test_backward_long_chain_2048_sampled_rows(device):
+# the query-chunk boundaries of the gradient at L = 4096, H = 12 (chunks of
+# 1344 rows keep a chunk's score rows under 2^26 floats; the last has 64)
+CHUNK_EDGES = {"long_chain_2048": [], "long_chain_4096": [1343, 1344, 2687, 2688, 4031, 4032]}
+
+
+@pytest.mark.parametrize("name", ["long_chain_2048", "long_chain_4096"])
+def test_backward_long_chain_sampled_rows(device, name):
     """The gradient at the benchmarked size (L = 2048, H = 12, c_z = 128,
-    R = 2; float32), in the configuration the benchmark times.
+    R = 2; float32), in the configuration the benchmark times, and at
+    L = 4096, where the queries run in four chunks (the key-side sums then
+    accumulate across chunks).
 
     The forward outputs handed over are the bf16 forward's, except on the
     sampled rows, which get the oracle's: a row's output enters only its own
@@ -117,14 +125,15 @@ def test_backward_long_chain_2048_sampled_rows(device):
     attention weights sum to 1), tolerance 1e-4 x sum_i |g_s,i|."""
     from geometric_invariant_attention_amd import IPABackward, IPAForward
     from oracle import ipa_forward
-    w = WORKLOADS["long_chain_2048"]
+    w = WORKLOADS[name]
     d = w.dims()
     print(f"[backward] {w.name} dims={d} sampled rows", flush=True)
     inp = make_inputs(w, seed=0)
     L = w.L
     edges = {i for t in range(0, L + 1, 64) for i in (t - 1, t) if 0 <= i < L}
     rng = np.random.default_rng(2)
-    rows = np.array(sorted(edges | set(rng.choice(L, 16, replace=False).tolist()))[::3])
+    rows = sorted(edges | set(rng.choice(L, 16, replace=False).tolist()))[::3]
+    rows = np.array(sorted(set(rows) | set(CHUNK_EDGES[name])))
     t = {n: torch.from_numpy(np.ascontiguousarray(inp[n], dtype=np.float32)).to(device) for n in NAMES}
     fwd = IPAForward(**d, dtype=torch.bfloat16, device=device)
     out = fwd(*(t[n].to(torch.bfloat16) if n not in ("rot", "trans", "w_b", "gamma") else t[n] for n in NAMES),
