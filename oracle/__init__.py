@@ -26,10 +26,12 @@ Pinning status of each function (see the tests under ``tests/``):
   ipa_backward    pinned: central finite differences of ipa_forward along
                   random directions for every input, its restated forward
                   equals ipa_forward, rigid-motion identities of the frame
-                  gradients, masked rows and keys.
+                  gradients, masked rows and keys; its row-restricted form
+                  (rows=) against the full gradient.
   ipa_layer       pinned: reduces to ipa_forward plus the readout with
                   selection weights, readout order by one-hot rows, the
-                  affine maps against a scalar loop, masked rows.
+                  affine maps against a scalar loop, masked rows; its
+                  row-restricted form against the full layer.
 """
 
 from .ipa_oracle import ipa_forward, ipa_logits, to_global
