@@ -511,6 +511,13 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(bwd_rows_kernel, dim3((qc + kRowsPerWG - 1) / kRowsPerWG, BH), dim3(256), 0, s, a, q0, qc);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    // Precision of the products: U = A z2 and dVA = A^T GA are sums of
+    // non-negative weights times bounded values, so they run on the split
+    // path (each fp32 operand as bf16 hi + lo, three bf16 products, about
+    // 2^-17 relative per term). The others stay on fp32 products: S feeds
+    // the exponent, dP the difference dP - D, and the point columns of dQA'
+    // and dKA' (sum_j dS_ij Kg_j against Qg_i sum_j dS_ij, coordinates of
+    // a hundred angstroms or more) cancel by an order of magnitude.
     // dQA' = dS KA' (rows q0 .. q0 + qc)
     g.M = qc; g.N = a.DAK; g.K = L;
     g.A = a.Y; g.sAb = xs; g.am = L; g.ak = 1;
@@ -518,18 +525,21 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     g.C = a.dQA + (size_t)q0 * a.DAK; g.sCb = rowsK; g.cm = a.DAK; g.acc = 0;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     // U = A z2
+    g.x3 = 1;
     g.N = RCz;
     g.A = a.X;
     g.B = a.KA + a.C;
     g.C = a.U + (size_t)q0 * RCz; g.sCb = (long long)L * RCz; g.cm = RCz;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     // dKA' += dS^T QA' (all keys)
+    g.x3 = 0;
     g.M = L; g.N = a.DAQ; g.K = qc;
     g.A = a.Y; g.sAb = xs; g.am = 1; g.ak = L;
     g.B = a.QA + (size_t)q0 * a.DAQ; g.sBb = rowsQ; g.bk = a.DAQ; g.bn = 1;
     g.C = a.dKA; g.sCb = rowsQ; g.cm = a.DAQ; g.acc = q0 > 0;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     // dVA += A^T GA
+    g.x3 = 1;
     g.N = a.DV;
     g.A = a.X;
     g.B = a.GA + (size_t)q0 * a.DV; g.sBb = rowsV; g.bk = a.DV; g.bn = 1;

@@ -10,6 +10,7 @@ namespace ipa {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Compiler fence: memory operations stay on their side of it.
 __device__ __forceinline__ void fence() { asm volatile("" ::: "memory"); }
@@ -36,10 +37,11 @@ __device__ __forceinline__ void pin(floatx16& acc) { asm volatile("" : "+a"(acc)
 // by a second kernel), and a segmented epilogue that writes column blocks to
 // separate arrays (fp32 or bf16).
 // ---------------------------------------------------------------------------
-template <int TM, int TN, bool AK1, bool BK1>
+template <int TM, int TN, bool AK1, bool BK1, bool X3>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(Gemm g) {
   constexpr int KS = 32;              // reduction step
   constexpr int PK = KS + 4;          // LDS row pitch (floats)
+  constexpr int PKB = KS + 8;         // LDS row pitch of the bf16 halves (elements)
   constexpr int BM = 64 * TM, BN = 64 * TN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w & 1, wn = w >> 1, half = lane >> 5, l32 = lane & 31;
@@ -50,9 +52,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   const float* A = g.A + (g.kpart ? 0 : (size_t)z * g.sAb);
   const float* B = g.B + (g.kpart ? 0 : (size_t)z * g.sBb);
   // two buffers per operand: step s reads buffer s & 1 while the next
-  // step's slices are written into the other
-  __shared__ __attribute__((aligned(16))) float As[2][BM][PK];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BN][PK];
+  // step's slices are written into the other. fp32 path: [buf][row][k]
+  // floats; split path (X3): [buf][hi / lo][row][k] bf16.
+  // (the arrays of the path not taken shrink to one row)
+  __shared__ __attribute__((aligned(16))) float As[2][X3 ? 1 : BM][PK];
+  __shared__ __attribute__((aligned(16))) float Bs[2][X3 ? 1 : BN][PK];
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][2][X3 ? BM : 1][PKB];
+  __shared__ __attribute__((aligned(16))) uint16_t Bh[2][2][X3 ? BN : 1][PKB];
   // Element u of this thread's share of the A slice (BM m x KS k) and of
   // the B slice (KS k x BN n), chosen so that consecutive threads read
   // consecutive addresses: along k when that stride is 1 (AK1 / BK1),
@@ -96,15 +102,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     if (u < NA) ra[u] = A[(unsigned)(oa[u] + k0 * ak)];
     else rb[u - NA] = B[(unsigned)(ob[u - NA] + k0 * bk)];
   };
+  // split path: x = hi + lo + O(2^-18 x), hi and lo bf16 (nearest even)
+  auto split = [](float x, uint16_t& hi, uint16_t& lo) {
+    uint32_t u = __float_as_uint(x);
+    hi = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    u = __float_as_uint(x - __uint_as_float((uint32_t)hi << 16));
+    lo = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  };
   auto stage_one = [&](int p, int u) {
     if (u < NA) {
       int m, k;
       a_mk(u, m, k);
-      As[p][m][k] = va[u] ? ra[u] : 0.f;
+      const float x = va[u] ? ra[u] : 0.f;
+      if constexpr (X3) split(x, Ah[p][0][m][k], Ah[p][1][m][k]);
+      else As[p][m][k] = x;
     } else {
       int k, n;
       b_kn(u - NA, k, n);
-      Bs[p][n][k] = vb[u - NA] ? rb[u - NA] : 0.f;
+      const float x = vb[u - NA] ? rb[u - NA] : 0.f;
+      if constexpr (X3) split(x, Bh[p][0][n][k], Bh[p][1][n][k]);
+      else Bs[p][n][k] = x;
     }
   };
   auto gload = [&](int k0) {
@@ -162,8 +179,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   // MODE 0: the next step is a full one (its loads spread over the
   // products); 1: the next step is the partial last one (its loads up
   // front); 2: no next step.
+  // split path: per step two reduction substeps of 16, each three bf16
+  // products per block pair (hi hi, hi lo, lo hi; the lo lo term is below
+  // the split's own error), the products of one kind taken over all block
+  // pairs before the next so consecutive products use different
+  // accumulators; the operands of substep 1 are read while substep 0 runs
+  constexpr int NMX = 2 * 3 * TM * TN, HALFX = NMX / 2;
+  auto read_x = [&](int p, int s2, bf16x8 (&ah)[TM], bf16x8 (&al)[TM], bf16x8 (&bh)[TN], bf16x8 (&bl)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = 32 * (wm * TM + i) + l32, kk = 16 * s2 + 8 * half;
+      ah[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ah[p][0][r][kk]));
+      al[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ah[p][1][r][kk]));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = 32 * (wn * TN + j) + l32, kk = 16 * s2 + 8 * half;
+      bh[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bh[p][0][r][kk]));
+      bl[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bh[p][1][r][kk]));
+    }
+  };
+  auto iter_x = [&](int k0, int p, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    if (MODE == 1) gload(k0 + KS);
+    bf16x8 ah[2][TM], al[2][TM], bh[2][TN], bl[2][TN];
+    read_x(p, 0, ah[0], al[0], bh[0], bl[0]);
+    fence();
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if (s2 == 0) read_x(p, 1, ah[1], al[1], bh[1], bl[1]);
+#pragma unroll
+      for (int kind = 0; kind < 3; ++kind)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int st = 3 * TM * TN * s2 + TM * TN * kind + TN * i + j;
+            const bf16x8 a = kind == 2 ? al[s2][i] : ah[s2][i];
+            const bf16x8 b = kind == 1 ? bl[s2][j] : bh[s2][j];
+            c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i][j], 0, 0, 0);
+            pin(c[i][j]);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              if (MODE == 0 && u * HALFX / NU == st) load_one(k0 + KS, u);
+              if (MODE != 2 && HALFX + u * HALFX / NU == st) stage_one(p ^ 1, u);
+            }
+            fence();
+          }
+    }
+    __syncthreads();
+  };
   auto iter = [&](int k0, int p, auto mode_c) {
     constexpr int MODE = decltype(mode_c)::value;
+    if constexpr (X3) {
+      iter_x(k0, p, mode_c);
+      return;
+    }
     if (MODE == 1) gload(k0 + KS);
     float4 av[2][TM], bv[2][TN];
     read_q(p, 0, av[0], bv[0]);
@@ -265,29 +336,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
 // operand more often; speeds and the single-workgroup penalty measured on
 // the gradient's and the layer's products).
 struct TileShape { int tm, tn; };
-TileShape pick_tile(int M, int N, int z) {
+TileShape pick_tile(int M, int N, int z, bool x3) {
   const TileShape cand[4] = {{2, 2}, {2, 1}, {1, 2}, {1, 1}};
   const double speed[4] = {1.0, 0.85, 0.85, 0.65};
   int best = 3;
   double best_cost = 0.0;
-  for (int c = 0; c < 4; ++c) {
+  // (the split path's LDS holds two bf16 halves per element: 128 x 64 at most)
+  for (int c = x3 ? 1 : 0; c < 4; ++c) {
     const long long gm = (M + 64 * cand[c].tm - 1) / (64 * cand[c].tm), gn = (N + 64 * cand[c].tn - 1) / (64 * cand[c].tn);
     const long long per_cu = (gm * gn * z + 255) / 256;
     // a unit left with one workgroup runs one wave per SIMD, which hides
     // less of the load and LDS latency
     const double cost = (double)per_cu * (64.0 * cand[c].tm) * (64.0 * cand[c].tn) / speed[c] * (per_cu == 1 ? 1.4 : 1.0);
-    if (c == 0 || cost < best_cost) { best = c; best_cost = cost; }
+    if (c == (x3 ? 1 : 0) || cost < best_cost) { best = c; best_cost = cost; }
   }
   return cand[best];
 }
 
+template <int TM, int TN, bool X3>
+void launch_layout(const Gemm& g, dim3 grid, hipStream_t s) {
+  const bool ak1 = g.ak == 1, bk1 = g.bk == 1;
+  if (ak1 && bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, true, X3>), grid, dim3(256), 0, s, g);
+  else if (ak1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, false, X3>), grid, dim3(256), 0, s, g);
+  else if (bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, false, true, X3>), grid, dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gemm_kernel<TM, TN, false, false, X3>), grid, dim3(256), 0, s, g);
+}
 template <int TM, int TN>
 void launch_shape(const Gemm& g, dim3 grid, hipStream_t s) {
-  const bool ak1 = g.ak == 1, bk1 = g.bk == 1;
-  if (ak1 && bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, true>), grid, dim3(256), 0, s, g);
-  else if (ak1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, false>), grid, dim3(256), 0, s, g);
-  else if (bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, false, true>), grid, dim3(256), 0, s, g);
-  else hipLaunchKernelGGL((gemm_kernel<TM, TN, false, false>), grid, dim3(256), 0, s, g);
+  if constexpr (TM == 2 && TN == 2) launch_layout<2, 2, false>(g, grid, s);   // split path: 128 x 64 at most
+  else if (g.x3) launch_layout<TM, TN, true>(g, grid, s);
+  else launch_layout<TM, TN, false>(g, grid, s);
 }
 
 hipError_t launch_gemm(const Gemm& g, int z, hipStream_t s) {
@@ -298,7 +376,7 @@ hipError_t launch_gemm(const Gemm& g, int z, hipStream_t s) {
       (double)(g.K - 1) * g.bk + (double)(g.N - 1) * g.bn >= 2147483647.0)
     return hipErrorInvalidValue;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  const TileShape t = pick_tile(g.M, g.N, z);
+  const TileShape t = pick_tile(g.M, g.N, z, g.x3 != 0);
   const dim3 grid((g.M + 64 * t.tm - 1) / (64 * t.tm), (g.N + 64 * t.tn - 1) / (64 * t.tn), z);
   if (t.tm == 2 && t.tn == 2) launch_shape<2, 2>(g, grid, s);
   else if (t.tm == 2) launch_shape<2, 1>(g, grid, s);

@@ -130,6 +130,8 @@ struct Gemm {
   int seg_start[9];         // first column of each block, then N
   void* seg_out[8];         // block b stored [M][width_b]
   int seg_bf16;             // blocks stored as bf16 (nearest even)
+  int x3;                   // each operand split into bf16 hi + lo, three
+                            // bf16 products (about 2^-17 relative per term)
 };
 hipError_t gemm(const Gemm& g, int batch, hipStream_t s);
 // the reduction split into `splits` slices along the grid; partials in
