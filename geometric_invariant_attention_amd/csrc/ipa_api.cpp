@@ -488,6 +488,9 @@ int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype, cons
   g.B = w_in; g.bk = ly.n_in; g.bn = 1;
   g.bias = b_in;
   g.nseg = 8; g.seg_bf16 = dtype == IPA_BF16;
+  // with bf16 storage the features are rounded to 2^-9 anyway: the split
+  // path (about 2^-17 per term) is ample; fp32 storage keeps fp32 products
+  g.x3 = dtype == IPA_BF16;
   int c0 = 0;
   for (int e = 0; e < 8; ++e) {
     g.seg_start[e] = c0;
@@ -522,6 +525,7 @@ int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype, cons
   q.A = ga.cat; q.am = ly.n_out; q.ak = 1;
   q.B = w_out; q.bk = c_s; q.bn = 1;
   q.C = out; q.cm = c_s; q.bias = b_out; q.rowmask = mask;
+  q.x3 = dtype == IPA_BF16;
   if (ipa::gemm_splitk(q, ly.splits, reinterpret_cast<float*>(ws + ly.off_part), st) != hipSuccess) return IPA_ERR_HIP;
   return IPA_OK;
 }
