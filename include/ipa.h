@@ -220,8 +220,10 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype,
  *   out    [B,L,c_s] float32, every element overwritten
  *   workspace ipa_layer_workspace_bytes(dims, c_s, dtype) bytes, 256-byte aligned
  * Pointers 16-byte aligned. The projections and the readout run on the
- * fp32 matrix cores; the attention's envelope and statuses are those of
- * ipa_forward. */
+ * matrix cores: fp32 products for IPA_F32; for IPA_BF16 (features rounded
+ * to bf16 anyway) each fp32 operand split into bf16 hi + lo, three bf16
+ * products, about 2^-17 relative per term. The attention's envelope and
+ * statuses are those of ipa_forward. */
 size_t ipa_layer_workspace_bytes(const ipa_dims* dims, int32_t c_s, int32_t dtype);
 int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype,
                           const float* s, const float* rot, const float* trans,
@@ -251,7 +253,11 @@ int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype,
  * 0 pass no gradient and receive none. Supported envelope: C <= 16,
  * Pqk <= 5, Pv <= 8, R*Cz <= 256, B*H <= 65535. Pointers 4-byte aligned,
  * workspace ipa_backward_workspace_bytes(dims) bytes, 256-byte aligned.
- * Deterministic: repeated calls give identical bits. */
+ * The score, dP and query/key-side products use fp32 matrix-core products;
+ * the two value-side products (A z2 and A^T GA, non-negative weights) split
+ * each fp32 operand into bf16 hi + lo and take three bf16 products (about
+ * 2^-17 relative per term). Deterministic: repeated calls give identical
+ * bits. */
 size_t ipa_backward_workspace_bytes(const ipa_dims* dims);
 int32_t ipa_backward(const ipa_dims* dims,
                      const float* q, const float* k, const float* v,
