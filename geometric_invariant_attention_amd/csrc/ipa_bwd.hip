@@ -511,18 +511,26 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(bwd_rows_kernel, dim3((qc + kRowsPerWG - 1) / kRowsPerWG, BH), dim3(256), 0, s, a, q0, qc);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    // Precision of the products: U = A z2 and dVA = A^T GA are sums of
-    // non-negative weights times bounded values, so they run on the split
-    // path (each fp32 operand as bf16 hi + lo, three bf16 products, about
-    // 2^-17 relative per term). The others stay on fp32 products: S feeds
-    // the exponent, dP the difference dP - D, and the point columns of dQA'
-    // and dKA' (sum_j dS_ij Kg_j against Qg_i sum_j dS_ij, coordinates of
-    // a hundred angstroms or more) cancel by an order of magnitude.
-    // dQA' = dS KA' (rows q0 .. q0 + qc)
-    g.M = qc; g.N = a.DAK; g.K = L;
+    // Precision of the products: U = A z2, dVA = A^T GA and the scalar and
+    // pair columns of dQA' do not cancel, so they run on the split path
+    // (each fp32 operand as bf16 hi + lo, three bf16 products, about 2^-17
+    // relative per term). The others stay on fp32 products: S feeds the
+    // exponent, dP the difference dP - D, and the point columns of dQA' and
+    // dKA' (sum_j dS_ij Kg_j against Qg_i sum_j dS_ij, coordinates of a
+    // hundred angstroms or more) cancel by an order of magnitude.
+    // dQA' = dS KA' (rows q0 .. q0 + qc): the scalar and pair columns on
+    // the split path, the point columns (which cancel, see above) on fp32
+    // products
+    g.x3 = 1;
+    g.M = qc; g.N = a.DA; g.K = L;
     g.A = a.Y; g.sAb = xs; g.am = L; g.ak = 1;
     g.B = a.KA; g.sBb = rowsK; g.bk = a.DAK; g.bn = 1;
     g.C = a.dQA + (size_t)q0 * a.DAK; g.sCb = rowsK; g.cm = a.DAK; g.acc = 0;
+    if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+    g.x3 = 0;
+    g.N = a.DAK - a.DA;
+    g.B = a.KA + a.DA;
+    g.C = a.dQA + (size_t)q0 * a.DAK + a.DA;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     // U = A z2
     g.x3 = 1;
