@@ -79,7 +79,7 @@ int32_t run(int stages, const ipa_dims* dims, int32_t dtype,
             float* out_s, float* out_pts, float* out_pts_norm,
             float* out_pair,
             void* workspace, size_t workspace_bytes,
-            void* stream) {
+            void* stream, const long long* out_pitch = nullptr) {
   int32_t dv[8];
   if (!valid_dims_struct(dims, dv)) return IPA_ERR_NULL;
   if (!basic_dims_ok(dv)) return IPA_ERR_DIMS;
@@ -102,6 +102,9 @@ int32_t run(int stages, const ipa_dims* dims, int32_t dtype,
   a.rot = rot; a.trans = trans; a.z1 = z1; a.z2 = z2; a.w_b = w_b; a.gamma = gamma;
   a.mask = mask; a.w_L = w_L; a.w_C = w_C;
   a.out_s = out_s; a.out_pts = out_pts; a.out_pts_norm = out_pts_norm; a.out_pair = out_pair;
+  const long long H = dims->H;
+  const long long packed[4] = {H * dims->C, 3 * H * dims->Pv, H * dims->Pv, H * dims->Cz};
+  for (int e = 0; e < 4; ++e) a.out_pitch[e] = out_pitch ? out_pitch[e] : packed[e];
   a.ws = static_cast<unsigned char*>(workspace);
   a.meet_rho = nullptr; a.meet_s = nullptr;
 
@@ -194,6 +197,8 @@ int32_t ipa_meet_forward(const ipa_meet_dims* dims, int32_t dtype, const void* q
   a.rot = nullptr; a.trans = x; a.z1 = nullptr; a.z2 = nullptr; a.w_b = nullptr; a.gamma = nullptr;
   a.mask = mask; a.w_L = 0.f; a.w_C = 0.f;
   a.out_s = out; a.out_pts = nullptr; a.out_pts_norm = nullptr; a.out_pair = nullptr;
+  a.out_pitch[0] = (long long)dims->H * dims->C;
+  a.out_pitch[1] = a.out_pitch[2] = a.out_pitch[3] = 0;
   a.ws = static_cast<unsigned char*>(workspace);
   a.meet_rho = rho; a.meet_s = s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -397,10 +402,12 @@ int32_t ipa_backward(const ipa_dims* dims, const float* q, const float* k, const
 
 namespace {
 
-// The full layer is four launches around the attention: x = s W_in + b_in
+// The full layer is three launches around the attention: x = s W_in + b_in
 // as one GEMM whose epilogue writes each column block straight into the
-// attention's input array in its storage type; the attention; a gather of
-// its four outputs into one row-major matrix; and
+// attention's input array in its storage type; the attention, which writes
+// its four outputs as the column blocks of one row-major matrix (or, when a
+// block would not start on a 16-byte boundary, into packed arrays followed
+// by a gather); and
 // y = [o_s | o_pts | o_norm | o_pair] W_out + b_out as one GEMM with the
 // reduction split across the grid, the partials added in order with the
 // bias by a second kernel that also zeroes masked rows.
@@ -499,30 +506,43 @@ int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype, cons
   }
   g.seg_start[8] = c0;
   if (ipa::gemm(g, 1, st) != hipSuccess) return IPA_ERR_HIP;
-  // the attention
-  float* o[4];
-  for (int e = 0; e < 4; ++e) o[e] = reinterpret_cast<float*>(ws + ly.off_out[e]);
-  const int32_t rc = ipa_forward(dims, dtype, feat[0], feat[1], feat[2], feat[3], feat[4], feat[5], rot, trans,
-                                 feat[6], feat[7], w_b, gamma, mask, w_L, w_C, o[0], o[1], o[2], o[3],
-                                 ws + ly.off_ipa, ly.ipa_bytes, stream);
-  if (rc != IPA_OK) return rc;
-  // y = [o_s | o_pts | o_norm | o_pair] W_out + b_out, masked rows 0
+  // the attention: its four outputs go straight into the columns of the
+  // readout's left operand [rows][n_out] when every block starts on a
+  // 16-byte boundary, else into packed arrays that a gather concatenates
   const int H = dims->H, C = dims->C, Pv = dims->Pv, Cz = dims->Cz;
-  ipa::LayerGather ga{};
   const int wo[4] = {H * C, H * Pv * 3, H * Pv, H * Cz};
-  int r0 = 0;
-  for (int e = 0; e < 4; ++e) {
-    ga.src[e] = o[e];
-    ga.start[e] = r0;
-    r0 += wo[e];
+  int start[5];
+  start[0] = 0;
+  for (int e = 0; e < 4; ++e) start[e + 1] = start[e] + wo[e];
+  float* const cat = reinterpret_cast<float*>(ws + ly.off_cat);
+  const bool direct = ly.n_out % 4 == 0 && start[1] % 4 == 0 && start[2] % 4 == 0 && start[3] % 4 == 0;
+  if (direct) {
+    const long long pitch[4] = {ly.n_out, ly.n_out, ly.n_out, ly.n_out};
+    const int32_t rc = run(kBoth, dims, dtype, feat[0], feat[1], feat[2], feat[3], feat[4], feat[5], rot, trans,
+                           feat[6], feat[7], w_b, gamma, mask, w_L, w_C, cat + start[0], cat + start[1],
+                           cat + start[2], cat + start[3], ws + ly.off_ipa, ly.ipa_bytes, stream, pitch);
+    if (rc != IPA_OK) return rc;
+  } else {
+    float* o[4];
+    for (int e = 0; e < 4; ++e) o[e] = reinterpret_cast<float*>(ws + ly.off_out[e]);
+    const int32_t rc = ipa_forward(dims, dtype, feat[0], feat[1], feat[2], feat[3], feat[4], feat[5], rot, trans,
+                                   feat[6], feat[7], w_b, gamma, mask, w_L, w_C, o[0], o[1], o[2], o[3],
+                                   ws + ly.off_ipa, ly.ipa_bytes, stream);
+    if (rc != IPA_OK) return rc;
+    ipa::LayerGather ga{};
+    for (int e = 0; e < 4; ++e) {
+      ga.src[e] = o[e];
+      ga.start[e] = start[e];
+    }
+    ga.start[4] = start[4];
+    ga.rows = rows; ga.n_out = ly.n_out;
+    ga.cat = cat;
+    if (ipa::launch_layer_gather(ga, st) != hipSuccess) return IPA_ERR_HIP;
   }
-  ga.start[4] = r0;
-  ga.rows = rows; ga.n_out = ly.n_out;
-  ga.cat = reinterpret_cast<float*>(ws + ly.off_cat);
-  if (ipa::launch_layer_gather(ga, st) != hipSuccess) return IPA_ERR_HIP;
+  // y = [o_s | o_pts | o_norm | o_pair] W_out + b_out, masked rows 0
   ipa::Gemm q{};
   q.M = (int)rows; q.N = c_s; q.K = ly.n_out;
-  q.A = ga.cat; q.am = ly.n_out; q.ak = 1;
+  q.A = cat; q.am = ly.n_out; q.ak = 1;
   q.B = w_out; q.bk = c_s; q.bn = 1;
   q.C = out; q.cm = c_s; q.bias = b_out; q.rowmask = mask;
   q.x3 = dtype == IPA_BF16;

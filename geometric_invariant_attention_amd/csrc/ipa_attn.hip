@@ -914,10 +914,11 @@ void ipa_attn_kernel(FwdArgs a) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[it]), rs, off[it], 0, 0);
   };
-  const size_t row0 = ((size_t)b * L + qw) * H + h;   // (b, qw, h) output row
-  store_rows(std::integral_constant<int, PS>{}, so, C, a.out_s, row0 * C, H * C);
-  store_rows(std::integral_constant<int, PP>{}, sp, 3 * Pv, a.out_pts, row0 * 3 * Pv, H * 3 * Pv);
-  store_rows(std::integral_constant<int, PN>{}, sn, Pv, a.out_pts_norm, row0 * Pv, H * Pv);
+  const size_t bi0 = (size_t)b * L + qw;   // residue (b, qw): first output row of this wave
+  const int pS = (int)a.out_pitch[0], pP = (int)a.out_pitch[1], pN = (int)a.out_pitch[2], pZ = (int)a.out_pitch[3];
+  store_rows(std::integral_constant<int, PS>{}, so, C, a.out_s, bi0 * pS + (size_t)h * C, pS);
+  store_rows(std::integral_constant<int, PP>{}, sp, 3 * Pv, a.out_pts, bi0 * pP + (size_t)h * 3 * Pv, pP);
+  store_rows(std::integral_constant<int, PN>{}, sn, Pv, a.out_pts_norm, bi0 * pN + (size_t)h * Pv, pN);
 
   // ---- pair channels: o_pair[c] = sum_r z1[r Cz + c] O[r Cz + c] / l ----
   // Lane (n, g) holds O at features 32 fb + 8 k + 4 g + e of query n: 4-wide
@@ -936,7 +937,7 @@ void ipa_attn_kernel(FwdArgs a) {
     if constexpr (S * 32 <= SM::kCzMax) {
       constexpr int RMAX = (NFB - 2) / S;
       const __amdgpu_buffer_rsrc_t rs =
-          rsrc_or_empty(a.out_pair, row0 * Cz * 4, nrow > 0 ? (uint32_t)(((nrow - 1) * H * Cz + Cz) * 4) : 0u);
+          rsrc_or_empty(a.out_pair, (bi0 * pZ + (size_t)h * Cz) * 4, nrow > 0 ? (uint32_t)(((nrow - 1) * pZ + Cz) * 4) : 0u);
 #pragma unroll
       for (int m = 0; m < S; ++m) {
         unsigned char* const pb = xs + (m & 1) * 4096;
@@ -961,7 +962,7 @@ void ipa_attn_kernel(FwdArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int r = (lane >> 3) + 8 * j, c = lane & 7;
           const u32x4 v = *reinterpret_cast<const u32x4*>(pb + r * 128 + 16 * (c ^ (r & 7)));
-          __builtin_amdgcn_raw_buffer_store_b128(v, rs, (r * H * Cz + 32 * m + 4 * c) * 4, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, (r * pZ + 32 * m + 4 * c) * 4, 0, 0);
         }
       }
       pair_done = true;
@@ -1015,7 +1016,7 @@ void ipa_attn_kernel(FwdArgs a) {
       int nn = lane / Cz, c = lane - nn * Cz;
       for (int e = lane; e < 32 * Cz; e += 64) {
         const int ii = qw + nn;
-        if (a.out_pair && ii < L) a.out_pair[(((size_t)b * L + ii) * H + h) * Cz + c] = pb[nn * SM::kPRow + c];
+        if (a.out_pair && ii < L) a.out_pair[((size_t)b * L + ii) * pZ + (size_t)h * Cz + c] = pb[nn * SM::kPRow + c];
         nn += dq;
         c += dr;
         if (c >= Cz) { c -= Cz; ++nn; }

@@ -64,6 +64,10 @@ struct FwdArgs {
   const uint8_t* mask;
   float w_L, w_C;
   float* out_s; float* out_pts; float* out_pts_norm; float* out_pair;
+  // floats between the outputs of consecutive residues (b, i) for o_s,
+  // o_pts, o_norm, o_pair: H C, 3 H Pv, H Pv, H Cz when packed, wider when
+  // the four are columns of one matrix (multiples of 4 there)
+  long long out_pitch[4];
   unsigned char* ws;
   // Distance-attention configuration (both NULL for the IPA forward): per
   // head, scalar weight rho_h replaces w_L / sqrt(C) and point weight

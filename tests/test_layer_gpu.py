@@ -94,3 +94,10 @@ def test_layer_long_chain_2048_sampled_rows(device):
     print(f"  {len(rows)} rows, rel error {err:.2e}", flush=True)
     assert np.isfinite(got).all()
     assert err < 3e-2, err
+
+
+def test_layer_unaligned_output_blocks(device):
+    """H C = 15 and H Pv = 9 floats: the attention's output blocks would not
+    start on 16-byte boundaries of the readout matrix, so the layer takes
+    its packed-output-plus-gather path."""
+    _check(WORKLOADS["tiny_fp32"].with_(L=45, H=3, C=5, Pv=3, Cz=8, R=1), device, 24, 1e-4, seed=6)
