@@ -410,8 +410,10 @@ def bench_backward(dev, steps: int, warmup: int, cpu: bool) -> dict:
            "pairs_per_s": pairs / (ms * 1e-3),
            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                         "frac": ach / PEAK_FP32_MFMA_TFLOPS, "flops_per_call": flops,
-                        "note": "whole gradient timed (preparation, 6 fp32 matrix-core GEMMs and a row "
-                                "kernel per query chunk, chain rule)"}}
+                        "note": "whole gradient timed (preparation, matrix-core GEMMs and a row kernel per "
+                                "query chunk, chain rule); flops counted once per product; U, dVA and the "
+                                "scalar and pair columns of dQA' run as three bf16 products on split "
+                                "fp32 operands, the rest as fp32 products, peak taken as fp32's"}}
     if cpu:
         from oracle import ipa_backward as oracle_backward
         ws = w.with_(L=256)
