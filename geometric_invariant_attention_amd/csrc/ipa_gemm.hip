@@ -37,14 +37,15 @@ __device__ __forceinline__ void pin(floatx16& acc) { asm volatile("" : "+a"(acc)
 // by a second kernel), and a segmented epilogue that writes column blocks to
 // separate arrays (fp32 or bf16).
 // ---------------------------------------------------------------------------
-template <int TM, int TN, bool AK1, bool BK1, bool X3>
+template <int TM, int TN, bool AK1, bool BK1, bool X3, int WGM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(Gemm g) {
   constexpr int KS = 32;              // reduction step
   constexpr int PK = KS + 4;          // LDS row pitch (floats)
   constexpr int PKB = KS + 8;         // LDS row pitch of the bf16 halves (elements)
-  constexpr int BM = 64 * TM, BN = 64 * TN;
+  // the four waves as WGM x (4 / WGM): 2 x 2, or 4 x 1 for narrow products
+  constexpr int BM = 32 * WGM * TM, BN = 32 * (4 / WGM) * TN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w & 1, wn = w >> 1, half = lane >> 5, l32 = lane & 31;
+  const int wm = w % WGM, wn = w / WGM, half = lane >> 5, l32 = lane & 31;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN, z = blockIdx.z;
   // z indexes the batch, or the slice of the reduction when it is split
   const int kbeg = g.kpart ? z * g.kpart : 0;
@@ -353,13 +354,13 @@ TileShape pick_tile(int M, int N, int z, bool x3) {
   return cand[best];
 }
 
-template <int TM, int TN, bool X3>
+template <int TM, int TN, bool X3, int WGM = 2>
 void launch_layout(const Gemm& g, dim3 grid, hipStream_t s) {
   const bool ak1 = g.ak == 1, bk1 = g.bk == 1;
-  if (ak1 && bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, true, X3>), grid, dim3(256), 0, s, g);
-  else if (ak1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, false, X3>), grid, dim3(256), 0, s, g);
-  else if (bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, false, true, X3>), grid, dim3(256), 0, s, g);
-  else hipLaunchKernelGGL((gemm_kernel<TM, TN, false, false, X3>), grid, dim3(256), 0, s, g);
+  if (ak1 && bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, true, X3, WGM>), grid, dim3(256), 0, s, g);
+  else if (ak1) hipLaunchKernelGGL((gemm_kernel<TM, TN, true, false, X3, WGM>), grid, dim3(256), 0, s, g);
+  else if (bk1) hipLaunchKernelGGL((gemm_kernel<TM, TN, false, true, X3, WGM>), grid, dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gemm_kernel<TM, TN, false, false, X3, WGM>), grid, dim3(256), 0, s, g);
 }
 template <int TM, int TN>
 void launch_shape(const Gemm& g, dim3 grid, hipStream_t s) {
@@ -376,6 +377,12 @@ hipError_t launch_gemm(const Gemm& g, int z, hipStream_t s) {
       (double)(g.K - 1) * g.bk + (double)(g.N - 1) * g.bn >= 2147483647.0)
     return hipErrorInvalidValue;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.N <= 32 && !g.x3) {
+    // narrow product: 128 x 32 tiles (the four waves stacked along M), a
+    // quarter of the padding of a 64-wide tile
+    launch_layout<1, 1, false, 4>(g, dim3((g.M + 127) / 128, (g.N + 31) / 32, z), s);
+    return hipGetLastError();
+  }
   const TileShape t = pick_tile(g.M, g.N, z, g.x3 != 0);
   const dim3 grid((g.M + 64 * t.tm - 1) / (64 * t.tm), (g.N + 64 * t.tn - 1) / (64 * t.tn), z);
   if (t.tm == 2 && t.tn == 2) launch_shape<2, 2>(g, grid, s);
