@@ -54,6 +54,13 @@ def test_layer_bf16_single_chain(device):
     _check(WORKLOADS["single_chain"].with_(L=200), device, 384, 3e-2)
 
 
+@pytest.mark.parametrize("c_s", [24, 72])
+def test_layer_bf16_narrow_readout(device, c_s):
+    """bf16 storage with a narrow single representation: the split-path
+    projection and readout on small output widths and a ragged row tail."""
+    _check(WORKLOADS["single_chain"].with_(L=77, H=4), device, c_s, 3e-2, seed=c_s)
+
+
 def test_layer_ragged_batch_masked_rows_zero(device):
     inp, got = _check(WORKLOADS["ragged_batch"].with_(B=4, L=70, ragged=(30, 70)), device, 128, 3e-2, seed=2)
     pad = inp["mask"] == 0
