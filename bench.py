@@ -536,8 +536,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(heads and batch elements shard without communication; see the design notes)",
+        print(f"bench.py: runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(heads and batch elements would shard without communication)",
               file=sys.stderr)
         return 2
 
