@@ -125,6 +125,23 @@ def _prep(t: torch.Tensor, dtype: torch.dtype, device, name: str) -> torch.Tenso
     return t
 
 
+def _order_on(stream, device, tensors) -> "torch.cuda.Stream":
+    """Return the stream the kernels run on (the current one if ``stream``
+    is None). The contiguous copies and mask conversions made while binding
+    run on the current stream; when the kernels go to another stream, that
+    stream first waits for the current one, and every tensor the kernels
+    touch is recorded on it so that the caching allocator does not hand its
+    memory out again before they finish."""
+    cur = torch.cuda.current_stream(device)
+    if stream is None or stream == cur:
+        return cur
+    stream.wait_stream(cur)
+    for t in tensors:
+        if isinstance(t, torch.Tensor):
+            t.record_stream(stream)
+    return stream
+
+
 class IPAForward:
     """Reusable forward plan: validated shapes, preallocated workspace and
     outputs on one device. ``__call__`` enqueues one forward on the current
@@ -186,9 +203,8 @@ class IPAForward:
         dwL, dwC = default_weights(Pqk)
         w_L = dwL if w_L is None else float(w_L)
         w_C = dwC if w_C is None else float(w_C)
-        if stream is None:
-            stream = torch.cuda.current_stream(dev)
         o = self.out
+        stream = _order_on(stream, dev, [*args.values(), m, self.workspace, *o.values()])
         self.bound = (args, m)
         return (ctypes.byref(self.dims), self.code,
                 *(_dev_ptr(args[n]) for n in ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot",
@@ -243,8 +259,7 @@ def frames_from_atoms(n: torch.Tensor, ca: torch.Tensor, c: torch.Tensor,
     B, L = n.shape[0], n.shape[1]
     rot = torch.empty(B, L, 3, 3, dtype=torch.float32, device=dev)
     trans = torch.empty(B, L, 3, dtype=torch.float32, device=dev)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
+    stream = _order_on(stream, dev, [n, ca, c, rot, trans])
     rc = load_library().ipa_frames_from_atoms(B, L, n.data_ptr(), ca.data_ptr(), c.data_ptr(),
                                               rot.data_ptr(), trans.data_ptr(),
                                               ctypes.c_void_p(stream.cuda_stream))
@@ -297,8 +312,7 @@ class MeetForward:
             if mask.device != dev:
                 raise ValueError(f"mask is on {mask.device}, expected {dev}")
             m = (mask.to(torch.uint8) if mask.dtype != torch.uint8 else mask).contiguous()
-        if stream is None:
-            stream = torch.cuda.current_stream(dev)
+        stream = _order_on(stream, dev, [*args.values(), m, self.workspace, self.out])
         self.bound = (args, m)
         return (ctypes.byref(self.dims), self.code,
                 *(args[n].data_ptr() for n in ("q", "k", "v", "x", "rho", "s")),
@@ -388,8 +402,8 @@ class DirDistForward:
             pm = pm.expand(B, H, N, N)               # broadcast dims get stride 0
             strides = (ctypes.c_int64 * 4)(*pm.stride())
             pm_ptr = pm.data_ptr()
-        if stream is None:
-            stream = torch.cuda.current_stream(dev)
+        stream = _order_on(stream, dev, [*args.values(), fm, pm, self.workspace, self.vectors,
+                                         self.output, self.attention])
         self.bound = (args, fm, pm, strides)
         return (ctypes.byref(self.dims),
                 *(args[n].data_ptr() for n in ("rot", "trans", "q_direction", "k_direction",
@@ -484,8 +498,8 @@ class IPABackward:
         m = None
         if mask is not None:
             m = (mask.to(torch.uint8) if mask.dtype != torch.uint8 else mask).contiguous()
-        if stream is None:
-            stream = torch.cuda.current_stream(dev)
+        stream = _order_on(stream, dev, [*t.values(), *o.values(), *g.values(), m, self.workspace,
+                                         *self.grads.values()])
         self.bound = (t, o, g, m)
         return (ctypes.byref(self.dims), *(t[n].data_ptr() for n in BACKWARD_INPUTS), _dev_ptr(m),
                 ctypes.c_float(w_L), ctypes.c_float(w_C),
@@ -548,8 +562,7 @@ class IPALayer:
         m = None
         if mask is not None:
             m = (mask.to(torch.uint8) if mask.dtype != torch.uint8 else mask).contiguous()
-        if stream is None:
-            stream = torch.cuda.current_stream(dev)
+        stream = _order_on(stream, dev, [*args.values(), bi, bo, m, self.workspace, self.out])
         self.bound = (args, bi, bo, m)
         return (ctypes.byref(self.dims), self.shape["c_s"], self.code,
                 args["s"].data_ptr(), args["rot"].data_ptr(), args["trans"].data_ptr(), _dev_ptr(m),

@@ -64,9 +64,18 @@ typedef struct {
 
 /* Storage type of q, k, v, q_pts, k_pts, v_pts, z1, z2.
  * IPA_F32: float32 storage, float32 arithmetic throughout.
- * IPA_BF16: bfloat16 storage, bf16 matrix-core products with float32
- * accumulation (point coordinates carried as bf16 hi/lo pairs). Frames,
- * w_b, gamma and every output are float32 for both. */
+ * IPA_BF16: bfloat16 storage, matrix-core products with float32
+ * accumulation:
+ *   - scalar and point columns of Q.K^T and all of P.V: bf16 products
+ *     (point coordinates centred per 64-residue block and carried as bf16
+ *     hi/lo pairs; their norms and block offsets stay float32);
+ *   - pair columns of Q.K^T: fp16 products of z2 and of the per-head query
+ *     operand w_L log2(e) W_b[c,h] z1[c] (rounded to nearest). Range: both
+ *     must lie within +-65504 (fp16's finite range) or they saturate there
+ *     and the logits are no longer those of the definition; magnitudes
+ *     below 2^-14 are fp16 subnormals and keep an absolute precision of
+ *     2^-24. Ordinary normalised pair factors sit far inside it.
+ * Frames, w_b, gamma and every output are float32 for both. */
 typedef enum { IPA_F32 = 0, IPA_BF16 = 1 } ipa_dtype;
 
 enum {
@@ -253,11 +262,12 @@ int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype,
  * 0 pass no gradient and receive none. Supported envelope: C <= 16,
  * Pqk <= 5, Pv <= 8, R*Cz <= 256, B*H <= 65535. Pointers 4-byte aligned,
  * workspace ipa_backward_workspace_bytes(dims) bytes, 256-byte aligned.
- * The score, dP and query/key-side products use fp32 matrix-core products;
- * the two value-side products (A z2 and A^T GA, non-negative weights) split
- * each fp32 operand into bf16 hi + lo and take three bf16 products (about
- * 2^-17 relative per term). Deterministic: repeated calls give identical
- * bits. */
+ * The score, dP and key-side products and the point columns of the
+ * query-side product use fp32 matrix-core products; the two value-side
+ * products (A z2 and A^T GA, non-negative weights) and the scalar and pair
+ * columns of the query-side product split each fp32 operand into bf16
+ * hi + lo and take three bf16 products (about 2^-17 relative per term).
+ * Deterministic: repeated calls give identical bits. */
 size_t ipa_backward_workspace_bytes(const ipa_dims* dims);
 int32_t ipa_backward(const ipa_dims* dims,
                      const float* q, const float* k, const float* v,

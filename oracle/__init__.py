@@ -9,7 +9,11 @@ Pinning status of each function (see the tests under ``tests/``):
   ipa_forward     pinned: textbook-attention reduction (library SDPA), MEET
                   lifting identity through library SDPA, SE(3) invariance,
                   L = 1 and two-residue closed forms, uniform-attention pair
-                  closed form, permutation equivariance, mask semantics.
+                  closed form, permutation equivariance, mask semantics
+                  (prefix and scattered masks: a masked batch element
+                  equals the oracle on its valid residues alone).
+  to_global       pinned by a closed form (a quarter turn about z plus a
+                  shift) and through the pins of ipa_forward.
   ipa_bruteforce  pinned against the same closed forms on tiny inputs.
   ipa_lifted      pinned to ipa_forward (exact algebra, 1e-12 relative).
   frames_from_atoms  pinned: orthonormal right-handed frames, local atom
@@ -27,14 +31,16 @@ Pinning status of each function (see the tests under ``tests/``):
                   random directions for every input, its restated forward
                   equals ipa_forward, rigid-motion identities of the frame
                   gradients, masked rows and keys; its row-restricted form
-                  (rows=) against the full gradient.
+                  (rows=) against the full gradient, and its sum over a
+                  partition of the rows into blocks equals the full
+                  gradient for every input.
   ipa_layer       pinned: reduces to ipa_forward plus the readout with
                   selection weights, readout order by one-hot rows, the
                   affine maps against a scalar loop, masked rows; its
                   row-restricted form against the full layer.
 """
 
-from .ipa_oracle import ipa_forward, ipa_logits, to_global
+from .ipa_oracle import ipa_forward, to_global
 from .bruteforce import ipa_bruteforce, dirdist_bruteforce
 from .lifted import ipa_lifted, block_centres
 from .geometry import frames_from_atoms, meet_attention
@@ -42,6 +48,6 @@ from .dirdist import dirdist_attention
 from .ipa_grad import ipa_backward
 from .layer import ipa_layer
 
-__all__ = ["ipa_forward", "ipa_logits", "to_global", "ipa_bruteforce",
+__all__ = ["ipa_forward", "to_global", "ipa_bruteforce",
            "ipa_lifted", "block_centres", "frames_from_atoms", "meet_attention",
            "dirdist_attention", "dirdist_bruteforce", "ipa_backward", "ipa_layer"]

@@ -150,18 +150,3 @@ def ipa_forward(inp: dict, rows=None, row_block: int | None = None) -> dict:
     for o in (out_s, out_pts, out_norm, out_pair):
         o += 0.0
     return {"s": out_s, "pts": out_pts, "pts_norm": out_norm, "pair": out_pair}
-
-
-def ipa_logits(inp: dict, b: int = 0) -> np.ndarray:
-    """Unmasked logits S[i, j, h] of batch element ``b`` (for pins on small L)."""
-    (q, k, v, q_pts, k_pts, v_pts, rot, trans, z1, z2, w_b, gamma, mask,
-     w_L, w_C) = _unpack(inp)
-    C = q.shape[3]
-    Qg = to_global(rot[b], trans[b], q_pts[b])
-    Kg = to_global(rot[b], trans[b], k_pts[b])
-    Z = np.einsum("irc,jrc->ijc", z1[b], z2[b])
-    bias = np.einsum("ijc,ch->ijh", Z, w_b)
-    diff = Qg[:, None] - Kg[None, :]
-    dist = np.einsum("ijhpx,ijhpx->ijh", diff, diff)
-    scal = np.einsum("ihc,jhc->ijh", q[b], k[b]) / math.sqrt(C)
-    return w_L * (scal + bias - (gamma * w_C / 2.0)[None, None, :] * dist)

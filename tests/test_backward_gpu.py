@@ -162,3 +162,29 @@ def test_backward_long_chain_sampled_rows(device, name):
     dev = float((np.abs(sv - sg) / scale).max())
     print(f"  sum_j dv_j - sum_i g_s,i: {dev:.2e} of sum |g_s|", flush=True)
     assert dev < 1e-4, dev
+
+
+def test_backward_multi_chunk_every_gradient(device):
+    """B H L^2 above 2^26, so the queries run in chunks of 896 rows (two
+    chunks per (batch, head): 896 + 204) and the key-side sums dK', dV
+    accumulate across them. All twelve gradient tensors are compared with
+    the oracle, which is summed over blocks of query rows (every row enters
+    the loss once, so the gradient is the sum of the row-restricted
+    gradients; pinned on the CPU). Block edges include the chunk edge."""
+    from oracle.ipa_grad import ipa_backward as oracle_rows
+    w = WORKLOADS["tiny_fp32"].with_(B=2, L=1100, H=32, C=4, Pqk=1, Pv=1, R=1, Cz=8)
+    assert w.B * w.H * w.L * w.L > 2 ** 26
+    print(f"[backward] multi-chunk dims={w.dims()}", flush=True)
+    inp = make_inputs(w, seed=41)
+    g = _cotangents(inp, 43)
+    got = _gpu_backward(inp, g, device)
+    ref = None
+    for r0 in range(0, w.L, 128):
+        part = oracle_rows(inp, g, rows=np.arange(r0, min(w.L, r0 + 128)))
+        ref = part if ref is None else {n: ref[n] + part[n] for n in NAMES}
+    errs = {}
+    for n in NAMES:
+        assert np.isfinite(got[n]).all(), n
+        errs[n] = float(np.abs(got[n] - ref[n]).max()) / max(1.0, float(np.abs(ref[n]).max()))
+    print("  rel errors", {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
+    assert max(errs.values()) < TOL, errs

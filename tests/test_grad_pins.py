@@ -112,3 +112,24 @@ def test_row_restricted_query_side_matches_full(w, rows):
     ref = ipa_forward(inp, rows=np.asarray(rows))
     for k in ref:
         assert np.abs(sub[k].numpy() - ref[k]).max() < 1e-12, k
+
+
+@pytest.mark.parametrize("w,cuts", [(TINY, [0, 2, 3, TINY.L]), (RAGGED, [0, 4, 5, RAGGED.L])])
+def test_row_block_partition_sums_to_full_gradient(w, cuts):
+    """Every output row enters the loss once, so the gradient is the sum of
+    the row-restricted gradients over any partition of the rows into
+    blocks: for every input, key-side, frame and weight gradients
+    included."""
+    inp = make_inputs(w, seed=23)
+    for n in INPUTS:
+        inp[n] = inp[n].astype(np.float64)
+    g = _grads(inp, 29)
+    full = ipa_backward(inp, g)
+    acc = {n: np.zeros_like(full[n]) for n in INPUTS}
+    for r0, r1 in zip(cuts[:-1], cuts[1:]):
+        part = ipa_backward(inp, g, rows=np.arange(r0, r1))
+        for n in INPUTS:
+            acc[n] += part[n]
+    for n in INPUTS:
+        scale = max(1.0, float(np.abs(full[n]).max()))
+        assert np.abs(acc[n] - full[n]).max() <= 1e-12 * scale, n

@@ -265,6 +265,42 @@ def test_masked_rows_exact_positive_zero_and_padding_ignored():
             np.testing.assert_allclose(out[key][b, :n], ref[key][0], rtol=0, atol=1e-12, err_msg=key)
 
 
+def test_scattered_mask_equals_valid_residues_alone():
+    """A non-prefix mask (fully masked interior blocks, lone valid residues,
+    masked first and last residues, an all-masked and a one-residue batch
+    element): every valid row equals the oracle run on that batch element's
+    valid residues alone, in order; masked rows are +0.0."""
+    w = WORKLOADS["tiny_fp32"].with_(B=5, L=200, H=2, C=4, Pqk=2, Pv=3, R=1, Cz=8, mask="scatter")
+    inp = make_inputs(w, seed=13)
+    out = ipa_forward(inp)
+    mask = inp["mask"].astype(bool)
+    assert not mask[2].any() and mask[3].sum() == 1 and not mask[0, 0] and not mask[0, -1]
+    for key, o in out.items():
+        sel = o[~mask]
+        assert np.all(sel == 0.0) and not np.any(np.signbit(sel)), key
+    for b in range(w.B):
+        idx = np.flatnonzero(mask[b])
+        if idx.size == 0:
+            continue
+        sub = {k: (v[b:b + 1][:, idx] if isinstance(v, np.ndarray) and v.ndim >= 2 and v.shape[:2] == (w.B, w.L) else v)
+               for k, v in inp.items()}
+        sub["dims"] = dict(inp["dims"], B=1, L=int(idx.size))
+        sub["mask"] = np.ones((1, idx.size), np.uint8)
+        ref = ipa_forward(sub)
+        for key in out:
+            np.testing.assert_allclose(out[key][b, idx], ref[key][0], rtol=0, atol=1e-12, err_msg=key)
+
+
+def test_to_global_closed_form():
+    """A quarter turn about z maps local (x, y, z) to (-y, x, z); the frame
+    origin is added after the turn."""
+    rot = np.array([[[0.0, -1.0, 0.0], [1.0, 0.0, 0.0], [0.0, 0.0, 1.0]]])
+    trans = np.array([[10.0, -2.0, 0.5]])
+    pts = np.array([1.0, 2.0, 3.0]).reshape(1, 1, 1, 3)
+    g = to_global(rot, trans, pts)
+    np.testing.assert_allclose(g.reshape(3), [10.0 - 2.0, -2.0 + 1.0, 0.5 + 3.0], rtol=0, atol=1e-15)
+
+
 def test_garbage_in_padding_does_not_change_valid_rows():
     w = WORKLOADS["ragged_batch"].with_(B=2, L=32, H=2, Cz=16, ragged=(10, 30), dtype="fp32")
     inp = make_inputs(w, seed=12)

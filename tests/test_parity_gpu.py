@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from oracle import ipa_forward as oracle_forward
-from workloads import WORKLOADS, make_inputs, stress_pair
+from workloads import WORKLOADS, make_inputs, round_to_bf16, stress_pair
 
 from ipa_gpu_util import (assert_masked_positive_zero, compare, run_gpu, to_device)
 
@@ -204,3 +204,79 @@ def test_binding_errors(device):
         plan(**dict(args, v=args["v"][:, :8]))
     with pytest.raises(ValueError):
         plan(**dict(args, z1=args["z1"].cpu()))
+
+
+@pytest.mark.parametrize("L", [1, 7, 33])
+def test_bf16_short_chains(device, L):
+    """bf16 storage below one 64-residue block: a single partial key tile,
+    query rows past L in the only query block."""
+    _check(WORKLOADS["single_chain"].with_(L=L, H=3), device, TOL_BF16, seed=L)
+
+
+def _pair_range_inputs(seed, big):
+    """Pair factors at the ends of fp16's range on the bf16 path (the pair
+    columns of Q.K^T are fp16 products). One rank-0 channel c0 of z2 is set
+    to +-6e4 (near the largest finite fp16, 65504) with z1 there at 3e-4,
+    or (big=False) to +-1.5e-5 (an fp16 subnormal, below 2^-14) with z1 there
+    at 5e4 and W_b[c0, :] = 1, so the query operand w_L log2(e) W_b z1 is
+    about 4.2e4. Either way that channel moves logits by several units and
+    the pair output by O(1)."""
+    w = WORKLOADS["single_chain"].with_(L=300, H=4, Cz=32, R=2)
+    inp = make_inputs(w, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    L, Cz = w.L, w.Cz
+    sign = np.where(rng.random((1, L)) < 0.5, -1.0, 1.0)
+    c0 = 5
+    z1, z2, wb = inp["z1"].copy(), inp["z2"].copy(), inp["w_b"].copy()
+    if big:
+        z2[:, :, 0, c0] = sign * 6.0e4 * rng.uniform(0.9, 1.0, size=(1, L))
+        z1[:, :, 0, c0] = 3.0e-4 * rng.uniform(0.5, 1.0, size=(1, L))
+    else:
+        z2[:, :, 0, c0] = sign * 1.5e-5 * rng.uniform(0.5, 1.0, size=(1, L))
+        z1[:, :, 0, c0] = 5.0e4 * rng.uniform(0.9, 1.0, size=(1, L))
+        wb[c0, :] = 1.0
+    inp["z1"] = round_to_bf16(z1)
+    inp["z2"] = round_to_bf16(z2)
+    inp["w_b"] = wb.astype(np.float32)
+    return w, inp
+
+
+@pytest.mark.parametrize("big", [True, False])
+def test_bf16_pair_fp16_range_ends(device, big):
+    """Inside the documented fp16 range of the pair columns the logits keep
+    their value at both ends: near +-65504 and below 2^-14. Errors are
+    taken relative to max(1, RMS) per output, as in the pair-stress test."""
+    w, inp = _pair_range_inputs(17 if big else 18, big)
+    _say(f"case pair fp16 range big={big} L={w.L} H={w.H} Cz={w.Cz}")
+    gpu = run_gpu(to_device(inp, device))
+    ref = oracle_forward(inp)
+    for k in ref:
+        assert np.all(np.isfinite(gpu[k])), k
+        err = float(np.abs(gpu[k].astype(np.float64) - ref[k]).max())
+        rms = float(np.sqrt(np.mean(ref[k] ** 2)))
+        _say(f"  {k}: max-abs {err:.3e}, rms {rms:.3e}")
+        assert err <= TOL_BF16 * max(rms, 1.0), (k, err, rms)
+
+
+def test_side_stream_binding(device):
+    """Kernels launched on a stream other than the current one, with inputs
+    that need contiguous copies: the copies are ordered before the kernels
+    and the result equals the current-stream call bit for bit."""
+    from geometric_invariant_attention_amd import IPAForward
+    w = WORKLOADS["single_chain"].with_(L=256, H=4)
+    inp = make_inputs(w, seed=31)
+    dev = to_device(inp, device)
+    base = run_gpu(dev)
+    names = ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2", "w_b", "gamma")
+    nc = {}
+    for k in names:
+        t = dev[k]
+        big = torch.zeros((2,) + tuple(t.shape), dtype=t.dtype, device=t.device)
+        big[1] = t
+        nc[k] = big.transpose(0, 1)[:, 1]
+    plan = IPAForward(**w.dims(), dtype=torch.bfloat16, device=device)
+    side = torch.cuda.Stream(device)
+    out = plan(**nc, w_L=dev["w_L"], w_C=dev["w_C"], stream=side)
+    side.synchronize()
+    for k in base:
+        assert np.array_equal(base[k].view(np.uint32), out[k].cpu().numpy().view(np.uint32)), k

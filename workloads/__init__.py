@@ -19,7 +19,11 @@ gamma logits, pair-bias weights, lengths, padding garbage):
 * gamma = softplus(N(0, 1)) per head, pair-bias weights W_b ~ N(0, 1);
 * ragged batches: true lengths uniform in [lo, hi], a prefix validity mask,
   and padded rows filled with finite garbage (N(0, 10^2) features,
-  non-orthogonal N(0, 1) "rotations", translations uniform in +-1e3).
+  non-orthogonal N(0, 1) "rotations", translations uniform in +-1e3);
+* scattered masks (``mask="scatter"``): a non-prefix validity mask drawn
+  after everything above from a generator of its own (``scatter_mask``),
+  with the same finite garbage in every masked row; the chain runs through
+  all L residues and is centred on its valid ones.
 
 For the bf16-storage workloads every per-residue feature tensor (q, k, v,
 points, z1, z2) is rounded to bfloat16 (round to nearest even) here, before
@@ -49,6 +53,7 @@ class IPAWorkload:
     step: float = 3.8            # chain step length in Angstrom
     ragged: tuple | None = None  # (lo, hi) true lengths, prefix mask
     seed: int = 0
+    mask: str | None = None      # "scatter": non-prefix mask (scatter_mask)
 
     def dims(self) -> dict:
         return dict(B=self.B, L=self.L, H=self.H, C=self.C, Pqk=self.Pqk,
@@ -112,6 +117,48 @@ def default_weights(Pqk: int) -> tuple[float, float]:
     return math.sqrt(1.0 / 3.0), math.sqrt(2.0 / (9.0 * Pqk))
 
 
+def scatter_mask(B: int, L: int, rng: np.random.Generator) -> np.ndarray:
+    """A non-prefix validity mask [B, L] (uint8) with the structures a mask
+    can take: batch element 0 has its first and last residues masked, whole
+    interior 64-residue blocks masked (one of them holding a single valid
+    residue) and the rest kept with probability ~0.75; element 1 has only
+    its last residue masked and sparse partial blocks (keep ~0.35);
+    element 2 is masked entirely; element 3 has exactly one valid residue;
+    further elements draw a keep rate in [0.2, 0.95] and mask their first
+    or last residue at random."""
+    m = np.zeros((B, L), dtype=np.uint8)
+    nblk = (L + 63) // 64
+    for b in range(B):
+        if b == 2:
+            continue
+        if b == 3:
+            m[b, rng.integers(L)] = 1
+            continue
+        keep = 0.75 if b == 0 else 0.35 if b == 1 else rng.uniform(0.2, 0.95)
+        row = rng.random(L) < keep
+        if nblk >= 3 and b != 1:
+            inner = np.arange(1, nblk - 1)
+            full = rng.choice(inner, size=max(1, len(inner) // 3), replace=False)
+            for J in full:
+                row[64 * J:min(L, 64 * J + 64)] = False
+            if len(full) >= 2:
+                J = int(full[0])
+                row[64 * J + rng.integers(min(64, L - 64 * J))] = True
+        if b == 0:
+            row[0] = row[-1] = False
+        elif b == 1:
+            row[0], row[-1] = True, False
+        else:
+            if rng.random() < 0.5:
+                row[0] = False
+            if rng.random() < 0.5:
+                row[-1] = False
+        if not row.any():
+            row[rng.integers(L)] = True
+        m[b] = row
+    return m
+
+
 def make_inputs(w: IPAWorkload, seed: int | None = None) -> dict:
     """Draw one seeded input set for workload ``w``.
 
@@ -153,7 +200,19 @@ def make_inputs(w: IPAWorkload, seed: int | None = None) -> dict:
             x[1:] = np.cumsum(w.step * g[1:], axis=0)
         trans[b, :n] = x - x.mean(axis=0)
 
-    if w.ragged is not None:
+    if w.mask == "scatter":
+        if w.ragged is not None:
+            raise ValueError("a workload takes either ragged lengths or a scattered mask")
+        # the mask and its garbage come from a generator of their own, so the
+        # draws above are those of the unmasked workload
+        rng = np.random.default_rng([w.seed if seed is None else seed, 0x5CA7])
+        mask = scatter_mask(B, L, rng)
+        lengths = mask.sum(axis=1).astype(np.int64)
+        for b in range(B):
+            vb = mask[b] != 0
+            if vb.any():
+                trans[b] -= trans[b][vb].mean(axis=0)
+    if w.ragged is not None or w.mask == "scatter":
         # finite garbage in every padded row
         pad = mask == 0
         npad = int(pad.sum())
@@ -179,7 +238,7 @@ def make_inputs(w: IPAWorkload, seed: int | None = None) -> dict:
         gamma=gamma.astype(np.float32), w_b=w_b.astype(np.float32),
         mask=mask, lengths=lengths.astype(np.int64),
         w_L=w_L, w_C=w_C, dtype=w.dtype, dims=w.dims(), workload=w.name,
-        has_mask=w.ragged is not None,
+        has_mask=w.ragged is not None or w.mask == "scatter",
     )
     return out
 
@@ -245,6 +304,7 @@ class MeetWorkload:
     step: float = 3.8
     ragged: tuple | None = None
     seed: int = 0
+    mask: str | None = None      # "scatter": non-prefix mask (scatter_mask)
 
     def dims(self) -> dict:
         return dict(B=self.B, L=self.L, H=self.H, C=self.C)
@@ -269,7 +329,9 @@ def make_meet_inputs(w: MeetWorkload, seed: int | None = None) -> dict:
     Draw order: chain steps, q, k, v, rho logits, s logits, lengths, padding
     garbage. x is the centred chain of the IPA recipe; q, k, v ~ N(0, 1);
     rho_h = softplus(N(0, 1)) / sqrt(C); s_h = 0.2 softplus(N(0, 1)) (per
-    A). Ragged batches get a prefix mask and finite garbage in padded rows.
+    A). Ragged batches get a prefix mask and finite garbage in padded rows;
+    ``mask="scatter"`` draws a non-prefix mask (``scatter_mask``) and its
+    garbage from a generator of their own after everything else.
     bf16 workloads round q, k, v to bfloat16 here; x, rho, s stay float32.
     """
     rng = np.random.default_rng(w.seed if seed is None else seed)
@@ -295,7 +357,17 @@ def make_meet_inputs(w: MeetWorkload, seed: int | None = None) -> dict:
         if n > 1:
             xb[1:] = np.cumsum(w.step * g[1:], axis=0)
         x[b, :n] = xb - xb.mean(axis=0)
-    if w.ragged is not None:
+    if w.mask == "scatter":
+        if w.ragged is not None:
+            raise ValueError("a workload takes either ragged lengths or a scattered mask")
+        rng = np.random.default_rng([w.seed if seed is None else seed, 0x5CA7])
+        mask = scatter_mask(B, L, rng)
+        lengths = mask.sum(axis=1).astype(np.int64)
+        for b in range(B):
+            vb = mask[b] != 0
+            if vb.any():
+                x[b] -= x[b][vb].mean(axis=0)
+    if w.ragged is not None or w.mask == "scatter":
         pad = mask == 0
         npad = int(pad.sum())
         if npad:
@@ -310,7 +382,7 @@ def make_meet_inputs(w: MeetWorkload, seed: int | None = None) -> dict:
     out = dict(feats)
     out.update(x=x.astype(np.float32), rho=rho.astype(np.float32), s=s.astype(np.float32),
                mask=mask, lengths=lengths.astype(np.int64), dtype=w.dtype, dims=w.dims(),
-               workload=w.name, has_mask=w.ragged is not None)
+               workload=w.name, has_mask=w.ragged is not None or w.mask == "scatter")
     return out
 
 
