@@ -524,56 +524,6 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 64; ++u) z[u] = (valid && 64 * P + u < RCz) ? z[u] : 0.f;
-    // bf16 path: this panel's share of each residue's pair bias with itself,
-    // sum_u w_L log2(e) W_b[u mod Cz, h] z1[u] z2[u], for every head: the
-    // pair part of the attention kernel's running-max seed. Wave w takes
-    // heads w, w + 4, ... in groups of four: lane u loads the weights of
-    // panel column u for the whole group at once, and they are broadcast
-    // through this wave's LDS block.
-    if constexpr (sizeof(T) == 2) {
-      float zz[64];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const u32x4 r = z1r[c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          zz[8 * c + 2 * e] = __uint_as_float(r[e] << 16) * z[8 * c + 2 * e];
-          zz[8 * c + 2 * e + 1] = __uint_as_float(r[e] & 0xFFFF0000u) * z[8 * c + 2 * e + 1];
-        }
-      }
-      float* const wt = wtab[w];
-      float4* const pd = reinterpret_cast<float4*>(a.ws + ly.off_pdiag);
-      for (int h0 = w; h0 < H; h0 += 16) {
-        float wl[4];
-        if (h0 == w) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) wl[c] = wl0[c];
-        } else {
-          weights(h0, wl);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) wt[64 * c + lane] = uu < RCz ? wl[c] : 0.f;
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float acc = 0.f;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(wt + 64 * c + 4 * q);
-            acc = fmaf(v.x, zz[4 * q], acc);
-            acc = fmaf(v.y, zz[4 * q + 1], acc);
-            acc = fmaf(v.z, zz[4 * q + 2], acc);
-            acc = fmaf(v.w, zz[4 * q + 3], acc);
-          }
-          const int h = h0 + 4 * c;
-          if (h < H) reinterpret_cast<float*>(pd + ((size_t)b * H + h) * Lp + i)[P] = acc;
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      }
-      if (w == 3) return;
-    }
     if (w == 0) {
       // key pair row of residue j: [64 features] in panel P
       S rowv[64];
@@ -582,7 +532,7 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       uint32_t wv[64 * ES / 4];
       pack_words(rowv, wv);
       ST::rows(xb, lane, wv, a.ws + ly.off_kz + ((((size_t)b * nJ + J) * (PW / 64) + P) * (64 * kTileN)) * ES);
-    } else {
+    } else if (w < 3) {
       // value pair block, feature-major: wave 1 features 0..31, wave 2 32..63
       const size_t blk = ((size_t)b * nJ + J) * PW + 64 * P;   // first feature row
       S out[32];
@@ -594,6 +544,99 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
         for (int f = 0; f < 32; ++f) out[f] = E::pack(z[32 + f]);
       }
       store_cols(xb, lane, out, a.ws + ly.off_vtz + (blk + (w - 1) * 32) * kTileN * ES);
+    }
+    // bf16 path: this panel's share of each residue's pair bias with itself,
+    // sum_u q[u] k[u] with the pair operands as the attention kernel's
+    // products take them: q[u] = w_L log2(e) W_b[u mod Cz, h] z1[u] and
+    // k[u] = z2[u], each saturated to fp16's finite range (+-65504), for
+    // every head: the pair part of the attention kernel's running-max seed,
+    // so that the seed is a logit of those products (it then never exceeds
+    // the row's largest logit by more than their rounding, whatever the
+    // inputs). Wave w takes heads w, w + 4, ... in groups of four: lane u
+    // loads the weights of panel column u for the whole group at once, and
+    // they are broadcast through this wave's LDS block.
+    if constexpr (sizeof(T) == 2) {
+      auto sat = [](float x) { return fminf(fmaxf(x, -65504.f), 65504.f); };
+      float z1f[64];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z1f[8 * c + 2 * e] = __uint_as_float(z1r[c][e] << 16);
+          z1f[8 * c + 2 * e + 1] = __uint_as_float(z1r[c][e] & 0xFFFF0000u);
+        }
+      }
+      // largest magnitudes of this residue's z1 and z2 segments: when no
+      // operand of the wave can reach the fp16 limit, saturation is the
+      // identity and the plain products below are the kernel's operands
+      float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+      for (int u = 0; u < 64; ++u) {
+        m1 = fmaxf(m1, fabsf(z1f[u]));
+        m2 = fmaxf(m2, fabsf(z[u]));
+      }
+      float* const wt = wtab[w];
+      float4* const pd = reinterpret_cast<float4*>(a.ws + ly.off_pdiag);
+      for (int h0 = w; h0 < H; h0 += 16) {
+        float wl[4];
+        if (h0 == w) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) wl[c] = wl0[c];
+        } else {
+          weights(h0, wl);
+        }
+        float mw = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float x = uu < RCz ? wl[c] : 0.f;
+          wt[64 * c + lane] = x;
+          mw = fmaxf(mw, fabsf(x));
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+        const bool plain = __all(m2 <= 65504.f && m1 * mw <= 65504.f);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (plain) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            float t[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[e] = z1f[4 * q + e] * z[4 * q + e];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float4 v = *reinterpret_cast<const float4*>(wt + 64 * c + 4 * q);
+              acc[c] = fmaf(v.x, t[0], acc[c]);
+              acc[c] = fmaf(v.y, t[1], acc[c]);
+              acc[c] = fmaf(v.z, t[2], acc[c]);
+              acc[c] = fmaf(v.w, t[3], acc[c]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            float k[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) k[e] = sat(z[4 * q + e]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float4 v = *reinterpret_cast<const float4*>(wt + 64 * c + 4 * q);
+              acc[c] = fmaf(sat(v.x * z1f[4 * q]), k[0], acc[c]);
+              acc[c] = fmaf(sat(v.y * z1f[4 * q + 1]), k[1], acc[c]);
+              acc[c] = fmaf(sat(v.z * z1f[4 * q + 2]), k[2], acc[c]);
+              acc[c] = fmaf(sat(v.w * z1f[4 * q + 3]), k[3], acc[c]);
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int h = h0 + 4 * c;
+          if (h < H) reinterpret_cast<float*>(pd + ((size_t)b * H + h) * Lp + i)[P] = acc[c];
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
     }
   }
 }
