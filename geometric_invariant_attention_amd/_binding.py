@@ -23,7 +23,7 @@ IPA_BF16 = 1
 STATUS = {
     0: "IPA_OK", -1: "IPA_ERR_NULL", -2: "IPA_ERR_DIMS", -3: "IPA_ERR_DTYPE",
     -4: "IPA_ERR_WORKSPACE", -5: "IPA_ERR_ALIGN", -6: "IPA_ERR_UNSUPPORTED",
-    -7: "IPA_ERR_HIP", -8: "IPA_ERR_ARG",
+    -7: "IPA_ERR_HIP", -8: "IPA_ERR_ARG", -9: "IPA_ERR_LIMIT",
 }
 
 
@@ -65,6 +65,8 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     for fn in (lib.ipa_forward, lib.ipa_lift, lib.ipa_attend):
         fn.argtypes = [ctypes.POINTER(IpaDims), i32] + [vp] * 13 + [f32, f32] + [vp] * 5 + [sz, vp]
         fn.restype = i32
+    lib.ipa_forward_noalloc.argtypes = [ctypes.POINTER(IpaDims), i32] + [vp] * 13 + [f32, f32] + [vp] * 4 + [vp]
+    lib.ipa_forward_noalloc.restype = i32
     lib.ipa_frames_from_atoms.argtypes = [i32, i32] + [vp] * 5 + [vp]
     lib.ipa_frames_from_atoms.restype = i32
     lib.ipa_meet_workspace_bytes.argtypes = [ctypes.POINTER(IpaMeetDims), i32]
@@ -221,6 +223,12 @@ class IPAForward:
 
     def forward_raw(self, raw: tuple) -> dict:
         self._call(self.lib.ipa_forward, raw)
+        return self.out
+
+    def forward_noalloc_raw(self, raw: tuple) -> dict:
+        """ipa_forward_noalloc on the arguments of ``bind`` (the plan's own
+        workspace is not passed: the library's static one is used)."""
+        self._call(self.lib.ipa_forward_noalloc, raw[:-3] + raw[-1:])
         return self.out
 
     def lift_raw(self, raw: tuple) -> None:

@@ -561,6 +561,8 @@ const char* ipa_status_string(int32_t status) {
     case IPA_ERR_UNSUPPORTED: return "dims outside the supported envelope";
     case IPA_ERR_HIP: return "a HIP kernel launch failed";
     case IPA_ERR_ARG: return "a scalar argument is out of range (w_L, w_C finite and >= 0; strides >= 0)";
+    case IPA_ERR_LIMIT:
+      return "the dims need more workspace than ipa_forward_noalloc's static array (IPA_NOALLOC_WORKSPACE_BYTES)";
     default: return "unknown status";
   }
 }

@@ -36,9 +36,11 @@
  *     status nothing was written.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream). The library allocates no device memory: scratch space
- *     is the caller's `workspace`, sized by ipa_workspace_bytes().
- *   - Reentrant; no global mutable state. Calls that share a workspace must
- *     be ordered on one stream.
+ *     is the caller's `workspace`, sized by ipa_workspace_bytes(), except
+ *     for ipa_forward_noalloc, whose workspace is a fixed static array.
+ *   - Reentrant; no global mutable state apart from ipa_forward_noalloc's
+ *     static workspace. Calls that share a workspace must be ordered on one
+ *     stream.
  */
 #ifndef IPA_MI355_H
 #define IPA_MI355_H
@@ -87,7 +89,9 @@ enum {
   IPA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned             */
   IPA_ERR_UNSUPPORTED = -6, /* dims outside the supported envelope          */
   IPA_ERR_HIP = -7,         /* a HIP launch failed                          */
-  IPA_ERR_ARG = -8          /* a scalar argument is not finite / negative   */
+  IPA_ERR_ARG = -8,         /* a scalar argument is not finite / negative   */
+  IPA_ERR_LIMIT = -9        /* ipa_forward_noalloc: the dims need more than
+                               IPA_NOALLOC_WORKSPACE_BYTES of workspace      */
 };
 
 /* Bytes of device workspace that ipa_forward needs for these dims and dtype.
@@ -162,6 +166,42 @@ int32_t ipa_attend(const ipa_dims* dims, int32_t dtype,
                    float* out_pair,
                    void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/* Size of the static device workspace of ipa_forward_noalloc: 64 MiB, one
+ * copy on each GPU the library runs on, held until the process ends. It
+ * covers ipa_workspace_bytes() up to, for example, B*L = 8192 residues with
+ * H = 12, C = 16, Pqk = 4, Pv = 8, R = 2, Cz = 128 in bf16 (48.5 MiB). */
+#define IPA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* ipa_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. It allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine); its workspace is a
+ * file-scope device array of IPA_NOALLOC_WORKSPACE_BYTES bytes in the
+ * library, whose address is looked up once per GPU, on the first call made
+ * with that GPU current.
+ * Arguments, layouts, results and status codes are ipa_forward's (the same
+ * kernels run), plus IPA_ERR_LIMIT, returned before anything is enqueued
+ * when ipa_workspace_bytes(dims, dtype) exceeds IPA_NOALLOC_WORKSPACE_BYTES,
+ * and IPA_ERR_HIP if the array's address cannot be obtained. `stream` must
+ * belong to the calling thread's current device.
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents (nothing in it needs clearing: all that the
+ * attention reads is written by the same call's lift). Calls ordered on
+ * one stream are safe; calls that overlap on one GPU (different streams, or
+ * threads without ordering between them) race on the array and their
+ * results are undefined. */
+int32_t ipa_forward_noalloc(const ipa_dims* dims, int32_t dtype,
+                            const void* q, const void* k, const void* v,
+                            const void* q_pts, const void* k_pts, const void* v_pts,
+                            const float* rot, const float* trans,
+                            const void* z1, const void* z2,
+                            const float* w_b, const float* gamma,
+                            const uint8_t* mask,
+                            float w_L, float w_C,
+                            float* out_s, float* out_pts, float* out_pts_norm,
+                            float* out_pair,
+                            void* stream);
 
 /* Residue frames from backbone atoms.
  * "Flash Invariant Point Attention", Figure 1: the C-alpha atom is the

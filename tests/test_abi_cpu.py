@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert names == ["ipa_attend", "ipa_backward", "ipa_backward_workspace_bytes",
                      "ipa_dirdist_forward", "ipa_dirdist_workspace_bytes",
-                     "ipa_forward", "ipa_frames_from_atoms", "ipa_layer_forward",
+                     "ipa_forward", "ipa_forward_noalloc", "ipa_frames_from_atoms", "ipa_layer_forward",
                      "ipa_layer_workspace_bytes", "ipa_lift",
                      "ipa_meet_forward", "ipa_meet_workspace_bytes", "ipa_status_string",
                      "ipa_version", "ipa_workspace_bytes"]
@@ -114,6 +114,25 @@ def test_forward_rejects_before_launch(lib):
     assert _call(lib, _dims(R=2, Cz=128), dtype=bd.IPA_F32) == -6
     need = bd.workspace_bytes(_dims(), bd.IPA_BF16)
     assert _call(lib, _dims(), ws_bytes=need - 1) == -4            # IPA_ERR_WORKSPACE
+
+
+def test_noalloc_rejects_before_launch(lib):
+    """ipa_forward_noalloc refuses dims beyond its static workspace, and
+    reports invalid arguments as ipa_forward does, before any HIP call."""
+    def call(dims, dtype=bd.IPA_BF16):
+        d = ctypes.byref(dims) if dims is not None else None
+        return lib.ipa_forward_noalloc(d, dtype, *([0x100000] * 12), None, ctypes.c_float(0.5),
+                                       ctypes.c_float(0.3), *([0x200000] * 4), None)
+    limit = 64 << 20
+    big = _dims(L=16384, H=8)
+    assert bd.workspace_bytes(big, bd.IPA_BF16) > limit
+    assert call(big) == -9                                          # IPA_ERR_LIMIT
+    assert "IPA_NOALLOC_WORKSPACE_BYTES" in bd.status_string(-9)
+    assert bd.workspace_bytes(_dims(L=8192), bd.IPA_BF16) <= limit
+    assert call(None) == -1
+    assert call(_dims(L=0)) == -2
+    assert call(_dims(), dtype=5) == -3
+    assert call(_dims(C=20)) == -6
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
