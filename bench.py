@@ -6,12 +6,20 @@ operands) followed by ipa_attend (fused online-softmax attention + output
 epilogue), on inputs already resident in device memory.
 
 Prints ONE JSON line: throughput in residue pairs per second (all heads, the
-whole job), achieved TFLOP/s against the algorithmic count
-2 H (d_qk + d_v) sum_b n_b^2 with d_qk = C + 3 Pqk + 2 + R Cz and
-d_v = C + 3 Pv + R Cz, the roofline of the dominant kernel (ipa_attend)
-from HIP events recorded on its own stream, peak device memory versus L,
-and the fp64 CPU oracle timed on a bounded row sample as a reported
-baseline.
+whole job) on the 2048-residue chain, achieved TFLOP/s against the
+algorithmic count 2 H (d_qk + d_v) sum_b n_b^2 with d_qk = C + 3 Pqk + 2 +
+R Cz and d_v = C + 3 Pv + R Cz, the roofline of the dominant kernel
+(ipa_attend) from HIP events recorded on its own stream, the same figures for
+the other workload sizes (512, 4096, the ragged batch, 8192 and 16384
+residues), the other entry points (distance attention, frames, layer,
+gradient, direction-and-distance attention), peak device memory versus L,
+and the fp64 CPU oracle timed on the host's cores as a reported baseline.
+
+Order of work: the CPU oracle runs first, before anything touches the GPU
+(its worker processes are forked from a process without a GPU context); then
+every GPU measurement runs back to back, the headline last, so that its
+timed steps see the clocks the chip holds under sustained load rather than
+the ramp of a cold start.
 """
 
 from __future__ import annotations
@@ -19,7 +27,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -30,11 +37,14 @@ if ROOT not in sys.path:
 
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-# MI355X fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed
-# fp32) x 2.4 GHz. Code built without packed fp32 issues at most half of it.
-PEAK_FP32_VECTOR_TFLOPS = 157.3
+# MI355X fp32 vector peak without packed fp32 instructions (this library is
+# built without them): 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz.
+PEAK_FP32_VECTOR_TFLOPS = 78.6
 PEAK_FP32_MFMA_TFLOPS = 157.3    # MI355X dense fp32 matrix peak
 METRIC = "IPA fwd pairs/s & TFLOP/s (% bf16 MFMA peak) at L=2048; peak HBM GB vs L"
+HEADLINE = "long_chain_2048"
+# the other workload sizes, timed like the headline and reported beside it
+CONFIGS = ("single_chain", "long_chain_4096", "ragged_batch", "very_long_8192", "very_long_16384")
 
 
 def algo_flops(d: dict, pairs: int) -> float:
@@ -53,9 +63,8 @@ def algo_bytes(d: dict, elem: int = 2) -> float:
 
 
 # Hardware byte counters of the dominant kernel, taken with rocprofv3 (one
-# FETCH_SIZE pass, one WRITE_SIZE pass) and committed as a summary together
-# with the hash of the kernel source they were taken on.
-PROFILE_PMC = os.path.join(ROOT, "profiles", "ipa_attend_long_chain_2048_pmc.md")
+# FETCH_SIZE pass, one WRITE_SIZE pass) per workload and committed as a
+# summary together with the hash of the kernel source they were taken on.
 KERNEL_SOURCES = ("ipa_attn.hip", "ipa_internal.h", "ipa_api.cpp")
 
 
@@ -69,11 +78,11 @@ def kernel_source_hash() -> str:
 
 def measured_traffic(workload: str):
     """HBM bytes of one ipa_attend launch from the committed counter summary
-    (each counter scaled by what it reads for a plain copy of known size), or
-    None when the summary was taken on another workload or on kernel source
-    that has changed since."""
+    of this workload (each counter scaled by what it reads for a plain copy
+    of known size), or None when there is none or it was taken on kernel
+    source that has changed since."""
     try:
-        with open(PROFILE_PMC) as fh:
+        with open(os.path.join(ROOT, "profiles", f"ipa_attend_{workload}_pmc.md")) as fh:
             lines = fh.read().splitlines()
     except OSError:
         return None
@@ -88,6 +97,257 @@ def measured_traffic(workload: str):
     return None
 
 
+# ---------------------------------------------------------------------------
+# CPU side: the fp64 oracle, timed before the GPU is touched
+# ---------------------------------------------------------------------------
+
+def cpu_workers() -> int:
+    """Worker processes for the oracle: the cores this process may run on,
+    at most 16 (one GPU's share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+# inputs by workload name, filled before the pool forks so that every worker
+# inherits them
+_CPU_INPUTS: dict = {}
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    global _WORKER_LIMITS
+    _WORKER_LIMITS = threadpool_limits(limits=1)
+
+
+def _oracle_rows(name: str, rows):
+    from oracle import ipa_forward as oracle_forward
+    t0 = time.perf_counter()
+    ref = oracle_forward(_CPU_INPUTS[name], rows=rows)
+    return rows, ref, time.perf_counter() - t0
+
+
+def cpu_headline(pool, P: int, name: str, budget_s: float) -> dict:
+    """The oracle on a bounded sample of the headline workload's query rows
+    (every row is independent), spread over P single-threaded workers."""
+    import numpy as np
+    inp = _CPU_INPUTS[name]
+    L, B = inp["dims"]["L"], inp["dims"]["B"]
+    order = np.random.default_rng(1234).permutation(L)
+    done, n, rows_all, refs = 0, 4, [], []
+    t0 = time.perf_counter()
+    while done < L and time.perf_counter() - t0 < budget_s:
+        chunks = [np.sort(order[done + k * n: done + (k + 1) * n]) for k in range(P)]
+        chunks = [c for c in chunks if len(c)]
+        for rows, ref, _ in pool.starmap(_oracle_rows, [(name, c) for c in chunks]):
+            rows_all.append(rows)
+            refs.append(ref)
+            done += len(rows)
+        n = min(2 * n, 32)
+    wall = time.perf_counter() - t0
+    pairs = B * done * L
+    return {
+        "baseline": {
+            "value": pairs / wall, "unit": "pairs/s", "cores": P, "kind": "oracle",
+            "threads": {"workers": P, "blas_threads_per_worker": 1}, "cpu_model": cpu_model(),
+            "sample": f"{done} of {L} query rows x {L} keys x B={B} (all {inp['dims']['H']} heads) of {name}, "
+                      f"fp64 numpy oracle split by query rows over {P} processes, {wall:.1f} s wall",
+        },
+        "rows": rows_all, "refs": refs,
+    }
+
+
+def cpu_single_thread(name: str, budget_s: float) -> dict:
+    """The oracle on one core (one process, one BLAS thread) on query rows of
+    the 512-residue chain."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import ipa_forward as oracle_forward
+    inp = _CPU_INPUTS[name]
+    L, B = inp["dims"]["L"], inp["dims"]["B"]
+    order = np.random.default_rng(99).permutation(L)
+    done, n, spent = 0, 8, 0.0
+    with threadpool_limits(limits=1):
+        while done < L and spent < budget_s:
+            rows = np.sort(order[done:done + n])
+            t0 = time.perf_counter()
+            oracle_forward(inp, rows=rows)
+            spent += time.perf_counter() - t0
+            done += len(rows)
+            n = min(2 * n, 128)
+    return {"value": B * done * L / spent, "unit": "pairs/s", "cores": 1, "kind": "oracle",
+            "threads": {"workers": 1, "blas_threads_per_worker": 1}, "cpu_model": cpu_model(),
+            "sample": f"{done} of {L} query rows x {L} keys of {name} (all heads), one core, {spent:.1f} s"}
+
+
+def config_sample_rows(inp, k: int = 6):
+    """Query rows whose oracle outputs check a configuration's GPU run: the
+    first and last rows and a few seeded interior ones."""
+    import numpy as np
+    L = inp["dims"]["L"]
+    rng = np.random.default_rng(77)
+    rows = {0, L - 1, L // 2} | set(int(x) for x in rng.integers(0, L, size=k))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _threads_note(P: int) -> dict:
+    return {"workers": 1, "blas_threads": P, "torch_threads": P}
+
+
+def cpu_meet(P: int) -> dict:
+    import numpy as np
+    from oracle import meet_attention
+    from workloads import MEET_WORKLOADS, make_meet_inputs
+    w = MEET_WORKLOADS["meet_chain_2048"]
+    inp = make_meet_inputs(w)
+    d = w.dims()
+    t0 = time.perf_counter()
+    ref = meet_attention(inp["q"], inp["k"], inp["v"], inp["x"], inp["rho"], inp["s"])
+    wall = time.perf_counter() - t0
+    pairs = d["B"] * d["L"] * d["L"]
+    return {"baseline": {"value": pairs / wall, "unit": "pairs/s", "cores": P, "kind": "oracle",
+                         "threads": _threads_note(P),
+                         "sample": f"the whole {w.name} workload ({d['L']} x {d['L']} pairs, {d['H']} heads), "
+                                   f"{wall:.2f} s"},
+            "ref": np.asarray(ref)}
+
+
+def cpu_frames(P: int) -> dict:
+    from oracle import frames_from_atoms
+    from workloads import make_backbone
+    B, L = 16, 16384
+    bb = make_backbone(B, L, seed=0)
+    t0 = time.perf_counter()
+    r_ref, _ = frames_from_atoms(bb["n"], bb["ca"], bb["c"])
+    wall = time.perf_counter() - t0
+    return {"baseline": {"value": B * L / wall, "unit": "residues/s", "cores": P, "kind": "oracle",
+                         "threads": _threads_note(P),
+                         "sample": f"the whole workload ({B * L} residues), {wall:.2f} s"},
+            "ref": r_ref}
+
+
+def cpu_layer(P: int) -> dict:
+    from oracle import ipa_layer
+    from workloads import WORKLOADS, make_layer_inputs
+    ci = make_layer_inputs(WORKLOADS[HEADLINE].with_(L=256), c_s=384)
+    t0 = time.perf_counter()
+    ipa_layer(ci)
+    wall = time.perf_counter() - t0
+    return {"baseline": {"value": 256 * 256 / wall, "unit": "pairs/s", "cores": P, "kind": "oracle",
+                         "threads": _threads_note(P),
+                         "sample": f"fp64 layer oracle on a 256-residue chain with the headline's dimensions "
+                                   f"(c_s = 384), {wall:.2f} s, scaled per pair"}}
+
+
+def cpu_backward(P: int) -> dict:
+    import numpy as np
+    from oracle import ipa_backward as oracle_backward
+    from workloads import WORKLOADS, make_inputs
+    ws = WORKLOADS[HEADLINE].with_(L=256)
+    ci = make_inputs(ws)
+    d = ws.dims()
+    shapes = {"s": (d["C"],), "pts": (d["Pv"], 3), "pts_norm": (d["Pv"],), "pair": (d["Cz"],)}
+    rng = np.random.default_rng(1)
+    cg = {k: rng.standard_normal((ws.B, ws.L, d["H"]) + v) for k, v in shapes.items()}
+    t0 = time.perf_counter()
+    oracle_backward(ci, cg)
+    wall = time.perf_counter() - t0
+    return {"baseline": {"value": ws.B * ws.L * ws.L / wall, "unit": "pairs/s", "cores": P, "kind": "oracle",
+                         "threads": _threads_note(P),
+                         "sample": f"fp64 autograd oracle on a {ws.L}-residue chain with the same H, C, points "
+                                   f"and pair factors, {wall:.1f} s, scaled per pair"}}
+
+
+DD_NAMES = ("rot", "trans", "q_direction", "k_direction", "q_point", "k_point", "values",
+            "direction_scale", "distance_scale", "output_weight", "output_bias")
+
+
+def cpu_dirdist(P: int, budget_s: float = 8.0) -> dict:
+    import numpy as np
+    from oracle import dirdist_attention
+    from workloads import DIRDIST_WORKLOADS, make_dirdist_inputs
+    w = DIRDIST_WORKLOADS["dd_chain_2048"]
+    inp = make_dirdist_inputs(w)
+    d = w.dims()
+    order = np.random.default_rng(7).permutation(d["N"])
+    done, spent, n, rows_all, refs = 0, 0.0, 16, [], []
+    while done < d["N"] and spent < budget_s:
+        rows = np.sort(order[done:done + n])
+        t0 = time.perf_counter()
+        ref = dirdist_attention(**{k: inp[k] for k in DD_NAMES}, frame_mask=inp["frame_mask"], rows=rows)
+        spent += time.perf_counter() - t0
+        rows_all.append(rows)
+        refs.append(ref)
+        done += len(rows)
+        n = min(2 * n, 256)
+    return {"baseline": {"value": d["B"] * done * d["N"] / spent, "unit": "pairs/s", "cores": P,
+                         "kind": "oracle", "threads": _threads_note(P),
+                         "sample": f"{done} of {d['N']} query rows x {d['N']} keys, all {d['H']} heads, "
+                                   f"fp64 numpy, {spent:.1f} s"},
+            "rows": rows_all, "refs": refs}
+
+
+def run_cpu_side(args, P: int) -> dict:
+    """Every oracle timing and every oracle output that a GPU result is
+    later compared with, computed before the GPU is initialised."""
+    import multiprocessing as mp
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from workloads import WORKLOADS, make_inputs
+
+    res = {"P": P}
+    names = [args.workload] + ([] if args.only_headline else [c for c in CONFIGS if c != args.workload])
+    for nm in names:
+        _CPU_INPUTS[nm] = make_inputs(WORKLOADS[nm])
+    ctx = mp.get_context("fork")
+    with ctx.Pool(P, initializer=_worker_init) as pool:
+        res["headline"] = cpu_headline(pool, P, args.workload, args.cpu_budget)
+        print(f"[bench] cpu oracle {res['headline']['baseline']['value']:.3e} pairs/s on {P} cores "
+              f"({res['headline']['baseline']['sample']})", file=sys.stderr, flush=True)
+        # oracle rows that check the other sizes' GPU outputs (not timed)
+        pending = {nm: config_sample_rows(_CPU_INPUTS[nm]) for nm in names[1:]}
+        done = pool.starmap(_oracle_rows, [(nm, rows) for nm, rows in pending.items()])
+        res["config_refs"] = {nm: (rows, ref) for nm, (rows, ref, _) in zip(pending, done)}
+    if args.only_headline:
+        return res
+    if "single_chain" not in _CPU_INPUTS:
+        _CPU_INPUTS["single_chain"] = make_inputs(WORKLOADS["single_chain"])
+    res["single_thread"] = cpu_single_thread("single_chain", min(10.0, args.cpu_budget))
+    print(f"[bench] cpu oracle, one core: {res['single_thread']['value']:.3e} pairs/s", file=sys.stderr,
+          flush=True)
+    import torch
+    nt = torch.get_num_threads()
+    torch.set_num_threads(P)
+    with threadpool_limits(limits=P):
+        res["meet"] = cpu_meet(P)
+        res["frames"] = cpu_frames(P)
+        res["layer"] = cpu_layer(P)
+        res["backward"] = cpu_backward(P)
+        res["dirdist"] = cpu_dirdist(P)
+    torch.set_num_threads(nt)
+    print("[bench] cpu side done", file=sys.stderr, flush=True)
+    del np
+    return res
+
+
+# ---------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------
+
 def to_device(inp, dev):
     import numpy as np
     import torch
@@ -100,12 +360,13 @@ def to_device(inp, dev):
     return t
 
 
-def run_timed(w, steps: int, warmup: int, dev):
+def run_timed(w, steps: int, warmup: int, dev, inp=None):
     import torch
     from geometric_invariant_attention_amd import IPAForward
     from workloads import make_inputs
 
-    inp = make_inputs(w)
+    if inp is None:
+        inp = make_inputs(w)
     t = to_device(inp, dev)
     d = w.dims()
     plan = IPAForward(**d, dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32, device=dev)
@@ -147,41 +408,66 @@ def run_timed(w, steps: int, warmup: int, dev):
     return inp, wall, lift_ms, attn_ms, out
 
 
-def cpu_baseline(inp, gpu_out, budget_s: float):
-    """Time the fp64 oracle on a bounded sample of query rows (every row is
-    independent) and compare the GPU output on those rows."""
+def parity_on_rows(out, rows_list, refs) -> dict:
     import numpy as np
-    from oracle import ipa_forward as oracle_forward
-
-    d = inp["dims"]
-    L, B = d["L"], d["B"]
-    rng = np.random.default_rng(1234)
-    order = rng.permutation(L)
-    done, rows_all, spent_wall, spent_cpu = 0, [], 0.0, 0.0
     errs = {}
-    n = 16
-    while done < L and spent_wall < budget_s:
-        rows = np.sort(order[done:done + n])
-        c0, w0 = time.process_time(), time.perf_counter()
-        ref = oracle_forward(inp, rows=rows)
-        spent_wall += time.perf_counter() - w0
-        spent_cpu += time.process_time() - c0
+    for rows, ref in zip(rows_list, refs):
         for k in ref:
-            e = float(np.abs(gpu_out[k][:, rows].astype(np.float64) - ref[k]).max())
+            e = float(np.abs(out[k][:, rows].astype(np.float64) - ref[k]).max())
             errs[k] = max(errs.get(k, 0.0), e)
-        done += len(rows)
-        rows_all.append(rows)
-        n = min(2 * n, 256)
-    pairs = B * done * L
-    cores = max(1, round(spent_cpu / max(spent_wall, 1e-9)))
-    return {
-        "value": pairs / spent_wall, "unit": "pairs/s", "cores": cores, "kind": "oracle",
-        "sample": f"{done} of {L} query rows x {L} keys x B={B} (all {d['H']} heads), "
-                  f"fp64 numpy, {spent_wall:.1f} s wall",
-    }, errs, done
+    return errs
 
 
-def bench_meet(dev, steps: int, warmup: int, cpu: bool) -> dict:
+def step_figures(w, inp, wall, steps, lift_ms, attn_ms) -> dict:
+    """Per-step throughput and the attention kernel's roofline figures."""
+    d = w.dims()
+    pairs = int((inp["lengths"].astype("int64") ** 2).sum())
+    flops = algo_flops(d, pairs)
+    ms_step = wall * 1e3 / steps
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    nbytes = algo_bytes(d, 2 if w.dtype == "bf16" else 4)
+    traffic = measured_traffic(w.name)
+    fig = {
+        "ms_per_step": ms_step, "pairs": pairs, "pairs_per_s": pairs / (ms_step * 1e-3),
+        "tflops": flops / (ms_step * 1e-3) / 1e12, "pct_bf16_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12
+        / PEAK_MFMA_TFLOPS,
+        "kernels_ms": {"ipa_lift": lift_ms, "ipa_attend": attn_ms},
+        "attend_roofline": {"kernel": "ipa_attend", "bound": "mfma", "achieved": attn_tflops,
+                            "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_MFMA_TFLOPS,
+                            "traffic": traffic["bytes"] if traffic else None, "algorithmic_flops": flops},
+        "step_hbm": {"algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms_step * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBS, "frac": nbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+    if traffic:
+        fig["attend_hbm_GBs_counters"] = traffic["bytes"] / (attn_ms * 1e-3) / 1e9
+    return fig
+
+
+def bench_config(name: str, dev, steps: int, warmup: int, cpu_ref) -> dict:
+    from workloads import WORKLOADS
+    w = WORKLOADS[name]
+    inp, wall, lift_ms, attn_ms, out = run_timed(w, steps, warmup, dev, inp=_CPU_INPUTS.get(name))
+    res = {"workload": name, "config": {**w.dims(), "storage": w.dtype,
+                                        "ragged": list(w.ragged) if w.ragged else None},
+           **step_figures(w, inp, wall, steps, lift_ms, attn_ms)}
+    if name == "ragged_batch":
+        # short rows: the step is bound by memory traffic and latency, not
+        # by the products
+        h = res["step_hbm"]
+        res["roofline"] = {"bound": "hbm", "achieved": h["achieved_GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": h["frac"], "algorithmic_bytes": h["algorithmic_bytes"],
+                           "note": "whole step (lift + attend), algorithmic bytes: every input read once, "
+                                   "every output written once"}
+    if cpu_ref is not None:
+        rows, ref = cpu_ref
+        res["parity_on_rows"] = {"rows": [int(r) for r in rows], "max_abs_err": parity_on_rows(out, [rows], [ref]),
+                                 "tol": 3e-2 if w.dtype == "bf16" else 1e-4}
+    print(f"[bench] {name}: {res['ms_per_step'] * 1e3:.1f} us/step, attend "
+          f"{res['attend_roofline']['frac']:.3f} of bf16 peak", file=sys.stderr, flush=True)
+    return res
+
+
+def bench_meet(dev, steps: int, warmup: int, cpu) -> dict:
     """Distance-penalised attention (ipa_meet_forward) on the 2048-residue
     chain: the forward timed like the IPA step, the fp64 oracle beside it on
     the whole workload (it is small enough), and parity on that output."""
@@ -215,43 +501,38 @@ def bench_meet(dev, steps: int, warmup: int, cpu: bool) -> dict:
            "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS,
            "executed_note": "runs on the IPA kernels with 128-wide lifted rows"}
     if cpu:
-        from oracle import meet_attention
-        c0, w0 = time.process_time(), time.perf_counter()
-        ref = meet_attention(inp["q"], inp["k"], inp["v"], inp["x"], inp["rho"], inp["s"])
-        wall = time.perf_counter() - w0
-        cores = max(1, round((time.process_time() - c0) / max(wall, 1e-9)))
         gpu = plan.out.cpu().numpy()
-        out["cpu_baseline"] = {"value": pairs / wall, "unit": "pairs/s", "cores": cores, "kind": "oracle",
-                               "sample": f"the whole {w.name} workload ({d['L']} x {d['L']} pairs, {d['H']} heads)"}
-        out["parity_max_abs_err"] = float(np.abs(gpu.astype(np.float64) - ref).max())
+        out["cpu_baseline"] = cpu["baseline"]
+        out["parity_max_abs_err"] = float(np.abs(gpu.astype(np.float64) - cpu["ref"]).max())
     return out
 
 
-def bench_frames(dev, steps: int, warmup: int, cpu: bool) -> dict:
+def bench_frames(dev, steps: int, warmup: int, cpu) -> dict:
     """Frames from backbone atoms (ipa_frames_from_atoms) over 16 chains of
     16384 residues: bytes moved per residue (36 read, 48 written) against
     the HBM peak, and the fp64 oracle on the same atoms."""
+    import ctypes
     import numpy as np
     import torch
     from geometric_invariant_attention_amd import load_library
     from workloads import make_backbone
-    import ctypes
     B, L = 16, 16384
     bb = make_backbone(B, L, seed=0)
     t = {k: torch.from_numpy(v).to(dev) for k, v in bb.items()}
     rot = torch.empty(B, L, 3, 3, dtype=torch.float32, device=dev)
     trans = torch.empty(B, L, 3, dtype=torch.float32, device=dev)
     lib = load_library()
-    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
     args = (B, L, t["n"].data_ptr(), t["ca"].data_ptr(), t["c"].data_ptr(), rot.data_ptr(), trans.data_ptr(), sp)
     for _ in range(warmup):
         lib.ipa_frames_from_atoms(*args)
     torch.cuda.synchronize(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
+    ev[0].record(stream)
     for _ in range(steps):
         rc = lib.ipa_frames_from_atoms(*args)
-    ev[1].record()
+    ev[1].record(stream)
     torch.cuda.synchronize(dev)
     assert rc == 0
     ms = ev[0].elapsed_time(ev[1]) / steps
@@ -261,31 +542,31 @@ def bench_frames(dev, steps: int, warmup: int, cpu: bool) -> dict:
                         "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                         "algorithmic_bytes": nbytes}}
     if cpu:
-        from oracle import frames_from_atoms
-        c0, w0 = time.process_time(), time.perf_counter()
-        r_ref, _ = frames_from_atoms(bb["n"], bb["ca"], bb["c"])
-        wall = time.perf_counter() - w0
-        cores = max(1, round((time.process_time() - c0) / max(wall, 1e-9)))
-        out["cpu_baseline"] = {"value": B * L / wall, "unit": "residues/s", "cores": cores, "kind": "oracle",
-                               "sample": f"the whole workload ({B * L} residues)"}
-        out["parity_max_abs_err"] = float(np.abs(rot.cpu().numpy().astype(np.float64) - r_ref).max())
+        out["cpu_baseline"] = cpu["baseline"]
+        out["parity_max_abs_err"] = float(np.abs(rot.cpu().numpy().astype(np.float64) - cpu["ref"]).max())
     return out
 
 
-def dirdist_flops_per_triple(M: int) -> int:
-    """Algorithmic fp32 operations per (query, key, head) of the
-    direction-and-distance attention, each operation counted once: direction
-    dot 5, point difference 3, squared norm 5, square root 1, the logit's
-    scale-and-subtract 2, running-max compare 1, subtract + exponential +
-    sum 3, weighted rotated values 2 * 3M."""
-    return 20 + 6 * M
+def dirdist_valu_flops_per_triple() -> int:
+    """Algorithmic fp32 vector operations per (query, key, head) of the
+    direction-and-distance attention's logit and softmax, each counted once:
+    direction dot 5, point difference 3, squared norm 5, square root 1, the
+    logit's scale-and-subtract 2, running-max compare 1, subtract +
+    exponential + sum 3."""
+    return 20
 
 
-def bench_dirdist(dev, steps: int, warmup: int, cpu: bool) -> dict:
+def dirdist_mfma_flops_per_triple(M: int) -> int:
+    """The weighted sum of the 3M rotated value coordinates per (query, key,
+    head): one multiply and one add each, run on the matrix cores."""
+    return 6 * M
+
+
+def bench_dirdist(dev, steps: int, warmup: int, cpu) -> dict:
     """Direction-and-distance attention (ipa_dirdist_forward) on the
     2048-residue chain, vectors and readout (no attention matrix): the whole
-    forward timed like the IPA step, its ALU roofline, the fp64 oracle on a
-    bounded sample of query rows beside it, and parity on that sample."""
+    forward timed like the IPA step, its vector-ALU roofline with the matrix
+    part reported apart, and parity on the oracle's sampled rows."""
     import numpy as np
     import torch
     from geometric_invariant_attention_amd import DirDistForward
@@ -293,13 +574,11 @@ def bench_dirdist(dev, steps: int, warmup: int, cpu: bool) -> dict:
     w = DIRDIST_WORKLOADS["dd_chain_2048"]
     inp = make_dirdist_inputs(w)
     d = w.dims()
-    names = ("rot", "trans", "q_direction", "k_direction", "q_point", "k_point", "values",
-             "direction_scale", "distance_scale", "output_weight", "output_bias")
-    t = {k: torch.from_numpy(inp[k]).to(dev) for k in names}
+    t = {k: torch.from_numpy(inp[k]).to(dev) for k in DD_NAMES}
     fm = torch.from_numpy(inp["frame_mask"]).to(dev)
     plan = DirDistForward(**d, device=dev, attention=False)
     stream = torch.cuda.current_stream(dev)
-    raw = plan.bind(*(t[k] for k in names), frame_mask=fm, stream=stream)
+    raw = plan.bind(*(t[k] for k in DD_NAMES), frame_mask=fm, stream=stream)
     for _ in range(warmup):
         plan.forward_raw(raw)
     torch.cuda.synchronize(dev)
@@ -316,37 +595,28 @@ def bench_dirdist(dev, steps: int, warmup: int, cpu: bool) -> dict:
     torch.cuda.synchronize(dev)
     ev_ms = ev[0].elapsed_time(ev[1]) / steps
     triples = d["B"] * d["N"] * d["N"] * d["H"]
-    flops = dirdist_flops_per_triple(d["M"]) * triples
-    ach = flops / (ev_ms * 1e-3) / 1e12
+    valu = dirdist_valu_flops_per_triple() * triples
+    mfma = dirdist_mfma_flops_per_triple(d["M"]) * triples
+    ach = valu / (ev_ms * 1e-3) / 1e12
     out = {"workload": w.name, "config": {**d, "storage": "fp32"}, "ms_per_call": ms,
            "ms_per_call_events": ev_ms, "pairs_per_s": d["B"] * d["N"] * d["N"] / (ms * 1e-3),
            "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK_FP32_VECTOR_TFLOPS,
-                        "unit": "TFLOP/s", "frac": ach / PEAK_FP32_VECTOR_TFLOPS,
-                        "flops_per_call": flops,
-                        "note": "whole forward (lift, loop, merge, readout) timed; flops of the loop"}}
+                        "unit": "TFLOP/s", "frac": ach / PEAK_FP32_VECTOR_TFLOPS, "flops_per_call": valu,
+                        "note": "whole forward (lift, loop, merge, readout) timed; vector fp32 operations of "
+                                "the logit and softmax against the peak without packed fp32"},
+           "mfma_part": {"flops_per_call": mfma, "achieved": mfma / (ev_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                         "peak": PEAK_MFMA_TFLOPS,
+                         "note": "probability-weighted rotated values, run as three bf16 products on split "
+                                 "fp32 operands; flops counted once"}}
     if cpu:
-        from oracle import dirdist_attention
         vec = plan.vectors.cpu().numpy()
         outp = plan.output.cpu().numpy()
-        rng = np.random.default_rng(7)
-        order = rng.permutation(d["N"])
-        done, spent, spent_cpu, n, err = 0, 0.0, 0.0, 16, 0.0
-        scale = None
-        while done < d["N"] and spent < 10.0:
-            rows = np.sort(order[done:done + n])
-            c0, w0 = time.process_time(), time.perf_counter()
-            ref = dirdist_attention(**{k: inp[k] for k in names}, frame_mask=inp["frame_mask"], rows=rows)
-            spent += time.perf_counter() - w0
-            spent_cpu += time.process_time() - c0
+        err = 0.0
+        for rows, ref in zip(cpu["rows"], cpu["refs"]):
             scale = max(1.0, float(np.abs(ref["output"]).max()))
             err = max(err, float(np.abs(vec[:, rows] - ref["vectors"]).max()),
                       float(np.abs(outp[:, rows] - ref["output"]).max()) / scale)
-            done += len(rows)
-            n = min(2 * n, 256)
-        out["cpu_baseline"] = {"value": d["B"] * done * d["N"] / spent, "unit": "pairs/s",
-                               "cores": max(1, round(spent_cpu / max(spent, 1e-9))), "kind": "oracle",
-                               "sample": f"{done} of {d['N']} query rows x {d['N']} keys, all {d['H']} heads, "
-                                         f"fp64 numpy, {spent:.1f} s wall"}
+        out["cpu_baseline"] = cpu["baseline"]
         out["parity_max_err"] = err
     return out
 
@@ -364,7 +634,7 @@ def backward_flops_per_pair(d: dict) -> int:
             + 2 * (DA + P3 + 1) + 2 * DV + 2)
 
 
-def bench_backward(dev, steps: int, warmup: int, cpu: bool) -> dict:
+def bench_backward(dev, steps: int, warmup: int, cpu) -> dict:
     """Gradient of the IPA forward (ipa_backward, float32) at the
     long_chain_2048 dimensions: the forward outputs come from the forward
     kernels on the same inputs (float32 copies of the bf16 workload), the
@@ -375,7 +645,7 @@ def bench_backward(dev, steps: int, warmup: int, cpu: bool) -> dict:
     import torch
     from geometric_invariant_attention_amd import IPABackward, IPAForward
     from workloads import WORKLOADS, make_inputs
-    w = WORKLOADS["long_chain_2048"]
+    w = WORKLOADS[HEADLINE]
     inp = make_inputs(w)
     d = w.dims()
     names = ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "z1", "z2", "w_b", "gamma")
@@ -407,40 +677,24 @@ def bench_backward(dev, steps: int, warmup: int, cpu: bool) -> dict:
     flops = backward_flops_per_pair(d) * pairs * d["H"]
     ach = flops / (ms * 1e-3) / 1e12
     res = {"workload": w.name, "config": {**d, "storage": "fp32"}, "calls": n, "ms_per_call": ms,
-           "pairs_per_s": pairs / (ms * 1e-3),
+           "pairs_per_s": pairs / (ms * 1e-3), "workspace_MB": bwd.ws_bytes / 2 ** 20,
            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                         "frac": ach / PEAK_FP32_MFMA_TFLOPS, "flops_per_call": flops,
-                        "note": "whole gradient timed (preparation, matrix-core GEMMs and a row kernel per "
-                                "query chunk, chain rule); flops counted once per product; U, dVA and the "
-                                "scalar and pair columns of dQA' run as three bf16 products on split "
-                                "fp32 operands, the rest as fp32 products, peak taken as fp32's"}}
+                        "note": "whole gradient timed; flops counted once per product, peak taken as fp32's"}}
     if cpu:
-        from oracle import ipa_backward as oracle_backward
-        ws = w.with_(L=256)
-        ci = make_inputs(ws)
-        cg = {k: np.random.default_rng(1).standard_normal(
-            (ws.B, ws.L) + tuple(v.shape[2:])) for k, v in g.items()}
-        c0, w0 = time.process_time(), time.perf_counter()
-        oracle_backward(ci, cg)
-        wall = time.perf_counter() - w0
-        res["cpu_baseline"] = {"value": ws.B * ws.L * ws.L / wall, "unit": "pairs/s",
-                               "cores": max(1, round((time.process_time() - c0) / max(wall, 1e-9))),
-                               "kind": "oracle",
-                               "sample": f"fp64 autograd oracle on a {ws.L}-residue chain with the same H, C, "
-                                         f"points and pair factors, {wall:.1f} s wall, scaled per pair"}
+        res["cpu_baseline"] = cpu["baseline"]
     return res
 
 
-def bench_layer(dev, steps: int, warmup: int, cpu: bool) -> dict:
+def bench_layer(dev, steps: int, warmup: int, cpu) -> dict:
     """The full IPA layer (ipa_layer_forward) at the long_chain_2048
     dimensions with a 384-wide single representation, bf16 attention: the
     whole layer timed like the IPA step; the projections' and readout's
     share is the difference to the bare attention step."""
-    import numpy as np
     import torch
     from geometric_invariant_attention_amd import IPALayer
     from workloads import WORKLOADS, make_layer_inputs
-    w = WORKLOADS["long_chain_2048"]
+    w = WORKLOADS[HEADLINE]
     c_s = 384
     inp = make_layer_inputs(w, c_s=c_s)
     d = w.dims()
@@ -459,27 +713,18 @@ def bench_layer(dev, steps: int, warmup: int, cpu: bool) -> dict:
     torch.cuda.synchronize(dev)
     ms = (time.perf_counter() - t0) * 1e3 / steps
     rows = d["B"] * d["L"]
-    n_in = layer.n_in
-    gemm_flops = 2.0 * rows * c_s * (n_in + layer.n_out)
+    gemm_flops = 2.0 * rows * c_s * (layer.n_in + layer.n_out)
     res = {"workload": w.name, "config": {**d, "c_s": c_s, "storage": "bf16"}, "ms_per_call": ms,
            "pairs_per_s": d["B"] * d["L"] * d["L"] / (ms * 1e-3),
            "projection_readout_gflop": gemm_flops / 1e9}
     if cpu:
-        from oracle import ipa_layer
-        ci = make_layer_inputs(w.with_(L=256), c_s=c_s)
-        c0, w0 = time.process_time(), time.perf_counter()
-        ipa_layer(ci)
-        wall = time.perf_counter() - w0
-        res["cpu_baseline"] = {"value": 256 * 256 / wall, "unit": "pairs/s",
-                               "cores": max(1, round((time.process_time() - c0) / max(wall, 1e-9))),
-                               "kind": "oracle",
-                               "sample": f"fp64 layer oracle on a 256-residue chain with the same dimensions, "
-                                         f"{wall:.2f} s wall, scaled per pair"}
+        res["cpu_baseline"] = cpu["baseline"]
     return res
 
 
 def memory_sweep(dev, Ls, H=12, Cz=128):
     """Peak device memory (inputs + outputs + workspace) of one forward."""
+    import numpy as np
     import torch
     from geometric_invariant_attention_amd import IPAForward
     res = []
@@ -513,7 +758,6 @@ def memory_sweep(dev, Ls, H=12, Cz=128):
                     "first_call_ms": ms})
         del plan, raw, t
     # least-squares y = a L^2 + b L
-    import numpy as np
     A = np.array([[r["L"] ** 2, r["L"]] for r in res], dtype=np.float64)
     y = np.array([r["peak_MB"] for r in res])
     coef = np.linalg.lstsq(A, y, rcond=None)[0]
@@ -524,11 +768,12 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # the clocks take a few tens of milliseconds of load to settle
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="long_chain_2048")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time only --workload (no other sizes, entry points or memory sweep)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
-                    help="seconds of fp64 oracle work for the CPU baseline (0 = skip)")
+                    help="seconds of fp64 oracle work for the CPU baseline (0 = skip every oracle)")
     ap.add_argument("--no-mem-sweep", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes (3 times) and exit; "
@@ -541,9 +786,15 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
-    import torch
     from workloads import WORKLOADS
+    w = WORKLOADS[args.workload]
+    d = w.dims()
+    cpu = {}
+    P = cpu_workers()
+    if args.cpu_budget > 0 and not args.copy_calibration:
+        cpu = run_cpu_side(args, P)
 
+    import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
@@ -557,71 +808,67 @@ def main(argv=None) -> int:
         torch.cuda.synchronize(dev)
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
         return 0
-    w = WORKLOADS[args.workload]
-    d = w.dims()
 
-    inp, wall, lift_ms, attn_ms, out = run_timed(w, args.steps, args.warmup, dev)
-    ms_step = wall * 1e3 / args.steps
-    pairs = int((inp["lengths"].astype("int64") ** 2).sum())
-    flops = algo_flops(d, pairs)
-    value = pairs / (ms_step * 1e-3)
-    tflops = flops / (ms_step * 1e-3) / 1e12
-    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    sub = {}
+    if not args.only_headline:
+        refs = cpu.get("config_refs", {})
+        sub["configs"] = {nm: bench_config(nm, dev, args.steps, args.warmup, refs.get(nm))
+                          for nm in CONFIGS if nm != args.workload}
+        sub["meet"] = bench_meet(dev, args.steps, args.warmup, cpu.get("meet"))
+        sub["frames"] = bench_frames(dev, args.steps, 20, cpu.get("frames"))
+        sub["layer"] = bench_layer(dev, args.steps, args.warmup, cpu.get("layer"))
+        sub["backward"] = bench_backward(dev, args.steps, args.warmup, cpu.get("backward"))
+        sub["dirdist"] = bench_dirdist(dev, args.steps, args.warmup, cpu.get("dirdist"))
+        print(f"[bench] distance attention {sub['meet']['ms_per_call'] * 1e3:.1f} us, layer "
+              f"{sub['layer']['ms_per_call'] * 1e3:.1f} us, gradient {sub['backward']['ms_per_call']:.3f} ms, "
+              f"direction-and-distance {sub['dirdist']['ms_per_call'] * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # the headline, last among the timed GPU work
+    inp, wall, lift_ms, attn_ms, out = run_timed(w, args.steps, args.warmup, dev, inp=_CPU_INPUTS.get(w.name))
+    fig = step_figures(w, inp, wall, args.steps, lift_ms, attn_ms)
+    ar = fig["attend_roofline"]
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": fig["pairs_per_s"],
         "unit": "pairs/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": fig["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, **d, "storage": w.dtype,
                    "mma": "bf16 (scalar/point columns, P.V) and fp16 (pair columns of Q.K^T), fp32 accumulate"},
-        "tflops": tflops,
-        "pct_bf16_peak": 100.0 * tflops / PEAK_MFMA_TFLOPS,
-        "kernels_ms": {"ipa_lift": lift_ms, "ipa_attend": attn_ms},
-        "roofline": {"kernel": "ipa_attend", "bound": "mfma", "achieved": attn_tflops,
-                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / PEAK_MFMA_TFLOPS,
-                     "traffic": traffic["bytes"] if traffic else None,
-                     "algorithmic_flops": flops},
+        "tflops": fig["tflops"],
+        "pct_bf16_peak": fig["pct_bf16_peak"],
+        "kernels_ms": fig["kernels_ms"],
+        "roofline": {"kernel": "ipa_attend", "bound": "mfma", "achieved": ar["achieved"],
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": ar["frac"],
+                     "traffic": ar["traffic"], "algorithmic_flops": ar["algorithmic_flops"]},
         "lift_GBs_algorithmic": algo_bytes(d) / (lift_ms * 1e-3) / 1e9,
     }
-    if traffic:
-        result["attend_hbm_GBs_counters"] = traffic["bytes"] / (attn_ms * 1e-3) / 1e9
-    print(f"[bench] {w.name}: {ms_step * 1e3:.1f} us/step (lift {lift_ms * 1e3:.1f} us, "
-          f"attend {attn_ms * 1e3:.1f} us), {tflops:.1f} TFLOP/s, {value:.3e} pairs/s", file=sys.stderr, flush=True)
+    if "attend_hbm_GBs_counters" in fig:
+        result["attend_hbm_GBs_counters"] = fig["attend_hbm_GBs_counters"]
+    print(f"[bench] {w.name}: {fig['ms_per_step'] * 1e3:.1f} us/step (lift {lift_ms * 1e3:.1f} us, "
+          f"attend {attn_ms * 1e3:.1f} us), {fig['tflops']:.1f} TFLOP/s, {fig['pairs_per_s']:.3e} pairs/s",
+          file=sys.stderr, flush=True)
 
-    if args.cpu_budget > 0:
-        cb, errs, rows = cpu_baseline(inp, out, args.cpu_budget)
-        result["cpu_baseline"] = cb
-        result["parity_on_cpu_sample"] = {"rows": rows, "max_abs_err": errs, "tol": 3e-2 if w.dtype == "bf16" else 1e-4}
-        print(f"[bench] cpu baseline {cb['value']:.3e} pairs/s ({cb['sample']}); max-abs errors {errs}",
-              file=sys.stderr, flush=True)
+    if "headline" in cpu:
+        hc = cpu["headline"]
+        result["cpu_baseline"] = hc["baseline"]
+        result["parity_on_cpu_sample"] = {"rows": int(sum(len(r) for r in hc["rows"])),
+                                          "max_abs_err": parity_on_rows(out, hc["rows"], hc["refs"]),
+                                          "tol": 3e-2 if w.dtype == "bf16" else 1e-4}
     else:
         result["cpu_baseline"] = None
+    if "single_thread" in cpu:
+        result["cpu_baseline_single_thread"] = cpu["single_thread"]
+    result.update(sub)
 
-    result["meet"] = bench_meet(dev, args.steps, args.warmup, args.cpu_budget > 0)
-    print(f"[bench] distance attention: {result['meet']['ms_per_call'] * 1e3:.1f} us/call, "
-          f"{result['meet']['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    result["frames"] = bench_frames(dev, args.steps, 20, args.cpu_budget > 0)
-    print("[bench] layer", file=sys.stderr, flush=True)
-    result["layer"] = bench_layer(dev, args.steps, args.warmup, args.cpu_budget > 0)
-    print("[bench] backward", file=sys.stderr, flush=True)
-    result["backward"] = bench_backward(dev, args.steps, args.warmup, args.cpu_budget > 0)
-    print("[bench] direction-and-distance attention", file=sys.stderr, flush=True)
-    result["dirdist"] = bench_dirdist(dev, args.steps, args.warmup, args.cpu_budget > 0)
-    print(f"[bench] frames: {result['frames']['ms_per_call'] * 1e3:.1f} us/call, "
-          f"{result['frames']['roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
-
-    if not args.no_mem_sweep:
+    if not (args.no_mem_sweep or args.only_headline):
         result["memory_vs_L"] = memory_sweep(dev, [512, 1024, 2048, 4096, 8192, 16384])
         print(f"[bench] memory fit {result['memory_vs_L']['fit_MB']}", file=sys.stderr, flush=True)
 
