@@ -524,27 +524,6 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < 64; ++u) z[u] = (valid && 64 * P + u < RCz) ? z[u] : 0.f;
-    if (w == 0) {
-      // key pair row of residue j: [64 features] in panel P
-      S rowv[64];
-#pragma unroll
-      for (int u = 0; u < 64; ++u) rowv[u] = E::pack_pair(z[u]);
-      uint32_t wv[64 * ES / 4];
-      pack_words(rowv, wv);
-      ST::rows(xb, lane, wv, a.ws + ly.off_kz + ((((size_t)b * nJ + J) * (PW / 64) + P) * (64 * kTileN)) * ES);
-    } else if (w < 3) {
-      // value pair block, feature-major: wave 1 features 0..31, wave 2 32..63
-      const size_t blk = ((size_t)b * nJ + J) * PW + 64 * P;   // first feature row
-      S out[32];
-      if (w == 1) {
-#pragma unroll
-        for (int f = 0; f < 32; ++f) out[f] = E::pack(z[f]);
-      } else {
-#pragma unroll
-        for (int f = 0; f < 32; ++f) out[f] = E::pack(z[32 + f]);
-      }
-      store_cols(xb, lane, out, a.ws + ly.off_vtz + (blk + (w - 1) * 32) * kTileN * ES);
-    }
     // bf16 path: this panel's share of each residue's pair bias with itself,
     // sum_u q[u] k[u] with the pair operands as the attention kernel's
     // products take them: q[u] = w_L log2(e) W_b[u mod Cz, h] z1[u] and
@@ -554,30 +533,66 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     // the row's largest logit by more than their rounding, whatever the
     // inputs). Wave w takes heads w, w + 4, ... in groups of four: lane u
     // loads the weights of panel column u for the whole group at once, and
-    // they are broadcast through this wave's LDS block.
-    if constexpr (sizeof(T) == 2) {
+    // they are broadcast through this wave's LDS block. When no operand of
+    // a group can reach the limit, saturation is the identity and the sum is
+    // taken here over the plain products z1[u] z2[u]. A group that can is
+    // done after the panel stores (seed_clamped below), from z1 and z2 read
+    // again, so that the common case keeps its registers.
+    uint32_t clamped = 0;   // bit g: head group g of this wave needs the clamps
+    auto seed_clamped = [&]() {
+      const __amdgpu_buffer_rsrc_t r1 = rsrc_or_empty(a.z1, rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
       auto sat = [](float x) { return fminf(fmaxf(x, -65504.f), 65504.f); };
-      float z1f[64];
+      float* const wt = wtab[w];
+      float4* const pd = reinterpret_cast<float4*>(a.ws + ly.off_pdiag);
+      for (int h0 = w, g0 = 0; h0 < H; h0 += 16, ++g0) {
+        if (!(clamped & (1u << g0))) continue;
+        float wl[4];
+        weights(h0, wl);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wt[64 * c + lane] = uu < RCz ? wl[c] : 0.f;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < 8; ++g) {
+          const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(r1, (ic * RCz + 64 * P) * ES + 16 * g, 0, 0);
+          const u32x4 r2 = __builtin_amdgcn_raw_buffer_load_b128(rz, (ic * RCz + 64 * P) * ES + 16 * g, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = 8 * g + e;
+            const uint32_t w1 = r[e / 2], w2 = r2[e / 2];
+            const float x1 = __uint_as_float(e & 1 ? w1 & 0xFFFF0000u : w1 << 16);
+            const float x2 = (valid && 64 * P + u < RCz) ? __uint_as_float(e & 1 ? w2 & 0xFFFF0000u : w2 << 16) : 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(sat(wt[64 * c + u] * x1), sat(x2), acc[c]);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int h = h0 + 4 * c;
+          if (h < H) reinterpret_cast<float*>(pd + ((size_t)b * H + h) * Lp + i)[P] = acc[c];
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+    };
+    if constexpr (sizeof(T) == 2) {
+      float zz[64];
+      float m1 = 0.f, m2 = 0.f;   // largest |z1|, |z2| of this residue's segment
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
+        const u32x4 r = z1r[c];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          z1f[8 * c + 2 * e] = __uint_as_float(z1r[c][e] << 16);
-          z1f[8 * c + 2 * e + 1] = __uint_as_float(z1r[c][e] & 0xFFFF0000u);
+          const float x0 = __uint_as_float(r[e] << 16), x1 = __uint_as_float(r[e] & 0xFFFF0000u);
+          m1 = fmaxf(m1, fmaxf(fabsf(x0), fabsf(x1)));
+          m2 = fmaxf(m2, fmaxf(fabsf(z[8 * c + 2 * e]), fabsf(z[8 * c + 2 * e + 1])));
+          zz[8 * c + 2 * e] = x0 * z[8 * c + 2 * e];
+          zz[8 * c + 2 * e + 1] = x1 * z[8 * c + 2 * e + 1];
         }
-      }
-      // largest magnitudes of this residue's z1 and z2 segments: when no
-      // operand of the wave can reach the fp16 limit, saturation is the
-      // identity and the plain products below are the kernel's operands
-      float m1 = 0.f, m2 = 0.f;
-#pragma unroll
-      for (int u = 0; u < 64; ++u) {
-        m1 = fmaxf(m1, fabsf(z1f[u]));
-        m2 = fmaxf(m2, fabsf(z[u]));
       }
       float* const wt = wtab[w];
       float4* const pd = reinterpret_cast<float4*>(a.ws + ly.off_pdiag);
-      for (int h0 = w; h0 < H; h0 += 16) {
+      for (int h0 = w, g0 = 0; h0 < H; h0 += 16, ++g0) {
         float wl[4];
         if (h0 == w) {
 #pragma unroll
@@ -594,49 +609,57 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
         }
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
-        const bool plain = __all(m2 <= 65504.f && m1 * mw <= 65504.f);
+        if (!__all(m2 <= 65504.f && m1 * mw <= 65504.f)) {
+          clamped |= 1u << g0;
+          continue;
+        }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        if (plain) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            float t[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) t[e] = z1f[4 * q + e] * z[4 * q + e];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float4 v = *reinterpret_cast<const float4*>(wt + 64 * c + 4 * q);
-              acc[c] = fmaf(v.x, t[0], acc[c]);
-              acc[c] = fmaf(v.y, t[1], acc[c]);
-              acc[c] = fmaf(v.z, t[2], acc[c]);
-              acc[c] = fmaf(v.w, t[3], acc[c]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            float k[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) k[e] = sat(z[4 * q + e]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float4 v = *reinterpret_cast<const float4*>(wt + 64 * c + 4 * q);
-              acc[c] = fmaf(sat(v.x * z1f[4 * q]), k[0], acc[c]);
-              acc[c] = fmaf(sat(v.y * z1f[4 * q + 1]), k[1], acc[c]);
-              acc[c] = fmaf(sat(v.z * z1f[4 * q + 2]), k[2], acc[c]);
-              acc[c] = fmaf(sat(v.w * z1f[4 * q + 3]), k[3], acc[c]);
-            }
-          }
-        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
+          float acc = 0.f;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(wt + 64 * c + 4 * q);
+            acc = fmaf(v.x, zz[4 * q], acc);
+            acc = fmaf(v.y, zz[4 * q + 1], acc);
+            acc = fmaf(v.z, zz[4 * q + 2], acc);
+            acc = fmaf(v.w, zz[4 * q + 3], acc);
+          }
           const int h = h0 + 4 * c;
-          if (h < H) reinterpret_cast<float*>(pd + ((size_t)b * H + h) * Lp + i)[P] = acc[c];
+          if (h < H) reinterpret_cast<float*>(pd + ((size_t)b * H + h) * Lp + i)[P] = acc;
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       }
+      if (w == 3) {
+        if (clamped) seed_clamped();
+        return;
+      }
+    }
+    if (w == 0) {
+      // key pair row of residue j: [64 features] in panel P
+      S rowv[64];
+#pragma unroll
+      for (int u = 0; u < 64; ++u) rowv[u] = E::pack_pair(z[u]);
+      uint32_t wv[64 * ES / 4];
+      pack_words(rowv, wv);
+      ST::rows(xb, lane, wv, a.ws + ly.off_kz + ((((size_t)b * nJ + J) * (PW / 64) + P) * (64 * kTileN)) * ES);
+    } else {
+      // value pair block, feature-major: wave 1 features 0..31, wave 2 32..63
+      const size_t blk = ((size_t)b * nJ + J) * PW + 64 * P;   // first feature row
+      S out[32];
+      if (w == 1) {
+#pragma unroll
+        for (int f = 0; f < 32; ++f) out[f] = E::pack(z[f]);
+      } else {
+#pragma unroll
+        for (int f = 0; f < 32; ++f) out[f] = E::pack(z[32 + f]);
+      }
+      store_cols(xb, lane, out, a.ws + ly.off_vtz + (blk + (w - 1) * 32) * kTileN * ES);
+    }
+    if constexpr (sizeof(T) == 2) {
+      if (clamped) seed_clamped();
     }
   }
 }
