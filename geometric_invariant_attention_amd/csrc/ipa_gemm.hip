@@ -41,7 +41,11 @@ template <int TM, int TN, bool AK1, bool BK1, bool X3, int WGM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(Gemm g) {
   constexpr int KS = 32;              // reduction step
   constexpr int PK = KS + 4;          // LDS row pitch (floats)
-  constexpr int PKB = KS + 8;         // LDS row pitch of the bf16 halves (elements)
+  // split path: an LDS row holds the step's 32 bf16 halves (64 bytes, no
+  // padding) as four 16-byte chunks, chunk c of row r in slot c ^ ((r / 4) % 4);
+  // 16 consecutive rows at one chunk then cover all 64 banks, for the
+  // operand reads and for the staging writes alike
+  constexpr int PKB = KS;
   // the four waves as WGM x (4 / WGM): 2 x 2, or 4 x 1 for narrow products
   constexpr int BM = 32 * WGM * TM, BN = 32 * (4 / WGM) * TN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -65,14 +69,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   // consecutive addresses: along k when that stride is 1 (AK1 / BK1),
   // along m / n otherwise (then that stride is 1).
   constexpr int NA = BM * KS / 256, NB = BN * KS / 256;
+  // Split path, operand with m (n) as the stride-1 dimension (BM, BN of 64
+  // or 128): consecutive threads take consecutive rows and each thread
+  // stages whole units of eight consecutive reduction indices of its row
+  // (element u is index u % 8 of unit u / 8), written as one 16-byte chunk
+  // per half once its last element is loaded; single 2-byte writes down a
+  // column of rows would hit each bank several times. With k as the
+  // stride-1 dimension a thread stages single elements along a row.
   auto a_mk = [&](int u, int& m, int& k) {
     if (AK1) { k = tid & (KS - 1); m = (tid >> 5) + 8 * u; }
+    else if (X3) { m = tid % BM; k = 8 * (tid / BM + (256 / BM) * (u >> 3)) + (u & 7); }
     else { m = tid % BM; k = tid / BM + (256 / BM) * u; }
   };
   auto b_kn = [&](int u, int& k, int& n) {
     if (BK1) { k = tid & (KS - 1); n = (tid >> 5) + 8 * u; }
+    else if (X3) { n = tid % BN; k = 8 * (tid / BN + (256 / BN) * (u >> 3)) + (u & 7); }
     else { n = tid % BN; k = tid / BN + (256 / BN) * u; }
   };
+  static_assert(!X3 || ((BM == 64 || BM == 128) && (BN == 64 || BN == 128)), "split path tiles");
+  // LDS element offset of reduction index k in row r of a split-path slice
+  auto xsw = [](int r, int k) { return r * PKB + ((((k >> 3) ^ (r >> 2)) & 3) << 3) + (k & 7); };
   // Offsets (in elements, below 2^31) of each element at reduction index 0;
   // rows past M and columns past N read row / column M - 1 / N - 1 and are
   // zeroed. Only a step that runs past kend clamps the reduction index.
@@ -110,19 +126,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     u = __float_as_uint(x - __uint_as_float((uint32_t)hi << 16));
     lo = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
   };
+  // eight values as 16 bytes of bf16 hi halves and 16 bytes of lo halves
+  auto split8 = [&](const float* x, uint4& hi, uint4& lo) {
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split(x[e], h[e], l[e]);
+    hi = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                    h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
+    lo = make_uint4(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16),
+                    l[4] | ((uint32_t)l[5] << 16), l[6] | ((uint32_t)l[7] << 16));
+  };
   auto stage_one = [&](int p, int u) {
+    if constexpr (X3) {
+      float x[8];
+      uint4 hi, lo;
+      if (u < NA) {
+        int m, k;
+        a_mk(u, m, k);
+        if (AK1) {
+          const int at = xsw(m, k);
+          split(va[u] ? ra[u] : 0.f, Ah[p][0][0][at], Ah[p][1][0][at]);
+        } else if ((u & 7) == 7) {   // the unit is written with its last element
+          const int u0 = u - 7;
+          a_mk(u0, m, k);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = va[u0 + e] ? ra[u0 + e] : 0.f;
+          split8(x, hi, lo);
+          *reinterpret_cast<uint4*>(&Ah[p][0][0][xsw(m, k)]) = hi;
+          *reinterpret_cast<uint4*>(&Ah[p][1][0][xsw(m, k)]) = lo;
+        }
+      } else {
+        const int ub = u - NA;
+        int k, n;
+        b_kn(ub, k, n);
+        if (BK1) {
+          const int at = xsw(n, k);
+          split(vb[ub] ? rb[ub] : 0.f, Bh[p][0][0][at], Bh[p][1][0][at]);
+        } else if ((ub & 7) == 7) {
+          const int u0 = ub - 7;
+          b_kn(u0, k, n);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = vb[u0 + e] ? rb[u0 + e] : 0.f;
+          split8(x, hi, lo);
+          *reinterpret_cast<uint4*>(&Bh[p][0][0][xsw(n, k)]) = hi;
+          *reinterpret_cast<uint4*>(&Bh[p][1][0][xsw(n, k)]) = lo;
+        }
+      }
+      return;
+    }
     if (u < NA) {
       int m, k;
       a_mk(u, m, k);
-      const float x = va[u] ? ra[u] : 0.f;
-      if constexpr (X3) split(x, Ah[p][0][m][k], Ah[p][1][m][k]);
-      else As[p][m][k] = x;
+      As[p][m][k] = va[u] ? ra[u] : 0.f;
     } else {
       int k, n;
       b_kn(u - NA, k, n);
-      const float x = vb[u - NA] ? rb[u - NA] : 0.f;
-      if constexpr (X3) split(x, Bh[p][0][n][k], Bh[p][1][n][k]);
-      else Bs[p][n][k] = x;
+      Bs[p][n][k] = vb[u - NA] ? rb[u - NA] : 0.f;
     }
   };
   auto gload = [&](int k0) {
@@ -189,15 +248,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   auto read_x = [&](int p, int s2, bf16x8 (&ah)[TM], bf16x8 (&al)[TM], bf16x8 (&bh)[TN], bf16x8 (&bl)[TN]) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int r = 32 * (wm * TM + i) + l32, kk = 16 * s2 + 8 * half;
-      ah[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ah[p][0][r][kk]));
-      al[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ah[p][1][r][kk]));
+      const int r = 32 * (wm * TM + i) + l32, at = xsw(r, 16 * s2 + 8 * half);
+      ah[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ah[p][0][0][at]));
+      al[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ah[p][1][0][at]));
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int r = 32 * (wn * TN + j) + l32, kk = 16 * s2 + 8 * half;
-      bh[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bh[p][0][r][kk]));
-      bl[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bh[p][1][r][kk]));
+      const int r = 32 * (wn * TN + j) + l32, at = xsw(r, 16 * s2 + 8 * half);
+      bh[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bh[p][0][0][at]));
+      bl[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Bh[p][1][0][at]));
     }
   };
   auto iter_x = [&](int k0, int p, auto mode_c) {
