@@ -54,6 +54,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLazy = 64.0f;
 // Keys per tile of the key loop (the centring blocks stay 64 residues).
 constexpr int kKT = 32;
+// Bytes of one head's key and value rows above which the query blocks of a
+// head start their key loop together (about three quarters of the 4 MB L2
+// of one XCD, on which the blocks of a head run).
+constexpr size_t kL2Share = (size_t)3 << 20;
 // Operand fragments read ahead of the matrix-core products that use them.
 constexpr int kLook = 6;
 
@@ -365,11 +369,18 @@ void ipa_attn_kernel(FwdArgs a) {
   }
   const uint32_t voK = KS::voff(lane, w, 64 * ES);
   const uint32_t voV = VS::voff(lane, w, 64 * ES);
-  // Key tiles are visited starting at this block's own diagonal tile; tiles
+  // Key tiles are visited starting at this block's own diagonal tile, or,
+  // on the bf16 path when a head's key and value rows exceed kL2Share
+  // bytes, at tile 0: the query blocks of a head then stream the same tiles
+  // at about the same time and share them in their XCD's L2 instead of each
+  // pulling a different part of a working set that no longer fits there
+  // (the running-max seed makes the first tile's position irrelevant to the
+  // softmax; the fp32 path has no seed and keeps the diagonal start). Tiles
   // whose 64-key block has no valid key are skipped (they could only add
   // zeros). seqS[0 .. nseq) lists the visited tiles in order: built once,
   // 64 candidates per ballot, so that the key loop does no searching.
-  const int T0 = (qb * kTileM / kKT) % nT;
+  const bool common_start = sizeof(T) == 2 && (size_t)Lp * (2 * kHeadW + 2 * (D - kHeadW)) * ES > kL2Share;
+  const int T0 = common_start ? 0 : (qb * kTileM / kKT) % nT;
   int nseq = 0;
   for (int c = 0; c < nT; c += 64) {
     const int uu = c + lane;
