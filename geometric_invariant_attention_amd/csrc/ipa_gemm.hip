@@ -11,6 +11,17 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Two values x as bf16 hi + lo halves (nearest even, the hardware's packed
+// conversion), x = hi + lo + O(2^-18 x); hi and lo packed two per word.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){x0, x1}, bf16x2));
+  const floatx2 r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xFFFF0000u)};
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
 
 // Compiler fence: memory operations stay on their side of it.
 __device__ __forceinline__ void fence() { asm volatile("" ::: "memory"); }
@@ -121,20 +132,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   };
   // split path: x = hi + lo + O(2^-18 x), hi and lo bf16 (nearest even)
   auto split = [](float x, uint16_t& hi, uint16_t& lo) {
-    uint32_t u = __float_as_uint(x);
-    hi = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-    u = __float_as_uint(x - __uint_as_float((uint32_t)hi << 16));
-    lo = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    uint32_t h, l;
+    split2(x, 0.f, h, l);
+    hi = (uint16_t)h;
+    lo = (uint16_t)l;
   };
   // eight values as 16 bytes of bf16 hi halves and 16 bytes of lo halves
   auto split8 = [&](const float* x, uint4& hi, uint4& lo) {
-    uint16_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) split(x[e], h[e], l[e]);
-    hi = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
-                    h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
-    lo = make_uint4(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16),
-                    l[4] | ((uint32_t)l[5] << 16), l[6] | ((uint32_t)l[7] << 16));
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
+    split2(x[4], x[5], hi.z, lo.z);
+    split2(x[6], x[7], hi.w, lo.w);
   };
   auto stage_one = [&](int p, int u) {
     if constexpr (X3) {
