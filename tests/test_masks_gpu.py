@@ -44,6 +44,24 @@ def test_forward_bf16_scattered_mask(device, L):
     _forward(w, device, TOL_BF16, seed=L)
 
 
+def test_forward_bf16_scattered_mask_common_start(device):
+    """L = 2600 with 320-wide rows: a head's key and value rows exceed the
+    L2 share above which every query block starts its key loop at tile 0,
+    so the skip list of masked interior blocks runs in that order too.
+    Compared on sampled rows of every batch element (the oracle restricted
+    to those rows), masked rows checked everywhere."""
+    w = WORKLOADS["long_chain_2048"].with_(B=3, L=2600, H=2, mask="scatter")
+    print(f"[mask] forward {w.name} B={w.B} L={w.L} H={w.H} (common start)", flush=True)
+    inp = make_inputs(w, seed=26)
+    gpu = run_gpu(to_device(inp, device))
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([np.arange(0, w.L, 97), rng.choice(w.L, 40, replace=False), [w.L - 1]]))
+    ref = oracle_forward(inp, rows=rows)
+    errs = compare(gpu, ref, TOL_BF16, valid_rows=inp["mask"].astype(bool), rows=rows)
+    assert_masked_positive_zero(gpu, inp["mask"])
+    print(f"  {len(rows)} rows, errors {errs}", flush=True)
+
+
 def test_forward_bf16_scattered_mask_narrow_rows(device):
     w = WORKLOADS["single_chain"].with_(B=4, L=520, H=2, R=1, Cz=32, mask="scatter")
     _forward(w, device, TOL_BF16, seed=7)
