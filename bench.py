@@ -44,7 +44,8 @@ PEAK_FP32_MFMA_TFLOPS = 157.3    # MI355X dense fp32 matrix peak
 METRIC = "IPA fwd pairs/s & TFLOP/s (% bf16 MFMA peak) at L=2048; peak HBM GB vs L"
 HEADLINE = "long_chain_2048"
 # the other workload sizes, timed like the headline and reported beside it
-CONFIGS = ("single_chain", "long_chain_4096", "ragged_batch", "very_long_8192", "very_long_16384")
+# (the longest last: the headline follows it directly)
+CONFIGS = ("single_chain", "ragged_batch", "long_chain_4096", "very_long_8192", "very_long_16384")
 
 
 def algo_flops(d: dict, pairs: int) -> float:
@@ -64,8 +65,9 @@ def algo_bytes(d: dict, elem: int = 2) -> float:
 
 # Hardware byte counters of the dominant kernel, taken with rocprofv3 (one
 # FETCH_SIZE pass, one WRITE_SIZE pass) per workload and committed as a
-# summary together with the hash of the kernel source they were taken on.
-KERNEL_SOURCES = ("ipa_attn.hip", "ipa_internal.h", "ipa_api.cpp")
+# summary together with the hash of the kernel source they were taken on
+# (the attention kernel, its launcher and the workspace layout it reads).
+KERNEL_SOURCES = ("ipa_attn.hip", "ipa_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -360,7 +362,8 @@ def to_device(inp, dev):
     return t
 
 
-def run_timed(w, steps: int, warmup: int, dev, inp=None):
+def prepare(w, dev, inp=None):
+    """Inputs of workload w on the device and a bound forward plan."""
     import torch
     from geometric_invariant_attention_amd import IPAForward
     from workloads import make_inputs
@@ -374,6 +377,14 @@ def run_timed(w, steps: int, warmup: int, dev, inp=None):
     raw = plan.bind(**{k: t[k] for k in ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans",
                                           "z1", "z2", "w_b", "gamma")},
                     mask=t["mask"], w_L=inp["w_L"], w_C=inp["w_C"], stream=stream)
+    return {"w": w, "inp": inp, "t": t, "plan": plan, "raw": raw, "stream": stream}
+
+
+def time_steps(prep, steps: int, warmup: int, dev):
+    """`warmup` untimed forwards, then exactly `steps` timed ones; then the
+    per-kernel durations. The outputs stay on the device (plan.out)."""
+    import torch
+    plan, raw, stream = prep["plan"], prep["raw"], prep["stream"]
     for _ in range(warmup):
         plan.lift_raw(raw)
         plan.attend_raw(raw)
@@ -402,10 +413,11 @@ def run_timed(w, steps: int, warmup: int, dev, inp=None):
         plan.attend_raw(raw)
     ev[3].record(stream)
     torch.cuda.synchronize(dev)
-    lift_ms = ev[0].elapsed_time(ev[1]) / steps
-    attn_ms = ev[2].elapsed_time(ev[3]) / steps
-    out = {k: v.detach().cpu().numpy() for k, v in plan.out.items()}
-    return inp, wall, lift_ms, attn_ms, out
+    return wall, ev[0].elapsed_time(ev[1]) / steps, ev[2].elapsed_time(ev[3]) / steps
+
+
+def outputs(prep) -> dict:
+    return {k: v.detach().cpu().numpy() for k, v in prep["plan"].out.items()}
 
 
 def parity_on_rows(out, rows_list, refs) -> dict:
@@ -443,13 +455,16 @@ def step_figures(w, inp, wall, steps, lift_ms, attn_ms) -> dict:
     return fig
 
 
-def bench_config(name: str, dev, steps: int, warmup: int, cpu_ref) -> dict:
+def bench_config(name: str, dev, steps: int, warmup: int):
+    """Time one workload size; returns its figures and its prepared plan
+    (outputs still on the device, checked later by config_parity)."""
     from workloads import WORKLOADS
     w = WORKLOADS[name]
-    inp, wall, lift_ms, attn_ms, out = run_timed(w, steps, warmup, dev, inp=_CPU_INPUTS.get(name))
+    prep = prepare(w, dev, inp=_CPU_INPUTS.get(name))
+    wall, lift_ms, attn_ms = time_steps(prep, steps, warmup, dev)
     res = {"workload": name, "config": {**w.dims(), "storage": w.dtype,
                                         "ragged": list(w.ragged) if w.ragged else None},
-           **step_figures(w, inp, wall, steps, lift_ms, attn_ms)}
+           **step_figures(w, prep["inp"], wall, steps, lift_ms, attn_ms)}
     if name == "ragged_batch":
         # short rows: the step is bound by memory traffic and latency, not
         # by the products
@@ -458,13 +473,18 @@ def bench_config(name: str, dev, steps: int, warmup: int, cpu_ref) -> dict:
                            "frac": h["frac"], "algorithmic_bytes": h["algorithmic_bytes"],
                            "note": "whole step (lift + attend), algorithmic bytes: every input read once, "
                                    "every output written once"}
-    if cpu_ref is not None:
-        rows, ref = cpu_ref
-        res["parity_on_rows"] = {"rows": [int(r) for r in rows], "max_abs_err": parity_on_rows(out, [rows], [ref]),
-                                 "tol": 3e-2 if w.dtype == "bf16" else 1e-4}
     print(f"[bench] {name}: {res['ms_per_step'] * 1e3:.1f} us/step, attend "
           f"{res['attend_roofline']['frac']:.3f} of bf16 peak", file=sys.stderr, flush=True)
-    return res
+    return res, prep
+
+
+def config_parity(res: dict, prep, cpu_ref) -> None:
+    if cpu_ref is None:
+        return
+    rows, ref = cpu_ref
+    res["parity_on_rows"] = {"rows": [int(r) for r in rows],
+                             "max_abs_err": parity_on_rows(outputs(prep), [rows], [ref]),
+                             "tol": 3e-2 if prep["w"].dtype == "bf16" else 1e-4}
 
 
 def bench_meet(dev, steps: int, warmup: int, cpu) -> dict:
@@ -809,22 +829,31 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
         return 0
 
-    sub = {}
+    # the headline's inputs and plan first, so that nothing but the launch
+    # loop stands between the last other GPU measurement and its steps
+    head = prepare(w, dev, inp=_CPU_INPUTS.get(w.name))
+    sub, cfg_preps = {}, {}
     if not args.only_headline:
-        refs = cpu.get("config_refs", {})
-        sub["configs"] = {nm: bench_config(nm, dev, args.steps, args.warmup, refs.get(nm))
-                          for nm in CONFIGS if nm != args.workload}
         sub["meet"] = bench_meet(dev, args.steps, args.warmup, cpu.get("meet"))
         sub["frames"] = bench_frames(dev, args.steps, 20, cpu.get("frames"))
         sub["layer"] = bench_layer(dev, args.steps, args.warmup, cpu.get("layer"))
-        sub["backward"] = bench_backward(dev, args.steps, args.warmup, cpu.get("backward"))
         sub["dirdist"] = bench_dirdist(dev, args.steps, args.warmup, cpu.get("dirdist"))
+        sub["backward"] = bench_backward(dev, args.steps, args.warmup, cpu.get("backward"))
         print(f"[bench] distance attention {sub['meet']['ms_per_call'] * 1e3:.1f} us, layer "
               f"{sub['layer']['ms_per_call'] * 1e3:.1f} us, gradient {sub['backward']['ms_per_call']:.3f} ms, "
               f"direction-and-distance {sub['dirdist']['ms_per_call'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+        sub["configs"] = {}
+        for nm in CONFIGS:
+            if nm != args.workload:
+                sub["configs"][nm], cfg_preps[nm] = bench_config(nm, dev, args.steps, args.warmup)
 
     # the headline, last among the timed GPU work
-    inp, wall, lift_ms, attn_ms, out = run_timed(w, args.steps, args.warmup, dev, inp=_CPU_INPUTS.get(w.name))
+    wall, lift_ms, attn_ms = time_steps(head, args.steps, args.warmup, dev)
+    inp, out = head["inp"], outputs(head)
+    refs = cpu.get("config_refs", {})
+    for nm, prep in cfg_preps.items():
+        config_parity(sub["configs"][nm], prep, refs.get(nm))
+    del cfg_preps
     fig = step_figures(w, inp, wall, args.steps, lift_ms, attn_ms)
     ar = fig["attend_roofline"]
     result = {
