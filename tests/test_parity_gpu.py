@@ -149,6 +149,17 @@ def test_long_sampled(device, name):
     _check(w, device, TOL_BF16, rows=_edge_rows(w.L, n_random=24)[::4])
 
 
+def test_max_length_sampled(device):
+    """L = 65536, the longest chain the envelope admits (1024 key blocks of
+    64 residues, the most the attention kernel's per-block tables hold),
+    with two heads; tile and block edges at the start and end of the chain
+    and random rows compared with the oracle."""
+    w = WORKLOADS["very_long_16384"].with_(L=65536, H=2)
+    rows = _edge_rows(w.L, n_random=16, seed=5)
+    rows = np.unique(np.concatenate([rows[:12], rows[-12:], rows[::len(rows) // 16]]))
+    _check(w, device, TOL_BF16, rows=rows)
+
+
 def test_determinism_and_noncontiguous(device):
     w = WORKLOADS["single_chain"].with_(L=300, H=4)
     inp = make_inputs(w, seed=21)
