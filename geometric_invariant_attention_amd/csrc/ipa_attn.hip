@@ -200,7 +200,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff
                                            voff, soff, 0, 0);
 }
 
-template <typename T, int D>
+// ZP: the pair panels are known to be zero (the distance attention, which
+// has no pair representation, runs on 128-wide rows whose pair panel the lift
+// leaves at zero): their copies, products and outputs are skipped, and so
+// is every read of z1.
+template <typename T, int D, bool ZP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ipa_attn_kernel(FwdArgs a) {
   using M = Mma<T>;
@@ -210,6 +214,7 @@ void ipa_attn_kernel(FwdArgs a) {
   constexpr int NKH = kHeadW / M::kStep;   // of which cover the head part
   constexpr int NFB = D / 32;              // 32-feature blocks of O^T
   constexpr int NP = SM::kNP;
+  constexpr int NPC = ZP ? 1 : NP;         // panels copied per tile
   constexpr int NST = kKT / M::kStep;      // products per O^T block per tile
   // the probabilities of a tile are formed two per score step (bf16)
   static_assert(sizeof(T) == 4 || NKS >= 8, "at least 8 score steps per tile");
@@ -291,7 +296,8 @@ void ipa_attn_kernel(FwdArgs a) {
       qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rQ, vq + 32 * s, 0, 0));
     u32x4 zr[NKS - NKH];
 #pragma unroll
-    for (int s = NKH; s < NKS; ++s) zr[s - NKH] = __builtin_amdgcn_raw_buffer_load_b128(rZ, vz + 32 * (s - NKH), 0, 0);
+    for (int s = NKH; s < NKS; ++s)
+      zr[s - NKH] = ZP ? u32x4{0u, 0u, 0u, 0u} : __builtin_amdgcn_raw_buffer_load_b128(rZ, vz + 32 * (s - NKH), 0, 0);
     // pair column u0 = 16 (s - NKH) + 8 g scales channel u0 mod Cz (stepped
     // without division; Cz >= 8)
     int c0 = 8 * g;
@@ -429,6 +435,7 @@ void ipa_attn_kernel(FwdArgs a) {
   // the product's shadow; scheduling fences keep exactly this order.
   auto phase_a = [&](const float4 cJ, const unsigned char* Kc, f32x16 sacc, auto&& side) -> f32x16 {
     auto kfrag = [&](int s) -> Frag {
+      if (ZP && s >= NKH) return Frag{};   // never used
       const int f = M::kStep * s;
       const unsigned char* r = Kc + (f / 64) * SM::kKPanel;
       if constexpr (sizeof(T) == 2)
@@ -446,7 +453,7 @@ void ipa_attn_kernel(FwdArgs a) {
       if (s + kLook < NKS) look[s % kLook] = kfrag(s + kLook);
       if (s < NKH)
         sacc = mma(cur, qf[s], sacc);
-      else
+      else if constexpr (!ZP)
         sacc = mma_pair(cur, qf[s], sacc);
       // ties the product to this step (an ordered, empty statement that the
       // next product depends on); without it the products, which have no
@@ -502,6 +509,7 @@ void ipa_attn_kernel(FwdArgs a) {
   auto phase_b = [&](const unsigned char* Vc, const Frag* pf, auto&& side) {
     auto vfrag = [&](int idx) -> Frag {
       const int fb = idx / NST, s2 = idx % NST;
+      if (ZP && fb >= kHeadW / 32) return Frag{};   // never used
       const unsigned char* r = Vc + 32 * fb * kKT * ES;
       if constexpr (sizeof(T) == 2)
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(r + VS::at(n, 16 * s2 + 8 * g, 2)));
@@ -517,7 +525,7 @@ void ipa_attn_kernel(FwdArgs a) {
     for (int idx = 0; idx < NB; ++idx) {
       const Frag cur = look[idx % kLook];
       if (idx + kLook < NB) look[idx % kLook] = vfrag(idx + kLook);
-      oacc[idx / NST] = mma(cur, pf[idx % NST], oacc[idx / NST]);
+      if (!ZP || idx / NST < kHeadW / 32) oacc[idx / NST] = mma(cur, pf[idx % NST], oacc[idx / NST]);
       side(idx);
       step_fence();
     }
@@ -540,7 +548,7 @@ void ipa_attn_kernel(FwdArgs a) {
   auto copy_k = [&](int t, unsigned char* Kd) {
     const int J = t >> 1, half = t & 1;
 #pragma unroll
-    for (int P = 0; P < NP; ++P) {
+    for (int P = 0; P < NPC; ++P) {
       const uint32_t kbase = P == 0 ? (uint32_t)(J * 64 + 32 * half) * 64 * ES
                                     : (uint32_t)((J * (NP - 1) + P - 1) * 64 + 32 * half) * 64 * ES;
 #pragma unroll
@@ -564,15 +572,15 @@ void ipa_attn_kernel(FwdArgs a) {
   };
   // Direct-to-LDS copy op k of a tile pair: ops 0 .. NP VJ - 1 copy the
   // value tile at vo into Vd, the next NP KJ ops the key tile at ko into Kd.
-  constexpr int NDMA = NP * (VJ + KJ);
+  constexpr int NDMA = NPC * (VJ + KJ);
   auto dma_op = [&](int k, TileOff vo, unsigned char* Vd, TileOff ko, unsigned char* Kd) {
-    if (k < NP * VJ) {
+    if (k < NPC * VJ) {
       const int P = k / VJ, j = k % VJ;
       const int kk = w + 4 * j;
       const uint32_t c = (P == 0 ? 0u : (uint32_t)(P - 1) * 4096 * ES) + (uint32_t)(kk * VS::kRPL * 64 * ES);
       dma16(P == 0 ? rVh : rVz, voV, (P == 0 ? vo.h : vo.z) + c, Vd + P * SM::kVPanel + kk * 1024);
     } else {
-      const int q = k - NP * VJ;
+      const int q = k - NPC * VJ;
       const int P = q / KJ, j = q % KJ;
       const int kk = w + 4 * j;
       const uint32_t c = (P == 0 ? 0u : (uint32_t)(P - 1) * 64 * 64 * ES) + (uint32_t)(kk * KS::kRPL * 64 * ES);
@@ -595,7 +603,7 @@ void ipa_attn_kernel(FwdArgs a) {
   auto copy_v = [&](int t, unsigned char* Vd) {
     const int J = t >> 1, half = t & 1;
 #pragma unroll
-    for (int P = 0; P < NP; ++P) {
+    for (int P = 0; P < NPC; ++P) {
       const uint32_t vbase = (P == 0 ? (uint32_t)J * 4096 * ES : (uint32_t)(J * (NP - 1) + P - 1) * 4096 * ES) +
                              (uint32_t)(32 * half * ES);
 #pragma unroll
@@ -817,7 +825,7 @@ void ipa_attn_kernel(FwdArgs a) {
     const int dr = 64 / CPR, dc = 64 - dr * CPR;
 #pragma unroll
     for (int s = 0; s < NZL; ++s) {
-      if (64 * s < 32 * CPR) zv[s] = __builtin_amdgcn_raw_buffer_load_b128(rZ, (qw + zr) * RB + 16 * zc, 0, 0);
+      if (!ZP && 64 * s < 32 * CPR) zv[s] = __builtin_amdgcn_raw_buffer_load_b128(rZ, (qw + zr) * RB + 16 * zc, 0, 0);
       zo[s] = zr * RB + 16 * (zc ^ (zr & zm));
       zr += dr;
       zc += dc;
@@ -830,7 +838,7 @@ void ipa_attn_kernel(FwdArgs a) {
     for (int s = 0; s < 2; ++s) tv[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rT, (qw * 3 + 64 * s + lane) * 4, 0, 0));
 #pragma unroll
     for (int s = 0; s < NZL; ++s)
-      if (64 * s + lane < 32 * CPR) *reinterpret_cast<u32x4*>(xs + zo[s]) = zv[s];
+      if (!ZP && 64 * s + lane < 32 * CPR) *reinterpret_cast<u32x4*>(xs + zo[s]) = zv[s];
 #pragma unroll
     for (int s = 0; s < 5; ++s)
       if (64 * s + lane < 32 * 9) fr[64 * s + lane] = rv[s];
@@ -930,6 +938,7 @@ void ipa_attn_kernel(FwdArgs a) {
   store_rows(std::integral_constant<int, PS>{}, so, C, a.out_s, bi0 * pS + (size_t)h * C, pS);
   store_rows(std::integral_constant<int, PP>{}, sp, 3 * Pv, a.out_pts, bi0 * pP + (size_t)h * 3 * Pv, pP);
   store_rows(std::integral_constant<int, PN>{}, sn, Pv, a.out_pts_norm, bi0 * pN + (size_t)h * Pv, pN);
+  if constexpr (ZP) return;   // no pair channels
 
   // ---- pair channels: o_pair[c] = sum_r z1[r Cz + c] O[r Cz + c] / l ----
   // Lane (n, g) holds O at features 32 fb + 8 k + 4 g + e of query n: 4-wide
@@ -1040,6 +1049,13 @@ void ipa_attn_kernel(FwdArgs a) {
 template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const int nwg = (a.lay.Lp / kTileM) * a.lay.H * a.lay.B;
+  // the distance attention: no pair factors, no pair output, one zero panel
+  if constexpr (D == 128) {
+    if (a.z1 == nullptr && a.z2 == nullptr && a.out_pair == nullptr) {
+      hipLaunchKernelGGL((ipa_attn_kernel<T, D, true>), dim3(nwg), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((ipa_attn_kernel<T, D>), dim3(nwg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
