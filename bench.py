@@ -196,14 +196,48 @@ def cpu_single_thread(name: str, budget_s: float) -> dict:
             "sample": f"{done} of {L} query rows x {L} keys of {name} (all heads), one core, {spent:.1f} s"}
 
 
-def config_sample_rows(inp, k: int = 6):
-    """Query rows whose oracle outputs check a configuration's GPU run: the
-    first and last rows and a few seeded interior ones."""
+def config_sample_rows(inp, n: int = 512):
+    """Query rows on which the oracle times and checks a workload size: all
+    of them up to 2048 residues, otherwise a seeded sample of n rows that
+    includes the tile and block edges of the first and last four 64-residue
+    blocks."""
     import numpy as np
     L = inp["dims"]["L"]
+    if L <= 2048:
+        return np.arange(L, dtype=np.int64)
+    edges = set()
+    for t in list(range(0, 4 * 64, 64)) + list(range(L - 4 * 64, L, 64)):
+        edges.update({t, t + 1, t + 31, t + 32, t + 63})
+    edges = {r for r in edges if 0 <= r < L}
     rng = np.random.default_rng(77)
-    rows = {0, L - 1, L // 2} | set(int(x) for x in rng.integers(0, L, size=k))
-    return np.array(sorted(rows), dtype=np.int64)
+    rest = rng.choice(np.setdiff1d(np.arange(L), np.array(sorted(edges))), size=n - len(edges), replace=False)
+    return np.array(sorted(edges | set(int(x) for x in rest)), dtype=np.int64)
+
+
+def cpu_config(pool, P: int, name: str) -> dict:
+    """The oracle on the rows config_sample_rows picks for a workload size,
+    split over P single-threaded workers: its timing (per pair, scaled from
+    the sample when it is one) and its outputs for the GPU's parity."""
+    import numpy as np
+    inp = _CPU_INPUTS[name]
+    L, B = inp["dims"]["L"], inp["dims"]["B"]
+    rows = config_sample_rows(inp)
+    chunks = [c for c in np.array_split(rows, P) if len(c)]
+    t0 = time.perf_counter()
+    parts = pool.starmap(_oracle_rows, [(name, c) for c in chunks])
+    wall = time.perf_counter() - t0
+    ref = {k: np.concatenate([pr[1][k] for pr in parts], axis=1) for k in parts[0][1]}
+    full = len(rows) == L
+    return {
+        "baseline": {
+            "value": B * len(rows) * L / wall, "unit": "pairs/s", "cores": P, "kind": "oracle",
+            "threads": {"workers": P, "blas_threads_per_worker": 1},
+            "sample": (f"the whole workload ({B} x {L} x {L} pairs)" if full else
+                       f"{len(rows)} of {L} query rows x {L} keys x B={B}, extrapolated per pair")
+                      + f", {wall:.2f} s wall",
+        },
+        "rows": rows, "ref": ref,
+    }
 
 
 def _threads_note(P: int) -> dict:
@@ -320,10 +354,9 @@ def run_cpu_side(args, P: int) -> dict:
         res["headline"] = cpu_headline(pool, P, args.workload, args.cpu_budget)
         print(f"[bench] cpu oracle {res['headline']['baseline']['value']:.3e} pairs/s on {P} cores "
               f"({res['headline']['baseline']['sample']})", file=sys.stderr, flush=True)
-        # oracle rows that check the other sizes' GPU outputs (not timed)
-        pending = {nm: config_sample_rows(_CPU_INPUTS[nm]) for nm in names[1:]}
-        done = pool.starmap(_oracle_rows, [(nm, rows) for nm, rows in pending.items()])
-        res["config_refs"] = {nm: (rows, ref) for nm, (rows, ref, _) in zip(pending, done)}
+        # the other sizes: the oracle's timing and the rows their GPU
+        # outputs are checked on
+        res["configs"] = {nm: cpu_config(pool, P, nm) for nm in names[1:]}
     if args.only_headline:
         return res
     if "single_chain" not in _CPU_INPUTS:
@@ -441,6 +474,7 @@ def step_figures(w, inp, wall, steps, lift_ms, attn_ms) -> dict:
     traffic = measured_traffic(w.name)
     fig = {
         "ms_per_step": ms_step, "pairs": pairs, "pairs_per_s": pairs / (ms_step * 1e-3),
+        "head_pairs_per_s": d["H"] * pairs / (ms_step * 1e-3),
         "tflops": flops / (ms_step * 1e-3) / 1e12, "pct_bf16_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12
         / PEAK_MFMA_TFLOPS,
         "kernels_ms": {"ipa_lift": lift_ms, "ipa_attend": attn_ms},
@@ -478,12 +512,13 @@ def bench_config(name: str, dev, steps: int, warmup: int):
     return res, prep
 
 
-def config_parity(res: dict, prep, cpu_ref) -> None:
-    if cpu_ref is None:
+def config_parity(res: dict, prep, cpu) -> None:
+    if cpu is None:
         return
-    rows, ref = cpu_ref
-    res["parity_on_rows"] = {"rows": [int(r) for r in rows],
-                             "max_abs_err": parity_on_rows(outputs(prep), [rows], [ref]),
+    rows, ref = cpu["rows"], cpu["ref"]
+    # rows whose own mask entry is 0 are compared too (both sides give +0.0)
+    res["cpu_baseline"] = cpu["baseline"]
+    res["parity_on_rows"] = {"rows": len(rows), "max_abs_err": parity_on_rows(outputs(prep), [rows], [ref]),
                              "tol": 3e-2 if prep["w"].dtype == "bf16" else 1e-4}
 
 
@@ -850,9 +885,9 @@ def main(argv=None) -> int:
     # the headline, last among the timed GPU work
     wall, lift_ms, attn_ms = time_steps(head, args.steps, args.warmup, dev)
     inp, out = head["inp"], outputs(head)
-    refs = cpu.get("config_refs", {})
+    cfg_cpu = cpu.get("configs", {})
     for nm, prep in cfg_preps.items():
-        config_parity(sub["configs"][nm], prep, refs.get(nm))
+        config_parity(sub["configs"][nm], prep, cfg_cpu.get(nm))
     del cfg_preps
     fig = step_figures(w, inp, wall, args.steps, lift_ms, attn_ms)
     ar = fig["attend_roofline"]
