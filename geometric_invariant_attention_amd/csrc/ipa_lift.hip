@@ -120,48 +120,57 @@ template <> struct Elt<float> {
   }
 };
 
-// Elements 0 .. NS-1 of the input row that starts `off` bytes into a buffer
-// resource, `wide` bytes per load: 16 when the row length and the base keep
-// 16-byte alignment, else 4, else one element. A lane reads its whole row
-// with a few wide loads instead of one load per element (each load touches
-// one cache line per lane, so the count of loads sets the cost). Elements
-// past the row's end come from whatever follows it, or are zero past the
-// end of the buffer; callers drop them.
+// 32-bit words that hold NS row elements of type T as issue_row loads them.
+template <typename T> constexpr int raw_words(int NS) { return sizeof(T) == 2 ? 4 * ((NS + 7) / 8) : NS; }
+
+// Issues the loads of elements 0 .. NS-1 of the input row that starts `off`
+// bytes into a buffer resource, `wide` bytes per load: 16 when the row
+// length and the base keep 16-byte alignment, else 4, else one element. A
+// lane reads its whole row with a few wide loads instead of one load per
+// element (each load touches one cache line per lane, so the count of loads
+// sets the cost). The raw words land in `raw` (bf16 rows: element k in half
+// k % 2 of word k / 2) and, for the wide loads, nothing here reads them, so
+// the loads stay in flight until unpack_row; element-wise bf16 loads (rows
+// that keep no 4-byte alignment) are packed here and wait. Elements past
+// the row's end come from whatever follows it, or are zero past the end of
+// the buffer; callers drop them.
 template <typename T, int NS>
-__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t r, int off, int wide, float (&out)[NS]) {
-  if constexpr (sizeof(T) == 2) {
-    if (wide == 16) {
+__device__ __forceinline__ void issue_row(__amdgpu_buffer_rsrc_t r, int off, int wide,
+                                          uint32_t (&raw)[raw_words<T>(NS)]) {
+  constexpr int EPL = 16 / sizeof(T);   // elements per 16-byte load
 #pragma unroll
-      for (int k = 0; k < (NS + 7) / 8; ++k) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0);
+  for (int k = 0; k < raw_words<T>(NS); ++k) raw[k] = 0;
+  if (wide == 16) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (8 * k + e < NS) out[8 * k + e] = __uint_as_float(e & 1 ? v[e / 2] & 0xFFFF0000u : v[e / 2] << 16);
-      }
-    } else if (wide == 4) {
+    for (int k = 0; k < (NS + EPL - 1) / EPL; ++k) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0);
 #pragma unroll
-      for (int k = 0; k < (NS + 1) / 2; ++k) {
-        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * k, 0, 0);
-        out[2 * k] = __uint_as_float(v << 16);
-        if (2 * k + 1 < NS) out[2 * k + 1] = __uint_as_float(v & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < NS; ++k) out[k] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * k, 0, 0));
+      for (int e = 0; e < 4; ++e)
+        if (4 * k + e < raw_words<T>(NS)) raw[4 * k + e] = v[e];
     }
+  } else if (sizeof(T) == 4 || wide == 4) {
+#pragma unroll
+    for (int k = 0; k < (NS * (int)sizeof(T) + 3) / 4; ++k) raw[k] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * k, 0, 0);
   } else {
-    if (wide == 16) {
 #pragma unroll
-      for (int k = 0; k < (NS + 3) / 4; ++k) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * k, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * k + e < NS) out[4 * k + e] = __uint_as_float(v[e]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < NS; ++k) out[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * k, 0, 0));
+    for (int k = 0; k < (NS + 1) / 2; ++k) {
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * k, 0, 0);
+      const uint32_t hi = 2 * k + 1 < NS ? __builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * k + 2, 0, 0) : 0u;
+      raw[k] = lo | hi << 16;
     }
+  }
+}
+
+// The row elements of issue_row's raw words, as float32.
+template <typename T, int NS, int NR>
+__device__ __forceinline__ void unpack_row(const uint32_t (&raw)[NR], float (&out)[NS]) {
+  static_assert(NR >= raw_words<T>(NS), "raw words too few for the row");
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    if constexpr (sizeof(T) == 2)
+      out[k] = __uint_as_float(k & 1 ? raw[k / 2] & 0xFFFF0000u : raw[k / 2] << 16);
+    else
+      out[k] = __uint_as_float(raw[k]);
   }
 }
 
@@ -260,11 +269,6 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
   using ST = Stage<ES>;
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[4][ST::kBytes];
   unsigned char* xb = xbuf[w];
-  // bf16 path: the key wave's lifted head rows and column terms, handed to
-  // the query wave for the logit of each query with its own key
-  constexpr int XR = sizeof(T) == 2 ? kTileN : 1;
-  __shared__ uint32_t kxr[XR][kHeadW / 2 + 1];
-  __shared__ float kxc[XR];
   // bf16 path, pair workgroups: per wave, W_b weights of four heads over the
   // 64 columns of the panel
   __shared__ __attribute__((aligned(16))) float wtab[4][sizeof(T) == 2 ? 4 * 64 : 4];
@@ -275,39 +279,30 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     // residue of this lane; value waves take the key of their position
     const int j = w >= 2 ? key_of_pos<T>(lane) : lane;
     const int i = J * kTileN + j, ic = i < L ? i : L - 1;
-    const bool valid = i < L && (a.mask == nullptr || a.mask[rb + ic] != 0);
+    const int row = ic * H + h;   // (residue, head) row within the batch
 
-    // frame of the residue and the block centre (mean translation of the
-    // block's valid residues; every wave forms it for itself)
+    // Every global load of the wave is issued here, before the first use of
+    // any of them, so that the wave waits out one memory latency rather than
+    // a chain of them. Absent inputs read through empty resources (zeros):
+    // no rotations (distance attention) make every local point zero, so the
+    // rotation never matters there.
+    const uint32_t mbyte = __builtin_amdgcn_raw_buffer_load_b8(rsrc_or_empty(a.mask, rb, (uint32_t)L), ic, 0, 0);
     float R[9], t[3];
     {
-      const __attribute__((address_space(1))) float* tp =
-          (const __attribute__((address_space(1))) float*)(a.trans + (rb + ic) * 3);
-      // no rotations (distance attention): every local point is zero, so
-      // the rotation never matters
-      if (a.rot) {
-        const __attribute__((address_space(1))) float* rp =
-            (const __attribute__((address_space(1))) float*)(a.rot + (rb + ic) * 9);
+      const __amdgpu_buffer_rsrc_t rr = rsrc_or_empty(a.rot, rb * 36, (uint32_t)((size_t)L * 36));
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(a.trans + rb * 3, (uint32_t)((size_t)L * 12));
 #pragma unroll
-        for (int e = 0; e < 9; ++e) R[e] = rp[e];
-      } else {
+      for (int e = 0; e < 9; ++e) R[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, ic * 36 + 4 * e, 0, 0));
 #pragma unroll
-        for (int e = 0; e < 9; ++e) R[e] = 0.f;
-      }
-#pragma unroll
-      for (int x = 0; x < 3; ++x) t[x] = tp[x];
+      for (int x = 0; x < 3; ++x) t[x] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rt, ic * 12 + 4 * x, 0, 0));
     }
-    const float vf = valid ? 1.f : 0.f;
-    const float cn = wave_sum(vf);
-    const float cinv = cn > 0.f ? 1.f / cn : 0.f;
-    const float cx = wave_sum(t[0] * vf) * cinv, cy = wave_sum(t[1] * vf) * cinv, cz = wave_sum(t[2] * vf) * cinv;
-    if (h == 0 && w == 0 && lane == 0)
-      reinterpret_cast<float4*>(a.ws + ly.off_cen)[(size_t)b * nJ + J] = make_float4(cx, cy, cz, cn);
-    const float tc[3] = {t[0] - cx, t[1] - cy, t[2] - cz};
+    // per-head weights: gamma_h, or rho_h and s_h for the distance attention
+    const float g_h = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_or_empty(a.gamma, 0, 4u * H), 4 * h, 0, 0));
+    const float rho_h = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_or_empty(a.meet_rho, 0, 4u * H), 4 * h, 0, 0));
+    const float s_h = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_or_empty(a.meet_s, 0, 4u * H), 4 * h, 0, 0));
 
     // this head's input rows of the residue, through buffer resources over
     // batch b (32-bit offsets; the range check never faults)
-    // (an absent input gets an empty range: its loads read zeros)
     auto in_rsrc = [&](const void* p, int per_row) {
       return rsrc_or_empty(p, rb * H * per_row * ES, (uint32_t)((size_t)L * H * per_row * ES));
     };
@@ -319,47 +314,70 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       if (rowb % 4 == 0 && base % 4 == 0) return 4;
       return ES;
     };
-    const int row = ic * H + h;   // (residue, head) row within the batch
+    // scalar and point rows: the query (wave 0) or key (wave 1) rows, or the
+    // value rows (waves 2, 3; only wave 2 writes the scalar part); on the
+    // bf16 path wave 0 also reads the key rows of its residue, for the logit
+    // of the query with its own key below (other waves read those through
+    // empty resources). One load sequence for every wave: point rows are
+    // read 3 kPvSlot elements long (the query and key waves drop the tail).
+    const void* sp = w == 0 ? a.q : w == 1 ? a.k : a.v;
+    const void* pp = w == 0 ? a.q_pts : w == 1 ? a.k_pts : a.v_pts;
+    const int np = w <= 1 ? 3 * Pqk : 3 * Pv;
+    const void* sp2 = sizeof(T) == 2 && w == 0 ? a.k : nullptr;
+    const void* pp2 = sizeof(T) == 2 && w == 0 ? a.k_pts : nullptr;
+    uint32_t rsc[raw_words<T>(kCSlot)], rpt[raw_words<T>(3 * kPvSlot)];
+    uint32_t rsk[raw_words<T>(kCSlot)], rpk[raw_words<T>(kPtSlot)];
+    issue_row<T, kCSlot>(in_rsrc(sp, C), row * C * ES, width_of(sp, C), rsc);
+    issue_row<T, 3 * kPvSlot>(in_rsrc(pp, np), row * np * ES, width_of(pp, np), rpt);
+    issue_row<T, kCSlot>(in_rsrc(sp2, C), row * C * ES, width_of(sp2, C), rsk);
+    issue_row<T, kPtSlot>(in_rsrc(pp2, 3 * Pqk), row * 3 * Pqk * ES, width_of(pp2, 3 * Pqk), rpk);
+
+    // the block centre: mean translation of the block's valid residues
+    // (every wave forms it for itself)
+    const bool valid = i < L && (a.mask == nullptr || mbyte != 0);
+    const float vf = valid ? 1.f : 0.f;
+    const float cn = wave_sum(vf);
+    const float cinv = cn > 0.f ? 1.f / cn : 0.f;
+    const float cx = wave_sum(t[0] * vf) * cinv, cy = wave_sum(t[1] * vf) * cinv, cz = wave_sum(t[2] * vf) * cinv;
+    if (h == 0 && w == 0 && lane == 0)
+      reinterpret_cast<float4*>(a.ws + ly.off_cen)[(size_t)b * nJ + J] = make_float4(cx, cy, cz, cn);
+    const float tc[3] = {t[0] - cx, t[1] - cy, t[2] - cz};
 
     const size_t o = ((size_t)b * H + h) * Lp + i;  // row of the per-(b, h) arrays
     // scalar and point weights (base 2): w_L / sqrt(C) and w_L gamma_h w_C / 2,
     // or rho_h and rho_h s_h^2 for the distance attention
-    const float alpha = (a.meet_rho ? a.meet_rho[h] : a.w_L * rsqrtf((float)C)) * kLog2e;
-    const float kap = (a.meet_rho ? a.meet_rho[h] * a.meet_s[h] * a.meet_s[h] : a.w_L * a.gamma[h] * a.w_C * 0.5f) * kLog2e;
+    const float alpha = (a.meet_rho ? rho_h : a.w_L * rsqrtf((float)C)) * kLog2e;
+    const float kap = (a.meet_rho ? rho_h * s_h * s_h : a.w_L * g_h * a.w_C * 0.5f) * kLog2e;
 
-    uint32_t own[kHeadW * ES / 4];   // query wave: its packed head row
-    float4 qrow_v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (w <= 1) {
-      // ---- query (wave 0) or key (wave 1) head row ----
-      const __amdgpu_buffer_rsrc_t rs = in_rsrc(w == 0 ? a.q : a.k, C);
-      const __amdgpu_buffer_rsrc_t rp = in_rsrc(w == 0 ? a.q_pts : a.k_pts, 3 * Pqk);
-      float sc[kCSlot], pt[kPtSlot];
-      load_row<T>(rs, row * C * ES, width_of(w == 0 ? a.q : a.k, C), sc);
-      load_row<T>(rp, row * 3 * Pqk * ES, width_of(w == 0 ? a.q_pts : a.k_pts, 3 * Pqk), pt);
+    // Lifted head row of a query (isq) or key from its input rows, packed
+    // into words, and the sums of its centred global points (x, y, z, and
+    // the squared norm in w).
+    auto head_row = [&](bool isq, const float (&s_in)[kCSlot], const float (&p_in)[kPtSlot],
+                        uint32_t (&wv)[kHeadW * ES / 4]) -> float4 {
       // global, centred points
       float P[kPtSlot];
 #pragma unroll
       for (int p = 0; p < 5; ++p)
 #pragma unroll
         for (int x = 0; x < 3; ++x) {
-          const float g = R[3 * x] * pt[3 * p] + R[3 * x + 1] * pt[3 * p + 1] + R[3 * x + 2] * pt[3 * p + 2] + tc[x];
+          const float g = R[3 * x] * p_in[3 * p] + R[3 * x + 1] * p_in[3 * p + 1] + R[3 * x + 2] * p_in[3 * p + 2] + tc[x];
           P[3 * p + x] = (valid && p < Pqk) ? g : 0.f;
         }
       S rowv[kHeadW];
 #pragma unroll
       for (int c = 0; c < kCSlot; ++c) {
-        const float s = (valid && c < C) ? sc[c] : 0.f;
-        rowv[c] = E::pack(w == 0 ? alpha * s : s);
+        const float s = (valid && c < C) ? s_in[c] : 0.f;
+        rowv[c] = E::pack(isq ? alpha * s : s);
       }
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int u = 0; u < kPtSlot; ++u) {
           S hi, lo;
-          E::split(w == 0 ? 2.f * kap * P[u] : P[u], hi, lo);
+          E::split(isq ? 2.f * kap * P[u] : P[u], hi, lo);
           // query [hi | hi | lo], key [hi | lo | hi]
           rowv[kCSlot + u] = hi;
-          rowv[kCSlot + kPtSlot + u] = w == 0 ? hi : lo;
-          rowv[kCSlot + 2 * kPtSlot + u] = w == 0 ? lo : hi;
+          rowv[kCSlot + kPtSlot + u] = isq ? hi : lo;
+          rowv[kCSlot + 2 * kPtSlot + u] = isq ? lo : hi;
         }
 #pragma unroll
         for (int f = kCSlot + 3 * kPtSlot; f < kHeadW; ++f) rowv[f] = 0;
@@ -369,7 +387,7 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
         // differences, so they must not meet in the product
 #pragma unroll
         for (int f = kCSlot; f < kHeadW; ++f) rowv[f] = 0.f;
-        if (w == 0) {
+        if (isq) {
 #pragma unroll
           for (int u = 0; u < kPtSlot; ++u) rowv[kFpQPts + u] = P[u];
         } else {
@@ -377,57 +395,76 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
           for (int u = 0; u < kPtSlot; ++u) rowv[kCSlot + u] = P[u];
         }
       }
-      uint32_t wv[kHeadW * ES / 4];
       pack_words(rowv, wv);
-      // rows J*64 .. J*64 + 63 of (b, h) are contiguous; lane j holds row j
-      unsigned char* dst = a.ws + (w == 0 ? ly.off_qh : ly.off_kh) +
-                           (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW * ES;
-      ST::rows(xb, lane, wv, dst);
       float sx = 0.f, sy = 0.f, sz = 0.f, sn = 0.f;
 #pragma unroll
       for (int p = 0; p < 5; ++p) {
         sx += P[3 * p]; sy += P[3 * p + 1]; sz += P[3 * p + 2];
         sn += P[3 * p] * P[3 * p] + P[3 * p + 1] * P[3 * p + 1] + P[3 * p + 2] * P[3 * p + 2];
       }
+      return make_float4(sx, sy, sz, sn);
+    };
+    // column term of a key (fp32 takes the whole point term from explicit
+    // differences)
+    auto key_col = [&](float4 ps) {
+      return !valid ? make_float4(0.f, 0.f, 0.f, -INFINITY)
+                    : (sizeof(T) == 2 ? make_float4(ps.x, ps.y, ps.z, -kap * ps.w) : make_float4(0.f, 0.f, 0.f, 0.f));
+    };
+
+    if (w <= 1) {
+      // ---- query (wave 0) or key (wave 1) head row ----
+      float sc[kCSlot], pt[kPtSlot];
+      unpack_row<T>(rsc, sc);
+      unpack_row<T>(rpt, pt);
+      uint32_t wv[kHeadW * ES / 4];
+      const float4 ps = head_row(w == 0, sc, pt, wv);
+      // rows J*64 .. J*64 + 63 of (b, h) are contiguous; lane j holds row j
+      unsigned char* dst = a.ws + (w == 0 ? ly.off_qh : ly.off_kh) +
+                           (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW * ES;
+      ST::rows(xb, lane, wv, dst);
       if (w == 0) {
-        qrow_v = make_float4(sx, sy, sz, 0.f);
-#pragma unroll
-        for (int e = 0; e < kHeadW * ES / 4; ++e) own[e] = wv[e];
-      } else {
-        // fp32 takes the whole point term from explicit differences
-        const float4 kc = !valid ? make_float4(0.f, 0.f, 0.f, -INFINITY)
-                                 : (sizeof(T) == 2 ? make_float4(sx, sy, sz, -kap * sn) : make_float4(0.f, 0.f, 0.f, 0.f));
-        reinterpret_cast<float4*>(a.ws + ly.off_kcol)[o] = kc;
+        // query row term; on the bf16 path its w holds the head part of the
+        // logit of the query with its own key (lifted rows as the attention
+        // products see them, plus the key's column term: the block offset
+        // is zero), the running-max seed of the attention kernel. The key
+        // row is formed here again, from the same inputs by the same code
+        // as the key wave's.
+        float4 qrow_v = make_float4(ps.x, ps.y, ps.z, 0.f);
         if constexpr (sizeof(T) == 2) {
+          float sk[kCSlot], pk[kPtSlot];
+          unpack_row<T>(rsk, sk);
+          unpack_row<T>(rpk, pk);
+          uint32_t kw[kHeadW * ES / 4];
+          const float4 kc = key_col(head_row(false, sk, pk, kw));
+          float d = 0.f;
 #pragma unroll
-          for (int e = 0; e < kHeadW / 2; ++e) kxr[lane][e] = wv[e];
-          kxc[lane] = kc.w;
+          for (int e = 0; e < kHeadW / 2; ++e)
+            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv[e]), __builtin_bit_cast(bf16x2, kw[e]), d, false);
+          qrow_v.w = d + kc.w;
         }
+        reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = qrow_v;
+      } else {
+        reinterpret_cast<float4*>(a.ws + ly.off_kcol)[o] = key_col(ps);
       }
     } else {
       // ---- value head block, feature-major [64 features][64 positions];
       //      wave 2 writes features 0..31, wave 3 features 32..63 ----
-      const __amdgpu_buffer_rsrc_t rs = in_rsrc(a.v, C);
-      const __amdgpu_buffer_rsrc_t rp = in_rsrc(a.v_pts, 3 * Pv);
+      float sc[kCSlot], pv[3 * kPvSlot];
+      if (w == 2) unpack_row<T>(rsc, sc);
+      unpack_row<T>(rpt, pv);
       float G[3][kPvSlot];
-      float vs[kCSlot];
-      if (w == 2) load_row<T>(rs, row * C * ES, width_of(a.v, C), vs);
-      {
-        float pv[3 * kPvSlot];
-        load_row<T>(rp, row * 3 * Pv * ES, width_of(a.v_pts, 3 * Pv), pv);
 #pragma unroll
-        for (int p = 0; p < kPvSlot; ++p)
+      for (int p = 0; p < kPvSlot; ++p)
 #pragma unroll
-          for (int x = 0; x < 3; ++x) {
-            const float g = R[3 * x] * pv[3 * p] + R[3 * x + 1] * pv[3 * p + 1] + R[3 * x + 2] * pv[3 * p + 2] + tc[x];
-            G[x][p] = (valid && p < Pv) ? g : 0.f;
-          }
-      }
+        for (int x = 0; x < 3; ++x) {
+          const float g = R[3 * x] * pv[3 * p] + R[3 * x + 1] * pv[3 * p + 1] + R[3 * x + 2] * pv[3 * p + 2] + tc[x];
+          G[x][p] = (valid && p < Pv) ? g : 0.f;
+        }
       S out[32];
       if (w == 2) {
         // v (16), G'hi x (8), G'hi y (8)
 #pragma unroll
-        for (int c = 0; c < kCSlot; ++c) out[c] = E::pack((valid && c < C) ? vs[c] : 0.f);
+        for (int c = 0; c < kCSlot; ++c) out[c] = E::pack((valid && c < C) ? sc[c] : 0.f);
 #pragma unroll
         for (int p = 0; p < kPvSlot; ++p) {
           S hi, lo;
@@ -451,23 +488,6 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       const size_t blk = ((size_t)b * H + h) * nJ + J;   // value block of (b, h, J)
       store_cols(xb, lane, out, a.ws + ly.off_vth + (blk * kHeadW + (w - 2) * 32) * kTileN * ES);
     }
-    // query row term; on the bf16 path its w holds the head part of the
-    // logit of the query with its own key (lifted rows as the attention
-    // products see them, plus the key's column term: the block offset is
-    // zero), the running-max seed of the attention kernel
-    if constexpr (sizeof(T) == 2) {
-      __syncthreads();   // kxr, kxc
-      if (w == 0) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < kHeadW / 2; ++e) {
-          const uint32_t qe = own[e], ke = kxr[lane][e];
-          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qe), __builtin_bit_cast(bf16x2, ke), d, false);
-        }
-        qrow_v.w = d + kxc[lane];
-      }
-    }
-    if (w == 0) reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = qrow_v;
   } else {
     // ================= pair workgroup: one 64-wide panel of z2 =================
     // waves 0-2 write the panel; on the bf16 path wave 3 joins the pair
@@ -476,7 +496,9 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     const int P = y - H;
     const int j = (w == 0 || w == 3) ? lane : key_of_pos<T>(lane);
     const int i = J * kTileN + j, ic = i < L ? i : L - 1;
-    const bool valid = i < L && (a.mask == nullptr || a.mask[rb + ic] != 0);
+    // every load is unconditional (absent inputs read zeros), so that all of
+    // them are in flight together
+    const uint32_t mbyte = __builtin_amdgcn_raw_buffer_load_b8(rsrc_or_empty(a.mask, rb, (uint32_t)L), ic, 0, 0);
     // z2 row segment u = 64 P .. 64 P + 63 of the residue (16-byte loads:
     // R Cz is a multiple of 8, so rows and panels are 16-byte aligned; a
     // segment past the end of the batch reads zeros)
@@ -488,11 +510,12 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     float wl0[4];
     const int uu = 64 * P + lane, cu = uu % ly.Cz;
     const float wsc = a.w_L * kLog2e;
+    const __amdgpu_buffer_rsrc_t rw = rsrc_or_empty(a.w_b, 0, (uint32_t)((size_t)ly.Cz * H * 4));
     auto weights = [&](int h0, float (&wl)[4]) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int hc = h0 + 4 * c < H ? h0 + 4 * c : H - 1;
-        wl[c] = a.w_b ? wsc * a.w_b[(size_t)cu * H + hc] : 0.f;
+        wl[c] = wsc * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (cu * H + hc) * 4, 0, 0));
       }
     };
     if constexpr (sizeof(T) == 2) {
@@ -508,6 +531,7 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     // keeps every load above in flight together (the compiler would
     // otherwise issue the z1 and weight loads only after the z2 work)
     asm volatile("" ::: "memory");
+    const bool valid = i < L && (a.mask == nullptr || mbyte != 0);
 #pragma unroll
     for (int c = 0; c < 64 * ES / 16; ++c) {
       const u32x4 r = z2r[c];
