@@ -67,6 +67,8 @@ namespace {
 constexpr int kPtSlot = 15;   // query/key point coordinates per group (3 Pqk <= 15)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -179,17 +181,28 @@ __device__ __forceinline__ void unpack_row(const uint32_t (&raw)[NR], float (&ou
 // bf16 (K = 16 per product) each group of 16 keys is stored as 0-3, 8-11,
 // 4-7, 12-15; for fp32 (K = 2 per product) each group of 32 keys is stored
 // as pairs (8k+e, 8k+4+e).
-template <typename T> __device__ __forceinline__ int key_of_pos(int pos);
-template <> __device__ __forceinline__ int key_of_pos<uint16_t>(int pos) {
-  int base = pos & ~15, p = pos & 15;
-  int g = p >> 3, s = p & 7;
-  return base + 8 * (s >> 2) + 4 * g + (s & 3);
-}
-template <> __device__ __forceinline__ int key_of_pos<float>(int pos) {
-  int base = pos & ~31, p = pos & 31;
-  int g = p & 1, st = p >> 1;
+template <typename T> __host__ __device__ constexpr int key_of_pos(int pos) {
+  if (sizeof(T) == 2) {
+    const int base = pos & ~15, p = pos & 15;
+    const int g = p >> 3, s = p & 7;
+    return base + 8 * (s >> 2) + 4 * g + (s & 3);
+  }
+  const int base = pos & ~31, p = pos & 31;
+  const int g = p & 1, st = p >> 1;
   return base + 8 * (st >> 2) + 4 * g + (st & 3);
 }
+
+// Position of key k in its 64-key value block (the inverse of key_of_pos).
+template <typename T> __host__ __device__ constexpr int pos_of_key(int k) {
+  return sizeof(T) == 2 ? (k & ~15) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3)
+                        : (k & ~31) + 8 * ((k & 31) >> 3) + 2 * (k & 3) + ((k >> 2) & 1);
+}
+template <typename T> constexpr bool positions_invert() {
+  for (int p = 0; p < 64; ++p)
+    if (pos_of_key<T>(key_of_pos<T>(p)) != p) return false;
+  return true;
+}
+static_assert(positions_invert<uint16_t>() && positions_invert<float>(), "pos_of_key inverts key_of_pos");
 
 // Pack N elements into 32-bit words.
 template <int N>
@@ -248,11 +261,28 @@ __device__ __forceinline__ void store_cols(unsigned char* xb, int lane, const S 
   }
 }
 
-// Sum over the 64 lanes of a wave.
+// x of another lane of the same 16-lane row, by a DPP lane pattern (CTRL:
+// 0x00-0xFF quad permutation, 0x140 row mirror, 0x141 half-row mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 4 lanes of a quad (lanes 4k .. 4k + 3), in every one of them.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp<0xB1>(x);   // lanes 1, 0, 3, 2 of the quad
+  return x + dpp<0x4E>(x);   // lanes 2, 3, 0, 1
+}
+
+// Sum over the 64 lanes of a wave: quads, half rows and rows by DPP, then
+// across rows. Every step adds two values that its partner lane adds in the
+// other order, so all lanes end with the same value.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  x = quad_sum(x);
+  x += dpp<0x141>(x);   // the other quad of the half row
+  x += dpp<0x140>(x);   // the other half of the row
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
 }
 
 template <typename T>
@@ -269,9 +299,10 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
   using ST = Stage<ES>;
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[4][ST::kBytes];
   unsigned char* xb = xbuf[w];
-  // bf16 path, pair workgroups: per wave, W_b weights of four heads over the
-  // 64 columns of the panel
-  __shared__ __attribute__((aligned(16))) float wtab[4][sizeof(T) == 2 ? 4 * 64 : 4];
+  // bf16 path, pair workgroups: W_b weights of 16 heads over the 64 columns
+  // of the panel, and the largest |weight| each wave staged
+  __shared__ __attribute__((aligned(16))) float wtab[sizeof(T) == 2 ? 16 : 1][64];
+  __shared__ float wmax[4];
 
   if (y < H) {
     // ================= head workgroup =================
@@ -490,64 +521,84 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     }
   } else {
     // ================= pair workgroup: one 64-wide panel of z2 =================
-    // waves 0-2 write the panel; on the bf16 path wave 3 joins the pair
-    // bias work below
-    if (sizeof(T) == 4 && w == 3) return;
+    // 64 residues x 64 features of the panel: wave w takes residues
+    // 16 w .. 16 w + 15 with four lanes per residue, lane 16 q + r' holding
+    // features 16 q .. 16 q + 15 of residue 16 w + r'. Every input is read
+    // once per workgroup, each lane does a quarter of a residue's work, and
+    // the key pair rows leave straight from registers (each lane's 16
+    // features are contiguous in the panel row).
     const int P = y - H;
-    const int j = (w == 0 || w == 3) ? lane : key_of_pos<T>(lane);
-    const int i = J * kTileN + j, ic = i < L ? i : L - 1;
+    const int r = 16 * w + (lane & 15), q = lane >> 4;
+    const int i = J * kTileN + r, ic = i < L ? i : L - 1;
+    constexpr int EQ = ES;   // 16-byte pieces of a lane's 16 features
     // every load is unconditional (absent inputs read zeros), so that all of
-    // them are in flight together
+    // them are in flight together; R Cz is a multiple of 8, so every piece
+    // is 16-byte aligned, and a piece past the end of the batch reads zeros
     const uint32_t mbyte = __builtin_amdgcn_raw_buffer_load_b8(rsrc_or_empty(a.mask, rb, (uint32_t)L), ic, 0, 0);
-    // z2 row segment u = 64 P .. 64 P + 63 of the residue (16-byte loads:
-    // R Cz is a multiple of 8, so rows and panels are 16-byte aligned; a
-    // segment past the end of the batch reads zeros)
     const __amdgpu_buffer_rsrc_t rz = rsrc_or_empty(a.z2, rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
-    // bf16 path: the z1 segment and the first head group's W_b weights for
-    // the pair bias below, issued together with the z2 loads
-    constexpr int NZ1 = sizeof(T) == 2 ? 8 : 1;
-    u32x4 z1r[NZ1];
-    float wl0[4];
-    const int uu = 64 * P + lane, cu = uu % ly.Cz;
+    const int zoff = (ic * RCz + 64 * P + 16 * q) * ES;
+    u32x4 z2r[EQ];
+#pragma unroll
+    for (int c = 0; c < EQ; ++c) z2r[c] = __builtin_amdgcn_raw_buffer_load_b128(rz, zoff + 16 * c, 0, 0);
+    // bf16 path: the lane's z1 features and the first chunk of W_b weights
+    // (entries tid, tid + 256, ... of a [16 heads][64 columns] block: column
+    // t = tid % 64 of the panel, heads tid / 64 + 4 k of the chunk)
+    u32x4 z1r[sizeof(T) == 2 ? EQ : 1];
+    const int tcol = threadIdx.x & 63, uu = 64 * P + tcol;
+    const int cu = uu % ly.Cz;
     const float wsc = a.w_L * kLog2e;
     const __amdgpu_buffer_rsrc_t rw = rsrc_or_empty(a.w_b, 0, (uint32_t)((size_t)ly.Cz * H * 4));
-    auto weights = [&](int h0, float (&wl)[4]) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int hc = h0 + 4 * c < H ? h0 + 4 * c : H - 1;
-        wl[c] = wsc * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (cu * H + hc) * 4, 0, 0));
-      }
+    auto weight = [&](int h) {
+      const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (cu * H + (h < H ? h : H - 1)) * 4, 0, 0));
+      return (h < H && uu < RCz) ? wsc * x : 0.f;
     };
+    float wl[4];
     if constexpr (sizeof(T) == 2) {
       const __amdgpu_buffer_rsrc_t r1 = rsrc_or_empty(a.z1, rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
 #pragma unroll
-      for (int c = 0; c < 8; ++c) z1r[c] = __builtin_amdgcn_raw_buffer_load_b128(r1, (ic * RCz + 64 * P) * ES + 16 * c, 0, 0);
-      weights(w, wl0);
-    }
-    float z[64];
-    u32x4 z2r[64 * ES / 16];
+      for (int c = 0; c < EQ; ++c) z1r[c] = __builtin_amdgcn_raw_buffer_load_b128(r1, zoff + 16 * c, 0, 0);
 #pragma unroll
-    for (int c = 0; c < 64 * ES / 16; ++c) z2r[c] = __builtin_amdgcn_raw_buffer_load_b128(rz, (ic * RCz + 64 * P) * ES + 16 * c, 0, 0);
-    // keeps every load above in flight together (the compiler would
-    // otherwise issue the z1 and weight loads only after the z2 work)
-    asm volatile("" ::: "memory");
+      for (int k = 0; k < 4; ++k) wl[k] = weight((threadIdx.x >> 6) + 4 * k);
+    }
     const bool valid = i < L && (a.mask == nullptr || mbyte != 0);
+
+    // z2 of the lane's features as float, zero for invalid residues and for
+    // features past R Cz
+    float z2f[16];
 #pragma unroll
-    for (int c = 0; c < 64 * ES / 16; ++c) {
-      const u32x4 r = z2r[c];
+    for (int e = 0; e < 16; ++e) {
+      float x;
       if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          z[8 * c + 2 * e] = __uint_as_float(r[e] << 16);
-          z[8 * c + 2 * e + 1] = __uint_as_float(r[e] & 0xFFFF0000u);
-        }
+        const uint32_t wd = z2r[e / 8][(e % 8) / 2];
+        x = __uint_as_float(e & 1 ? wd & 0xFFFF0000u : wd << 16);
       } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[4 * c + e] = __uint_as_float(r[e]);
+        x = __uint_as_float(z2r[e / 4][e % 4]);
       }
+      z2f[e] = (valid && 64 * P + 16 * q + e < RCz) ? x : 0.f;
     }
+
+    // key pair row piece: features 16 q .. 16 q + 15 of residue r
+    {
+      S kv[16];
 #pragma unroll
-    for (int u = 0; u < 64; ++u) z[u] = (valid && 64 * P + u < RCz) ? z[u] : 0.f;
+      for (int e = 0; e < 16; ++e) kv[e] = E::pack_pair(z2f[e]);
+      uint32_t kw[16 * ES / 4];
+      pack_words(kv, kw);
+      unsigned char* dst = a.ws + ly.off_kz +
+                           ((((size_t)b * nJ + J) * (PW / 64) + P) * (64 * kTileN) + (size_t)r * 64 + 16 * q) * ES;
+#pragma unroll
+      for (int c = 0; c < EQ; ++c)
+        *reinterpret_cast<uint4*>(dst + 16 * c) = make_uint4(kw[4 * c], kw[4 * c + 1], kw[4 * c + 2], kw[4 * c + 3]);
+    }
+    // value pair block, feature-major [64 features][64 positions] (position
+    // of key r: pos_of_key), transposed through LDS
+    unsigned char* const vs = &xbuf[0][0];
+    {
+      const int pos = pos_of_key<T>(r);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) *reinterpret_cast<S*>(vs + (16 * q + e) * ST::kPitch + pos * ES) = E::pack(z2f[e]);
+    }
+
     // bf16 path: this panel's share of each residue's pair bias with itself,
     // sum_u q[u] k[u] with the pair operands as the attention kernel's
     // products take them: q[u] = w_L log2(e) W_b[u mod Cz, h] z1[u] and
@@ -555,135 +606,102 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
     // every head: the pair part of the attention kernel's running-max seed,
     // so that the seed is a logit of those products (it then never exceeds
     // the row's largest logit by more than their rounding, whatever the
-    // inputs). Wave w takes heads w, w + 4, ... in groups of four: lane u
-    // loads the weights of panel column u for the whole group at once, and
-    // they are broadcast through this wave's LDS block. When no operand of
-    // a group can reach the limit, saturation is the identity and the sum is
-    // taken here over the plain products z1[u] z2[u]. A group that can is
-    // done after the panel stores (seed_clamped below), from z1 and z2 read
-    // again, so that the common case keeps its registers.
-    uint32_t clamped = 0;   // bit g: head group g of this wave needs the clamps
-    auto seed_clamped = [&]() {
-      const __amdgpu_buffer_rsrc_t r1 = rsrc_or_empty(a.z1, rb * RCz * ES, (uint32_t)((size_t)L * RCz * ES));
-      auto sat = [](float x) { return fminf(fmaxf(x, -65504.f), 65504.f); };
-      float* const wt = wtab[w];
-      float4* const pd = reinterpret_cast<float4*>(a.ws + ly.off_pdiag);
-      for (int h0 = w, g0 = 0; h0 < H; h0 += 16, ++g0) {
-        if (!(clamped & (1u << g0))) continue;
-        float wl[4];
-        weights(h0, wl);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) wt[64 * c + lane] = uu < RCz ? wl[c] : 0.f;
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int g = 0; g < 8; ++g) {
-          const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(r1, (ic * RCz + 64 * P) * ES + 16 * g, 0, 0);
-          const u32x4 r2 = __builtin_amdgcn_raw_buffer_load_b128(rz, (ic * RCz + 64 * P) * ES + 16 * g, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int u = 8 * g + e;
-            const uint32_t w1 = r[e / 2], w2 = r2[e / 2];
-            const float x1 = __uint_as_float(e & 1 ? w1 & 0xFFFF0000u : w1 << 16);
-            const float x2 = (valid && 64 * P + u < RCz) ? __uint_as_float(e & 1 ? w2 & 0xFFFF0000u : w2 << 16) : 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = fmaf(sat(wt[64 * c + u] * x1), sat(x2), acc[c]);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int h = h0 + 4 * c;
-          if (h < H) reinterpret_cast<float*>(pd + ((size_t)b * H + h) * Lp + i)[P] = acc[c];
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      }
-    };
+    // inputs). Heads go in chunks of 16, whose weights over the panel's 64
+    // columns are staged in LDS. When no operand can reach the limit (the
+    // largest |z1| of the lane times the largest staged |weight|, and |z2|,
+    // within range) saturation is the identity, and the sums of a wave's 16
+    // residues for 16 heads are one matrix product, [16 residues x 64
+    // features] (z1 z2, fp16) times [64 features x 16 heads] (W_b, fp16),
+    // four 16x16x16 products with float32 accumulation (feature 16 q + 4 s
+    // + j of lane 16 q + r' is the reduction index 4 q + j of step s, on
+    // both operands). Otherwise each lane sums its 16 saturated products and
+    // the four lanes of a residue combine their sums.
     if constexpr (sizeof(T) == 2) {
-      float zz[64];
-      float m1 = 0.f, m2 = 0.f;   // largest |z1|, |z2| of this residue's segment
+      float z1f[16], zz[16];
+      float m1 = 0.f, m2 = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const u32x4 r = z1r[c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = __uint_as_float(r[e] << 16), x1 = __uint_as_float(r[e] & 0xFFFF0000u);
-          m1 = fmaxf(m1, fmaxf(fabsf(x0), fabsf(x1)));
-          m2 = fmaxf(m2, fmaxf(fabsf(z[8 * c + 2 * e]), fabsf(z[8 * c + 2 * e + 1])));
-          zz[8 * c + 2 * e] = x0 * z[8 * c + 2 * e];
-          zz[8 * c + 2 * e + 1] = x1 * z[8 * c + 2 * e + 1];
-        }
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t wd = z1r[e / 8][(e % 8) / 2];
+        z1f[e] = __uint_as_float(e & 1 ? wd & 0xFFFF0000u : wd << 16);
+        m1 = fmaxf(m1, fabsf(z1f[e]));
+        m2 = fmaxf(m2, fabsf(z2f[e]));
+        zz[e] = z1f[e] * z2f[e];
       }
-      float* const wt = wtab[w];
       float4* const pd = reinterpret_cast<float4*>(a.ws + ly.off_pdiag);
-      for (int h0 = w, g0 = 0; h0 < H; h0 += 16, ++g0) {
-        float wl[4];
-        if (h0 == w) {
+      for (int h0 = 0; h0 < H; h0 += 16) {
+        if (h0 > 0) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) wl[c] = wl0[c];
-        } else {
-          weights(h0, wl);
+          for (int k = 0; k < 4; ++k) wl[k] = weight(h0 + (threadIdx.x >> 6) + 4 * k);
         }
-        float mw = 0.f;
+        float mx = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float x = uu < RCz ? wl[c] : 0.f;
-          wt[64 * c + lane] = x;
-          mw = fmaxf(mw, fabsf(x));
+        for (int k = 0; k < 4; ++k) {
+          wtab[(threadIdx.x >> 6) + 4 * k][tcol] = wl[k];
+          mx = fmaxf(mx, fabsf(wl[k]));
         }
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
-        if (!__all(m2 <= 65504.f && m1 * mw <= 65504.f)) {
-          clamped |= 1u << g0;
+        for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        if (lane == 0) wmax[w] = mx;
+        __syncthreads();   // wtab, wmax (and, in the first chunk, the value block)
+        const float mw = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        const bool plain = __all(m2 <= 65504.f && m1 * mw <= 65504.f);
+        auto sat = [](float x) { return fminf(fmaxf(x, -65504.f), 65504.f); };
+        const int nh = H - h0 < 16 ? H - h0 : 16;
+        // (the products z1 z2 must be within fp16 range too; wave-uniform, as
+        // the matrix-core products run on the whole wave)
+        if (__all(plain && m1 * m2 <= 65504.f)) {
+          f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const float4 wv = *reinterpret_cast<const float4*>(&wtab[lane & 15][16 * q + 4 * st]);
+            const f16x4 bo = {(_Float16)wv.x, (_Float16)wv.y, (_Float16)wv.z, (_Float16)wv.w};
+            const f16x4 ao = {(_Float16)zz[4 * st], (_Float16)zz[4 * st + 1], (_Float16)zz[4 * st + 2],
+                              (_Float16)zz[4 * st + 3]};
+            d = __builtin_amdgcn_mfma_f32_16x16x16f16(ao, bo, d, 0, 0, 0);
+          }
+          // lane l: residues 16 w + 4 (l / 16) + v, head h0 + l % 16
+          const int hd = h0 + (lane & 15);
+          if (hd < H) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              reinterpret_cast<float*>(pd + ((size_t)b * H + hd) * Lp + J * kTileN + 16 * w + 4 * q + v)[P] = d[v];
+          }
+          if (h0 + 16 < H) __syncthreads();   // wtab is refilled
           continue;
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        float acc[16];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float acc = 0.f;
+        for (int hh = 0; hh < 16; ++hh) {
+          const float* wr = &wtab[hh][16 * q];
+          float x = 0.f;
+          if (hh < nh) {
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const float4 v = *reinterpret_cast<const float4*>(wt + 64 * c + 4 * q);
-            acc = fmaf(v.x, zz[4 * q], acc);
-            acc = fmaf(v.y, zz[4 * q + 1], acc);
-            acc = fmaf(v.z, zz[4 * q + 2], acc);
-            acc = fmaf(v.w, zz[4 * q + 3], acc);
+            for (int e = 0; e < 16; ++e) x = fmaf(plain ? wr[e] * z1f[e] : sat(wr[e] * z1f[e]), plain ? z2f[e] : sat(z2f[e]), x);
           }
-          const int h = h0 + 4 * c;
-          if (h < H) reinterpret_cast<float*>(pd + ((size_t)b * H + h) * Lp + i)[P] = acc;
+          acc[hh] = x;
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      }
-      if (w == 3) {
-        if (clamped) seed_clamped();
-        return;
-      }
-    }
-    if (w == 0) {
-      // key pair row of residue j: [64 features] in panel P
-      S rowv[64];
+        // the four lanes of the residue (lanes r', r' + 16, r' + 32, r' + 48)
+        // combine their sums; lane 16 q + r' stores heads q, q + 4, ...
 #pragma unroll
-      for (int u = 0; u < 64; ++u) rowv[u] = E::pack_pair(z[u]);
-      uint32_t wv[64 * ES / 4];
-      pack_words(rowv, wv);
-      ST::rows(xb, lane, wv, a.ws + ly.off_kz + ((((size_t)b * nJ + J) * (PW / 64) + P) * (64 * kTileN)) * ES);
+        for (int hh = 0; hh < 16; ++hh) {
+          float x = acc[hh] + __shfl_xor(acc[hh], 16, 64);
+          x += __shfl_xor(x, 32, 64);
+          if (hh < nh && q == (hh & 3)) reinterpret_cast<float*>(pd + ((size_t)b * H + h0 + hh) * Lp + i)[P] = x;
+        }
+        if (h0 + 16 < H) __syncthreads();   // wtab is refilled
+      }
     } else {
-      // value pair block, feature-major: wave 1 features 0..31, wave 2 32..63
-      const size_t blk = ((size_t)b * nJ + J) * PW + 64 * P;   // first feature row
-      S out[32];
-      if (w == 1) {
-#pragma unroll
-        for (int f = 0; f < 32; ++f) out[f] = E::pack(z[f]);
-      } else {
-#pragma unroll
-        for (int f = 0; f < 32; ++f) out[f] = E::pack(z[32 + f]);
-      }
-      store_cols(xb, lane, out, a.ws + ly.off_vtz + (blk + (w - 1) * 32) * kTileN * ES);
+      __syncthreads();   // the value block
     }
-    if constexpr (sizeof(T) == 2) {
-      if (clamped) seed_clamped();
+    // rows 16 w .. 16 w + 15 of the value block, 16 bytes per lane per store
+    {
+      unsigned char* dst = a.ws + ly.off_vtz + (((size_t)b * nJ + J) * PW + 64 * P) * kTileN * ES;
+#pragma unroll
+      for (int k = 0; k < 16 * ST::kNC / 64; ++k) {
+        const int c = lane + 64 * k, f = 16 * w + c / ST::kNC, ch = c % ST::kNC;
+        *reinterpret_cast<uint4*>(dst + (size_t)f * ST::kRowB + 16 * ch) =
+            *reinterpret_cast<const uint4*>(vs + f * ST::kPitch + 16 * ch);
+      }
     }
   }
 }
