@@ -4,11 +4,11 @@
 // writes the operands that the fused attention kernel consumes, so that the
 // logit of "Flash Invariant Point Attention" (TL;DR: lift every IPA term
 // into one regular attention) is a plain dot product plus cheap per-row /
-// per-column terms. On the bf16 path (point groups of 15 slots; unused
-// slots, 3 Pqk .. 14, are zero):
+// per-column terms. On the bf16 path (point groups of 16 slots, 15 for the
+// coordinates and one zero; unused slots, 3 Pqk .. 14, are zero too):
 //
-//   query head row  [ a q (16) | 2k A'hi (15) | 2k A'hi (15) | 2k A'lo (15) | 0 (3) ]
-//   key head row    [   k (16) |    B'hi (15) |    B'lo (15) |    B'hi (15) | 0 (3) ]
+//   query head row  [ a q (16) | 2k A'hi (15) 0 | 2k A'hi (15) 0 | 2k A'lo (15) 0 ]
+//   key head row    [   k (16) |    B'hi (15) 0 |    B'lo (15) 0 |    B'hi (15) 0 ]
 //   key pair row    [ z2_j1 | ... | z2_jR | 0 ]   (shared by all heads, 64x64 panels)
 //   value head row  [ v (16) | G'hi x, y, z (8 each) | G'lo x, y, z (8 each) ]
 //   value pair row  [ z2_j1 | ... | z2_jR | 0 ]   (shared by all heads)
@@ -40,24 +40,27 @@
 // Residues with mask 0 and rows past L get all-zero rows and a key column
 // term of -inf, so padding garbage never reaches a valid output.
 //
-// Work split. Grid (block J, head h or pair panel, batch b), 4 waves, one
-// residue per lane: in a head workgroup wave 0 writes the query rows, wave 1
-// the key rows and the key column terms, waves 2 and 3 the two halves of the
-// value block (lane = key position); every wave forms the block centre
-// itself with cross-lane sums. In a pair workgroup wave 0 writes the key
-// pair panel and waves 1 and 2 the two halves of the value pair panel. Rows
-// are assembled in registers and written through per-wave LDS staging with
-// 16-byte stores (value blocks: one coalesced row of 64 positions per
-// store); all loads are unconditional buffer loads (rows past L read row
-// L - 1) whose values invalid residues drop, each lane reading its input
-// rows with 16-byte loads where their length and alignment allow.
+// Work split. Grid (block J, head h or pair panel, batch b), 4 waves. In a
+// head workgroup (one residue per lane) wave 0 writes the query rows, wave
+// 1 the key rows and the key column terms, waves 2 and 3 the two halves of
+// the value block (lane = key position); every wave forms the block centre
+// itself with cross-lane sums. Rows are assembled in registers and written
+// through per-wave LDS staging with 16-byte stores (value blocks: one
+// coalesced row of 64 positions per store). In a pair workgroup each
+// residue's 64-wide panel segment is split over four lanes (16 features
+// each, wave w taking residues 16 w .. 16 w + 15): key pair rows leave
+// straight from registers, the value pair block goes through one LDS
+// transpose. All loads are unconditional buffer loads (rows past L read row
+// L - 1) whose values invalid residues drop, issued before the first of
+// them is used, each lane reading its input rows with 16-byte loads where
+// their length and alignment allow.
 //
 // On the bf16 path the kernel also assembles, for every query and head, the
 // logit of the query with its own key, which the attention kernel takes as
 // the start of its running max: the head part (the key wave hands its rows
 // to the query wave through LDS) plus the key's column term in the w of the
 // query row term, and the pair part per 64-wide panel from the pair
-// workgroups (all four waves, heads split between them).
+// workgroups (matrix-core products when no operand nears fp16's limit).
 
 #include "ipa_internal.h"
 
@@ -69,6 +72,7 @@ constexpr int kPtSlot = 15;   // query/key point coordinates per group (3 Pqk <=
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -299,6 +303,11 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
   using ST = Stage<ES>;
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[4][ST::kBytes];
   unsigned char* xb = xbuf[w];
+  // bf16 path: the key wave's lifted head rows and column terms, handed to
+  // the query wave for the logit of each query with its own key
+  constexpr int XR = sizeof(T) == 2 ? kTileN : 1;
+  __shared__ uint32_t kxr[XR][kHeadW / 2 + 1];
+  __shared__ float kxc[XR];
   // bf16 path, pair workgroups: W_b weights of 16 heads over the 64 columns
   // of the panel, and the largest |weight| each wave staged
   __shared__ __attribute__((aligned(16))) float wtab[sizeof(T) == 2 ? 16 : 1][64];
@@ -346,22 +355,15 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
       return ES;
     };
     // scalar and point rows: the query (wave 0) or key (wave 1) rows, or the
-    // value rows (waves 2, 3; only wave 2 writes the scalar part); on the
-    // bf16 path wave 0 also reads the key rows of its residue, for the logit
-    // of the query with its own key below (other waves read those through
-    // empty resources). One load sequence for every wave: point rows are
-    // read 3 kPvSlot elements long (the query and key waves drop the tail).
+    // value rows (waves 2, 3; only wave 2 writes the scalar part). One load
+    // sequence for every wave: point rows are read 3 kPvSlot elements long
+    // (the query and key waves drop the tail).
     const void* sp = w == 0 ? a.q : w == 1 ? a.k : a.v;
     const void* pp = w == 0 ? a.q_pts : w == 1 ? a.k_pts : a.v_pts;
     const int np = w <= 1 ? 3 * Pqk : 3 * Pv;
-    const void* sp2 = sizeof(T) == 2 && w == 0 ? a.k : nullptr;
-    const void* pp2 = sizeof(T) == 2 && w == 0 ? a.k_pts : nullptr;
     uint32_t rsc[raw_words<T>(kCSlot)], rpt[raw_words<T>(3 * kPvSlot)];
-    uint32_t rsk[raw_words<T>(kCSlot)], rpk[raw_words<T>(kPtSlot)];
     issue_row<T, kCSlot>(in_rsrc(sp, C), row * C * ES, width_of(sp, C), rsc);
     issue_row<T, 3 * kPvSlot>(in_rsrc(pp, np), row * np * ES, width_of(pp, np), rpt);
-    issue_row<T, kCSlot>(in_rsrc(sp2, C), row * C * ES, width_of(sp2, C), rsk);
-    issue_row<T, kPtSlot>(in_rsrc(pp2, 3 * Pqk), row * 3 * Pqk * ES, width_of(pp2, 3 * Pqk), rpk);
 
     // the block centre: mean translation of the block's valid residues
     // (every wave forms it for itself)
@@ -394,25 +396,38 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
           const float g = R[3 * x] * p_in[3 * p] + R[3 * x + 1] * p_in[3 * p + 1] + R[3 * x + 2] * p_in[3 * p + 2] + tc[x];
           P[3 * p + x] = (valid && p < Pqk) ? g : 0.f;
         }
-      S rowv[kHeadW];
-#pragma unroll
-      for (int c = 0; c < kCSlot; ++c) {
-        const float s = (valid && c < C) ? s_in[c] : 0.f;
-        rowv[c] = E::pack(isq ? alpha * s : s);
-      }
       if constexpr (sizeof(T) == 2) {
+        // two elements per word, converted in pairs (round to nearest even):
+        // the scalar part, then three 16-slot point groups, each 15
+        // coordinates and a zero, query [hi | hi | lo], key [hi | lo | hi]
 #pragma unroll
-        for (int u = 0; u < kPtSlot; ++u) {
-          S hi, lo;
-          E::split(isq ? 2.f * kap * P[u] : P[u], hi, lo);
-          // query [hi | hi | lo], key [hi | lo | hi]
-          rowv[kCSlot + u] = hi;
-          rowv[kCSlot + kPtSlot + u] = isq ? hi : lo;
-          rowv[kCSlot + 2 * kPtSlot + u] = isq ? lo : hi;
+        for (int k = 0; k < kCSlot / 2; ++k) {
+          f32x2 x;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float v = (valid && 2 * k + e < C) ? s_in[2 * k + e] : 0.f;
+            x[e] = isq ? alpha * v : v;
+          }
+          wv[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
         }
+        const float ps = isq ? 2.f * kap : 1.f;
 #pragma unroll
-        for (int f = kCSlot + 3 * kPtSlot; f < kHeadW; ++f) rowv[f] = 0;
+        for (int k = 0; k < 8; ++k) {
+          const f32x2 x = {ps * P[2 * k], 2 * k + 1 < kPtSlot ? ps * P[2 * k + 1] : 0.f};
+          const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+          const f32x2 r = {x[0] - __uint_as_float(hw << 16), x[1] - __uint_as_float(hw & 0xFFFF0000u)};
+          const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+          wv[kCSlot / 2 + k] = hw;
+          wv[kCSlot / 2 + 8 + k] = isq ? hw : lw;
+          wv[kCSlot / 2 + 16 + k] = isq ? lw : hw;
+        }
       } else {
+        S rowv[kHeadW];
+#pragma unroll
+        for (int c = 0; c < kCSlot; ++c) {
+          const float v = (valid && c < C) ? s_in[c] : 0.f;
+          rowv[c] = E::pack(isq ? alpha * v : v);
+        }
         // fp32: key points at kCSlot.., unscaled query points at kFpQPts..;
         // the attention kernel forms the point term from explicit
         // differences, so they must not meet in the product
@@ -425,8 +440,8 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
 #pragma unroll
           for (int u = 0; u < kPtSlot; ++u) rowv[kCSlot + u] = P[u];
         }
+        pack_words(rowv, wv);
       }
-      pack_words(rowv, wv);
       float sx = 0.f, sy = 0.f, sz = 0.f, sn = 0.f;
 #pragma unroll
       for (int p = 0; p < 5; ++p) {
@@ -442,40 +457,23 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
                     : (sizeof(T) == 2 ? make_float4(ps.x, ps.y, ps.z, -kap * ps.w) : make_float4(0.f, 0.f, 0.f, 0.f));
     };
 
+    // Every wave forms its rows first; on the bf16 path the key wave hands
+    // its rows and column terms to the query wave through LDS, and after one
+    // barrier every wave writes its rows out while the query wave takes the
+    // logit of each query with its own key.
+    uint32_t wv[kHeadW * ES / 4];   // query or key wave: its packed head row
+    float4 ps = make_float4(0.f, 0.f, 0.f, 0.f);
+    S out[32];                      // value waves: their 32 feature rows
     if (w <= 1) {
       // ---- query (wave 0) or key (wave 1) head row ----
       float sc[kCSlot], pt[kPtSlot];
       unpack_row<T>(rsc, sc);
       unpack_row<T>(rpt, pt);
-      uint32_t wv[kHeadW * ES / 4];
-      const float4 ps = head_row(w == 0, sc, pt, wv);
-      // rows J*64 .. J*64 + 63 of (b, h) are contiguous; lane j holds row j
-      unsigned char* dst = a.ws + (w == 0 ? ly.off_qh : ly.off_kh) +
-                           (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW * ES;
-      ST::rows(xb, lane, wv, dst);
-      if (w == 0) {
-        // query row term; on the bf16 path its w holds the head part of the
-        // logit of the query with its own key (lifted rows as the attention
-        // products see them, plus the key's column term: the block offset
-        // is zero), the running-max seed of the attention kernel. The key
-        // row is formed here again, from the same inputs by the same code
-        // as the key wave's.
-        float4 qrow_v = make_float4(ps.x, ps.y, ps.z, 0.f);
-        if constexpr (sizeof(T) == 2) {
-          float sk[kCSlot], pk[kPtSlot];
-          unpack_row<T>(rsk, sk);
-          unpack_row<T>(rpk, pk);
-          uint32_t kw[kHeadW * ES / 4];
-          const float4 kc = key_col(head_row(false, sk, pk, kw));
-          float d = 0.f;
+      ps = head_row(w == 0, sc, pt, wv);
+      if (sizeof(T) == 2 && w == 1) {
 #pragma unroll
-          for (int e = 0; e < kHeadW / 2; ++e)
-            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv[e]), __builtin_bit_cast(bf16x2, kw[e]), d, false);
-          qrow_v.w = d + kc.w;
-        }
-        reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = qrow_v;
-      } else {
-        reinterpret_cast<float4*>(a.ws + ly.off_kcol)[o] = key_col(ps);
+        for (int e = 0; e < kHeadW / 2; ++e) kxr[lane][e] = wv[e];
+        kxc[lane] = key_col(ps).w;
       }
     } else {
       // ---- value head block, feature-major [64 features][64 positions];
@@ -491,7 +489,6 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
           const float g = R[3 * x] * pv[3 * p] + R[3 * x + 1] * pv[3 * p + 1] + R[3 * x + 2] * pv[3 * p + 2] + tc[x];
           G[x][p] = (valid && p < Pv) ? g : 0.f;
         }
-      S out[32];
       if (w == 2) {
         // v (16), G'hi x (8), G'hi y (8)
 #pragma unroll
@@ -516,6 +513,31 @@ __global__ __launch_bounds__(256) void ipa_lift_kernel(FwdArgs a) {
           out[24 + p] = lz;
         }
       }
+    }
+    if constexpr (sizeof(T) == 2) __syncthreads();   // kxr, kxc
+    if (w <= 1) {
+      // rows J*64 .. J*64 + 63 of (b, h) are contiguous; lane j holds row j
+      unsigned char* dst = a.ws + (w == 0 ? ly.off_qh : ly.off_kh) +
+                           (((size_t)b * H + h) * Lp + (size_t)J * kTileN) * kHeadW * ES;
+      ST::rows(xb, lane, wv, dst);
+      if (w == 0) {
+        // query row term; on the bf16 path its w holds the head part of the
+        // logit of the query with its own key (lifted rows as the attention
+        // products see them, plus the key's column term: the block offset
+        // is zero), the running-max seed of the attention kernel
+        float4 qrow_v = make_float4(ps.x, ps.y, ps.z, 0.f);
+        if constexpr (sizeof(T) == 2) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < kHeadW / 2; ++e)
+            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv[e]), __builtin_bit_cast(bf16x2, kxr[lane][e]), d, false);
+          qrow_v.w = d + kxc[lane];
+        }
+        reinterpret_cast<float4*>(a.ws + ly.off_qrow)[o] = qrow_v;
+      } else {
+        reinterpret_cast<float4*>(a.ws + ly.off_kcol)[o] = key_col(ps);
+      }
+    } else {
       const size_t blk = ((size_t)b * H + h) * nJ + J;   // value block of (b, h, J)
       store_cols(xb, lane, out, a.ws + ly.off_vth + (blk * kHeadW + (w - 2) * 32) * kTileN * ES);
     }
