@@ -804,23 +804,32 @@ void ipa_attn_kernel(FwdArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   };
 
-  // (1) z1 rows qw .. qw + 31 as [32][R Cz] (chunk c of row r in slot
-  //     c ^ (r & zm): the 8 rows that 8 lanes read at once fall on distinct
-  //     banks), then the frames of the same rows as [32][9] rotations and
-  //     [32][3] translations. Rows past L read zeros.
+  // (1) the frames of rows qw .. qw + 31, then their z1 rows, are loaded;
+  //     the frames go to LDS as [32][9] rotations and [32][3] translations
+  //     at the end of the staging block, while the z1 loads stay in flight
+  //     through the scalar and point outputs below. Rows past L read zeros.
   const int RB = RCz * ES;                      // bytes per z1 row, a multiple of 16
   const int CPR = RB / 16;                      // 16-byte chunks per row
   const int zm = (CPR & 7) == 0 ? 7 : (CPR & 3) == 0 ? 3 : (CPR & 1) == 0 ? 1 : 0;
-  float* const fr = reinterpret_cast<float*>(xs + 32 * RB);
+  constexpr int kFrBytes = 32 * 12 * 4;
+  static_assert(32 * (kCSlot + 3 * kPvSlot + kPvSlot + 3) * 4 + kFrBytes <= SM::kKBuf &&
+                32 * SM::kPW * ES + kFrBytes <= SM::kKBuf, "staged outputs or z1 rows reach the frames");
+  float* const fr = reinterpret_cast<float*>(xs + SM::kKBuf - kFrBytes);
+  constexpr int NZL = (SM::kPW * ES / 16 + 1) / 2;   // loads for the widest z1 row
+  u32x4 zv[NZL];
+  int zo[NZL];
   {
     const __amdgpu_buffer_rsrc_t rZ = rsrc_or_empty(a.z1, (size_t)b * L * RB, (uint32_t)L * RB);
     const __amdgpu_buffer_rsrc_t rR = rsrc_or_empty(a.rot, (size_t)b * L * 36, (uint32_t)L * 36);
     const __amdgpu_buffer_rsrc_t rT = rsrc_or_empty(a.trans, (size_t)b * L * 12, (uint32_t)L * 12);
-    constexpr int NZL = (SM::kPW * ES / 16 + 1) / 2;   // loads for the widest z1 row
-    u32x4 zv[NZL];
-    int zo[NZL];
+    float rv[5], tv[2];
+#pragma unroll
+    for (int s = 0; s < 5; ++s) rv[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rR, (qw * 9 + 64 * s + lane) * 4, 0, 0));
+#pragma unroll
+    for (int s = 0; s < 2; ++s) tv[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rT, (qw * 3 + 64 * s + lane) * 4, 0, 0));
     // chunk 64 s + lane of the block: row zr, chunk zc (stepped, no division
-    // in the loop)
+    // in the loop); chunk c of row r goes to slot c ^ (r & zm), so that the
+    // 8 rows that 8 lanes read at once fall on distinct banks
     int zr = lane / CPR, zc = lane - zr * CPR;
     const int dr = 64 / CPR, dc = 64 - dr * CPR;
 #pragma unroll
@@ -831,14 +840,6 @@ void ipa_attn_kernel(FwdArgs a) {
       zc += dc;
       if (zc >= CPR) { zc -= CPR; ++zr; }
     }
-    float rv[5], tv[2];
-#pragma unroll
-    for (int s = 0; s < 5; ++s) rv[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rR, (qw * 9 + 64 * s + lane) * 4, 0, 0));
-#pragma unroll
-    for (int s = 0; s < 2; ++s) tv[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rT, (qw * 3 + 64 * s + lane) * 4, 0, 0));
-#pragma unroll
-    for (int s = 0; s < NZL; ++s)
-      if (!ZP && 64 * s + lane < 32 * CPR) *reinterpret_cast<u32x4*>(xs + zo[s]) = zv[s];
 #pragma unroll
     for (int s = 0; s < 5; ++s)
       if (64 * s + lane < 32 * 9) fr[64 * s + lane] = rv[s];
@@ -847,29 +848,7 @@ void ipa_attn_kernel(FwdArgs a) {
       if (64 * s + lane < 32 * 3) fr[32 * 9 + 64 * s + lane] = tv[s];
   }
   wave_sync();
-
-  // (2) this lane's z1 groups 8 q + 4 g .. + 3 of row n (kept packed until
-  //     used) and its frame
-  constexpr int NG = (NFB - 2) * 4;              // pair feature groups per lane
-  constexpr int ZW = sizeof(T) == 2 ? 2 : 4;     // 32-bit words per group
-  uint32_t zp[NG][ZW];
-#pragma unroll
-  for (int q = 0; q < NG; ++q) {
-    if constexpr (sizeof(T) == 2) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(xs + n * RB + 16 * (q ^ (n & zm)) + 8 * g);
-      zp[q][0] = v[0]; zp[q][1] = v[1];
-    } else {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + n * RB + 16 * ((2 * q + g) ^ (n & zm)));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) zp[q][e] = v[e];
-    }
-  }
-  auto zval = [&](int q, int e) -> float {
-    if constexpr (sizeof(T) == 2)
-      return __uint_as_float(e & 1 ? zp[q][e >> 1] & 0xFFFF0000u : zp[q][e >> 1] << 16);
-    else
-      return __uint_as_float(zp[q][e]);
-  };
+  // (2) this lane's frame
   float R[9], tr[3];
 #pragma unroll
   for (int e = 0; e < 9; ++e) R[e] = fr[9 * n + e];
@@ -939,6 +918,36 @@ void ipa_attn_kernel(FwdArgs a) {
   store_rows(std::integral_constant<int, PP>{}, sp, 3 * Pv, a.out_pts, bi0 * pP + (size_t)h * 3 * Pv, pP);
   store_rows(std::integral_constant<int, PN>{}, sn, Pv, a.out_pts_norm, bi0 * pN + (size_t)h * Pv, pN);
   if constexpr (ZP) return;   // no pair channels
+
+  // (4) the z1 rows into the staging block (over the staged outputs above,
+  //     whose reads precede these writes in this wave's LDS order), then
+  //     this lane's z1 groups 8 q + 4 g .. + 3 of row n, kept packed until
+  //     used
+  wave_sync();
+#pragma unroll
+  for (int s = 0; s < NZL; ++s)
+    if (!ZP && 64 * s + lane < 32 * CPR) *reinterpret_cast<u32x4*>(xs + zo[s]) = zv[s];
+  wave_sync();
+  constexpr int NG = (NFB - 2) * 4;              // pair feature groups per lane
+  constexpr int ZW = sizeof(T) == 2 ? 2 : 4;     // 32-bit words per group
+  uint32_t zp[NG][ZW];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(xs + n * RB + 16 * (q ^ (n & zm)) + 8 * g);
+      zp[q][0] = v[0]; zp[q][1] = v[1];
+    } else {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + n * RB + 16 * ((2 * q + g) ^ (n & zm)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zp[q][e] = v[e];
+    }
+  }
+  auto zval = [&](int q, int e) -> float {
+    if constexpr (sizeof(T) == 2)
+      return __uint_as_float(e & 1 ? zp[q][e >> 1] & 0xFFFF0000u : zp[q][e >> 1] << 16);
+    else
+      return __uint_as_float(zp[q][e]);
+  };
 
   // ---- pair channels: o_pair[c] = sum_r z1[r Cz + c] O[r Cz + c] / l ----
   // Lane (n, g) holds O at features 32 fb + 8 k + 4 g + e of query n: 4-wide
