@@ -27,7 +27,7 @@
 //               KA' = [KA | Kg], VA, GA, the points and D_i.
 //   per chunk of QC query rows (QC bounds the two score buffers to
 //   2 x 2^26 floats, so memory stays linear in L):
-//     gemm      S = QA KA^T and dP = GA VA^T (fp32 matrix cores)
+//     gemm      S = QA KA^T (split path) and dP = GA VA^T (fp32 products)
 //     bwd_rows  per query row: the point term -kappa |Qg_i - Kg_j|^2 from
 //               explicit differences, the masked softmax A, dS, and the
 //               row sums of dS and of dS |Qg_i - Kg_j|^2
@@ -502,8 +502,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     g.A = a.QA + (size_t)q0 * a.DAQ; g.sAb = rowsQ; g.am = a.DAQ; g.ak = 1;
     g.B = a.KA; g.sBb = rowsK; g.bk = 1; g.bn = a.DAK;
     g.C = a.X; g.sCb = xs; g.cm = L; g.acc = 0;
+    g.x3 = 1;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     // dP = GA VA^T
+    g.x3 = 0;
     g.K = a.DV;
     g.A = a.GA + (size_t)q0 * a.DV; g.sAb = rowsV; g.am = a.DV;
     g.B = a.VA; g.sBb = rowsV; g.bk = 1; g.bn = a.DV;
@@ -511,12 +513,17 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(bwd_rows_kernel, dim3((qc + kRowsPerWG - 1) / kRowsPerWG, BH), dim3(256), 0, s, a, q0, qc);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    // Precision of the products: U = A z2, dVA = A^T GA and the scalar and
-    // pair columns of dQA' do not cancel, so they run on the split path
-    // (each fp32 operand as bf16 hi + lo, three bf16 products, about 2^-17
-    // relative per term). The others stay on fp32 products: S feeds the
-    // exponent, dP the difference dP - D, and the point columns of dQA' and
-    // dKA' (sum_j dS_ij Kg_j against Qg_i sum_j dS_ij, coordinates of a
+    // Precision of the products: S, U = A z2, dVA = A^T GA and the scalar and
+    // pair columns of dQA' and dKA' run on the split path (each fp32 operand
+    // as bf16 hi + lo, three bf16 products, about 2^-17 relative per term).
+    // S holds the lifted dot only (its point term is added from explicit
+    // differences in the row kernel), scalar and pair products of random
+    // sign with no large common part: its error, about 2^-17 of the sum of
+    // the terms' magnitudes, moved every gradient by about 1e-5 relative at
+    // L = 2048 and 4096, a twentieth of the 2e-4 bar. The others stay on
+    // fp32 products: dP enters the difference dP - D (the split there moved
+    // the gamma gradient by 2.8e-4 relative), and the point columns of dQA'
+    // and dKA' (sum_j dS_ij Kg_j against Qg_i sum_j dS_ij, coordinates of a
     // hundred angstroms or more) cancel by an order of magnitude.
     // dQA' = dS KA' (rows q0 .. q0 + qc): the scalar and pair columns on
     // the split path, the point columns (which cancel, see above) on fp32
@@ -539,12 +546,18 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     g.B = a.KA + a.C;
     g.C = a.U + (size_t)q0 * RCz; g.sCb = (long long)L * RCz; g.cm = RCz;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
-    // dKA' += dS^T QA' (all keys)
-    g.x3 = 0;
-    g.M = L; g.N = a.DAQ; g.K = qc;
+    // dKA' += dS^T QA' (all keys): the scalar and pair columns on the split
+    // path, the point columns on fp32 products, as for dQA'
+    g.x3 = 1;
+    g.M = L; g.N = a.DA; g.K = qc;
     g.A = a.Y; g.sAb = xs; g.am = 1; g.ak = L;
     g.B = a.QA + (size_t)q0 * a.DAQ; g.sBb = rowsQ; g.bk = a.DAQ; g.bn = 1;
     g.C = a.dKA; g.sCb = rowsQ; g.cm = a.DAQ; g.acc = q0 > 0;
+    if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+    g.x3 = 0;
+    g.N = a.DAQ - a.DA;
+    g.B = a.QA + (size_t)q0 * a.DAQ + a.DA;
+    g.C = a.dKA + a.DA;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
     // dVA += A^T GA
     g.x3 = 1;
