@@ -86,56 +86,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   // (element u is index u % 8 of unit u / 8), written as one 16-byte chunk
   // per half once its last element is loaded; single 2-byte writes down a
   // column of rows would hit each bank several times. With k as the
-  // stride-1 dimension a thread stages single elements along a row.
+  // stride-1 dimension a thread stages pairs of consecutive reduction
+  // indices (element u is index u % 2 of pair u / 2; sixteen threads cover
+  // a row), each pair converted together and written as one 4-byte word
+  // per half; the fp32 path stages single elements along a row.
   auto a_mk = [&](int u, int& m, int& k) {
-    if (AK1) { k = tid & (KS - 1); m = (tid >> 5) + 8 * u; }
+    if (AK1 && X3) { k = 2 * (tid & 15) + (u & 1); m = (tid >> 4) + 16 * (u >> 1); }
+    else if (AK1) { k = tid & (KS - 1); m = (tid >> 5) + 8 * u; }
     else if (X3) { m = tid % BM; k = 8 * (tid / BM + (256 / BM) * (u >> 3)) + (u & 7); }
     else { m = tid % BM; k = tid / BM + (256 / BM) * u; }
   };
   auto b_kn = [&](int u, int& k, int& n) {
-    if (BK1) { k = tid & (KS - 1); n = (tid >> 5) + 8 * u; }
+    if (BK1 && X3) { k = 2 * (tid & 15) + (u & 1); n = (tid >> 4) + 16 * (u >> 1); }
+    else if (BK1) { k = tid & (KS - 1); n = (tid >> 5) + 8 * u; }
     else if (X3) { n = tid % BN; k = 8 * (tid / BN + (256 / BN) * (u >> 3)) + (u & 7); }
     else { n = tid % BN; k = tid / BN + (256 / BN) * u; }
   };
   static_assert(!X3 || ((BM == 64 || BM == 128) && (BN == 64 || BN == 128)), "split path tiles");
   // LDS element offset of reduction index k in row r of a split-path slice
   auto xsw = [](int r, int k) { return r * PKB + ((((k >> 3) ^ (r >> 2)) & 3) << 3) + (k & 7); };
-  // Offsets (in elements, below 2^31) of each element at reduction index 0;
-  // rows past M and columns past N read row / column M - 1 / N - 1 and are
-  // zeroed. Only a step that runs past kend clamps the reduction index.
-  int oa[NA], ob[NB];
-  bool va[NA], vb[NB];
+  // Operands are read through buffer resources over their slices (below
+  // 2^29 elements, checked at launch). The per-lane byte offset is that of
+  // the first element of a group of elements on one row (one element on
+  // the fp32 path; a pair or a unit of eight reduction indices on the split
+  // path); the element's place in its group and the step's reduction index
+  // go into the scalar offset, which the buffer's range check leaves out.
+  // Groups outside the product (rows past M, columns past N) and, in the
+  // last step, elements past kend take the per-lane offset kOut, beyond
+  // every slice, and load 0.
+  constexpr uint32_t kOut = 0x80000000u;
+  constexpr int GA = X3 ? (AK1 ? 2 : 8) : 1, GB = X3 ? (BK1 ? 2 : 8) : 1;
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(A), (short)0, (int)(((long long)(g.M - 1) * g.am + (long long)(g.K - 1) * g.ak + 1) * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(B), (short)0, (int)(((long long)(g.K - 1) * g.bk + (long long)(g.N - 1) * g.bn + 1) * 4), 0x00020000);
+  uint32_t oa[NA / GA], ob[NB / GB];
 #pragma unroll
-  for (int u = 0; u < NA; ++u) {
+  for (int v = 0; v < NA / GA; ++v) {
     int m, k;
-    a_mk(u, m, k);
-    va[u] = m0 + m < g.M;
-    const int mm = va[u] ? m0 + m : g.M - 1;
-    oa[u] = AK1 ? mm * (int)g.am + k : mm + k * (int)g.ak;
+    a_mk(v * GA, m, k);
+    const int mm = m0 + m;
+    oa[v] = mm < g.M ? (uint32_t)(AK1 ? mm * (int)g.am + k : mm + k * (int)g.ak) * 4u : kOut;
   }
 #pragma unroll
-  for (int u = 0; u < NB; ++u) {
+  for (int v = 0; v < NB / GB; ++v) {
     int k, n;
-    b_kn(u, k, n);
-    vb[u] = n0 + n < g.N;
-    const int nn = vb[u] ? n0 + n : g.N - 1;
-    ob[u] = BK1 ? nn * (int)g.bn + k : nn + k * (int)g.bk;
+    b_kn(v * GB, k, n);
+    const int nn = n0 + n;
+    ob[v] = nn < g.N ? (uint32_t)(BK1 ? nn * (int)g.bn + k : nn + k * (int)g.bk) * 4u : kOut;
   }
   const int ak = AK1 ? 1 : (int)g.ak, bk = BK1 ? 1 : (int)g.bk;
+  // scalar byte offset of element u (of A, of B) in a step at k0: the
+  // group members are consecutive reduction indices
+  auto sa = [&](int k0, int u) { return (uint32_t)(k0 + u % GA) * (uint32_t)ak * 4u; };
+  auto sb = [&](int k0, int u) { return (uint32_t)(k0 + u % GB) * (uint32_t)bk * 4u; };
   float ra[NA], rb[NB];
   // element u of a full step: A for u < NA, then B
-  // (rows / columns out of range are zeroed when staged, so that nothing
-  // waits for a load before its LDS write)
   auto load_one = [&](int k0, int u) {
-    if (u < NA) ra[u] = A[(unsigned)(oa[u] + k0 * ak)];
-    else rb[u - NA] = B[(unsigned)(ob[u - NA] + k0 * bk)];
-  };
-  // split path: x = hi + lo + O(2^-18 x), hi and lo bf16 (nearest even)
-  auto split = [](float x, uint16_t& hi, uint16_t& lo) {
-    uint32_t h, l;
-    split2(x, 0.f, h, l);
-    hi = (uint16_t)h;
-    lo = (uint16_t)l;
+    if (u < NA) ra[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rA, oa[u / GA], sa(k0, u), 0));
+    else rb[u - NA] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rB, ob[(u - NA) / GB], sb(k0, u - NA), 0));
   };
   // eight values as 16 bytes of bf16 hi halves and 16 bytes of lo halves
   auto split8 = [&](const float* x, uint4& hi, uint4& lo) {
@@ -152,13 +161,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         int m, k;
         a_mk(u, m, k);
         if (AK1) {
-          const int at = xsw(m, k);
-          split(va[u] ? ra[u] : 0.f, Ah[p][0][0][at], Ah[p][1][0][at]);
+          if (u & 1) {   // the pair is written with its second element
+            const int at = xsw(m, k - 1);
+            split2(ra[u - 1], ra[u], *reinterpret_cast<uint32_t*>(&Ah[p][0][0][at]),
+                   *reinterpret_cast<uint32_t*>(&Ah[p][1][0][at]));
+          }
         } else if ((u & 7) == 7) {   // the unit is written with its last element
           const int u0 = u - 7;
           a_mk(u0, m, k);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = va[u0 + e] ? ra[u0 + e] : 0.f;
+          for (int e = 0; e < 8; ++e) x[e] = ra[u0 + e];
           split8(x, hi, lo);
           *reinterpret_cast<uint4*>(&Ah[p][0][0][xsw(m, k)]) = hi;
           *reinterpret_cast<uint4*>(&Ah[p][1][0][xsw(m, k)]) = lo;
@@ -168,13 +180,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         int k, n;
         b_kn(ub, k, n);
         if (BK1) {
-          const int at = xsw(n, k);
-          split(vb[ub] ? rb[ub] : 0.f, Bh[p][0][0][at], Bh[p][1][0][at]);
+          if (ub & 1) {
+            const int at = xsw(n, k - 1);
+            split2(rb[ub - 1], rb[ub], *reinterpret_cast<uint32_t*>(&Bh[p][0][0][at]),
+                   *reinterpret_cast<uint32_t*>(&Bh[p][1][0][at]));
+          }
         } else if ((ub & 7) == 7) {
           const int u0 = ub - 7;
           b_kn(u0, k, n);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = vb[u0 + e] ? rb[u0 + e] : 0.f;
+          for (int e = 0; e < 8; ++e) x[e] = rb[u0 + e];
           split8(x, hi, lo);
           *reinterpret_cast<uint4*>(&Bh[p][0][0][xsw(n, k)]) = hi;
           *reinterpret_cast<uint4*>(&Bh[p][1][0][xsw(n, k)]) = lo;
@@ -185,11 +200,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     if (u < NA) {
       int m, k;
       a_mk(u, m, k);
-      As[p][m][k] = va[u] ? ra[u] : 0.f;
+      As[p][m][k] = ra[u];
     } else {
       int k, n;
       b_kn(u - NA, k, n);
-      Bs[p][n][k] = vb[u - NA] ? rb[u - NA] : 0.f;
+      Bs[p][n][k] = rb[u - NA];
     }
   };
   auto gload = [&](int k0) {
@@ -197,24 +212,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
       for (int u = 0; u < NA + NB; ++u) load_one(k0, u);
     } else {
-      // last, partial step: indices past kend read index kend - 1, zeroed
+      // last, partial step: indices past kend load 0
 #pragma unroll
       for (int u = 0; u < NA; ++u) {
         int m, k;
         a_mk(u, m, k);
-        const bool in = k0 + k < kend;
-        const int back = in ? 0 : (k0 + k - (kend - 1)) * ak;
-        const float v = A[(unsigned)(oa[u] + k0 * ak - back)];
-        ra[u] = (va[u] && in) ? v : 0.f;
+        ra[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              rA, k0 + k < kend ? oa[u / GA] : kOut, sa(k0, u), 0));
       }
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         int k, n;
         b_kn(u, k, n);
-        const bool in = k0 + k < kend;
-        const int back = in ? 0 : (k0 + k - (kend - 1)) * bk;
-        const float v = B[(unsigned)(ob[u] + k0 * bk - back)];
-        rb[u] = (vb[u] && in) ? v : 0.f;
+        rb[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              rB, k0 + k < kend ? ob[u / GB] : kOut, sb(k0, u), 0));
       }
     }
   };
@@ -436,14 +447,8 @@ void launch_shape(const Gemm& g, dim3 grid, hipStream_t s) {
   else launch_layout<TM, TN, false>(g, grid, s);
 }
 
-hipError_t launch_gemm(const Gemm& g, int z, hipStream_t s) {
-  // one of each operand's two strides is 1, and every element of one
-  // batch slice lies within 2^31 elements of its start
-  if (!(g.ak == 1 || g.am == 1) || !(g.bk == 1 || g.bn == 1)) return hipErrorInvalidValue;
-  if ((double)(g.M - 1) * g.am + (double)(g.K - 1) * g.ak >= 2147483647.0 ||
-      (double)(g.K - 1) * g.bk + (double)(g.N - 1) * g.bn >= 2147483647.0)
-    return hipErrorInvalidValue;
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+// One launch; every operand slice spans fewer than 2^29 elements.
+hipError_t launch_one(const Gemm& g, int z, hipStream_t s) {
   if (g.N <= 32 && !g.x3) {
     // narrow product: 128 x 32 tiles (the four waves stacked along M), a
     // quarter of the padding of a 64-wide tile
@@ -457,6 +462,37 @@ hipError_t launch_gemm(const Gemm& g, int z, hipStream_t s) {
   else if (t.tn == 2) launch_shape<1, 2>(g, grid, s);
   else launch_shape<1, 1>(g, grid, s);
   return hipGetLastError();
+}
+
+// The kernel addresses each operand slice through a buffer resource with
+// 32-bit byte offsets, so a launch's slices must span fewer than 2^29
+// elements. B must on its own; A is split along M into launches that do
+// (the rows of one launch are a contiguous run of A, C, the row mask and
+// the segmented outputs).
+hipError_t launch_gemm(const Gemm& g, int z, hipStream_t s) {
+  if (!(g.ak == 1 || g.am == 1) || !(g.bk == 1 || g.bn == 1)) return hipErrorInvalidValue;
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  constexpr double kMaxExt = 536870912.0;   // 2^29
+  if ((double)(g.K - 1) * g.bk + (double)(g.N - 1) * g.bn + 1.0 >= kMaxExt) return hipErrorInvalidValue;
+  const double krun = (double)(g.K - 1) * g.ak + 1.0;
+  if ((double)(g.M - 1) * g.am + krun < kMaxExt) return launch_one(g, z, s);
+  // rows per launch: a multiple of 128 (whole tiles of every shape)
+  const long long rows = (long long)((kMaxExt - 1.0 - krun) / (double)g.am) / 128 * 128;
+  if (rows < 128) return hipErrorInvalidValue;
+  for (long long m0 = 0; m0 < g.M; m0 += rows) {
+    Gemm c = g;
+    c.M = (int)(g.M - m0 < rows ? g.M - m0 : rows);
+    c.A = g.A + m0 * g.am;
+    if (g.C) c.C = g.C + m0 * g.cm;
+    if (g.rowmask) c.rowmask = g.rowmask + m0;
+    for (int b = 0; b < g.nseg; ++b) {
+      const long long wd = g.seg_start[b + 1] - g.seg_start[b];
+      c.seg_out[b] = static_cast<unsigned char*>(g.seg_out[b]) + m0 * wd * (g.seg_bf16 ? 2 : 4);
+    }
+    const hipError_t e = launch_one(c, z, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

@@ -108,3 +108,38 @@ def test_layer_unaligned_output_blocks(device):
     start on 16-byte boundaries of the readout matrix, so the layer takes
     its packed-output-plus-gather path."""
     _check(WORKLOADS["tiny_fp32"].with_(L=45, H=3, C=5, Pv=3, Cz=8, R=1), device, 24, 1e-4, seed=6)
+
+
+def test_layer_readout_split_along_rows(device):
+    """A readout whose gathered operand spans 2^29 elements or more runs as
+    several launches along its rows (the matrix kernels address an operand
+    slice with 32-bit byte offsets). 500 copies of one fp32 chain of 512
+    residues (H = 12, c_z = 128, R = 1) make 256000 rows x 2112 gathered
+    columns, split into a launch
+    of 254080 rows and one of 1920; the first and the last copy, which fall
+    in different launches, are compared with the oracle on the one chain."""
+    from geometric_invariant_attention_amd import IPALayer
+    w1 = WORKLOADS["single_chain"].with_(dtype="fp32", R=1)   # fp32 storage: R c_z <= 128
+    one = make_layer_inputs(w1, c_s=64, seed=13)
+    copies = 500
+    big = dict(one)
+    for k in ("s", "rot", "trans", "mask"):
+        big[k] = np.ascontiguousarray(np.repeat(one[k], copies, axis=0))
+    d = dict(one["dims"], B=copies)
+    assert d["B"] * d["L"] * d["H"] * (d["C"] + 4 * d["Pv"] + d["Cz"]) >= 2 ** 29
+    print(f"[layer] {copies} copies of {w1.name} (fp32, c_s=64): readout split along rows", flush=True)
+    t = {k: torch.from_numpy(big[k]).to(device) for k in ("s", "rot", "trans", "w_in", "b_in", "w_b",
+                                                          "gamma", "w_out", "b_out")}
+    m = torch.from_numpy(big["mask"]).to(device) if big.get("has_mask") else None
+    layer = IPALayer(**d, c_s=64, dtype=torch.float32, device=device)
+    y = layer(t["s"], t["rot"], t["trans"], t["w_in"], t["b_in"], t["w_b"], t["gamma"], t["w_out"],
+              t["b_out"], mask=m, w_L=big["w_L"], w_C=big["w_C"])
+    torch.cuda.synchronize()
+    got = y[[0, copies - 1]].cpu().numpy()
+    del y, layer, t
+    ref = ipa_layer(one)[0]
+    scale = max(1.0, float(np.abs(ref).max()))
+    for c, g in zip((0, copies - 1), got):
+        err = float(np.abs(g - ref).max()) / scale
+        print(f"  copy {c}: rel error {err:.2e}", flush=True)
+        assert np.isfinite(g).all() and err < 1e-4, (c, err)
