@@ -716,11 +716,11 @@ def bench_backward(dev, steps: int, warmup: int, cpu) -> dict:
     stream = torch.cuda.current_stream(dev)
     raw = bwd.bind(t, {"s": out["s"], "pts": out["pts"], "pair": out["pair"]}, g,
                    w_L=inp["w_L"], w_C=inp["w_C"], stream=stream)
-    nw = max(2, warmup // 20)
+    nw = max(3, warmup // 20)
     for _ in range(nw):
         bwd.backward_raw(raw)
     torch.cuda.synchronize(dev)
-    n = max(2, steps // 10)
+    n = max(10, steps // 10)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(n):

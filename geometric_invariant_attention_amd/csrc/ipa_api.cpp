@@ -329,7 +329,9 @@ bool bwd_layout(const ipa_dims* d, BwdLayout* o) {
   if (B * H * (int64_t)QC * L >= (int64_t(1) << 31)) return false;
   o->QC = QC;
   const size_t rows = (size_t)(B * H * L), DA = (size_t)(C + R * Cz), DV = (size_t)(C + 3 * Pv + R * Cz);
-  const size_t P3 = (size_t)(3 * P), DAQ = DA + P3 + 1, DAK = DA + P3, xs = (size_t)(B * H) * QC * L;
+  // lifted rows padded to a multiple of 4 floats (16-byte aligned rows)
+  const size_t P3 = (size_t)(3 * P), DAQ = (DA + P3 + 4) & ~(size_t)3, DAK = (DA + P3 + 3) & ~(size_t)3,
+               xs = (size_t)(B * H) * QC * L;
   const size_t sizes[18] = {rows * DAQ, rows * DAK, rows * DV, rows * DV, rows * P3, rows * P3, rows,
                             rows * DAK, rows * R * Cz, rows, rows,
                             rows * DAQ, rows * DV,
@@ -382,7 +384,7 @@ int32_t ipa_backward(const ipa_dims* dims, const float* q, const float* k, const
   a.B = dims->B; a.L = dims->L; a.H = dims->H; a.C = dims->C; a.Pqk = dims->Pqk; a.Pv = dims->Pv;
   a.R = dims->R; a.Cz = dims->Cz;
   a.DA = a.C + a.R * a.Cz; a.DV = a.C + 3 * a.Pv + a.R * a.Cz; a.P3 = 3 * a.Pqk;
-  a.DAQ = a.DA + a.P3 + 1; a.DAK = a.DA + a.P3; a.QC = ly.QC;
+  a.DAQ = (a.DA + a.P3 + 4) & ~3; a.DAK = (a.DA + a.P3 + 3) & ~3; a.QC = ly.QC;
   a.w_L = w_L; a.w_C = w_C;
   a.q = q; a.k = k; a.v = v; a.q_pts = q_pts; a.k_pts = k_pts; a.v_pts = v_pts;
   a.rot = rot; a.trans = trans; a.z1 = z1; a.z2 = z2; a.w_b = w_b; a.gamma = gamma; a.mask = mask;

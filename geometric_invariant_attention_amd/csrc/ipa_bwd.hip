@@ -109,7 +109,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
       a.QP[row * a.P3 + e] = vq;
       a.KP[row * a.P3 + e] = vk;
     } else {
-      vq = 1.f;   // dS^T times this column: the column sums of dS
+      // dS^T times this column: the column sums of dS; then zero padding
+      vq = c == a.DA + a.P3 ? 1.f : 0.f;
     }
     qa[c] = vq;
     if (c < a.DAK) ka[c] = vk;

@@ -13,6 +13,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Two values x as bf16 hi + lo halves (nearest even, the hardware's packed
 // conversion), x = hi + lo + O(2^-18 x); hi and lo packed two per word.
@@ -28,6 +29,58 @@ __device__ __forceinline__ void fence() { asm volatile("" ::: "memory"); }
 // An empty, ordered statement that takes an accumulator tile in place: a
 // product whose result passes through it stays between its fences.
 __device__ __forceinline__ void pin(floatx16& acc) { asm volatile("" : "+a"(acc)); }
+
+// Epilogue shared by the GEMM kernels: wave (wm, wn) writes its TM x TN
+// blocks of 32 x 32 (lane (l32, half) holds column l32 and rows
+// 8 (e / 4) + 4 half + e % 4 of each block), with the accumulate, bias,
+// row-mask and segmented-output options.
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile(const Gemm& g, floatx16 (&c)[TM][TN], int m0, int n0, int wm, int wn,
+                                           int half, int l32, int z) {
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + 32 * (wn * TN + j) + l32;
+    if (n >= g.N) continue;
+    if (g.nseg > 0) {
+      // segmented output: column n belongs to block blk of width wd, stored
+      // [m][wd] in fp32 or bf16 (nearest even)
+      int blk = 0;
+      while (blk + 1 < g.nseg && n >= g.seg_start[blk + 1]) ++blk;
+      const int wd = g.seg_start[blk + 1] - g.seg_start[blk], nc = n - g.seg_start[blk];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + 32 * (wm * TM + i) + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (m >= g.M) continue;
+          float v = c[i][j][e];
+          if (g.bias) v += g.bias[n];
+          const size_t at = (size_t)m * wd + nc;
+          if (g.seg_bf16) {
+            const uint32_t u = __float_as_uint(v);
+            reinterpret_cast<uint16_t*>(g.seg_out[blk])[at] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+          } else {
+            reinterpret_cast<float*>(g.seg_out[blk])[at] = v;
+          }
+        }
+      continue;
+    }
+    float* C = g.C + (size_t)z * g.sCb;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * (wm * TM + i) + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (m < g.M) {
+          float* dst = C + (size_t)m * g.cm + n;
+          float v = g.acc ? *dst + c[i][j][e] : c[i][j][e];
+          if (g.bias) v += g.bias[n];
+          if (g.rowmask && !g.rowmask[m]) v = 0.f;
+          *dst = v;
+        }
+      }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Batched fp32 GEMM on v_mfma_f32_32x32x2f32:
@@ -348,49 +401,267 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     p ^= 1;
   }
   if (k0 < kend) iter(k0, p, std::integral_constant<int, 2>{});
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + 32 * (wn * TN + j) + l32;
-    if (n >= g.N) continue;
-    if (g.nseg > 0) {
-      // segmented output: column n belongs to block blk of width wd, stored
-      // [m][wd] in fp32 or bf16 (nearest even)
-      int blk = 0;
-      while (blk + 1 < g.nseg && n >= g.seg_start[blk + 1]) ++blk;
-      const int wd = g.seg_start[blk + 1] - g.seg_start[blk], nc = n - g.seg_start[blk];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + 32 * (wm * TM + i) + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (m >= g.M) continue;
-          float v = c[i][j][e];
-          if (g.bias) v += g.bias[n];
-          const size_t at = (size_t)m * wd + nc;
-          if (g.seg_bf16) {
-            const uint32_t u = __float_as_uint(v);
-            reinterpret_cast<uint16_t*>(g.seg_out[blk])[at] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-          } else {
-            reinterpret_cast<float*>(g.seg_out[blk])[at] = v;
-          }
-        }
-      continue;
+  store_tile<TM, TN>(g, c, m0, n0, wm, wn, half, l32, z);
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations of the wave are outstanding, the other counters free
+constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Workgroup barrier for LDS traffic only: the wave's LDS operations
+// complete, then s_barrier; the memory clobber keeps the compiler from
+// moving memory operations across it. Unlike __syncthreads() it adds no
+// wait for outstanding global loads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// Split-path GEMM with the reduction steps copied global -> LDS ahead of
+// their use, for operands whose rows along the stride-1 dimension are
+// 16-byte aligned, K a multiple of 4, no split reduction. The split path's
+// steps are short (twelve bf16 products per wave per 32 reduction indices),
+// too short to hide a global load issued one step ahead; here each step's
+// raw fp32 slices are copied by direct-to-LDS buffer loads NS - 1 steps
+// ahead, into NS stage arrays (separate LDS arrays, so that the compiler
+// can see that a read of one stage never waits for copies into another),
+// and the bf16 hi / lo halves are formed when a wave reads its operands.
+//
+// A stage holds the step's A slice, then its B slice. An operand with k as
+// its stride-1 dimension (AK1 / BK1) is held as rows of 32 k (8 chunks of
+// 16 bytes), chunk c of row r in slot c ^ (r % 8); one wave-wide copy fills
+// 8 rows (lane l: row l / 8, slot l % 8) and a fragment (8 consecutive k of
+// one row) is two 16-byte reads. An operand with m (n) as its stride-1
+// dimension is held as 32 rows of k, each the tile's R = BM (BN) values,
+// element x of row k at x ^ (32 ((k / 8) % 2)) (chunk-granular, so that
+// the two lane halves of a fragment read, k and k + 8 apart, fall on
+// different banks); one copy fills 256 / R rows (lane l: row l / (R / 4),
+// slot l % (R / 4)) and a fragment is eight 4-byte reads. Rows past M or N
+// (chunks past M or N: those extents are then multiples of 4) and, in the
+// last step, chunks or rows past K take an offset beyond the resource's
+// range and read 0; past-K values are never read otherwise (K is a
+// multiple of 4).
+// The steps end in a plain barrier after each wave's counted wait for its
+// own copies of the next step: __syncthreads() would add a fence that
+// waits for every outstanding copy, the ones issued ahead included.
+// ---------------------------------------------------------------------------
+template <int TM, int TN, int NS, bool AK1, bool BK1>
+__global__ __launch_bounds__(256) void gemm_x3k_kernel(Gemm g) {
+  constexpr int KS = 32;
+  constexpr int BM = 64 * TM, BN = 64 * TN;
+  // 1 KB copies per stage and wave: OPA of A, OPB of B
+  constexpr int OPA = BM / 32, OPB = BN / 32, OPW = OPA + OPB;
+  constexpr uint32_t kOut = 0x80000000u;
+  constexpr int SA = BM * KS, SF = (BM + BN) * KS;    // floats: A part, whole stage
+  constexpr int kWaitAhead = vm_wait(OPW * (NS - 2));
+  __shared__ __attribute__((aligned(16))) float S0[SF];
+  __shared__ __attribute__((aligned(16))) float S1[SF];
+  __shared__ __attribute__((aligned(16))) float S2[NS > 2 ? SF : 4];
+  __shared__ __attribute__((aligned(16))) float S3[NS > 3 ? SF : 4];
+  __shared__ __attribute__((aligned(16))) float S4[NS > 4 ? SF : 4];
+  static_assert(NS >= 2 && NS <= 5, "stages");
+  // (the wave index made visibly uniform: the copies' LDS addresses are)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w & 1, wn = w >> 1, half = lane >> 5, l32 = lane & 31;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN, z = blockIdx.z;
+  const float* A = g.A + (size_t)z * g.sAb;
+  const float* B = g.B + (size_t)z * g.sBb;
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(A), (short)0, (int)(((long long)(g.M - 1) * g.am + (long long)(g.K - 1) * g.ak + 1) * 4),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(B), (short)0, (int)(((long long)(g.N - 1) * g.bn + (long long)(g.K - 1) * g.bk + 1) * 4),
+      0x00020000);
+  // Per copy q of this wave: the per-lane byte offset at reduction index 0
+  // (kOut outside the product), the k of the lane's row (rows of k only,
+  // else -1: then the chunk's k decides) and the LDS row of the copy.
+  // x0, X: the tile's first m (n) and the extent; rs: stride of the row
+  // dimension (k-contiguous), ks: stride of k (mn-contiguous).
+  struct Copy { uint32_t vo; int krow, kchunk; };
+  auto geom = [&](bool k1, int R, int q, int x0, int X, int rs, int ks) -> Copy {
+    Copy c;
+    if (k1) {
+      const int r = 8 * (w + 4 * q) + (lane >> 3), ch = (lane & 7) ^ (lane >> 3);
+      c.vo = x0 + r < X ? (uint32_t)((x0 + r) * rs + 4 * ch) * 4u : kOut;
+      c.krow = -1;
+      c.kchunk = 4 * ch;
+    } else {
+      const int cpr = R / 4, kr = (256 / R) * (w + 4 * q) + lane / cpr;
+      const int ch = (lane % cpr) ^ (8 * ((kr >> 3) & 1));
+      c.vo = x0 + 4 * ch < X ? (uint32_t)(kr * ks + x0 + 4 * ch) * 4u : kOut;
+      c.krow = kr;
+      c.kchunk = 0;
     }
-    float* C = g.C + (size_t)z * g.sCb;
+    return c;
+  };
+  uint32_t vo[OPW];
+  int kq[OPW];   // reduction index (within a step) below which the lane's chunk or row lies
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + 32 * (wm * TM + i) + 8 * (e >> 2) + 4 * half + (e & 3);
-        if (m < g.M) {
-          float* dst = C + (size_t)m * g.cm + n;
-          float v = g.acc ? *dst + c[i][j][e] : c[i][j][e];
-          if (g.bias) v += g.bias[n];
-          if (g.rowmask && !g.rowmask[m]) v = 0.f;
-          *dst = v;
-        }
-      }
+  for (int q = 0; q < OPA; ++q) {
+    const Copy c = geom(AK1, BM, q, m0, g.M, (int)g.am, (int)g.ak);
+    vo[q] = c.vo;
+    kq[q] = AK1 ? c.kchunk : c.krow;
   }
+#pragma unroll
+  for (int q = 0; q < OPB; ++q) {
+    const Copy c = geom(BK1, BN, q, n0, g.N, (int)g.bn, (int)g.bk);
+    vo[OPA + q] = c.vo;
+    kq[OPA + q] = BK1 ? c.kchunk : c.krow;
+  }
+  const uint32_t aks = AK1 ? 4u : (uint32_t)g.ak * 4u, bks = BK1 ? 4u : (uint32_t)g.bk * 4u;
+  auto stage_ptr = [&](auto sc) -> float* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return S0;
+    else if constexpr (S == 1) return S1;
+    else if constexpr (S == 2) return S2;
+    else if constexpr (S == 3) return S3;
+    else return S4;
+  };
+  // copies of the step at k0 into stage S. In the last, partial step
+  // (TAIL) the step's offset moves into the per-lane offset, so that the
+  // range check sees it, and chunks or rows past K take kOut (selects, no
+  // branches: the compiler's wait tracking then keeps the stages apart).
+  auto issue_t = [&](int k0, auto sc, auto tc) {
+    constexpr bool tail = decltype(tc)::value;
+    float* st = stage_ptr(sc);
+#pragma unroll
+    for (int q = 0; q < OPW; ++q) {
+      const bool isA = q < OPA;
+      const uint32_t step = (uint32_t)k0 * (isA ? aks : bks);
+      // (kOut + step keeps bit 31 set: still beyond every range)
+      const uint32_t past = (tail && k0 + kq[q] >= g.K) ? kOut : 0u;
+      const uint32_t v = tail ? ((vo[q] + step) | past) : vo[q];
+      const int qq = isA ? q : q - OPA;
+      const int at = isA ? (AK1 ? 8 * (w + 4 * qq) * KS : (256 / BM) * (w + 4 * qq) * BM)
+                         : SA + (BK1 ? 8 * (w + 4 * qq) * KS : (256 / BN) * (w + 4 * qq) * BN);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (__attribute__((address_space(3))) void*)(st + at), 16,
+                                               v, tail ? 0u : step, 0, 0);
+    }
+  };
+  auto issue = [&](int k0, auto sc) {
+    if (k0 + KS > g.K) issue_t(k0, sc, std::true_type{});
+    else issue_t(k0, sc, std::false_type{});
+  };
+  floatx16 c[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) c[i][j] = floatx16{};
+  // fragment of tile row (column) r of an operand part p: reduction indices
+  // 16 s2 + 8 half + 0..7 of the step, split into bf16 hi and lo
+  auto frag = [&](const float* p, bool k1, int R, int r, int s2, bf16x8& hi, bf16x8& lo) {
+    float x[8];
+    if (k1) {
+      const int c0 = 4 * s2 + 2 * half, sw = r & 7;
+      // whole 16-byte reads (an empty asm takes each as one value): a read
+      // split into single floats and merged again later loses the alias
+      // scope that keeps it from waiting for the copies into other stages
+      u32x4 u0 = *reinterpret_cast<const u32x4*>(p + r * KS + 4 * (c0 ^ sw));
+      u32x4 u1 = *reinterpret_cast<const u32x4*>(p + r * KS + 4 * ((c0 + 1) ^ sw));
+      asm("" : "+v"(u0));
+      asm("" : "+v"(u1));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = __uint_as_float(u0[e]);
+        x[4 + e] = __uint_as_float(u1[e]);
+      }
+    } else {
+      const float* col = p + (16 * s2 + 8 * half) * R + (r ^ (32 * half));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = col[e * R];
+    }
+    uint4 h, l;
+    split2(x[0], x[1], h.x, l.x);
+    split2(x[2], x[3], h.y, l.y);
+    split2(x[4], x[5], h.z, l.z);
+    split2(x[6], x[7], h.w, l.w);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+  };
+  // step at k0 on stage S; the copies of step k0 + (NS - 1) KS go into the
+  // stage that step k0 - KS read (every wave has passed the barrier after
+  // it). STEADY: that step exists and is a full one (no tail code, so that
+  // nothing merges in front of the stage reads).
+  auto step = [&](int k0, auto sc, auto steady_c) {
+    constexpr int S = decltype(sc)::value;
+    constexpr bool steady = decltype(steady_c)::value;
+    using Ahead = std::integral_constant<int, (S + NS - 1) % NS>;
+    const bool more = steady || k0 + (NS - 1) * KS < g.K;
+    if constexpr (steady) issue_t(k0 + (NS - 1) * KS, Ahead{}, std::false_type{});
+    else if (more) issue(k0 + (NS - 1) * KS, Ahead{});
+    const float* st = stage_ptr(sc);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 ah[TM], al[TM], bh[TN], bl[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) frag(st, AK1, BM, 32 * (wm * TM + i) + l32, s2, ah[i], al[i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) frag(st + SA, BK1, BN, 32 * (wn * TN + j) + l32, s2, bh[j], bl[j]);
+#pragma unroll
+      for (int kind = 0; kind < 3; ++kind)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const bf16x8 a = kind == 2 ? al[i] : ah[i];
+            const bf16x8 b = kind == 1 ? bl[j] : bh[j];
+            c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i][j], 0, 0, 0);
+          }
+    }
+    // this wave's copies of the next step have landed once no more than
+    // the copies issued after them (NS - 2 steps' worth, when all exist)
+    // are outstanding; the barrier then makes every wave's copies visible
+    // and closes the reads of stage S
+    if (more) __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    lds_barrier();
+  };
+  // prologue: steps 0 .. NS - 2 into stages 0 .. NS - 2
+  issue(0, std::integral_constant<int, 0>{});
+  if constexpr (NS > 2)
+    if (KS < g.K) issue(KS, std::integral_constant<int, 1>{});
+  if constexpr (NS > 3)
+    if (2 * KS < g.K) issue(2 * KS, std::integral_constant<int, 2>{});
+  if constexpr (NS > 4)
+    if (3 * KS < g.K) issue(3 * KS, std::integral_constant<int, 3>{});
+  if ((NS - 2) * KS < g.K) __builtin_amdgcn_s_waitcnt(kWaitAhead);
+  else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  lds_barrier();
+  using Steady = std::true_type;
+  using Any = std::false_type;
+  int k0 = 0;
+  // steady state: the step issued ahead is a full one
+  for (;;) {
+    if (k0 + NS * KS > g.K) break;
+    step(k0, std::integral_constant<int, 0>{}, Steady{});
+    k0 += KS;
+    if (k0 + NS * KS > g.K) break;
+    step(k0, std::integral_constant<int, 1>{}, Steady{});
+    k0 += KS;
+    if constexpr (NS > 2) {
+      if (k0 + NS * KS > g.K) break;
+      step(k0, std::integral_constant<int, 2>{}, Steady{});
+      k0 += KS;
+    }
+    if constexpr (NS > 3) {
+      if (k0 + NS * KS > g.K) break;
+      step(k0, std::integral_constant<int, 3>{}, Steady{});
+      k0 += KS;
+    }
+    if constexpr (NS > 4) {
+      if (k0 + NS * KS > g.K) break;
+      step(k0, std::integral_constant<int, 4>{}, Steady{});
+      k0 += KS;
+    }
+  }
+  // the last steps (at most NS), the stages continuing the rotation
+  for (; k0 < g.K; k0 += KS) {
+    const int st = (k0 / KS) % NS;
+    if (st == 0) step(k0, std::integral_constant<int, 0>{}, Any{});
+    else if (st == 1) step(k0, std::integral_constant<int, 1>{}, Any{});
+    else if (NS > 2 && st == 2) step(k0, std::integral_constant<int, (NS > 2 ? 2 : 0)>{}, Any{});
+    else if (NS > 3 && st == 3) step(k0, std::integral_constant<int, (NS > 3 ? 3 : 0)>{}, Any{});
+    else if (NS > 4) step(k0, std::integral_constant<int, (NS > 4 ? 4 : 0)>{}, Any{});
+  }
+  store_tile<TM, TN>(g, c, m0, n0, wm, wn, half, l32, z);
 }
 
 // out(m, n) = sum_z part[z](m, n) (+ bias[n]), rows with rowmask[m] == 0
@@ -447,8 +718,60 @@ void launch_shape(const Gemm& g, dim3 grid, hipStream_t s) {
   else launch_layout<TM, TN, false>(g, grid, s);
 }
 
+// Stages of the direct-to-LDS split-path kernel (copies run NS - 1 steps
+// ahead; 3 x 24 KB of LDS, two workgroups per compute unit).
+constexpr int kX3Stages = 3;
+
+// Tile of the direct-to-LDS kernel for an M x N product over z slices:
+// 128 x 64, 64 x 128 or 64 x 64, the one that finishes first when
+// workgroups run in rounds of c per compute unit (c = 2 for the two larger
+// tiles, 3 for the smallest, by LDS), each round costing c tile areas over
+// the shape's speed (the 64 x 64 tile splits a third more operand values
+// per product).
+TileShape pick_tile_x3k(int M, int N, int z) {
+  const TileShape cand[3] = {{2, 1}, {1, 2}, {1, 1}};
+  const int conc[3] = {2, 2, 3};
+  const double speed[3] = {1.0, 1.0, 0.75};
+  int best = 0;
+  double best_cost = 0.0;
+  for (int c = 0; c < 3; ++c) {
+    const long long gm = (M + 64 * cand[c].tm - 1) / (64 * cand[c].tm), gn = (N + 64 * cand[c].tn - 1) / (64 * cand[c].tn);
+    const long long rounds = (gm * gn * z + 256LL * conc[c] - 1) / (256LL * conc[c]);
+    const double cost = (double)rounds * conc[c] * (64.0 * cand[c].tm) * (64.0 * cand[c].tn) / speed[c];
+    if (c == 0 || cost < best_cost) { best = c; best_cost = cost; }
+  }
+  return cand[best];
+}
+
+template <int TM, int TN, bool AK1, bool BK1>
+void launch_x3k_shape(const Gemm& g, int z, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_x3k_kernel<TM, TN, kX3Stages, AK1, BK1>),
+                     dim3((g.M + 64 * TM - 1) / (64 * TM), (g.N + 64 * TN - 1) / (64 * TN), z), dim3(256), 0, s, g);
+}
+
+template <bool AK1, bool BK1>
+void launch_x3k(const Gemm& g, int z, hipStream_t s) {
+  const TileShape t = pick_tile_x3k(g.M, g.N, z);
+  if (t.tm == 2) launch_x3k_shape<2, 1, AK1, BK1>(g, z, s);
+  else if (t.tn == 2) launch_x3k_shape<1, 2, AK1, BK1>(g, z, s);
+  else launch_x3k_shape<1, 1, AK1, BK1>(g, z, s);
+}
+
 // One launch; every operand slice spans fewer than 2^29 elements.
 hipError_t launch_one(const Gemm& g, int z, hipStream_t s) {
+  // split path whose operands suit the copies to LDS: rows along the
+  // stride-1 dimension 16-byte aligned, the extents along it (K for a
+  // k-contiguous operand, M or N otherwise) multiples of 4
+  const bool ak1 = g.ak == 1, bk1 = g.bk == 1;
+  if (g.x3 && g.kpart == 0 && g.K % 4 == 0 && (ak1 ? g.am % 4 == 0 : (g.ak % 4 == 0 && g.M % 4 == 0)) &&
+      (bk1 ? g.bn % 4 == 0 : (g.bk % 4 == 0 && g.N % 4 == 0)) && g.sAb % 4 == 0 && g.sBb % 4 == 0 &&
+      ((uintptr_t)g.A & 15) == 0 && ((uintptr_t)g.B & 15) == 0) {
+    if (ak1 && bk1) launch_x3k<true, true>(g, z, s);
+    else if (ak1) launch_x3k<true, false>(g, z, s);
+    else if (bk1) launch_x3k<false, true>(g, z, s);
+    else launch_x3k<false, false>(g, z, s);
+    return hipGetLastError();
+  }
   if (g.N <= 32 && !g.x3) {
     // narrow product: 128 x 32 tiles (the four waves stacked along M), a
     // quarter of the padding of a 64-wide tile

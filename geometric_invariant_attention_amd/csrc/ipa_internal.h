@@ -162,7 +162,8 @@ hipError_t launch_layer_gather(const LayerGather& g, hipStream_t s);
 struct BwdArgs {
   int B, L, H, C, Pqk, Pv, R, Cz;
   int DA, DV, P3;   // C + R Cz, C + 3 Pv + R Cz, 3 Pqk
-  int DAQ, DAK;     // DA + P3 + 1 (QA' = [QA | Qg | 1]), DA + P3 (KA' = [KA | Kg])
+  int DAQ, DAK;     // DA + P3 + 1 (QA' = [QA | Qg | 1]), DA + P3 (KA' = [KA | Kg]),
+                    // each rounded up to a multiple of 4 (zero columns)
   int QC;           // query rows per chunk of the score buffers
   float w_L, w_C;
   const float* q; const float* k; const float* v;
