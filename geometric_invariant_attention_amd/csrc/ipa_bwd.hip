@@ -168,8 +168,14 @@ constexpr int kRowsPerWG = 8, kKeyBlock = 512, kUnroll = 8;
 // e^x for x <= 0 through the hardware base-2 exponential (about 1 ulp)
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+template <int KPL>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc) {
-  __shared__ float kps[kMaxP3 + 1][kKeyBlock];   // rows 0 .. P3 - 1: points; row kMaxP3: key bias
+  // KPL consecutive keys per lane and group (4: 16-byte loads and stores,
+  // rows of L a multiple of 4), U groups per lane per pass over a key block
+  constexpr int U = kUnroll / KPL;
+  static_assert(KPL * U == kUnroll && 64 * kUnroll == kKeyBlock, "one group sweep per key block");
+  typedef float fvec __attribute__((ext_vector_type(KPL)));
+  __shared__ __attribute__((aligned(16))) float kps[kMaxP3 + 1][kKeyBlock];   // rows 0 .. P3 - 1: points; row kMaxP3: key bias
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int bh = blockIdx.y, H = a.H, L = a.L, P3 = a.P3;
   const int b = bh / H, h = bh - b * H;
@@ -200,16 +206,23 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
     }
     __syncthreads();
   };
-  auto dist = [&](const float (&q)[kMaxP3], int jj) {
-    float d = 0.f;
+  // first key (within the block) of group t of this lane
+  auto key0 = [&](int t) { return (64 * t + lane) * KPL; };
+  // squared distances of row point set q to the KPL keys of group t, and their biases
+  auto dist = [&](const float (&q)[kMaxP3], int j0, fvec& d, fvec& bias) {
+    d = fvec{};
 #pragma unroll
     for (int c = 0; c < kMaxP3; ++c) {
       if (c < P3) {
-        const float e = q[c] - kps[c][jj];
-        d = fmaf(e, e, d);
+        const fvec kv = *reinterpret_cast<const fvec*>(&kps[c][j0]);
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          const float df = q[c] - kv[e];
+          d[e] = fmaf(df, df, d[e]);
+        }
       }
     }
-    return d;
+    bias = *reinterpret_cast<const fvec*>(&kps[kMaxP3][j0]);
   };
   // pass 1: the wave's rows side by side, so that all their loads of a
   // group are in flight together
@@ -217,34 +230,39 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
   for (int k0 = 0; k0 < L; k0 += kKeyBlock) {
     const int nk = L - k0 < kKeyBlock ? L - k0 : kKeyBlock;
     stage(k0, nk);
-    for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
-      float sv[NR][kUnroll];
+    fvec sv[NR][U];
 #pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const float* X = a.X + ((size_t)bh * a.QC + r0 + w + 4 * u) * L + k0;
+    for (int u = 0; u < NR; ++u) {
+      const float* X = a.X + ((size_t)bh * a.QC + r0 + w + 4 * u) * L + k0;
 #pragma unroll
-        for (int t = 0; t < kUnroll; ++t) {
-          const int jj = jb + 64 * t + lane;
-          sv[u][t] = (qv[u] && jj < nk) ? X[jj] : 0.f;
+      for (int t = 0; t < U; ++t) {
+        const int jj = key0(t);
+        sv[u][t] = (qv[u] && jj < nk) ? *reinterpret_cast<const fvec*>(X + jj) : fvec{};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      float mt = m[u];
+#pragma unroll
+      for (int t = 0; t < U; ++t) {
+        const int jj = key0(t);
+        fvec d, bias;
+        dist(qp[u], jj, d, bias);
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          sv[u][t][e] = (qv[u] && jj + e < nk) ? fmaf(-kappa, d[e], sv[u][t][e]) + bias[e] : -INFINITY;
+          mt = fmaxf(mt, sv[u][t][e]);
         }
       }
+      // every key so far masked: nothing to add yet
+      const float sc = mt == -INFINITY ? 0.f : mt;
+      float acc = l[u] * fexp(m[u] - sc);
 #pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        float mt = m[u];
+      for (int t = 0; t < U; ++t)
 #pragma unroll
-        for (int t = 0; t < kUnroll; ++t) {
-          const int jj = jb + 64 * t + lane;
-          sv[u][t] = (qv[u] && jj < nk) ? fmaf(-kappa, dist(qp[u], jj), sv[u][t]) + kps[kMaxP3][jj] : -INFINITY;
-          mt = fmaxf(mt, sv[u][t]);
-        }
-        // every key so far masked: nothing to add yet
-        const float sc = mt == -INFINITY ? 0.f : mt;
-        float acc = l[u] * fexp(m[u] - sc);
-#pragma unroll
-        for (int t = 0; t < kUnroll; ++t) acc += fexp(sv[u][t] - sc);
-        l[u] = acc;
-        m[u] = mt;
-      }
+        for (int e = 0; e < KPL; ++e) acc += fexp(sv[u][t][e] - sc);
+      l[u] = acc;
+      m[u] = mt;
     }
   }
   float inv[kRowsPerWG / 4];
@@ -272,40 +290,42 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int q0, int qc
   for (int k0 = 0; k0 < L; k0 += kKeyBlock) {
     const int nk = L - k0 < kKeyBlock ? L - k0 : kKeyBlock;
     if (k0 > 0 || L > kKeyBlock) stage(k0, nk);
-    for (int jb = 0; jb < nk; jb += 64 * kUnroll) {
-      float xv[NR][kUnroll], yv[NR][kUnroll];
+    fvec xv[NR][U], yv[NR][U];
 #pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const size_t row = (size_t)bh * a.QC + r0 + w + 4 * u;
-        const bool rin = r0 + w + 4 * u < qc;
+    for (int u = 0; u < NR; ++u) {
+      const size_t row = (size_t)bh * a.QC + r0 + w + 4 * u;
+      const bool rin = r0 + w + 4 * u < qc;
 #pragma unroll
-        for (int t = 0; t < kUnroll; ++t) {
-          const int jj = jb + 64 * t + lane;
-          xv[u][t] = (rin && jj < nk) ? a.X[row * L + k0 + jj] : 0.f;
-          yv[u][t] = (rin && jj < nk) ? a.Y[row * L + k0 + jj] : 0.f;
-        }
+      for (int t = 0; t < U; ++t) {
+        const int jj = key0(t);
+        xv[u][t] = (rin && jj < nk) ? *reinterpret_cast<const fvec*>(a.X + row * L + k0 + jj) : fvec{};
+        yv[u][t] = (rin && jj < nk) ? *reinterpret_cast<const fvec*>(a.Y + row * L + k0 + jj) : fvec{};
       }
+    }
 #pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int r = r0 + w + 4 * u;
-        if (r >= qc) continue;
-        float* X = a.X + ((size_t)bh * a.QC + r) * L + k0;
-        float* Y = a.Y + ((size_t)bh * a.QC + r) * L + k0;
+    for (int u = 0; u < NR; ++u) {
+      const int r = r0 + w + 4 * u;
+      if (r >= qc) continue;
+      float* X = a.X + ((size_t)bh * a.QC + r) * L + k0;
+      float* Y = a.Y + ((size_t)bh * a.QC + r) * L + k0;
 #pragma unroll
-        for (int t = 0; t < kUnroll; ++t) {
-          const int jj = jb + 64 * t + lane;
-          if (jj >= nk) continue;
-          float p = 0.f, ds = 0.f;
-          if (qv[u]) {
-            const float d = dist(qp[u], jj);
-            p = fexp(fmaf(-kappa, d, xv[u][t]) + kps[kMaxP3][jj] - mu[u]) * inv[u];
-            ds = p * (yv[u][t] - Dr[u]);
-            rs[u] += ds;
-            gs[u] = fmaf(ds, d, gs[u]);
+      for (int t = 0; t < U; ++t) {
+        const int jj = key0(t);
+        if (jj >= nk) continue;   // (nk is a multiple of KPL)
+        fvec p = fvec{}, ds = fvec{};
+        if (qv[u]) {
+          fvec d, bias;
+          dist(qp[u], jj, d, bias);
+#pragma unroll
+          for (int e = 0; e < KPL; ++e) {
+            p[e] = fexp(fmaf(-kappa, d[e], xv[u][t][e]) + bias[e] - mu[u]) * inv[u];
+            ds[e] = p[e] * (yv[u][t][e] - Dr[u]);
+            rs[u] += ds[e];
+            gs[u] = fmaf(ds[e], d[e], gs[u]);
           }
-          X[jj] = p;
-          Y[jj] = ds;
         }
+        *reinterpret_cast<fvec*>(X + jj) = p;
+        *reinterpret_cast<fvec*>(Y + jj) = ds;
       }
     }
   }
@@ -512,7 +532,11 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     g.B = a.VA; g.sBb = rowsV; g.bk = 1; g.bn = a.DV;
     g.C = a.Y;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(bwd_rows_kernel, dim3((qc + kRowsPerWG - 1) / kRowsPerWG, BH), dim3(256), 0, s, a, q0, qc);
+    // four keys per lane when the score rows are 16-byte aligned
+    if (L % 4 == 0)
+      hipLaunchKernelGGL(bwd_rows_kernel<4>, dim3((qc + kRowsPerWG - 1) / kRowsPerWG, BH), dim3(256), 0, s, a, q0, qc);
+    else
+      hipLaunchKernelGGL(bwd_rows_kernel<1>, dim3((qc + kRowsPerWG - 1) / kRowsPerWG, BH), dim3(256), 0, s, a, q0, qc);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     // Precision of the products: S, U = A z2, dVA = A^T GA and the scalar and
     // pair columns of dQA' and dKA' run on the split path (each fp32 operand
