@@ -27,7 +27,7 @@
 //               KA' = [KA | Kg], VA, GA, the points and D_i.
 //   per chunk of QC query rows (QC bounds the two score buffers to
 //   2 x 2^26 floats, so memory stays linear in L):
-//     gemm      S = QA KA^T (split path) and dP = GA VA^T (fp32 products)
+//     gemm      S = QA KA^T (split path) and dP = GA VA^T (fp32-accurate)
 //     bwd_rows  per query row: the point term -kappa |Qg_i - Kg_j|^2 from
 //               explicit differences, the masked softmax A, dS, and the
 //               row sums of dS and of dS |Qg_i - Kg_j|^2
@@ -525,13 +525,15 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     g.C = a.X; g.sCb = xs; g.cm = L; g.acc = 0;
     g.x3 = 1;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
-    // dP = GA VA^T
+    // dP = GA VA^T, fp32-accurate (three-way split where it applies)
     g.x3 = 0;
+    g.x6 = 1;
     g.K = a.DV;
     g.A = a.GA + (size_t)q0 * a.DV; g.sAb = rowsV; g.am = a.DV;
     g.B = a.VA; g.sBb = rowsV; g.bk = 1; g.bn = a.DV;
     g.C = a.Y;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
+    g.x6 = 0;
     // four keys per lane when the score rows are 16-byte aligned
     if (L % 4 == 0)
       hipLaunchKernelGGL(bwd_rows_kernel<4>, dim3((qc + kRowsPerWG - 1) / kRowsPerWG, BH), dim3(256), 0, s, a, q0, qc);
@@ -545,11 +547,13 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     // differences in the row kernel), scalar and pair products of random
     // sign with no large common part: its error, about 2^-17 of the sum of
     // the terms' magnitudes, moved every gradient by about 1e-5 relative at
-    // L = 2048 and 4096, a twentieth of the 2e-4 bar. The others stay on
-    // fp32 products: dP enters the difference dP - D (the split there moved
-    // the gamma gradient by 2.8e-4 relative), and the point columns of dQA'
-    // and dKA' (sum_j dS_ij Kg_j against Qg_i sum_j dS_ij, coordinates of a
-    // hundred angstroms or more) cancel by an order of magnitude.
+    // L = 2048 and 4096, a twentieth of the 2e-4 bar. dP enters the
+    // difference dP - D (the two-way split there moved the gamma gradient by
+    // 2.8e-4 relative): it takes fp32-accurate products, the three-way split
+    // (hi + mid + lo, six bf16 products) where the operands suit it. The
+    // point columns of dQA' and dKA' (sum_j dS_ij Kg_j against
+    // Qg_i sum_j dS_ij, coordinates of a hundred angstroms or more) cancel by
+    // an order of magnitude and stay on fp32 products (narrow tiles).
     // dQA' = dS KA' (rows q0 .. q0 + qc): the scalar and pair columns on
     // the split path, the point columns (which cancel, see above) on fp32
     // products

@@ -24,6 +24,18 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
 }
 
+// Two values x as bf16 hi + mid + lo (each nearest even from the residue
+// of the one before), x = hi + mid + lo + O(2^-26 x); packed two per word.
+__device__ __forceinline__ void split3(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  uint32_t h, r;
+  split2(x0, x1, h, r);   // r: bf16 of the residue x - hi, itself rounded
+  const floatx2 r1 = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xFFFF0000u)};
+  const floatx2 r2 = {r1[0] - __uint_as_float(r << 16), r1[1] - __uint_as_float(r & 0xFFFF0000u)};
+  hi = h;
+  mid = r;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2));
+}
+
 // Compiler fence: memory operations stay on their side of it.
 __device__ __forceinline__ void fence() { asm volatile("" ::: "memory"); }
 // An empty, ordered statement that takes an accumulator tile in place: a
@@ -443,7 +455,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // own copies of the next step: __syncthreads() would add a fence that
 // waits for every outstanding copy, the ones issued ahead included.
 // ---------------------------------------------------------------------------
-template <int TM, int TN, int NS, bool AK1, bool BK1>
+template <int TM, int TN, int NS, bool AK1, bool BK1, bool X6>
 __global__ __launch_bounds__(256) void gemm_x3k_kernel(Gemm g) {
   constexpr int KS = 32;
   constexpr int BM = 64 * TM, BN = 64 * TN;
@@ -546,8 +558,9 @@ __global__ __launch_bounds__(256) void gemm_x3k_kernel(Gemm g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) c[i][j] = floatx16{};
   // fragment of tile row (column) r of an operand part p: reduction indices
-  // 16 s2 + 8 half + 0..7 of the step, split into bf16 hi and lo
-  auto frag = [&](const float* p, bool k1, int R, int r, int s2, bf16x8& hi, bf16x8& lo) {
+  // 16 s2 + 8 half + 0..7 of the step, split into bf16 hi and lo (X6: hi,
+  // mid and lo, the residue after hi split again)
+  auto frag = [&](const float* p, bool k1, int R, int r, int s2, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
     float x[8];
     if (k1) {
       const int c0 = 4 * s2 + 2 * half, sw = r & 7;
@@ -569,10 +582,19 @@ __global__ __launch_bounds__(256) void gemm_x3k_kernel(Gemm g) {
       for (int e = 0; e < 8; ++e) x[e] = col[e * R];
     }
     uint4 h, l;
-    split2(x[0], x[1], h.x, l.x);
-    split2(x[2], x[3], h.y, l.y);
-    split2(x[4], x[5], h.z, l.z);
-    split2(x[6], x[7], h.w, l.w);
+    if constexpr (X6) {
+      uint4 m;
+      split3(x[0], x[1], h.x, m.x, l.x);
+      split3(x[2], x[3], h.y, m.y, l.y);
+      split3(x[4], x[5], h.z, m.z, l.z);
+      split3(x[6], x[7], h.w, m.w, l.w);
+      mid = __builtin_bit_cast(bf16x8, m);
+    } else {
+      split2(x[0], x[1], h.x, l.x);
+      split2(x[2], x[3], h.y, l.y);
+      split2(x[4], x[5], h.z, l.z);
+      split2(x[6], x[7], h.w, l.w);
+    }
     hi = __builtin_bit_cast(bf16x8, h);
     lo = __builtin_bit_cast(bf16x8, l);
   };
@@ -590,19 +612,26 @@ __global__ __launch_bounds__(256) void gemm_x3k_kernel(Gemm g) {
     const float* st = stage_ptr(sc);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 ah[TM], al[TM], bh[TN], bl[TN];
+      bf16x8 ah[TM], am[TM], al[TM], bh[TN], bm[TN], bl[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) frag(st, AK1, BM, 32 * (wm * TM + i) + l32, s2, ah[i], al[i]);
+      for (int i = 0; i < TM; ++i) frag(st, AK1, BM, 32 * (wm * TM + i) + l32, s2, ah[i], am[i], al[i]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) frag(st + SA, BK1, BN, 32 * (wn * TN + j) + l32, s2, bh[j], bl[j]);
+      for (int j = 0; j < TN; ++j) frag(st + SA, BK1, BN, 32 * (wn * TN + j) + l32, s2, bh[j], bm[j], bl[j]);
+      // the products as (part of A, part of B): split path hi hi, hi lo,
+      // lo hi (0 hi, 1 lo); X6 hi hi, hi mid, mid hi, hi lo, lo hi, mid mid
+      // (0 hi, 1 mid, 2 lo), the terms left out below 2^-24 relative
+      constexpr int NK = X6 ? 6 : 3;
+      constexpr int ka3[3] = {0, 0, 1}, kb3[3] = {0, 1, 0};
+      constexpr int ka6[6] = {0, 0, 1, 0, 2, 1}, kb6[6] = {0, 1, 0, 2, 0, 1};
 #pragma unroll
-      for (int kind = 0; kind < 3; ++kind)
+      for (int kind = 0; kind < NK; ++kind)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const bf16x8 a = kind == 2 ? al[i] : ah[i];
-            const bf16x8 b = kind == 1 ? bl[j] : bh[j];
+            const int pa = X6 ? ka6[kind] : ka3[kind], pb = X6 ? kb6[kind] : kb3[kind];
+            const bf16x8 a = X6 ? (pa == 2 ? al[i] : pa == 1 ? am[i] : ah[i]) : (pa == 1 ? al[i] : ah[i]);
+            const bf16x8 b = X6 ? (pb == 2 ? bl[j] : pb == 1 ? bm[j] : bh[j]) : (pb == 1 ? bl[j] : bh[j]);
             c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i][j], 0, 0, 0);
           }
     }
@@ -743,18 +772,27 @@ TileShape pick_tile_x3k(int M, int N, int z) {
   return cand[best];
 }
 
-template <int TM, int TN, bool AK1, bool BK1>
+template <int TM, int TN, bool AK1, bool BK1, bool X6>
 void launch_x3k_shape(const Gemm& g, int z, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_x3k_kernel<TM, TN, kX3Stages, AK1, BK1>),
+  hipLaunchKernelGGL((gemm_x3k_kernel<TM, TN, kX3Stages, AK1, BK1, X6>),
                      dim3((g.M + 64 * TM - 1) / (64 * TM), (g.N + 64 * TN - 1) / (64 * TN), z), dim3(256), 0, s, g);
 }
 
-template <bool AK1, bool BK1>
+template <bool AK1, bool BK1, bool X6>
 void launch_x3k(const Gemm& g, int z, hipStream_t s) {
   const TileShape t = pick_tile_x3k(g.M, g.N, z);
-  if (t.tm == 2) launch_x3k_shape<2, 1, AK1, BK1>(g, z, s);
-  else if (t.tn == 2) launch_x3k_shape<1, 2, AK1, BK1>(g, z, s);
-  else launch_x3k_shape<1, 1, AK1, BK1>(g, z, s);
+  if (t.tm == 2) launch_x3k_shape<2, 1, AK1, BK1, X6>(g, z, s);
+  else if (t.tn == 2) launch_x3k_shape<1, 2, AK1, BK1, X6>(g, z, s);
+  else launch_x3k_shape<1, 1, AK1, BK1, X6>(g, z, s);
+}
+
+template <bool X6>
+void launch_x3k_layout(const Gemm& g, int z, hipStream_t s) {
+  const bool ak1 = g.ak == 1, bk1 = g.bk == 1;
+  if (ak1 && bk1) launch_x3k<true, true, X6>(g, z, s);
+  else if (ak1) launch_x3k<true, false, X6>(g, z, s);
+  else if (bk1) launch_x3k<false, true, X6>(g, z, s);
+  else launch_x3k<false, false, X6>(g, z, s);
 }
 
 // One launch; every operand slice spans fewer than 2^29 elements.
@@ -762,14 +800,18 @@ hipError_t launch_one(const Gemm& g, int z, hipStream_t s) {
   // split path whose operands suit the copies to LDS: rows along the
   // stride-1 dimension 16-byte aligned, the extents along it (K for a
   // k-contiguous operand, M or N otherwise) multiples of 4
+  // (x6: the three-way split there, for N wider than the narrow tiles;
+  // otherwise fp32 products below)
   const bool ak1 = g.ak == 1, bk1 = g.bk == 1;
-  if (g.x3 && g.kpart == 0 && g.K % 4 == 0 && (ak1 ? g.am % 4 == 0 : (g.ak % 4 == 0 && g.M % 4 == 0)) &&
-      (bk1 ? g.bn % 4 == 0 : (g.bk % 4 == 0 && g.N % 4 == 0)) && g.sAb % 4 == 0 && g.sBb % 4 == 0 &&
-      ((uintptr_t)g.A & 15) == 0 && ((uintptr_t)g.B & 15) == 0) {
-    if (ak1 && bk1) launch_x3k<true, true>(g, z, s);
-    else if (ak1) launch_x3k<true, false>(g, z, s);
-    else if (bk1) launch_x3k<false, true>(g, z, s);
-    else launch_x3k<false, false>(g, z, s);
+  const bool fits = g.kpart == 0 && g.K % 4 == 0 && (ak1 ? g.am % 4 == 0 : (g.ak % 4 == 0 && g.M % 4 == 0)) &&
+                    (bk1 ? g.bn % 4 == 0 : (g.bk % 4 == 0 && g.N % 4 == 0)) && g.sAb % 4 == 0 && g.sBb % 4 == 0 &&
+                    ((uintptr_t)g.A & 15) == 0 && ((uintptr_t)g.B & 15) == 0;
+  if (fits && g.x3) {
+    launch_x3k_layout<false>(g, z, s);
+    return hipGetLastError();
+  }
+  if (fits && g.x6 && g.N > 32) {
+    launch_x3k_layout<true>(g, z, s);
     return hipGetLastError();
   }
   if (g.N <= 32 && !g.x3) {

@@ -136,6 +136,11 @@ struct Gemm {
   int seg_bf16;             // blocks stored as bf16 (nearest even)
   int x3;                   // each operand split into bf16 hi + lo, three
                             // bf16 products (about 2^-17 relative per term)
+  int x6;                   // fp32-accurate products: where the operands
+                            // suit the copies to LDS, each split into bf16
+                            // hi + mid + lo and six bf16 products (terms
+                            // below 2^-24 relative dropped), else fp32
+                            // products; x3 must be 0
 };
 hipError_t gemm(const Gemm& g, int batch, hipStream_t s);
 // the reduction split into `splits` slices along the grid; partials in
