@@ -302,12 +302,15 @@ int32_t ipa_layer_forward(const ipa_dims* dims, int32_t c_s, int32_t dtype,
  * 0 pass no gradient and receive none. Supported envelope: C <= 16,
  * Pqk <= 5, Pv <= 8, R*Cz <= 256, B*H <= 65535. Pointers 4-byte aligned,
  * workspace ipa_backward_workspace_bytes(dims) bytes, 256-byte aligned.
- * The score, dP and key-side products and the point columns of the
- * query-side product use fp32 matrix-core products; the two value-side
- * products (A z2 and A^T GA, non-negative weights) and the scalar and pair
- * columns of the query-side product split each fp32 operand into bf16
- * hi + lo and take three bf16 products (about 2^-17 relative per term).
- * Deterministic: repeated calls give identical bits. */
+ * Products: the scores QA KA^T (lifted dot only), the two value-side
+ * products (A z2 and A^T GA) and the scalar and pair columns of the query-
+ * and key-side products split each fp32 operand into bf16 hi + lo and take
+ * three bf16 products (about 2^-17 relative per term); dP = GA VA^T is
+ * fp32-accurate (hi + mid + lo, six bf16 products, or fp32 products where
+ * the operands' alignment does not allow the copies the split kernel
+ * uses); the point columns of the query- and key-side products, which
+ * cancel, use fp32 products. Deterministic: repeated calls give identical
+ * bits. */
 size_t ipa_backward_workspace_bytes(const ipa_dims* dims);
 int32_t ipa_backward(const ipa_dims* dims,
                      const float* q, const float* k, const float* v,
