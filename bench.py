@@ -689,16 +689,17 @@ def backward_flops_per_pair(d: dict) -> int:
             + 2 * (DA + P3 + 1) + 2 * DV + 2)
 
 
-def bench_backward(dev, steps: int, warmup: int, cpu) -> dict:
-    """Gradient of the IPA forward (ipa_backward, float32) at the
-    long_chain_2048 dimensions: the forward outputs come from the forward
-    kernels on the same inputs (float32 copies of the bf16 workload), the
+def bench_backward(dev, steps: int, warmup: int, cpu, flash: bool = False) -> dict:
+    """Gradient of the IPA forward at the long_chain_2048 dimensions:
+    ipa_backward (float32 features, score rows of a query chunk stored) or,
+    with ``flash``, ipa_backward_flash (bf16 features, no score rows). The
+    forward outputs come from the forward kernels on the same inputs, the
     cotangents are N(0, 1). Timed between HIP events over back-to-back
     calls; the fp64 oracle is timed on a 256-residue chain of the same
     dimensions and scaled per pair."""
     import numpy as np
     import torch
-    from geometric_invariant_attention_amd import IPABackward, IPAForward
+    from geometric_invariant_attention_amd import IPABackward, IPABackwardFlash, IPAForward
     from workloads import WORKLOADS, make_inputs
     w = WORKLOADS[HEADLINE]
     inp = make_inputs(w)
@@ -712,7 +713,11 @@ def bench_backward(dev, steps: int, warmup: int, cpu) -> dict:
     g = {"s": (d["B"], d["L"], d["H"], d["C"]), "pts": (d["B"], d["L"], d["H"], d["Pv"], 3),
          "pts_norm": (d["B"], d["L"], d["H"], d["Pv"]), "pair": (d["B"], d["L"], d["H"], d["Cz"])}
     g = {k: torch.from_numpy(rng.standard_normal(v).astype(np.float32)).to(dev) for k, v in g.items()}
-    bwd = IPABackward(**d, device=dev)
+    if flash:
+        bwd = IPABackwardFlash(**d, dtype=torch.bfloat16, device=dev)
+        t = {n: (x.to(torch.bfloat16) if n in IPABackwardFlash._FEATURES else x) for n, x in t.items()}
+    else:
+        bwd = IPABackward(**d, device=dev)
     stream = torch.cuda.current_stream(dev)
     raw = bwd.bind(t, {"s": out["s"], "pts": out["pts"], "pair": out["pair"]}, g,
                    w_L=inp["w_L"], w_C=inp["w_C"], stream=stream)
@@ -731,11 +736,15 @@ def bench_backward(dev, steps: int, warmup: int, cpu) -> dict:
     pairs = d["B"] * d["L"] * d["L"]
     flops = backward_flops_per_pair(d) * pairs * d["H"]
     ach = flops / (ms * 1e-3) / 1e12
-    res = {"workload": w.name, "config": {**d, "storage": "fp32"}, "calls": n, "ms_per_call": ms,
+    peak = PEAK_MFMA_TFLOPS if flash else PEAK_FP32_MFMA_TFLOPS
+    res = {"workload": w.name, "config": {**d, "storage": "bf16" if flash else "fp32"},
+           "form": "flash (no score rows)" if flash else "query chunks (score rows stored)",
+           "calls": n, "ms_per_call": ms,
            "pairs_per_s": pairs / (ms * 1e-3), "workspace_MB": bwd.ws_bytes / 2 ** 20,
-           "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                        "frac": ach / PEAK_FP32_MFMA_TFLOPS, "flops_per_call": flops,
-                        "note": "whole gradient timed; flops counted once per product, peak taken as fp32's"}}
+           "roofline": {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                        "frac": ach / peak, "flops_per_call": flops,
+                        "note": "whole gradient timed; flops counted once per product, peak taken as "
+                                + ("bf16's" if flash else "fp32's")}}
     if cpu:
         res["cpu_baseline"] = cpu["baseline"]
     return res
@@ -874,8 +883,10 @@ def main(argv=None) -> int:
         sub["layer"] = bench_layer(dev, args.steps, args.warmup, cpu.get("layer"))
         sub["dirdist"] = bench_dirdist(dev, args.steps, args.warmup, cpu.get("dirdist"))
         sub["backward"] = bench_backward(dev, args.steps, args.warmup, cpu.get("backward"))
+        sub["backward_flash"] = bench_backward(dev, args.steps, args.warmup, cpu.get("backward"), flash=True)
         print(f"[bench] distance attention {sub['meet']['ms_per_call'] * 1e3:.1f} us, layer "
-              f"{sub['layer']['ms_per_call'] * 1e3:.1f} us, gradient {sub['backward']['ms_per_call']:.3f} ms, "
+              f"{sub['layer']['ms_per_call'] * 1e3:.1f} us, gradient {sub['backward']['ms_per_call']:.3f} ms "
+              f"(flash {sub['backward_flash']['ms_per_call']:.3f} ms), "
               f"direction-and-distance {sub['dirdist']['ms_per_call'] * 1e3:.1f} us", file=sys.stderr, flush=True)
         sub["configs"] = {}
         for nm in CONFIGS:

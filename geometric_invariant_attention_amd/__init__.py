@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     frames_from_atoms, meet_attention, MeetForward, IpaMeetDims, meet_workspace_bytes,
     DirDistForward, IpaDirDistDims, dirdist_workspace_bytes, geometric_reasoning_attention,
     IPABackward, backward_workspace_bytes, IPALayer,
+    IPABackwardFlash, backward_flash_workspace_bytes,
 )
 
 __all__ = ["ipa_forward", "IPAForward", "IPAError", "load_library", "workspace_bytes",
@@ -17,4 +18,5 @@ __all__ = ["ipa_forward", "IPAForward", "IPAError", "load_library", "workspace_b
            "IPA_BF16", "LIB_PATH", "frames_from_atoms", "meet_attention", "MeetForward",
            "IpaMeetDims", "meet_workspace_bytes", "DirDistForward", "IpaDirDistDims",
            "dirdist_workspace_bytes", "geometric_reasoning_attention", "IPABackward",
-           "backward_workspace_bytes", "IPALayer"]
+           "backward_workspace_bytes", "IPALayer", "IPABackwardFlash",
+           "backward_flash_workspace_bytes"]

@@ -81,6 +81,10 @@ def load_library(path: str | os.PathLike | None = None) -> ctypes.CDLL:
     lib.ipa_backward_workspace_bytes.restype = sz
     lib.ipa_backward.argtypes = [ctypes.POINTER(IpaDims)] + [vp] * 13 + [f32, f32] + [vp] * 20 + [sz, vp]
     lib.ipa_backward.restype = i32
+    lib.ipa_backward_flash_workspace_bytes.argtypes = [ctypes.POINTER(IpaDims)]
+    lib.ipa_backward_flash_workspace_bytes.restype = sz
+    lib.ipa_backward_flash.argtypes = [ctypes.POINTER(IpaDims), i32] + [vp] * 13 + [f32, f32] + [vp] * 20 + [sz, vp]
+    lib.ipa_backward_flash.restype = i32
     lib.ipa_layer_workspace_bytes.argtypes = [ctypes.POINTER(IpaDims), i32, i32]
     lib.ipa_layer_workspace_bytes.restype = sz
     lib.ipa_layer_forward.argtypes = [ctypes.POINTER(IpaDims), i32, i32] + [vp] * 8 + [f32, f32] + [vp] * 4 + [sz, vp]
@@ -481,6 +485,10 @@ class IPABackward:
                        "w_b": (Cz, H), "gamma": (H,)}
         self.grads = {n: torch.empty(shp, dtype=f32, device=dev) for n, shp in self.shapes.items()}
 
+    # storage dtype of each input (the flash form may take bf16 features)
+    def _in_dtype(self, name: str) -> torch.dtype:
+        return torch.float32
+
     def bind(self, inputs: dict, outputs: dict, cotangents: dict, mask=None, w_L=None, w_C=None,
              stream=None) -> tuple:
         B, L, H, C, Pv, Cz = (self.shape[n] for n in ("B", "L", "H", "C", "Pv", "Cz"))
@@ -494,7 +502,7 @@ class IPABackward:
             x = inputs[n]
             if tuple(x.shape) != shp:
                 raise ValueError(f"{n} has shape {tuple(x.shape)}, expected {shp}")
-            t[n] = _prep(x, f32, dev, n)
+            t[n] = _prep(x, self._in_dtype(n), dev, n)
         oshapes = {"s": (B, L, H, C), "pts": (B, L, H, Pv, 3), "pts_norm": (B, L, H, Pv), "pair": (B, L, H, Cz)}
         o = {n: _prep(outputs[n], f32, dev, "out_" + n) for n in ("s", "pts", "pair")}
         g = {}
@@ -524,6 +532,54 @@ class IPABackward:
 
     def __call__(self, *args, **kw) -> dict:
         return self.backward_raw(self.bind(*args, **kw))
+
+
+def backward_flash_workspace_bytes(B, L, H, C, Pqk, Pv, R, Cz) -> int:
+    d = make_dims(B, L, H, C, Pqk, Pv, R, Cz)
+    return int(load_library().ipa_backward_flash_workspace_bytes(ctypes.byref(d)))
+
+
+class IPABackwardFlash(IPABackward):
+    """Reusable plan of the IPA gradient in flash form (ipa_backward_flash):
+    no score rows are stored, the workspace is linear in L. ``dtype`` is the
+    storage of q, k, v, the points, z1 and z2 (torch.bfloat16 or
+    torch.float32); frames, W_b, gamma, outputs, cotangents and gradients are
+    float32."""
+
+    _FEATURES = ("q", "k", "v", "q_pts", "k_pts", "v_pts", "z1", "z2")
+
+    def __init__(self, B, L, H, C, Pqk, Pv, R, Cz, dtype=torch.bfloat16, device=None):
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("dtype must be torch.bfloat16 or torch.float32")
+        self.in_dtype = dtype
+        self.code = IPA_BF16 if dtype == torch.bfloat16 else IPA_F32
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.dims = make_dims(B, L, H, C, Pqk, Pv, R, Cz)
+        self.shape = dict(B=B, L=L, H=H, C=C, Pqk=Pqk, Pv=Pv, R=R, Cz=Cz)
+        self.lib = load_library()
+        self.ws_bytes = int(self.lib.ipa_backward_flash_workspace_bytes(ctypes.byref(self.dims)))
+        if self.ws_bytes == 0:
+            raise IPAError(-6, f"unsupported dims {self.shape}")
+        dev, f32 = self.device, torch.float32
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.shapes = {"q": (B, L, H, C), "k": (B, L, H, C), "v": (B, L, H, C),
+                       "q_pts": (B, L, H, Pqk, 3), "k_pts": (B, L, H, Pqk, 3), "v_pts": (B, L, H, Pv, 3),
+                       "rot": (B, L, 3, 3), "trans": (B, L, 3), "z1": (B, L, R, Cz), "z2": (B, L, R, Cz),
+                       "w_b": (Cz, H), "gamma": (H,)}
+        self.grads = {n: torch.empty(shp, dtype=f32, device=dev) for n, shp in self.shapes.items()}
+
+    def _in_dtype(self, name: str) -> torch.dtype:
+        return self.in_dtype if name in self._FEATURES else torch.float32
+
+    def bind(self, *args, **kw) -> tuple:
+        raw = super().bind(*args, **kw)
+        return (raw[0], ctypes.c_int32(self.code), *raw[1:])
+
+    def backward_raw(self, raw: tuple) -> dict:
+        rc = self.lib.ipa_backward_flash(*raw)
+        if rc != 0:
+            raise IPAError(rc, status_string(rc))
+        return self.grads
 
 
 # ---------------------------------------------------------------------------

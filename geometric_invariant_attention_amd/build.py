@@ -15,7 +15,7 @@ LIB_NAME = "libipa_mi355.so"
 LIB_PATH = PKG / LIB_NAME
 BUILD_DIR = PKG / "_build"
 
-SOURCES = ["ipa_api.cpp", "ipa_lift.hip", "ipa_attn.hip", "ipa_frames.hip", "ipa_dirdist.hip", "ipa_bwd.hip", "ipa_gemm.hip", "ipa_layer.hip", "ipa_noalloc.hip"]
+SOURCES = ["ipa_api.cpp", "ipa_lift.hip", "ipa_attn.hip", "ipa_frames.hip", "ipa_dirdist.hip", "ipa_bwd.hip", "ipa_bwd_flash.hip", "ipa_gemm.hip", "ipa_layer.hip", "ipa_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

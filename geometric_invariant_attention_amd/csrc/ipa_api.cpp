@@ -346,9 +346,105 @@ bool bwd_layout(const ipa_dims* d, BwdLayout* o) {
   return true;
 }
 
+struct BwdfLayout {
+  size_t off[17];
+  size_t total;
+  int WQ, WG;
+};
+
+// flash form: every buffer is linear in B L H (no score rows)
+bool bwdf_layout(const ipa_dims* d, BwdfLayout* o) {
+  if (!d) return false;
+  const int64_t B = d->B, L = d->L, H = d->H, C = d->C, P = d->Pqk, Pv = d->Pv, R = d->R, Cz = d->Cz;
+  if (B < 1 || L < 1 || H < 1 || C < 1 || P < 1 || Pv < 1 || R < 1 || Cz < 1) return false;
+  if (C > 16 || P > 5 || Pv > 8 || R * Cz > 256) return false;
+  const int64_t WQ = (C + ((R * Cz + 31) & ~int64_t(31)) + 31) & ~int64_t(31);
+  const int64_t WG = (C + 9 * Pv + R * Cz + 31) & ~int64_t(31);
+  if (B * H > 65535 || B * L * H * WG >= (int64_t(1) << 31) || B * L * (Cz * H + H) >= (int64_t(1) << 31))
+    return false;
+  o->WQ = (int)WQ;
+  o->WG = (int)WG;
+  const size_t rows = (size_t)(B * H * L), DA = (size_t)(C + R * Cz), DV = (size_t)(C + 3 * Pv + R * Cz);
+  const size_t P3 = (size_t)(3 * P), DAQ = (DA + P3 + 4) & ~(size_t)3, DAK = (DA + P3 + 3) & ~(size_t)3;
+  // bytes of: QX, KX, GX, VX (bf16), QP, KP, Dv, ST, dQA, U, gam, rsum, dKA, dVA, fpart, share, red1
+  const size_t sizes[17] = {rows * WQ * 2, rows * WQ * 2, rows * WG * 2, rows * WG * 2,
+                            rows * P3 * 4, rows * P3 * 4, rows * 4, rows * 8,
+                            rows * DAK * 4, rows * R * Cz * 4, rows * 4, rows * 4,
+                            rows * DAQ * 4, rows * DV * 4,
+                            (size_t)(B * L * H) * 12 * 4, (size_t)(B * L) * (size_t)(Cz * H + H) * 4,
+                            (size_t)((B * L + 127) / 128) * (size_t)(Cz * H + H) * 4};
+  size_t off = 0;
+  for (int e = 0; e < 17; ++e) {
+    o->off[e] = off;
+    off = ipa::align256(off + sizes[e]);
+  }
+  o->total = off;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t ipa_backward_flash_workspace_bytes(const ipa_dims* dims) {
+  BwdfLayout ly;
+  return bwdf_layout(dims, &ly) ? ly.total : 0;
+}
+
+int32_t ipa_backward_flash(const ipa_dims* dims, int32_t dtype, const void* q, const void* k, const void* v,
+                           const void* q_pts, const void* k_pts, const void* v_pts,
+                           const float* rot, const float* trans, const void* z1, const void* z2,
+                           const float* w_b, const float* gamma, const uint8_t* mask, float w_L, float w_C,
+                           const float* out_s, const float* out_pts, const float* out_pair,
+                           const float* g_s, const float* g_pts, const float* g_pts_norm, const float* g_pair,
+                           float* dq, float* dk, float* dv, float* dq_pts, float* dk_pts, float* dv_pts,
+                           float* drot, float* dtrans, float* dz1, float* dz2, float* dw_b, float* dgamma,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dims) return IPA_ERR_NULL;
+  if (dims->B < 1 || dims->L < 1 || dims->H < 1 || dims->C < 1 || dims->Pqk < 1 || dims->Pv < 1 ||
+      dims->R < 1 || dims->Cz < 1)
+    return IPA_ERR_DIMS;
+  if (dtype != IPA_F32 && dtype != IPA_BF16) return IPA_ERR_DTYPE;
+  const uintptr_t in_align = dtype == IPA_BF16 ? 1u : 3u;
+  const void* ins[] = {q, k, v, q_pts, k_pts, v_pts, z1, z2};
+  for (const void* p : ins) {
+    if (!p) return IPA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(p) & in_align) != 0) return IPA_ERR_ALIGN;
+  }
+  const void* ptrs[] = {rot, trans, w_b, gamma, out_s, out_pts, out_pair, g_s, g_pts, g_pts_norm, g_pair,
+                        dq, dk, dv, dq_pts, dk_pts, dv_pts, drot, dtrans, dz1, dz2, dw_b, dgamma, workspace};
+  for (const void* p : ptrs) {
+    if (!p) return IPA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return IPA_ERR_ALIGN;
+  }
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return IPA_ERR_ALIGN;
+  if (!std::isfinite(w_L) || !std::isfinite(w_C) || w_L < 0.f || w_C < 0.f) return IPA_ERR_ARG;
+  BwdfLayout ly;
+  if (!bwdf_layout(dims, &ly)) return IPA_ERR_UNSUPPORTED;
+  if (workspace_bytes < ly.total) return IPA_ERR_WORKSPACE;
+  ipa::BwdArgs a{};
+  a.B = dims->B; a.L = dims->L; a.H = dims->H; a.C = dims->C; a.Pqk = dims->Pqk; a.Pv = dims->Pv;
+  a.R = dims->R; a.Cz = dims->Cz;
+  a.DA = a.C + a.R * a.Cz; a.DV = a.C + 3 * a.Pv + a.R * a.Cz; a.P3 = 3 * a.Pqk;
+  a.DAQ = (a.DA + a.P3 + 4) & ~3; a.DAK = (a.DA + a.P3 + 3) & ~3; a.QC = a.L;
+  a.WQ = ly.WQ; a.WG = ly.WG;
+  a.w_L = w_L; a.w_C = w_C;
+  a.in_bf16 = dtype == IPA_BF16;
+  a.q = q; a.k = k; a.v = v; a.q_pts = q_pts; a.k_pts = k_pts; a.v_pts = v_pts;
+  a.rot = rot; a.trans = trans; a.z1 = z1; a.z2 = z2; a.w_b = w_b; a.gamma = gamma; a.mask = mask;
+  a.o_s = out_s; a.o_pts = out_pts; a.o_pair = out_pair;
+  a.g_s = g_s; a.g_pts = g_pts; a.g_norm = g_pts_norm; a.g_pair = g_pair;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dq_pts = dq_pts; a.dk_pts = dk_pts; a.dv_pts = dv_pts;
+  a.drot = drot; a.dtrans = dtrans; a.dz1 = dz1; a.dz2 = dz2; a.dw_b = dw_b; a.dgamma = dgamma;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t** h16[4] = {&a.QX, &a.KX, &a.GX, &a.VX};
+  for (int e = 0; e < 4; ++e) *h16[e] = reinterpret_cast<uint16_t*>(ws + ly.off[e]);
+  float** f32s[13] = {&a.QP, &a.KP, &a.Dv, &a.ST, &a.dQA, &a.U, &a.gam, &a.rsum, &a.dKA, &a.dVA,
+                      &a.fpart, &a.share, &a.red1};
+  for (int e = 0; e < 13; ++e) *f32s[e] = reinterpret_cast<float*>(ws + ly.off[4 + e]);
+  if (ipa::launch_backward_flash(a, static_cast<hipStream_t>(stream)) != hipSuccess) return IPA_ERR_HIP;
+  return IPA_OK;
+}
 
 size_t ipa_backward_workspace_bytes(const ipa_dims* dims) {
   BwdLayout ly;

@@ -90,22 +90,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   float* va = a.VA + row * a.DV;
   float* ga = a.GA + row * a.DV;
   // global point coordinate x of local point pt: R[x] . pt + t[x]
-  auto gpt = [&](const float* pt, int x) {
-    return R[3 * x] * pt[0] + R[3 * x + 1] * pt[1] + R[3 * x + 2] * pt[2] + T[x];
+  auto gpt = [&](const void* base, size_t e, int x) {
+    const float p0 = ldin(base, e, a.in_bf16), p1 = ldin(base, e + 1, a.in_bf16), p2 = ldin(base, e + 2, a.in_bf16);
+    return R[3 * x] * p0 + R[3 * x + 1] * p1 + R[3 * x + 2] * p2 + T[x];
   };
   for (int c = lane; c < a.DAQ; c += 64) {
     float vq, vk = 0.f;
     if (c < C) {
-      vq = alpha * a.q[bih * C + c];
-      vk = a.k[bih * C + c];
+      vq = alpha * ldin(a.q, bih * C + c, a.in_bf16);
+      vk = ldin(a.k, bih * C + c, a.in_bf16);
     } else if (c < a.DA) {
       const int rc = c - C;
-      vq = a.w_L * a.w_b[(size_t)(rc % Cz) * H + h] * a.z1[bi * RCz + rc];
-      vk = a.z2[bi * RCz + rc];
+      vq = a.w_L * a.w_b[(size_t)(rc % Cz) * H + h] * ldin(a.z1, bi * RCz + rc, a.in_bf16);
+      vk = ldin(a.z2, bi * RCz + rc, a.in_bf16);
     } else if (c < a.DA + a.P3) {
       const int e = c - a.DA, p = e / 3, x = e - 3 * p;
-      vq = gpt(a.q_pts + (bih * P + p) * 3, x);
-      vk = gpt(a.k_pts + (bih * P + p) * 3, x);
+      vq = gpt(a.q_pts, (bih * P + p) * 3, x);
+      vk = gpt(a.k_pts, (bih * P + p) * 3, x);
       a.QP[row * a.P3 + e] = vq;
       a.KP[row * a.P3 + e] = vk;
     } else {
@@ -121,14 +122,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   for (int c = lane; c < a.DV; c += 64) {
     float vv, gv = 0.f;
     if (c < C) {
-      vv = a.v[bih * C + c];
+      vv = ldin(a.v, bih * C + c, a.in_bf16);
       if (valid) {
         gv = a.g_s[bih * C + c];
         D = fmaf(gv, a.o_s[bih * C + c], D);
       }
     } else if (c < C + 3 * Pv) {
       const int e = c - C, p = e / 3, x = e - 3 * p;
-      vv = gpt(a.v_pts + (bih * Pv + p) * 3, x);
+      vv = gpt(a.v_pts, (bih * Pv + p) * 3, x);
       if (valid) {
         const float* op = a.o_pts + (bih * Pv + p) * 3;
         const float* gp = a.g_pts + (bih * Pv + p) * 3;
@@ -136,12 +137,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
         const float s = n2 > 0.f ? a.g_norm[bih * Pv + p] / sqrtf(n2) : 0.f;
         const float gt[3] = {gp[0] + s * op[0], gp[1] + s * op[1], gp[2] + s * op[2]};
         gv = R[3 * x] * gt[0] + R[3 * x + 1] * gt[1] + R[3 * x + 2] * gt[2];   // R g_tot
-        D = fmaf(gv, gpt(op, x), D);                                            // . (R o_pts + t)
+        D = fmaf(gv, R[3 * x] * op[0] + R[3 * x + 1] * op[1] + R[3 * x + 2] * op[2] + T[x], D);                                      // . (R o_pts + t)
       }
     } else {
       const int rc = c - C - 3 * Pv;
-      vv = a.z2[bi * RCz + rc];
-      if (valid) gv = a.z1[bi * RCz + rc] * a.g_pair[bih * Cz + rc % Cz];
+      vv = ldin(a.z2, bi * RCz + rc, a.in_bf16);
+      if (valid) gv = ldin(a.z1, bi * RCz + rc, a.in_bf16) * a.g_pair[bih * Cz + rc % Cz];
     }
     va[c] = vv;
     ga[c] = gv;
@@ -377,7 +378,8 @@ __global__ __launch_bounds__(64) void bwd_post_kernel(BwdArgs a) {
   float dR[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, dT[3] = {0.f, 0.f, 0.f};
   // global-frame point gradient u of local point x: d(local) = R^T u,
   // dR += u x^T, dt += u
-  auto through_frame = [&](const float* u, const float* x, float* dloc) {
+  auto through_frame = [&](const float* u, const void* base, size_t e, float* dloc) {
+    const float x[3] = {ldin(base, e, a.in_bf16), ldin(base, e + 1, a.in_bf16), ldin(base, e + 2, a.in_bf16)};
     rot3t(R, u, dloc);
     for (int r = 0; r < 3; ++r) {
       dT[r] += u[r];
@@ -390,19 +392,19 @@ __global__ __launch_bounds__(64) void bwd_post_kernel(BwdArgs a) {
       const int c = 3 * p + x;
       u[x] = -2.f * kappa * (a.QP[row * a.P3 + c] * rsum - a.dQA[row * a.DAK + a.DA + c]);
     }
-    through_frame(u, a.q_pts + (bih * P + p) * 3, dl);
+    through_frame(u, a.q_pts, (bih * P + p) * 3, dl);
     for (int x = 0; x < 3; ++x) a.dq_pts[(bih * P + p) * 3 + x] = dl[x];
     for (int x = 0; x < 3; ++x) {
       const int c = 3 * p + x;
       u[x] = 2.f * kappa * (a.dKA[row * a.DAQ + a.DA + c] - a.KP[row * a.P3 + c] * csum);
     }
-    through_frame(u, a.k_pts + (bih * P + p) * 3, dl);
+    through_frame(u, a.k_pts, (bih * P + p) * 3, dl);
     for (int x = 0; x < 3; ++x) a.dk_pts[(bih * P + p) * 3 + x] = dl[x];
   }
   for (int p = 0; p < Pv; ++p) {
     float u[3], dl[3];
     for (int x = 0; x < 3; ++x) u[x] = a.dVA[row * a.DV + C + 3 * p + x];
-    through_frame(u, a.v_pts + (bih * Pv + p) * 3, dl);
+    through_frame(u, a.v_pts, (bih * Pv + p) * 3, dl);
     for (int x = 0; x < 3; ++x) a.dv_pts[(bih * Pv + p) * 3 + x] = dl[x];
     // the output o_pts = R^T (og - t): with g_tot its cotangent,
     // dR += (og - t) g_tot^T = (R o_pts) g_tot^T and dt -= R g_tot
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(64) void bwd_z_kernel(BwdArgs a) {
   }
   for (int r = 0; r < R; ++r) {
     const int rc = r * Cz + c;
-    const float z1 = a.z1[bi * RCz + rc];
+    const float z1 = ldin(a.z1, bi * RCz + rc, a.in_bf16);
     float d1 = 0.f, d2 = 0.f;
     for (int h = 0; h < H; ++h) {
       const size_t row = ((size_t)b * H + h) * L + i;
@@ -509,7 +511,6 @@ __global__ __launch_bounds__(256) void bwd_reduce2_kernel(BwdArgs a, int nblk) {
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   const long long bih = (long long)a.B * a.L * a.H;
-  const unsigned g64 = (unsigned)((bih + 63) / 64);
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((bih + 3) / 4)), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const int BH = a.B * a.H, L = a.L, RCz = a.R * a.Cz;
@@ -596,6 +597,12 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     g.C = a.dVA; g.sCb = rowsV; g.cm = a.DV;
     if (gemm(g, BH, s) != hipSuccess) return hipErrorLaunchFailure;
   }
+  return launch_backward_tail(a, s);
+}
+
+hipError_t launch_backward_tail(const BwdArgs& a, hipStream_t s) {
+  const long long bih = (long long)a.B * a.L * a.H;
+  const unsigned g64 = (unsigned)((bih + 63) / 64);
   hipLaunchKernelGGL(bwd_post_kernel, dim3(g64), dim3(64), 0, s, a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   const long long biz = (long long)a.B * a.L * a.Cz;

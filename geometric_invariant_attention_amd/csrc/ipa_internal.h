@@ -171,10 +171,12 @@ struct BwdArgs {
                     // each rounded up to a multiple of 4 (zero columns)
   int QC;           // query rows per chunk of the score buffers
   float w_L, w_C;
-  const float* q; const float* k; const float* v;
-  const float* q_pts; const float* k_pts; const float* v_pts;
+  // q, k, v, the points, z1 and z2: float32, or bf16 when in_bf16 (read by ldin)
+  int in_bf16;
+  const void* q; const void* k; const void* v;
+  const void* q_pts; const void* k_pts; const void* v_pts;
   const float* rot; const float* trans;
-  const float* z1; const float* z2; const float* w_b; const float* gamma;
+  const void* z1; const void* z2; const float* w_b; const float* gamma;
   const uint8_t* mask;
   const float* o_s; const float* o_pts; const float* o_pair;   // forward outputs
   const float* g_s; const float* g_pts; const float* g_norm; const float* g_pair;
@@ -188,8 +190,22 @@ struct BwdArgs {
   float* fpart;   // [B][L][H][12]  per-head frame gradient shares
   float* share;   // [B][L][H Cz + H] per-residue shares of dW_b ([h][c]) and dgamma
   float* red1;    // [ceil(B L / 128)][Cz H + H] partial column sums of the shares
+  // flash form (ipa_backward_flash): bf16 lifted rows, widths multiples of 32
+  int WQ, WG;     // pad32(C + pad32(R Cz)), pad32(C + 9 Pv + R Cz)
+  uint16_t* QX; uint16_t* KX;   // [B H][L][WQ]  [w_L/sqrt(C) q | w_L W_b z1 | 0], [k | z2 | 0]
+  uint16_t* GX; uint16_t* VX;   // [B H][L][WG]  [g_s | Rg hi | Rg hi | Rg lo | z1 g_pair | 0],
+                                //               [v | Vg hi | Vg lo | Vg hi | z2 | 0]
+  float* ST;      // [B H][L] float2: row max (base 2) and 1 / row sum of the softmax
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+hipError_t launch_backward_flash(const BwdArgs& a, hipStream_t s);
+// per-residue chain rule shared by both gradient forms (post, z, frames, reductions)
+hipError_t launch_backward_tail(const BwdArgs& a, hipStream_t s);
+
+// an input element stored as float32 or (bf) as bf16
+__device__ __forceinline__ float ldin(const void* p, size_t i, int bf) {
+  return bf ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16) : static_cast<const float*>(p)[i];
+}
 
 int dd_splits(int B, int N, int H);
 int dd_padded_keys(int N);

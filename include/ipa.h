@@ -329,6 +329,45 @@ int32_t ipa_backward(const ipa_dims* dims,
                      void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Gradient of ipa_forward in flash form: the same result as ipa_backward,
+ * with scores, probabilities and their derivative formed tile by tile and
+ * never stored, so the workspace is linear in L ("Flash Invariant Point
+ * Attention", abstract: training at lengths that quadratic memory rules out;
+ * TL;DR: linear memory).
+ *   dtype         storage of q, k, v, q_pts, k_pts, v_pts, z1, z2: IPA_F32
+ *                 (4-byte aligned) or IPA_BF16 (2-byte aligned); rot, trans,
+ *                 w_b, gamma, the outputs, the cotangents and every gradient
+ *                 are float32 (4-byte aligned)
+ *   other arguments as ipa_backward; workspace
+ *   ipa_backward_flash_workspace_bytes(dims) bytes (linear in B L H),
+ *   256-byte aligned.
+ * Two passes over bf16 lifted rows: a query pass (online softmax; dq side,
+ * the row statistics) and a key pass (dk, dv side). Products: the lifted
+ * dot, the scalar and pair parts of dP and the accumulating products take
+ * one bf16 product per term (probabilities and dS rounded to bf16), fp32
+ * accumulation; the point part of dP takes bf16 hi + lo splits (three
+ * products, about 2^-17 relative); the distance term and every sum against
+ * the points run in float32 from explicit differences. Accuracy is that of
+ * the bf16 forward, not of ipa_backward. Same envelope and statuses as
+ * ipa_backward, plus IPA_ERR_DTYPE. Deterministic. */
+size_t ipa_backward_flash_workspace_bytes(const ipa_dims* dims);
+int32_t ipa_backward_flash(const ipa_dims* dims, int32_t dtype,
+                           const void* q, const void* k, const void* v,
+                           const void* q_pts, const void* k_pts, const void* v_pts,
+                           const float* rot, const float* trans,
+                           const void* z1, const void* z2,
+                           const float* w_b, const float* gamma,
+                           const uint8_t* mask, float w_L, float w_C,
+                           const float* out_s, const float* out_pts, const float* out_pair,
+                           const float* g_s, const float* g_pts, const float* g_pts_norm,
+                           const float* g_pair,
+                           float* dq, float* dk, float* dv,
+                           float* dq_pts, float* dk_pts, float* dv_pts,
+                           float* drot, float* dtrans, float* dz1, float* dz2,
+                           float* dw_b, float* dgamma,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Geometric direction-and-distance attention (ESM3-style).
  * "Geometric direction-and-distance attention" (BioTorch), Required
  * behavior. Per batch b, head h, query i and key j, with frames (R, t) that

@@ -29,7 +29,8 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert names == ["ipa_attend", "ipa_backward", "ipa_backward_workspace_bytes",
+    assert names == ["ipa_attend", "ipa_backward", "ipa_backward_flash",
+                     "ipa_backward_flash_workspace_bytes", "ipa_backward_workspace_bytes",
                      "ipa_dirdist_forward", "ipa_dirdist_workspace_bytes",
                      "ipa_forward", "ipa_forward_noalloc", "ipa_frames_from_atoms", "ipa_layer_forward",
                      "ipa_layer_workspace_bytes", "ipa_lift",
@@ -280,6 +281,54 @@ def test_backward_workspace_linear_in_L(lib):
     # L adds less than the per-row arrays of L more rows plus the buffers
     grow = sizes[65536] - sizes[32768]
     assert sizes[65536] <= 2 * grow + 2 * 4 * (1 << 26) + 17 * 256
+
+
+def test_backward_flash_rejects_before_launch(lib):
+    good = bd.make_dims(1, 64, 4, 16, 4, 8, 2, 16)
+    ptrs = [0x1000 * (n + 1) for n in range(33)]
+
+    def call(dims, dtype=1, p=ptrs, mask=0, wl=1.0, wc=1.0, ws_bytes=1 << 34, ws=0x100000):
+        return lib.ipa_backward_flash(ctypes.byref(dims) if dims is not None else None, dtype, *p[:12], mask,
+                                      ctypes.c_float(wl), ctypes.c_float(wc), *p[12:31], ws,
+                                      ctypes.c_size_t(ws_bytes), None)
+    assert call(None) == -1
+    assert call(bd.make_dims(1, 0, 4, 16, 4, 8, 2, 16)) == -2
+    assert call(good, dtype=2) == -3
+    assert call(bd.make_dims(1, 64, 4, 32, 4, 8, 2, 16)) == -6       # C > 16
+    assert call(bd.make_dims(1, 64, 4, 16, 6, 8, 2, 16)) == -6       # Pqk > 5
+    assert call(bd.make_dims(1, 64, 4, 16, 4, 8, 4, 128)) == -6      # R Cz > 256
+    for k in range(31):
+        p = list(ptrs)
+        p[k] = 0
+        assert call(good, p=p) == -1, k
+    p = list(ptrs)
+    p[5] += 2                       # bf16 features need 2-byte alignment only
+    assert call(good, p=p, ws_bytes=0) == -4
+    assert call(good, dtype=0, p=p) == -5
+    p = list(ptrs)
+    p[6] += 2                       # rot is float32 in either storage
+    assert call(good, p=p) == -5
+    assert call(good, ws=0x100010) == -5
+    assert call(good, wl=float("nan")) == -8
+    need = lib.ipa_backward_flash_workspace_bytes(ctypes.byref(good))
+    assert need > 0 and call(good, ws_bytes=need - 1) == -4
+
+
+def test_backward_flash_workspace_linear_in_L(lib):
+    """The flash form stores no score rows: every buffer is a per-row
+    array, so the workspace is a * L + b up to the 256-byte alignment of its
+    17 buffers."""
+    def ws(L):
+        return lib.ipa_backward_flash_workspace_bytes(ctypes.byref(bd.make_dims(1, L, 12, 16, 4, 8, 2, 128)))
+    Ls = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
+    sizes = [ws(L) for L in Ls]
+    assert all(v > 0 for v in sizes)
+    per_row = (sizes[-1] - sizes[0]) / (Ls[-1] - Ls[0])
+    for L, v in zip(Ls, sizes):
+        assert abs(v - (sizes[0] + per_row * (L - Ls[0]))) <= 17 * 256, (L, v)
+    # about 93 KB per residue at 12 heads (bf16 lifted rows, fp32 lifted
+    # gradients and the pair sums U): 6 GB at L = 65536
+    assert per_row < 128 * 1024
 
 
 def test_layer_rejects_before_launch(lib):
