@@ -447,8 +447,6 @@ void bwdf_pass_kernel(BwdArgs a) {
             acc[j] = fmma(first ? aS[kk] : aP[kk], __builtin_bit_cast(fbf16x8, v), acc[j]);
           }
         }
-        // one block's operand reads at a time (hoisting them all costs registers)
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
