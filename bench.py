@@ -66,15 +66,21 @@ def algo_bytes(d: dict, elem: int = 2) -> float:
 # Hardware byte counters of the dominant kernel, taken with rocprofv3 (one
 # FETCH_SIZE pass, one WRITE_SIZE pass) per workload and committed as a
 # summary together with the hash of the kernel source they were taken on
-# (the attention kernel, its launcher and the workspace layout it reads).
+# (the attention kernel, its launcher and the workspace layout it reads: the
+# whole of ipa_attn.hip and ipa_internal.h up to the gradient's argument
+# block, which the attention does not include).
 KERNEL_SOURCES = ("ipa_attn.hip", "ipa_internal.h")
+_INTERNAL_CUT = b"struct BwdArgs"
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "geometric_invariant_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+            data = fh.read()
+        if f == "ipa_internal.h" and _INTERNAL_CUT in data:
+            data = data[:data.index(_INTERNAL_CUT)]
+        h.update(data)
     return h.hexdigest()
 
 
