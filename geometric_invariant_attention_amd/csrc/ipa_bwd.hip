@@ -40,6 +40,8 @@
 //               residue's share of dW_b and dgamma.
 //   bwd_frames  per (b, i): drot, dtrans (summed over heads).
 //   bwd_reduce1/2  column sums of the shares: dW_b, dgamma (fixed order).
+// The last four stages (launch_backward_tail) also finish the flash form
+// (ipa_bwd_flash.hip), which fills the same per-row arrays without score rows.
 // The point sums of dS against Qg, Kg come from the GEMMs and the
 // corrections Qg_i sum_j dS_ij, Kg_j sum_i dS_ij; the coordinates are a
 // few hundred A at most and the dS sums vanish up to rounding, so the
